@@ -1,0 +1,245 @@
+"""Throughput of the tiled extract + blend hot path on one MI355X.
+
+One step = tdp_extract + tdp_blend over one synthetic latent (all tiles, run
+locally; the per-tile denoiser is not part of the path and is the identity
+here).  Inputs are resident in HBM before the timed region starts.
+
+Caches: the 4K working set (~204 MB) fits the 256 MB Infinity Cache, so a
+loop over one buffer set would time cache hits.  The bench rotates over
+``--sets`` independent buffer sets (default 4, ~560 MB) and pipelines them:
+step i extracts set i mod R and blends set (i - 2) mod R, so every launch
+reads data last touched two or more steps (>300 MB of traffic) earlier.
+
+Prints one JSON line (stdout): GB/s of compulsory bytes (each input read
+once, each output written once; overlap re-reads not credited), the
+fraction of the 8 TB/s HBM peak, a roofline entry for the dominant op timed
+with HIP events on the launch stream, and the CPU oracle's rate on the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def compulsory_bytes(wl, counts, num_tiles, e_in, e_out):
+    """Algorithmic bytes of one extract and one blend.
+
+    S = sum of used tile rows (generated + kept conditioning).
+    extract: latent read B*(N+Nc)*C*e + positions read B*(N+Nc)*24
+             + tile rows written S*B*C*e + tile positions S*B*24 + index 4*S
+             + counts / selection tables (4*T + 4*T*Nc + 4*Nc)
+    blend:   tile rows read S*B*C*e + output written B*(N+Nc)*C*e_out
+             + selection tables read (4*T*Nc + 4*Nc)
+    """
+    B, C, Nc = wl.batch, wl.channels, wl.num_cond
+    rows = wl.tokens + Nc
+    S = int(sum(counts))
+    sel = 4 * num_tiles * Nc + 4 * Nc
+    extract = B * rows * C * e_in + B * rows * 24 + S * B * C * e_in + S * B * 24 + 4 * S + 4 * num_tiles + sel
+    blend = S * B * C * e_in + B * rows * C * e_out + sel
+    return extract, blend, S
+
+
+def cpu_baseline(wl, inp, extract_bytes, blend_bytes, budget_s=12.0):
+    """The oracle (numpy, fp64 blend) on the same workload, repeated ~budget_s."""
+    import numpy as np
+    import oracle as O
+    wall = cpu = 0.0
+    reps = 0
+    while wall < budget_s or reps == 0:
+        c0, t0 = time.process_time(), time.perf_counter()
+        ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+        ys = [O.bf16_bits_to_f32(et["latent"]) if et["latent"].dtype == np.uint16 else et["latent"]
+              for et in ex["tiles"]]
+        O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        reps += 1
+    per = wall / reps
+    return {
+        "value": round((extract_bytes + blend_bytes) / per / 1e9, 4),
+        "unit": "GB/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"full {wl.name} workload, oracle extract+blend x{reps} ({wall:.1f} s wall, "
+                  f"{per * 1e3:.0f} ms per step); host has {os.cpu_count()} CPUs, "
+                  f"{len(os.sched_getaffinity(0))} in affinity",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="4k")
+    ap.add_argument("--sets", type=int, default=4, help="rotating buffer sets (cache-cold launches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the tiled hot path has no cross-GPU step here "
+              "(every tile runs locally). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import overlap_tiling_trapezoidal_amd as tdp
+    from synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    inp = make_inputs(wl)
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond,
+                          in_dtype=wl.dtype, out_dtype=wl.dtype)
+    plan = tdp.tdp_plan_create(cfg)
+    T = tdp.tdp_plan_num_tiles(plan)
+    R = max(3, args.sets)
+    D = 2  # blend runs D steps behind extract
+
+    def to_dev_latent(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    sets = []
+    for r in range(R):
+        bufs = tdp.allocate_extract_outputs(plan, dev)
+        sets.append({
+            "latent": to_dev_latent(inp["latent"]),
+            "pos": torch.from_numpy(inp["pos"]).to(dev),
+            "bufs": bufs,
+            "out": tdp.allocate_output(plan, dev),
+        })
+    stream = torch.cuda.current_stream(dev)
+
+    def extract(s):
+        b = s["bufs"]
+        tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
+                        b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"], stream)
+
+    def blend(s):
+        b = s["bufs"]
+        tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], b["cond_k"], s["out"], stream)
+
+    # prime every set, then warm up the pipeline
+    for s in sets:
+        extract(s)
+    for i in range(args.warmup):
+        extract(sets[i % R])
+        blend(sets[(i - D) % R])
+    torch.cuda.synchronize()
+    counts = sets[0]["bufs"]["tile_count"].cpu().numpy()
+    e_in = 2 if wl.dtype == "bf16" else 4
+    ex_bytes, bl_bytes, S = compulsory_bytes(wl, counts, T, e_in, e_in)
+    step_bytes = ex_bytes + bl_bytes
+
+    # timed region: K steps, events on the launch stream around every op
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        extract(sets[i % R])
+        ev[i][1].record(stream)
+        blend(sets[(i - D) % R])
+        ev[i][2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    t_ex = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    t_bl = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    ms_per_step = total_ms / K
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # plain device copy of the same size as a practical ceiling
+    nbytes = 256 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(3)]
+    for d in dst:
+        d.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for i in range(12):
+        dst[i % 3].copy_(src if i % 2 == 0 else dst[(i + 1) % 3])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 12 * 2 * nbytes / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    ex_ms, bl_ms = float(np.mean(t_ex)), float(np.mean(t_bl))
+    dom = ("extract", ex_bytes, ex_ms, "extents_kernel + gather_kernel") if ex_ms >= bl_ms else \
+          ("blend", bl_bytes, bl_ms, "blend_kernel")
+    achieved = dom[1] / (dom[2] * 1e-3) / 1e9
+    result = {
+        "metric": "tiled extract+blend GB/s on 1 MI355X; fraction of HBM peak",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) latent, grid positions)",
+        "config": {
+            "workload": f"{wl.name}: B={wl.batch} C={wl.channels} (F,H,W)={wl.shape} {wl.dtype}, "
+                        f"tiles {tuple(n for n, _ in wl.tiling)} overlap {tuple(o for _, o in wl.tiling)}, "
+                        f"{T} tiles, {wl.num_cond} conditioning tokens",
+            "tokens": wl.tokens,
+            "tile_rows": S,
+            "bytes_per_step": step_bytes,
+            "buffer_sets": R,
+        },
+        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "ops": {
+            "extract_ms": round(ex_ms, 5), "extract_p10_p90_ms": [round(float(np.percentile(t_ex, q)), 5) for q in (10, 90)],
+            "extract_bytes": ex_bytes, "extract_gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
+            "blend_ms": round(bl_ms, 5), "blend_p10_p90_ms": [round(float(np.percentile(t_bl, q)), 5) for q in (10, 90)],
+            "blend_bytes": bl_bytes, "blend_gbs": round(bl_bytes / (bl_ms * 1e-3) / 1e9, 1),
+        },
+        "copy_ceiling_gbs": round(copy_gbs, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{dom[0]} ({dom[3]})",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(wl, inp, ex_bytes, bl_bytes, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

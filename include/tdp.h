@@ -1,0 +1,223 @@
+/*
+ * tdp.h — tiled-data-parallel (TDP) latent tiling on one MI355X (gfx950).
+ *
+ * Three operations, after the pages that describe TDP:
+ *   plan    split a patchified (frames, height, width) latent into
+ *           count-specified overlapping tiles, with trapezoidal windows
+ *           (LTX-2 docs, "Tiled Data Parallelism (TDP)", sections "What it is"
+ *           and "API"; mold issue #673, "Scope" and "A bug found while
+ *           porting");
+ *   extract gather each tile's latent rows, its normalized positions and the
+ *           conditioning tokens it keeps (TDP docs, "Position normalization"
+ *           and "Shared negative (reference) positions");
+ *   blend   add the tile outputs back with the separable trapezoidal
+ *           partition of unity, weight 1/k for a token kept by k tiles
+ *           (TDP docs, "What it is" and "Shared negative (reference)
+ *           positions").
+ *
+ * All tiles run on the calling GPU; what the multi-GPU form sums with one
+ * all_reduce is accumulated in place here, with no GPU-to-GPU traffic.
+ *
+ * Conventions
+ *   - Every function returns TDP_OK (0) or a negative status; the message of
+ *     the last failure on the calling thread is in tdp_last_error().
+ *   - The library owns only the host plan.  Every device buffer is allocated
+ *     and freed by the caller; the library never allocates device memory.
+ *   - tdp_extract and tdp_blend only enqueue work on `stream` (a hipStream_t,
+ *     NULL = the null stream) and return without synchronizing.  All
+ *     arguments are validated before anything is enqueued, so an error
+ *     leaves every output untouched.
+ *   - Results are deterministic: every output element has one writer and
+ *     sums run in a fixed order; there are no atomics.
+ *
+ * Token and position layout (caller's tensors)
+ *   latent    (B, N + Nc, C) row-major, dtype in_dtype; N = F*H*W generated
+ *             tokens in patchified order n = (f*H + h)*W + w, followed by Nc
+ *             conditioning tokens (TDP docs, "Shared negative (reference)
+ *             positions": conditioning tokens are appended).
+ *   pos       (B, 3, N + Nc, 2) float32: per token and axis (time, height,
+ *             width) a [start, end) interval.
+ *
+ * Tile-major buffers (outputs of extract, input of blend)
+ *   Tile t owns a fixed slot of capacity_t = gen_t + Nc rows per batch
+ *   element; tile_count[t] = gen_t + kept_t rows of it are used: the gen_t
+ *   generated tokens in tile-local row-major order, then the kept
+ *   conditioning tokens in ascending original order.  Slot offsets are
+ *   reported by tdp_plan_tile():
+ *     tile_lat  + lat_offset   : (B, capacity_t, C)      dtype in_dtype
+ *     tile_pos  + pos_offset   : (B, 3, capacity_t, 2)   float32
+ *     tile_index+ index_offset : (capacity_t)            int32 source token
+ *   Rows at and past tile_count[t] are not written.
+ */
+#ifndef TDP_H
+#define TDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define TDP_OK 0
+#define TDP_EINVAL (-1) /* null pointer, bad count, bad dtype or flag       */
+#define TDP_EGUARD (-2) /* overlap > dim/(n+1), or overlap on a 1-tile axis */
+#define TDP_ESHAPE (-3) /* sizes out of the supported range                 */
+#define TDP_EHIP (-4)   /* a HIP call or kernel launch failed               */
+
+/* ---- dtypes and flags ---------------------------------------------------- */
+#define TDP_F32 0
+#define TDP_BF16 1
+
+/* Shift each tile's positions so its generated tokens start at zero on every
+ * axis (TDP docs, "Position normalization"; on by default upstream). */
+#define TDP_NORMALIZE_POSITIONS 0x1u
+/* Skip the overlap guard.  Plans built with it can be queried (intervals,
+ * windows: used to study stacked windows) but tdp_extract and tdp_blend
+ * refuse them with TDP_EGUARD. */
+#define TDP_UNGUARDED 0x2u
+
+#define TDP_MAX_TILES_PER_AXIS 32
+#define TDP_MAX_WIDTH 4096
+#define TDP_MAX_BATCH 1024
+
+/* One axis of the tiling: a tile COUNT and an overlap in latent grid cells
+ * (TDP docs, "API": DimensionTilingConfig(num_tiles, overlap)). */
+typedef struct {
+  int32_t num_tiles;
+  int32_t overlap;
+} tdp_axis_tiling;
+
+typedef struct {
+  int32_t batch;        /* 1 <= B <= TDP_MAX_BATCH                            */
+  int32_t channels;     /* C >= 1; C * sizeof(in_dtype) a multiple of 16 B,   */
+                        /* at most 1024 B                                     */
+  int32_t frames;       /* F >= 1 latent grid                                 */
+  int32_t height;       /* H >= 1                                             */
+  int32_t width;        /* 1 <= W <= TDP_MAX_WIDTH                            */
+  int32_t num_cond;     /* Nc >= 0 conditioning tokens after the N generated  */
+  tdp_axis_tiling axis[3]; /* frames, height, width (TDP docs, "API":       */
+                           /* TileCountConfig)                                */
+  int32_t in_dtype;     /* latent / tile dtype: TDP_F32 or TDP_BF16           */
+  int32_t out_dtype;    /* blended output dtype: TDP_F32 or TDP_BF16 (RNE)    */
+  uint32_t flags;       /* TDP_NORMALIZE_POSITIONS | TDP_UNGUARDED            */
+} tdp_config;
+
+typedef struct tdp_plan tdp_plan; /* opaque host object owned by the library */
+
+typedef struct {
+  int32_t index;         /* t = (i_f * n_h + i_h) * n_w + i_w                 */
+  int32_t grid[3];       /* (i_f, i_h, i_w)                                   */
+  int32_t origin[3];     /* first latent cell on each axis                    */
+  int32_t shape[3];      /* cells on each axis                                */
+  int32_t gen_tokens;    /* shape[0] * shape[1] * shape[2]                    */
+  int32_t capacity;      /* gen_tokens + num_cond: slot rows per batch elem.  */
+  int64_t lat_offset;    /* element offset of the slot in tile_lat/tile_out   */
+  int64_t pos_offset;    /* float offset of the slot in tile_pos              */
+  int64_t index_offset;  /* int32 offset of the slot in tile_index            */
+} tdp_tile_info;
+
+typedef struct {
+  int32_t num_tiles;        /* T                                              */
+  int64_t tile_lat_elems;   /* elements of tile_lat (and tile_out)            */
+  int64_t tile_pos_floats;  /* floats of tile_pos                             */
+  int64_t tile_index_ints;  /* int32 entries of tile_index                    */
+  int64_t cond_row_ints;    /* int32 entries of cond_row: T * Nc              */
+  int64_t out_elems;        /* elements of out: B * (N + Nc) * C              */
+  int64_t workspace_bytes;  /* device scratch that tdp_extract needs          */
+} tdp_sizes;
+
+/* ---- plan (host only; no GPU needed) ------------------------------------ */
+
+/* Build a plan: split every axis with split_by_count, build the trapezoidal
+ * windows and enumerate the tiles (mold #673, "Scope"; TDP docs, "API").
+ *   split  a_i = floor(i * (dim - o) / n) for i = 0..n, tile i = [a_i,
+ *          a_{i+1} + o); neighbours share exactly o cells, the last tile
+ *          ends at dim.
+ *   guard  o * (n + 1) <= dim (mold #673, "A bug found while porting":
+ *          tile_size >= 2 * overlap); a 1-tile axis needs o == 0.
+ *          Violations return TDP_EGUARD with a message naming the axis and
+ *          the largest allowed overlap, unless TDP_UNGUARDED is set.
+ *   also   n >= 1, o >= 0 (TDP_EINVAL); n <= dim - o, i.e. strides of at
+ *          least one cell, and n <= TDP_MAX_TILES_PER_AXIS (TDP_ESHAPE).
+ * On success *out receives a plan to release with tdp_plan_destroy. */
+int tdp_plan_create(const tdp_config* cfg, tdp_plan** out);
+void tdp_plan_destroy(tdp_plan* plan);
+
+/* Number of tiles T (row-major over the three axes). */
+int tdp_plan_num_tiles(const tdp_plan* plan, int32_t* num_tiles);
+
+/* The n intervals [starts[i], ends[i]) of one axis (0 frames, 1 height,
+ * 2 width); both arrays hold at least n entries. */
+int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t* ends);
+
+/* The 1-D trapezoidal window of tile i on one axis, one fp32 per cell of
+ * the interval (w has room for ends[i] - starts[i] floats): (j+1)/(o+1) on
+ * the first o cells when a left neighbour exists, mirrored on the last o
+ * cells when a right neighbour exists, 1 elsewhere, the product where both
+ * apply (mold #673, "A bug found while porting"; TDP docs, "What it is").
+ * Each value is the correctly rounded fp32 of the exact ratio. */
+int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w);
+
+/* Geometry and slot offsets of tile t. */
+int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info);
+
+/* Sizes of every buffer the caller allocates for tdp_extract / tdp_blend. */
+int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes);
+
+/* Round-robin owner of tile t among `world` ranks: t mod world (TDP docs,
+ * "What it is").  On one GPU every tile is local. */
+int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* rank);
+
+/* ---- device operations (enqueue on `stream`) ----------------------------- */
+
+/* Gather all tiles in one pass of the latent.
+ *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
+ *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
+ *        tile_count (T) int32: gen_t + kept_t.
+ *        cond_row (T * Nc) int32: row of conditioning token c inside tile
+ *          t's slot, or -1 when t does not keep c.  Unused when Nc == 0.
+ *        cond_k (Nc) int32: number of tiles that keep token c.
+ *   scratch workspace: tdp_sizes.workspace_bytes of device memory, 16-byte
+ *        aligned; its contents on entry do not matter.
+ * Positions: the tile's offset on axis d for batch element b is the minimum
+ * start over its generated tokens; with TDP_NORMALIZE_POSITIONS it is
+ * subtracted from both ends of every row the tile holds (one fp32
+ * subtraction each), otherwise positions are copied (TDP docs, "Position
+ * normalization").
+ * Selection: tile t keeps conditioning token c when, for some batch
+ * element, c's interval overlaps the tile's extent [min start, max end) on
+ * all three axes (half-open: touching or empty intervals do not overlap) or
+ * c's time start is negative (TDP docs, "Shared negative (reference)
+ * positions"); tested on positions before normalization.
+ * All pointers are device pointers except `plan`; buffers must not overlap;
+ * cond_row / cond_k may be NULL when Nc == 0.  Returns TDP_EGUARD for
+ * unguarded plans, TDP_EINVAL for null pointers, TDP_EHIP on launch
+ * failure. */
+int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
+                void* tile_lat, float* tile_pos, int32_t* tile_index,
+                int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
+                void* workspace, void* stream);
+
+/* Blend tile outputs (tile-major slots with tile_lat's layout and dtype,
+ * rows as tdp_extract placed them) into out (B, N+Nc, C) out_dtype:
+ *   generated token:    sum over covering tiles t, ascending, of
+ *                       wF*wH*wW * y_t  (separable trapezoid),
+ *   conditioning token: (1/k) * sum over tiles that keep it of y_t,
+ *                       and 0 when k == 0,
+ * fp32 accumulation, no normalization pass (mold #673, "A bug found while
+ * porting"), bf16 output rounded to nearest even.  cond_row / cond_k are
+ * tdp_extract's outputs for the same plan (may be NULL when Nc == 0).
+ * Device pointers except `plan`. */
+int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row,
+              const int32_t* cond_k, void* out, void* stream);
+
+/* ---- errors ------------------------------------------------------------ */
+const char* tdp_status_string(int status);
+const char* tdp_last_error(void); /* thread-local, never NULL */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TDP_H */

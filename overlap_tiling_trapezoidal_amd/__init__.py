@@ -1,0 +1,367 @@
+"""Python binding of libtdp: tiled-data-parallel latent tiling on MI355X.
+
+Thin ctypes layer over the C ABI declared in ``include/tdp.h``: the names are
+the C names, and every step of the hot path runs in the library's HIP
+kernels.  This module only marshals arguments: it checks tensors (device,
+dtype, contiguity and size against the plan) before any pointer reaches the
+library, so a wrong buffer raises here instead of reaching a kernel.
+
+PyTorch supplies device memory and streams; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtdp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp.h")
+
+# ---- constants (mirror include/tdp.h) --------------------------------------
+TDP_OK = 0
+TDP_EINVAL = -1
+TDP_EGUARD = -2
+TDP_ESHAPE = -3
+TDP_EHIP = -4
+TDP_F32 = 0
+TDP_BF16 = 1
+TDP_NORMALIZE_POSITIONS = 0x1
+TDP_UNGUARDED = 0x2
+TDP_MAX_TILES_PER_AXIS = 32
+
+_DTYPES = {"f32": TDP_F32, "float32": TDP_F32, "bf16": TDP_BF16, "bfloat16": TDP_BF16}
+
+
+class tdp_axis_tiling(ctypes.Structure):
+    _fields_ = [("num_tiles", ctypes.c_int32), ("overlap", ctypes.c_int32)]
+
+
+class tdp_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("frames", ctypes.c_int32),
+        ("height", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("num_cond", ctypes.c_int32),
+        ("axis", tdp_axis_tiling * 3),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class tdp_tile_info(ctypes.Structure):
+    _fields_ = [
+        ("index", ctypes.c_int32),
+        ("grid", ctypes.c_int32 * 3),
+        ("origin", ctypes.c_int32 * 3),
+        ("shape", ctypes.c_int32 * 3),
+        ("gen_tokens", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("lat_offset", ctypes.c_int64),
+        ("pos_offset", ctypes.c_int64),
+        ("index_offset", ctypes.c_int64),
+    ]
+
+
+class tdp_sizes(ctypes.Structure):
+    _fields_ = [
+        ("num_tiles", ctypes.c_int32),
+        ("tile_lat_elems", ctypes.c_int64),
+        ("tile_pos_floats", ctypes.c_int64),
+        ("tile_index_ints", ctypes.c_int64),
+        ("cond_row_ints", ctypes.c_int64),
+        ("out_elems", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+class TdpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtdp.so; raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libtdp.so not found at {path}: build it first "
+                          "(python overlap_tiling_trapezoidal_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "tdp_plan_create": (ctypes.c_int, [ctypes.POINTER(tdp_config), ctypes.POINTER(vp)]),
+        "tdp_plan_destroy": (None, [vp]),
+        "tdp_plan_num_tiles": (ctypes.c_int, [vp, i32p]),
+        "tdp_plan_intervals": (ctypes.c_int, [vp, ctypes.c_int, i32p, i32p]),
+        "tdp_plan_window": (ctypes.c_int, [vp, ctypes.c_int, i32, ctypes.POINTER(ctypes.c_float)]),
+        "tdp_plan_tile": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_tile_info)]),
+        "tdp_plan_sizes": (ctypes.c_int, [vp, ctypes.POINTER(tdp_sizes)]),
+        "tdp_plan_tile_rank": (ctypes.c_int, [vp, i32, i32, i32p]),
+        "tdp_extract": (ctypes.c_int, [vp] * 11),
+        "tdp_blend": (ctypes.c_int, [vp] * 6),
+        "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "tdp_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/tdp.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tdp_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != TDP_OK:
+        lib = load_library()
+        raise TdpError(status, lib.tdp_last_error().decode())
+
+
+# ---- plan -----------------------------------------------------------------
+
+def make_config(batch, channels, shape, tiling, num_cond=0, in_dtype="bf16", out_dtype=None,
+                normalize=True, unguarded=False) -> tdp_config:
+    """Fill a tdp_config.  ``shape`` = (F, H, W); ``tiling`` = ((n, o),) * 3."""
+    cfg = tdp_config()
+    cfg.batch, cfg.channels = batch, channels
+    cfg.frames, cfg.height, cfg.width = shape
+    cfg.num_cond = num_cond
+    for d, (n, o) in enumerate(tiling):
+        cfg.axis[d].num_tiles, cfg.axis[d].overlap = n, o
+    cfg.in_dtype = _DTYPES[in_dtype] if isinstance(in_dtype, str) else in_dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    cfg.out_dtype = _DTYPES[out_dtype] if isinstance(out_dtype, str) else out_dtype
+    cfg.flags = (TDP_NORMALIZE_POSITIONS if normalize else 0) | (TDP_UNGUARDED if unguarded else 0)
+    return cfg
+
+
+class Plan:
+    """Owns a tdp_plan handle (host memory only)."""
+
+    def __init__(self, handle: int, cfg: tdp_config):
+        self._h = ctypes.c_void_p(handle)
+        self.cfg = cfg
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("plan was destroyed")
+        return self._h
+
+    def destroy(self):
+        if self._h:
+            load_library().tdp_plan_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    # derived geometry
+    @property
+    def shape(self):
+        return (self.cfg.frames, self.cfg.height, self.cfg.width)
+
+    @property
+    def tokens(self):
+        F, H, W = self.shape
+        return F * H * W
+
+
+def tdp_plan_create(cfg: tdp_config) -> Plan:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.tdp_plan_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return Plan(h.value, cfg)
+
+
+def tdp_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def tdp_plan_num_tiles(plan: Plan) -> int:
+    n = ctypes.c_int32()
+    _check(load_library().tdp_plan_num_tiles(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def tdp_plan_intervals(plan: Plan, axis: int) -> list[tuple[int, int]]:
+    n = plan.cfg.axis[axis].num_tiles if 0 <= axis < 3 else 1
+    starts = (ctypes.c_int32 * max(n, 1))()
+    ends = (ctypes.c_int32 * max(n, 1))()
+    _check(load_library().tdp_plan_intervals(plan.handle, axis, starts, ends))
+    return [(starts[i], ends[i]) for i in range(n)]
+
+
+def tdp_plan_window(plan: Plan, axis: int, i: int):
+    import numpy as np
+    ivs = tdp_plan_intervals(plan, axis)
+    if not 0 <= i < len(ivs):
+        raise IndexError(i)
+    size = ivs[i][1] - ivs[i][0]
+    buf = (ctypes.c_float * size)()
+    _check(load_library().tdp_plan_window(plan.handle, axis, i, buf))
+    return np.ctypeslib.as_array(buf).copy()
+
+
+def tdp_plan_tile(plan: Plan, t: int) -> tdp_tile_info:
+    info = tdp_tile_info()
+    _check(load_library().tdp_plan_tile(plan.handle, t, ctypes.byref(info)))
+    return info
+
+
+def tdp_plan_sizes(plan: Plan) -> tdp_sizes:
+    s = tdp_sizes()
+    _check(load_library().tdp_plan_sizes(plan.handle, ctypes.byref(s)))
+    return s
+
+
+def tdp_plan_tile_rank(plan: Plan, t: int, world: int) -> int:
+    r = ctypes.c_int32()
+    _check(load_library().tdp_plan_tile_rank(plan.handle, t, world, ctypes.byref(r)))
+    return r.value
+
+
+def tdp_status_string(status: int) -> str:
+    return load_library().tdp_status_string(status).decode()
+
+
+def tdp_last_error() -> str:
+    return load_library().tdp_last_error().decode()
+
+
+# ---- device buffers (torch) ----------------------------------------------
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == TDP_BF16 else torch.float32
+
+
+def _ptr(t, name, dtype, numel, device):
+    """Pointer of a CUDA tensor after checking it can hold ``numel`` elements."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device or 'a GPU'}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def allocate_extract_outputs(plan: Plan, device="cuda"):
+    """Caller-owned buffers for tdp_extract / tdp_blend, sized by the plan."""
+    import torch
+    s = tdp_plan_sizes(plan)
+    dev = torch.device(device)
+    return {
+        "tile_lat": torch.empty(s.tile_lat_elems, dtype=_torch_dtype(plan.cfg.in_dtype), device=dev),
+        "tile_pos": torch.empty(s.tile_pos_floats, dtype=torch.float32, device=dev),
+        "tile_index": torch.empty(s.tile_index_ints, dtype=torch.int32, device=dev),
+        "tile_count": torch.empty(s.num_tiles, dtype=torch.int32, device=dev),
+        "cond_row": torch.empty(max(s.cond_row_ints, 1), dtype=torch.int32, device=dev),
+        "cond_k": torch.empty(max(plan.cfg.num_cond, 1), dtype=torch.int32, device=dev),
+        "workspace": torch.empty(max(s.workspace_bytes, 16), dtype=torch.uint8, device=dev),
+    }
+
+
+def allocate_output(plan: Plan, device="cuda"):
+    import torch
+    s = tdp_plan_sizes(plan)
+    c = plan.cfg
+    return torch.empty(s.out_elems, dtype=_torch_dtype(c.out_dtype),
+                       device=torch.device(device)).view(c.batch, plan.tokens + c.num_cond, c.channels)
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
+                cond_row=None, cond_k=None, workspace=None, stream=None):
+    """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    rows = plan.tokens + c.num_cond
+    dev = latent.device
+    args = [
+        plan.handle,
+        _ptr(latent, "latent", _torch_dtype(c.in_dtype), c.batch * rows * c.channels, dev),
+        _ptr(pos, "pos", torch.float32, c.batch * 3 * rows * 2, dev),
+        _ptr(tile_lat, "tile_lat", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
+        _ptr(tile_pos, "tile_pos", torch.float32, s.tile_pos_floats, dev),
+        _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
+        _ptr(tile_count, "tile_count", torch.int32, s.num_tiles, dev),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(cond_k, "cond_k", torch.int32, c.num_cond, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes
+        else ctypes.c_void_p(None),
+        _stream_handle(stream, dev),
+    ]
+    _check(load_library().tdp_extract(*args))
+
+
+def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):
+    """Enqueue the blend of tile outputs into ``out`` on ``stream``."""
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    dev = tile_out.device
+    args = [
+        plan.handle,
+        _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(cond_k, "cond_k", torch.int32, c.num_cond, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(out, "out", _torch_dtype(c.out_dtype), s.out_elems, dev),
+        _stream_handle(stream, dev),
+    ]
+    _check(load_library().tdp_blend(*args))
+
+
+def tile_views(plan: Plan, buffers, counts=None):
+    """Per-tile torch views into the tile-major buffers.
+
+    ``counts`` (host list of tile_count) trims each view to its used rows;
+    without it the views span the whole slot.  Returns a list of dicts with
+    ``lat`` (B, rows, C), ``pos`` (B, 3, rows, 2) and ``index`` (rows,).
+    """
+    c = plan.cfg
+    views = []
+    for t in range(tdp_plan_num_tiles(plan)):
+        info = tdp_plan_tile(plan, t)
+        cap = info.capacity
+        used = cap if counts is None else int(counts[t])
+        lat = buffers["tile_lat"][info.lat_offset: info.lat_offset + c.batch * cap * c.channels]
+        pos = buffers["tile_pos"][info.pos_offset: info.pos_offset + c.batch * 6 * cap]
+        idx = buffers["tile_index"][info.index_offset: info.index_offset + cap]
+        views.append({
+            "lat": lat.view(c.batch, cap, c.channels)[:, :used],
+            "pos": pos.view(c.batch, 3, cap, 2)[:, :, :used],
+            "index": idx[:used],
+            "info": info,
+        })
+    return views

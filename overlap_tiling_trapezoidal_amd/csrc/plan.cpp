@@ -1,0 +1,266 @@
+// Host planner: split_by_count, overlap guard, trapezoidal windows, tile
+// enumeration and buffer sizes.  Pure host code; it needs no GPU.
+//
+// Sources: LTX-2 docs, "Tiled Data Parallelism (TDP)", sections "What it is"
+// and "API"; mold issue #673, sections "Scope" and "A bug found while
+// porting".
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "plan_internal.h"
+
+namespace tdp {
+
+static thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+}
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int dtype_bytes(int32_t dtype) {
+  switch (dtype) {
+    case TDP_F32: return 4;
+    case TDP_BF16: return 2;
+    default: return 0;
+  }
+}
+
+static const char* kAxisName[3] = {"frames", "height", "width"};
+
+// Validate one axis and fill its intervals.  The split: a_i =
+// floor(i*(dim-o)/n), tile i = [a_i, a_{i+1} + o), so neighbours overlap by
+// exactly o cells and the last tile ends at dim.
+static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisDev* ax) {
+  const char* name = kAxisName[d];
+  if (t.num_tiles < 1) return fail(TDP_EINVAL, "%s: num_tiles must be >= 1 (got %d)", name, t.num_tiles);
+  if (t.overlap < 0) return fail(TDP_EINVAL, "%s: overlap must be >= 0 (got %d)", name, t.overlap);
+  if (t.num_tiles > kMaxTiles)
+    return fail(TDP_ESHAPE, "%s: %d tiles exceed the limit of %d per axis", name, t.num_tiles, kMaxTiles);
+  if (t.num_tiles == 1 && t.overlap != 0)
+    return fail(TDP_EGUARD, "%s: an untiled axis (1 tile) must request overlap 0 (got %d)", name, t.overlap);
+  const int64_t free_len = (int64_t)dim - t.overlap;
+  if (free_len < t.num_tiles)
+    return fail(TDP_ESHAPE,
+                "%s: %d tiles with overlap %d on %d cells leave a stride below one cell; "
+                "use at most %lld tiles or a smaller overlap",
+                name, t.num_tiles, t.overlap, dim, (long long)(free_len > 0 ? free_len : 0));
+  if (guarded && (int64_t)t.overlap * (t.num_tiles + 1) > dim)
+    return fail(TDP_EGUARD,
+                "%s: overlap %d exceeds dim/(n+1) = %d/%d, so three windows would stack; "
+                "reduce overlap on %s to <= %d or use fewer tiles",
+                name, t.overlap, dim, t.num_tiles + 1, name, dim / (t.num_tiles + 1));
+  ax->dim = dim;
+  ax->n = t.num_tiles;
+  ax->o = t.overlap;
+  ax->pre[0] = 0;
+  for (int i = 0; i < t.num_tiles; ++i) {
+    const int64_t a = (int64_t)i * free_len / t.num_tiles;
+    const int64_t a_next = (int64_t)(i + 1) * free_len / t.num_tiles;
+    ax->start[i] = (int32_t)a;
+    ax->size[i] = (int32_t)(a_next + t.overlap - a);
+    ax->pre[i + 1] = ax->pre[i] + ax->size[i];
+  }
+  for (int i = t.num_tiles; i < kMaxTiles; ++i) {
+    ax->start[i] = 0;
+    ax->size[i] = 0;
+    ax->pre[i + 1] = ax->pre[i];
+  }
+  return TDP_OK;
+}
+
+}  // namespace tdp
+
+using namespace tdp;
+
+extern "C" {
+
+int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
+  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_plan_create: null argument");
+  *out = nullptr;
+  const tdp_config c = *cfg;
+  if (c.batch < 1 || c.channels < 1 || c.frames < 1 || c.height < 1 || c.width < 1)
+    return fail(TDP_EINVAL, "batch, channels, frames, height and width must all be >= 1");
+  if (c.num_cond < 0) return fail(TDP_EINVAL, "num_cond must be >= 0 (got %d)", c.num_cond);
+  if (c.batch > TDP_MAX_BATCH) return fail(TDP_ESHAPE, "batch %d exceeds %d", c.batch, TDP_MAX_BATCH);
+  const int ein = dtype_bytes(c.in_dtype), eout = dtype_bytes(c.out_dtype);
+  if (!ein) return fail(TDP_EINVAL, "in_dtype must be TDP_F32 or TDP_BF16 (got %d)", c.in_dtype);
+  if (!eout) return fail(TDP_EINVAL, "out_dtype must be TDP_F32 or TDP_BF16 (got %d)", c.out_dtype);
+  if (c.flags & ~(TDP_NORMALIZE_POSITIONS | TDP_UNGUARDED))
+    return fail(TDP_EINVAL, "unknown flag bits 0x%x", c.flags & ~(TDP_NORMALIZE_POSITIONS | TDP_UNGUARDED));
+  const int64_t row_bytes = (int64_t)c.channels * ein;
+  if (row_bytes % 16 != 0 || row_bytes > 1024)
+    return fail(TDP_ESHAPE,
+                "channels * element size must be a multiple of 16 bytes and at most 1024 bytes (got %lld)",
+                (long long)row_bytes);
+  if (c.width > TDP_MAX_WIDTH) return fail(TDP_ESHAPE, "width %d exceeds %d", c.width, TDP_MAX_WIDTH);
+  const int64_t N = (int64_t)c.frames * c.height * c.width;
+  const int64_t rows = N + c.num_cond;
+  if ((int64_t)c.batch * rows > INT32_MAX || N > INT32_MAX)
+    return fail(TDP_ESHAPE, "batch * (tokens + conditioning) = %lld exceeds the int32 range",
+                (long long)((int64_t)c.batch * rows));
+
+  const bool guarded = !(c.flags & TDP_UNGUARDED);
+  PlanDev dev;
+  memset(&dev, 0, sizeof dev);
+  const int32_t dims[3] = {c.frames, c.height, c.width};
+  for (int d = 0; d < 3; ++d) {
+    const int st = build_axis(d, dims[d], c.axis[d], guarded, &dev.ax[d]);
+    if (st != TDP_OK) return st;
+  }
+  dev.B = c.batch;
+  dev.C = c.channels;
+  dev.F = c.frames;
+  dev.H = c.height;
+  dev.W = c.width;
+  dev.N = (int32_t)N;
+  dev.Nc = c.num_cond;
+  dev.T = dev.ax[0].n * dev.ax[1].n * dev.ax[2].n;
+  dev.rows = (int32_t)rows;
+  dev.vin = (int32_t)(row_bytes / 16);
+  dev.in_dtype = c.in_dtype;
+  dev.out_dtype = c.out_dtype;
+  dev.normalize = (c.flags & TDP_NORMALIZE_POSITIONS) ? 1 : 0;
+
+  // Tile slots: sum over tiles of capacity = (sum of gen) + T * Nc.
+  const int64_t total_gen =
+      (int64_t)dev.ax[0].pre[dev.ax[0].n] * dev.ax[1].pre[dev.ax[1].n] * dev.ax[2].pre[dev.ax[2].n];
+  const int64_t total_index = total_gen + (int64_t)dev.T * c.num_cond;
+  if (total_index * c.batch > INT32_MAX)
+    return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
+                (long long)(total_index * c.batch));
+
+  // Extent partials: enough chunks that each covers about 2048 tokens.
+  int64_t max_gen = 0;
+  for (int i = 0; i < dev.ax[0].n; ++i)
+    for (int j = 0; j < dev.ax[1].n; ++j)
+      for (int k = 0; k < dev.ax[2].n; ++k) {
+        const int64_t g = (int64_t)dev.ax[0].size[i] * dev.ax[1].size[j] * dev.ax[2].size[k];
+        if (g > max_gen) max_gen = g;
+      }
+  int64_t chunks = (max_gen + 2047) / 2048;
+  if (chunks < 1) chunks = 1;
+  if (chunks > 64) chunks = 64;
+  dev.chunks = (int32_t)chunks;
+
+  tdp_plan* p = new (std::nothrow) tdp_plan;
+  if (!p) return fail(TDP_EINVAL, "out of host memory");
+  p->cfg = c;
+  p->dev = dev;
+  p->guarded = guarded;
+  p->total_index = total_index;
+  *out = p;
+  return TDP_OK;
+}
+
+void tdp_plan_destroy(tdp_plan* plan) { delete plan; }
+
+int tdp_plan_num_tiles(const tdp_plan* plan, int32_t* num_tiles) {
+  if (!plan || !num_tiles) return fail(TDP_EINVAL, "tdp_plan_num_tiles: null argument");
+  *num_tiles = plan->dev.T;
+  return TDP_OK;
+}
+
+int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t* ends) {
+  if (!plan || !starts || !ends) return fail(TDP_EINVAL, "tdp_plan_intervals: null argument");
+  if (axis < 0 || axis > 2) return fail(TDP_EINVAL, "axis must be 0, 1 or 2 (got %d)", axis);
+  const AxisDev& ax = plan->dev.ax[axis];
+  for (int i = 0; i < ax.n; ++i) {
+    starts[i] = ax.start[i];
+    ends[i] = ax.start[i] + ax.size[i];
+  }
+  return TDP_OK;
+}
+
+int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w) {
+  if (!plan || !w) return fail(TDP_EINVAL, "tdp_plan_window: null argument");
+  if (axis < 0 || axis > 2) return fail(TDP_EINVAL, "axis must be 0, 1 or 2 (got %d)", axis);
+  const AxisDev& ax = plan->dev.ax[axis];
+  if (i < 0 || i >= ax.n) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", i, ax.n);
+  const int size = ax.size[i], o = ax.o;
+  for (int j = 0; j < size; ++j) {
+    // Exact ratios are formed in double (numerator and denominator are
+    // small integers, so each ratio is one rounding) and the product of the
+    // two ramps, when both apply, is rounded once more to float.
+    double v = 1.0;
+    if (i > 0 && j < o) v *= (double)(j + 1) / (double)(o + 1);
+    if (i < ax.n - 1 && j >= size - o) v *= (double)(size - j) / (double)(o + 1);
+    w[j] = (float)v;
+  }
+  return TDP_OK;
+}
+
+int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info) {
+  if (!plan || !info) return fail(TDP_EINVAL, "tdp_plan_tile: null argument");
+  const PlanDev& p = plan->dev;
+  if (t < 0 || t >= p.T) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", t, p.T);
+  int i, j, k;
+  tile_grid(p, t, i, j, k);
+  const TileSlot s = tile_slot(p, i, j, k);
+  info->index = t;
+  info->grid[0] = i;
+  info->grid[1] = j;
+  info->grid[2] = k;
+  const int g[3] = {i, j, k};
+  for (int d = 0; d < 3; ++d) {
+    info->origin[d] = p.ax[d].start[g[d]];
+    info->shape[d] = p.ax[d].size[g[d]];
+  }
+  info->gen_tokens = s.gen;
+  info->capacity = s.cap;
+  info->lat_offset = s.row_base * p.C;
+  info->pos_offset = s.row_base * 6;
+  info->index_offset = s.index_base;
+  return TDP_OK;
+}
+
+int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes) {
+  if (!plan || !sizes) return fail(TDP_EINVAL, "tdp_plan_sizes: null argument");
+  const PlanDev& p = plan->dev;
+  sizes->num_tiles = p.T;
+  sizes->tile_lat_elems = plan->total_index * p.B * p.C;
+  sizes->tile_pos_floats = plan->total_index * p.B * 6;
+  sizes->tile_index_ints = plan->total_index;
+  sizes->cond_row_ints = (int64_t)p.T * p.Nc;
+  sizes->out_elems = (int64_t)p.B * p.rows * p.C;
+  // extent partials: (T, B, chunks, 3 axes, {min start, max end}) floats
+  sizes->workspace_bytes = (int64_t)p.T * p.B * p.chunks * 6 * (int64_t)sizeof(float);
+  return TDP_OK;
+}
+
+int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* rank) {
+  if (!plan || !rank) return fail(TDP_EINVAL, "tdp_plan_tile_rank: null argument");
+  if (t < 0 || t >= plan->dev.T) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", t, plan->dev.T);
+  if (world < 1) return fail(TDP_EINVAL, "world must be >= 1 (got %d)", world);
+  *rank = t % world;
+  return TDP_OK;
+}
+
+const char* tdp_status_string(int status) {
+  switch (status) {
+    case TDP_OK: return "TDP_OK";
+    case TDP_EINVAL: return "TDP_EINVAL: invalid argument";
+    case TDP_EGUARD: return "TDP_EGUARD: overlap guard violated (overlap > dim/(n+1))";
+    case TDP_ESHAPE: return "TDP_ESHAPE: size out of the supported range";
+    case TDP_EHIP: return "TDP_EHIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* tdp_last_error(void) { return g_last_error; }
+
+}  // extern "C"

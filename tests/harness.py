@@ -1,0 +1,161 @@
+"""Test-side glue between seeded inputs, the GPU library and the oracle.
+
+Moves numpy inputs to the GPU, runs the library through its Python binding
+(which calls the C ABI), copies results back and re-arranges the oracle's
+per-tile results into the library's tile-major layout for comparison.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+import overlap_tiling_trapezoidal_amd as tdp
+
+POISON = -7
+
+
+def note(msg: str):
+    """Name the GPU step about to run (flushed, so a fault still shows it)."""
+    print(f"[gpu-step] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_device_latent(latent: np.ndarray, device):
+    if latent.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(latent).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(latent)).to(device)
+
+
+def latent_bits(t: torch.Tensor) -> np.ndarray:
+    """Bit pattern of a latent-like tensor: uint16 for bf16, uint32 for fp32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.int32).numpy().view(np.uint32)
+
+
+def as_float(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def plan_for(wl, out_dtype=None, normalize=True):
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond,
+                          in_dtype=wl.dtype, out_dtype=out_dtype or wl.dtype, normalize=normalize)
+    return tdp.tdp_plan_create(cfg)
+
+
+def poisoned_buffers(plan, device):
+    bufs = tdp.allocate_extract_outputs(plan, device)
+    bufs["tile_lat"].view(torch.int16 if bufs["tile_lat"].dtype == torch.bfloat16 else torch.int32).fill_(POISON)
+    bufs["tile_pos"].fill_(float("nan"))
+    for k in ("tile_index", "tile_count", "cond_row", "cond_k"):
+        bufs[k].fill_(POISON)
+    bufs["workspace"].fill_(0xAB)
+    return bufs
+
+
+def gpu_extract(plan, inp, device, label=""):
+    lat = to_device_latent(inp["latent"], device)
+    pos = torch.from_numpy(inp["pos"]).to(device)
+    bufs = poisoned_buffers(plan, device)
+    note(f"extract {label}")
+    tdp.tdp_extract(plan, lat, pos, **bufs)
+    torch.cuda.synchronize()
+    return lat, pos, bufs
+
+
+def check_extract(plan, bufs, ex, num_cond):
+    """Bit-exact comparison of the GPU extract with the oracle's."""
+    counts = bufs["tile_count"].cpu().numpy()
+    views = tdp.tile_views(plan, bufs, counts)
+    T = len(ex["tiles"])
+    assert len(views) == T
+    for t, (v, et) in enumerate(zip(views, ex["tiles"])):
+        n_t = len(et["rows"])
+        assert counts[t] == n_t, (t, counts[t], n_t)
+        assert np.array_equal(v["index"].cpu().numpy(), et["rows"].astype(np.int32)), t
+        got_lat = latent_bits(v["lat"])
+        want_lat = et["latent"] if et["latent"].dtype == np.uint16 else et["latent"].view(np.uint32)
+        assert np.array_equal(got_lat, want_lat), f"tile {t} latent differs"
+        got_pos = v["pos"].cpu().contiguous().numpy()
+        assert np.array_equal(got_pos.view(np.uint32), et["pos"].view(np.uint32)), f"tile {t} positions differ"
+    if num_cond:
+        cond_row = bufs["cond_row"][:T * num_cond].cpu().numpy().reshape(T, num_cond)
+        want = np.full((T, num_cond), -1, np.int32)
+        for t, et in enumerate(ex["tiles"]):
+            want[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
+        assert np.array_equal(cond_row, want)
+        assert np.array_equal(bufs["cond_k"][:num_cond].cpu().numpy(), ex["k"].astype(np.int32))
+
+
+def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
+    """Pack per-tile (B, N_t, C) arrays into a tile-major slot buffer (numpy).
+
+    Unused slot rows get random garbage (when ``rng`` is given) so a blend
+    that reads them would be caught.
+    """
+    s = tdp.tdp_plan_sizes(plan)
+    c = plan.cfg
+    np_dtype = np.uint16 if dtype_code == tdp.TDP_BF16 else np.float32
+    buf = np.empty(s.tile_lat_elems, dtype=np_dtype)
+    if rng is not None:
+        if np_dtype == np.uint16:
+            buf[:] = rng.integers(0, 2**16, size=buf.size, dtype=np.uint16)
+            buf[(buf & 0x7F80) == 0x7F80] = 0x7F00   # finite but huge instead of NaN/Inf
+        else:
+            buf[:] = rng.standard_normal(buf.size).astype(np.float32) * 1e30
+    for t, arr in enumerate(tile_arrays):
+        info = tdp.tdp_plan_tile(plan, t)
+        slot = buf[info.lat_offset: info.lat_offset + c.batch * info.capacity * c.channels]
+        slot = slot.reshape(c.batch, info.capacity, c.channels)
+        slot[:, :arr.shape[1], :] = arr
+    return buf
+
+
+def gpu_blend(plan, tile_out_np, cond_row, cond_k, device, label=""):
+    c = plan.cfg
+    if tile_out_np.dtype == np.uint16:
+        y = torch.from_numpy(tile_out_np.view(np.int16)).view(torch.bfloat16).to(device)
+    else:
+        y = torch.from_numpy(tile_out_np).to(device)
+    out = tdp.allocate_output(plan, device)
+    out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32).fill_(POISON)
+    note(f"blend {label}")
+    tdp.tdp_blend(plan, y, cond_row, cond_k, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def cond_tables(plan, ex, num_cond, device):
+    """The oracle's selection in the library's (cond_row, cond_k) format."""
+    T = len(ex["tiles"])
+    cond_row = np.full((T, max(num_cond, 1)), -1, np.int32)
+    for t, et in enumerate(ex["tiles"]):
+        cond_row[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
+    k = ex["k"].astype(np.int32) if num_cond else np.zeros(1, np.int32)
+    return (torch.from_numpy(cond_row.reshape(-1)).to(device), torch.from_numpy(k).to(device))
+
+
+def check_blend(out: torch.Tensor, ref: np.ndarray, mag: np.ndarray, out_dtype: int):
+    """Tolerance: fp32 |d| <= 2e-6*sum|w y|; bf16 adds 4e-3*|ref| for rounding."""
+    got = as_float(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    if out_dtype == tdp.TDP_F32:
+        bound = 2e-6 * mag
+    else:
+        bound = 4e-3 * np.abs(ref) + 2e-6 * mag
+    bad = err > bound
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{bad.sum()} elements out of tolerance; first {tuple(i)}: "
+                             f"got {got[tuple(i)]!r} ref {ref[tuple(i)]!r} mag {mag[tuple(i)]!r}")
+    return float((err / np.maximum(mag, 1e-30)).max())
+
+
+def oracle_tile_floats(et):
+    lat = et["latent"]
+    return O.bf16_bits_to_f32(lat) if lat.dtype == np.uint16 else lat

@@ -1,0 +1,196 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library loads and exports every function include/tdp.h declares; the
+host planner agrees bit for bit with the oracle on intervals, windows, tile
+enumeration and slot layout; every error path returns its status and a
+message naming the limit.  No device function is called here.
+"""
+import ctypes
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import overlap_tiling_trapezoidal_amd as tdp
+from synth import WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tdp.load_library()
+
+
+def plan_for(wl, **kw):
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond,
+                          in_dtype=wl.dtype, **kw)
+    return tdp.tdp_plan_create(cfg)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = tdp.header_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def fp32_rne(q: Fraction) -> np.float32:
+    """Correctly rounded float32 of an exact rational (ties to even)."""
+    f = np.float32(float(q))
+    best = None
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - q)
+        if best is None or err < best[0] or (err == best[0] and (int(cand.view(np.uint32)) & 1) == 0):
+            best = (err, cand)
+    return best[1]
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_matches_oracle(name):
+    wl = WORKLOADS[name]
+    plan = plan_for(wl)
+    ivs = [O.split_by_count(d, n, o) for d, (n, o) in zip(wl.shape, wl.tiling)]
+    for d in range(3):
+        assert tdp.tdp_plan_intervals(plan, d) == ivs[d]
+        for i in range(len(ivs[d])):
+            got = tdp.tdp_plan_window(plan, d, i)
+            want = np.array([fp32_rne(w) for w in O.window_exact(ivs[d], i, wl.tiling[d][1])], np.float32)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    tiles = O.enumerate_tiles(wl.shape, wl.tiling)
+    assert tdp.tdp_plan_num_tiles(plan) == len(tiles)
+    lat_off = pos_off = idx_off = 0
+    for t, tile in enumerate(tiles):
+        info = tdp.tdp_plan_tile(plan, t)
+        assert info.index == t
+        assert tuple(info.grid) == tile["grid"]
+        assert tuple(info.origin) == tile["origin"]
+        assert tuple(info.shape) == tile["size"]
+        gen = int(np.prod(tile["size"]))
+        assert info.gen_tokens == gen
+        assert info.capacity == gen + wl.num_cond
+        # slots are packed back to back in tile order
+        assert (info.lat_offset, info.pos_offset, info.index_offset) == (lat_off, pos_off, idx_off)
+        lat_off += wl.batch * info.capacity * wl.channels
+        pos_off += wl.batch * info.capacity * 6
+        idx_off += info.capacity
+        assert tdp.tdp_plan_tile_rank(plan, t, 4) == O.round_robin_rank(t, 4)
+    s = tdp.tdp_plan_sizes(plan)
+    assert (s.tile_lat_elems, s.tile_pos_floats, s.tile_index_ints) == (lat_off, pos_off, idx_off)
+    assert s.cond_row_ints == len(tiles) * wl.num_cond
+    assert s.out_elems == wl.batch * (wl.tokens + wl.num_cond) * wl.channels
+
+
+def test_plan_matches_oracle_random_guarded():
+    rng = np.random.default_rng(11)
+    done = 0
+    while done < 300:
+        shape = tuple(int(x) for x in rng.integers(1, 70, size=3))
+        tiling = []
+        for dim in shape:
+            n = int(rng.integers(1, 7))
+            o = 0 if n == 1 else int(rng.integers(0, dim // (n + 1) + 1))
+            if dim - o < n:
+                n, o = 1, 0
+            tiling.append((n, o))
+        cfg = tdp.make_config(1, 8, shape, tiling, in_dtype="bf16")
+        plan = tdp.tdp_plan_create(cfg)
+        for d in range(3):
+            assert tdp.tdp_plan_intervals(plan, d) == O.split_by_count(shape[d], *tiling[d])
+        assert tdp.tdp_plan_num_tiles(plan) == len(O.enumerate_tiles(shape, tiling))
+        done += 1
+
+
+def test_unguarded_window_sums_reproduce_table():
+    # The 1-D table of mold #673 through the library: dim 21, overlap 8.
+    for n, want_max in [(2, 1.0), (3, 1.074), (4, 1.161)]:
+        cfg = tdp.make_config(1, 8, (1, 1, 21), ((1, 0), (1, 0), (n, 8)), unguarded=True)
+        plan = tdp.tdp_plan_create(cfg)
+        sums = np.zeros(21, np.float32)   # fp32 sums, as a blend would form them
+        for i, (a, b) in enumerate(tdp.tdp_plan_intervals(plan, 2)):
+            sums[a:b] += tdp.tdp_plan_window(plan, 2, i)
+        assert abs(float(sums.max()) - want_max) <= 1e-3
+        if n == 2:
+            assert np.all(sums == np.float32(1.0))
+
+
+def test_fp32_ramps_sum_to_one():
+    # Complementary ramps (j+1)/(o+1) and (o-j)/(o+1) add to exactly 1 in fp32.
+    for o in range(1, 300):
+        dim = 3 * o + 3
+        cfg = tdp.make_config(1, 8, (1, 1, dim), ((1, 0), (1, 0), (2, o)))
+        plan = tdp.tdp_plan_create(cfg)
+        (a0, b0), (a1, b1) = tdp.tdp_plan_intervals(plan, 2)
+        w0, w1 = tdp.tdp_plan_window(plan, 2, 0), tdp.tdp_plan_window(plan, 2, 1)
+        s = np.zeros(dim, np.float32)
+        s[a0:b0] += w0
+        s[a1:b1] += w1
+        assert np.all(s == np.float32(1.0)), o
+
+
+@pytest.mark.parametrize("kw,status,fragment", [
+    (dict(tiling=((1, 0), (2, 8), (1, 0)), shape=(4, 21, 8)), tdp.TDP_EGUARD, "reduce overlap on height to <= 7"),
+    (dict(tiling=((1, 1), (1, 0), (1, 0))), tdp.TDP_EGUARD, "untiled axis"),
+    (dict(tiling=((0, 0), (1, 0), (1, 0))), tdp.TDP_EINVAL, "num_tiles"),
+    (dict(tiling=((1, 0), (2, -1), (1, 0))), tdp.TDP_EINVAL, "overlap must be >= 0"),
+    (dict(tiling=((1, 0), (1, 0), (9, 0)), shape=(4, 8, 8)), tdp.TDP_ESHAPE, "stride below one cell"),
+    (dict(tiling=((1, 0), (1, 0), (33, 0)), shape=(4, 8, 100)), tdp.TDP_ESHAPE, "limit of 32"),
+    (dict(channels=12), tdp.TDP_ESHAPE, "multiple of 16 bytes"),
+    (dict(channels=1024), tdp.TDP_ESHAPE, "at most 1024"),
+    (dict(batch=0), tdp.TDP_EINVAL, ">= 1"),
+    (dict(num_cond=-1), tdp.TDP_EINVAL, "num_cond"),
+    (dict(in_dtype=7), tdp.TDP_EINVAL, "in_dtype"),
+    (dict(shape=(4, 8, 5000)), tdp.TDP_ESHAPE, "width 5000"),
+    (dict(shape=(1024, 1024, 4096), num_cond=0), tdp.TDP_ESHAPE, "int32"),
+])
+def test_plan_errors(kw, status, fragment):
+    args = dict(batch=1, channels=128, shape=(4, 8, 8), tiling=((1, 0), (1, 0), (1, 0)), num_cond=0,
+                in_dtype="bf16")
+    args.update(kw)
+    cfg = tdp.make_config(args["batch"], args["channels"], args["shape"], args["tiling"], args["num_cond"],
+                          in_dtype=args["in_dtype"])
+    with pytest.raises(tdp.TdpError) as ei:
+        tdp.tdp_plan_create(cfg)
+    assert ei.value.status == status
+    assert fragment in str(ei.value), str(ei.value)
+
+
+def test_unknown_flags_and_nulls(lib):
+    cfg = tdp.make_config(1, 128, (4, 8, 8), ((1, 0),) * 3)
+    cfg.flags = 0x80
+    with pytest.raises(tdp.TdpError) as ei:
+        tdp.tdp_plan_create(cfg)
+    assert ei.value.status == tdp.TDP_EINVAL
+    assert lib.tdp_plan_create(None, None) == tdp.TDP_EINVAL
+    assert lib.tdp_plan_num_tiles(None, None) == tdp.TDP_EINVAL
+    assert lib.tdp_status_string(tdp.TDP_EGUARD).startswith(b"TDP_EGUARD")
+
+
+def test_device_calls_reject_bad_plans_before_launch(lib):
+    # Validation happens on the host before anything is enqueued, so these
+    # run without a GPU.
+    cfg = tdp.make_config(1, 8, (1, 1, 21), ((1, 0), (1, 0), (3, 8)), unguarded=True)
+    plan = tdp.tdp_plan_create(cfg)
+    null = ctypes.c_void_p(None)
+    assert lib.tdp_extract(plan.handle, *([null] * 10)) == tdp.TDP_EGUARD
+    assert lib.tdp_blend(plan.handle, *([null] * 5)) == tdp.TDP_EGUARD
+    good = tdp.tdp_plan_create(tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2))))
+    assert lib.tdp_extract(good.handle, *([null] * 10)) == tdp.TDP_EINVAL
+    assert "null" in tdp.tdp_last_error()
+    assert lib.tdp_blend(good.handle, *([null] * 5)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(None, *([null] * 10)) == tdp.TDP_EINVAL
+    # misaligned pointers are refused too
+    odd = ctypes.c_void_p(0x1002)
+    al = ctypes.c_void_p(0x1000)
+    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, null, al, null) == tdp.TDP_EINVAL
+    assert "aligned" in tdp.tdp_last_error()
+
+
+def test_workspace_and_chunks_sizes():
+    plan = plan_for(WORKLOADS["4k"])
+    s = tdp.tdp_plan_sizes(plan)
+    assert s.num_tiles == 16
+    assert s.tile_index_ints == 247296
+    assert s.tile_lat_elems == 247296 * 128
+    assert s.workspace_bytes > 0 and s.workspace_bytes % 24 == 0
