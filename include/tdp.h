@@ -81,6 +81,7 @@ extern "C" {
 #define TDP_MAX_TILES_PER_AXIS 32
 #define TDP_MAX_WIDTH 4096
 #define TDP_MAX_BATCH 1024
+#define TDP_MAX_AXIS (1 << 26) /* cells per axis */
 
 /* One axis of the tiling: a tile COUNT and an overlap in latent grid cells
  * (TDP docs, "API": DimensionTilingConfig(num_tiles, overlap)). */
@@ -93,8 +94,8 @@ typedef struct {
   int32_t batch;        /* 1 <= B <= TDP_MAX_BATCH                            */
   int32_t channels;     /* C >= 1; C * sizeof(in_dtype) a multiple of 16 B,   */
                         /* at most 1024 B                                     */
-  int32_t frames;       /* F >= 1 latent grid                                 */
-  int32_t height;       /* H >= 1                                             */
+  int32_t frames;       /* 1 <= F <= TDP_MAX_AXIS latent grid                 */
+  int32_t height;       /* 1 <= H <= TDP_MAX_AXIS                             */
   int32_t width;        /* 1 <= W <= TDP_MAX_WIDTH                            */
   int32_t num_cond;     /* Nc >= 0 conditioning tokens after the N generated  */
   tdp_axis_tiling axis[3]; /* frames, height, width (TDP docs, "API":       */
@@ -125,7 +126,7 @@ typedef struct {
   int64_t tile_index_ints;  /* int32 entries of tile_index                    */
   int64_t cond_row_ints;    /* int32 entries of cond_row: T * Nc              */
   int64_t out_elems;        /* elements of out: B * (N + Nc) * C              */
-  int64_t workspace_bytes;  /* device scratch that tdp_extract needs          */
+  int64_t workspace_bytes;  /* device scratch of tdp_extract (extent partials) */
 } tdp_sizes;
 
 /* ---- plan (host only; no GPU needed) ------------------------------------ */
@@ -160,6 +161,11 @@ int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t*
  * Each value is the correctly rounded fp32 of the exact ratio. */
 int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w);
 
+/* Tiles of one axis that contain cell x, ascending: tiles[0..*count), with
+ * *count 1 or 2 (at most two overlap under the guard).  This is the lookup
+ * the kernels run for every latent row.  Guarded plans only. */
+int tdp_plan_cell_tiles(const tdp_plan* plan, int axis, int32_t x, int32_t* tiles, int32_t* count);
+
 /* Geometry and slot offsets of tile t. */
 int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info);
 
@@ -172,15 +178,16 @@ int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* 
 
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
 
-/* Gather all tiles in one pass of the latent.
+/* Gather all tiles, every latent row read once.  Two launches: a short
+ * reduction of each tile's position extent into `workspace`, then one
+ * kernel for rows, positions and selection.
  *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
  *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
  *        tile_count (T) int32: gen_t + kept_t.
  *        cond_row (T * Nc) int32: row of conditioning token c inside tile
- *          t's slot, or -1 when t does not keep c.  Unused when Nc == 0.
- *        cond_k (Nc) int32: number of tiles that keep token c.
- *   scratch workspace: tdp_sizes.workspace_bytes of device memory, 16-byte
- *        aligned; its contents on entry do not matter.
+ *          t's slot, or -1 when t does not keep it; the number of
+ *          non-negative entries in column c is k, the count of tiles that
+ *          keep c.  May be NULL when Nc == 0.
  * Positions: the tile's offset on axis d for batch element b is the minimum
  * start over its generated tokens; with TDP_NORMALIZE_POSITIONS it is
  * subtracted from both ends of every row the tile holds (one fp32
@@ -190,28 +197,33 @@ int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* 
  * element, c's interval overlaps the tile's extent [min start, max end) on
  * all three axes (half-open: touching or empty intervals do not overlap) or
  * c's time start is negative (TDP docs, "Shared negative (reference)
- * positions"); tested on positions before normalization.
- * All pointers are device pointers except `plan`; buffers must not overlap;
- * cond_row / cond_k may be NULL when Nc == 0.  Returns TDP_EGUARD for
- * unguarded plans, TDP_EINVAL for null pointers, TDP_EHIP on launch
- * failure. */
+ * positions"); tested on positions before normalization.  Positions must be
+ * finite.
+ * All pointers are device pointers except `plan`; latent/tile_lat 16-byte
+ * aligned, pos/tile_pos 8-byte aligned; buffers must not overlap and hold
+ * the sizes tdp_plan_sizes() reports (the library cannot check sizes).
+ * workspace: tdp_sizes.workspace_bytes of device scratch, 8-byte aligned;
+ *   its contents on entry do not matter and on return are unspecified.  It
+ *   may be NULL only when the plan neither normalizes nor has Nc > 0.
+ *   Calls that share a workspace must not overlap in time.
+ * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
+ * pointers, TDP_EHIP on launch failure. */
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 void* tile_lat, float* tile_pos, int32_t* tile_index,
-                int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
-                void* workspace, void* stream);
+                int32_t* tile_count, int32_t* cond_row, void* workspace, void* stream);
 
 /* Blend tile outputs (tile-major slots with tile_lat's layout and dtype,
  * rows as tdp_extract placed them) into out (B, N+Nc, C) out_dtype:
  *   generated token:    sum over covering tiles t, ascending, of
- *                       wF*wH*wW * y_t  (separable trapezoid),
- *   conditioning token: (1/k) * sum over tiles that keep it of y_t,
- *                       and 0 when k == 0,
+ *                       (wF*wH)*wW * y_t  (separable trapezoid),
+ *   conditioning token: (1/k) * sum over the k tiles that keep it, ascending
+ *                       (k read off cond_row); 0 when k == 0,
  * fp32 accumulation, no normalization pass (mold #673, "A bug found while
- * porting"), bf16 output rounded to nearest even.  cond_row / cond_k are
- * tdp_extract's outputs for the same plan (may be NULL when Nc == 0).
- * Device pointers except `plan`. */
+ * porting"), bf16 output rounded to nearest even.  cond_row is tdp_extract's
+ * output for the same plan (may be NULL when Nc == 0).  Device pointers
+ * except `plan`; tile_out/out 16-byte aligned. */
 int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row,
-              const int32_t* cond_k, void* out, void* stream);
+              void* out, void* stream);
 
 /* ---- errors ------------------------------------------------------------ */
 const char* tdp_status_string(int status);

@@ -104,10 +104,11 @@ def load_library(path: str = LIB_PATH):
         "tdp_plan_intervals": (ctypes.c_int, [vp, ctypes.c_int, i32p, i32p]),
         "tdp_plan_window": (ctypes.c_int, [vp, ctypes.c_int, i32, ctypes.POINTER(ctypes.c_float)]),
         "tdp_plan_tile": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_tile_info)]),
+        "tdp_plan_cell_tiles": (ctypes.c_int, [vp, ctypes.c_int, i32, i32p, i32p]),
         "tdp_plan_sizes": (ctypes.c_int, [vp, ctypes.POINTER(tdp_sizes)]),
         "tdp_plan_tile_rank": (ctypes.c_int, [vp, i32, i32, i32p]),
-        "tdp_extract": (ctypes.c_int, [vp] * 11),
-        "tdp_blend": (ctypes.c_int, [vp] * 6),
+        "tdp_extract": (ctypes.c_int, [vp] * 10),
+        "tdp_blend": (ctypes.c_int, [vp] * 5),
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tdp_last_error": (ctypes.c_char_p, []),
     }
@@ -221,6 +222,13 @@ def tdp_plan_window(plan: Plan, axis: int, i: int):
     return np.ctypeslib.as_array(buf).copy()
 
 
+def tdp_plan_cell_tiles(plan: Plan, axis: int, x: int) -> list[int]:
+    tiles = (ctypes.c_int32 * 2)()
+    n = ctypes.c_int32()
+    _check(load_library().tdp_plan_cell_tiles(plan.handle, axis, x, tiles, ctypes.byref(n)))
+    return [tiles[i] for i in range(n.value)]
+
+
 def tdp_plan_tile(plan: Plan, t: int) -> tdp_tile_info:
     info = tdp_tile_info()
     _check(load_library().tdp_plan_tile(plan.handle, t, ctypes.byref(info)))
@@ -280,7 +288,6 @@ def allocate_extract_outputs(plan: Plan, device="cuda"):
         "tile_index": torch.empty(s.tile_index_ints, dtype=torch.int32, device=dev),
         "tile_count": torch.empty(s.num_tiles, dtype=torch.int32, device=dev),
         "cond_row": torch.empty(max(s.cond_row_ints, 1), dtype=torch.int32, device=dev),
-        "cond_k": torch.empty(max(plan.cfg.num_cond, 1), dtype=torch.int32, device=dev),
         "workspace": torch.empty(max(s.workspace_bytes, 16), dtype=torch.uint8, device=dev),
     }
 
@@ -301,7 +308,7 @@ def _stream_handle(stream, device):
 
 
 def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
-                cond_row=None, cond_k=None, workspace=None, stream=None):
+                cond_row=None, workspace=None, stream=None):
     """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
     import torch
     c = plan.cfg
@@ -317,7 +324,6 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
         _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
         _ptr(tile_count, "tile_count", torch.int32, s.num_tiles, dev),
         _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
-        _ptr(cond_k, "cond_k", torch.int32, c.num_cond, dev) if c.num_cond else ctypes.c_void_p(None),
         _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes
         else ctypes.c_void_p(None),
         _stream_handle(stream, dev),
@@ -325,7 +331,7 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
     _check(load_library().tdp_extract(*args))
 
 
-def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):
+def tdp_blend(plan: Plan, tile_out, cond_row, out, stream=None):
     """Enqueue the blend of tile outputs into ``out`` on ``stream``."""
     import torch
     c = plan.cfg
@@ -335,11 +341,17 @@ def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):
         plan.handle,
         _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
         _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
-        _ptr(cond_k, "cond_k", torch.int32, c.num_cond, dev) if c.num_cond else ctypes.c_void_p(None),
         _ptr(out, "out", _torch_dtype(c.out_dtype), s.out_elems, dev),
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_blend(*args))
+
+
+def cond_keep_counts(plan: Plan, cond_row):
+    """k per conditioning token: tiles whose cond_row entry is non-negative."""
+    c = plan.cfg
+    T = tdp_plan_num_tiles(plan)
+    return (cond_row[: T * c.num_cond].view(T, c.num_cond) >= 0).sum(dim=0)
 
 
 def tile_views(plan: Plan, buffers, counts=None):

@@ -1,15 +1,26 @@
-// gfx950 kernels for the tiled hot path: extract (extents, conditioning
-// selection, gather) and blend (owner-computes weighted sum).
+// gfx950 kernels for the tiled hot path: extract and blend.
 //
 // Sources: LTX-2 docs, "Tiled Data Parallelism (TDP)", sections "What it is",
 // "Position normalization" and "Shared negative (reference) positions";
-// mold issue #673, "A bug found while porting" (blend has no normalization
-// pass).
+// mold issue #673, "A bug found while porting" (the blend has no
+// normalization pass).
 //
-// Data movement is the whole cost: every kernel is bound by HBM bandwidth.
-// Latent rows move as 16-byte vectors (one global_load/store_dwordx4 per
-// lane), V lanes per row, 256 / V rows per 256-thread workgroup pass.
-// Nothing is a contraction, so no MFMA is used.
+// Both operations are bound by HBM bandwidth: nothing is a contraction, so
+// no MFMA is used.  Latent rows move as 16-byte vectors (global_load /
+// global_store_dwordx4), V lanes per row, 256 / V rows per workgroup pass.
+// Hot loops are straight-line: every load is unconditional (out-of-range
+// lanes re-read a valid row and discard it), so the compiler keeps all of a
+// thread's loads in flight instead of waiting before each one.
+//
+// extract is ONE launch with three kinds of workgroups:
+//   selection  (tile, chunk of conditioning tokens): tile extents, keep
+//              test, ordered compaction, copy of the kept rows;
+//   positions  (tile, batch, axis, part): minimum start over the tile's
+//              generated tokens, then the shifted positions of one part of
+//              the tile and its source indices;
+//   latent     (batch, frame, row): every latent row of one (f, h) line is
+//              read once and written to each tile that covers it.
+// The kinds are independent, so they overlap in one grid.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -21,46 +32,95 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kGatherUnroll = 8;   // latent rows in flight per thread (extract)
-constexpr int kCondRowsPerBlock = 64;
+constexpr int kLatUnroll = 8;      // latent rows in flight per thread (extract)
+constexpr int kPosUnroll = 4;      // position lines in flight per thread
+constexpr int kExtUnroll = 4;      // extent-reduction lines in flight per thread
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
+constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kNoTile = 0xFF;
+constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
+constexpr int kCondRowsPerBlock = 64;
+
+// 16-byte vector as a native clang vector: HIP's uint4 wrapper (a union)
+// keeps arrays of it out of registers, which would serialize the loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming accesses: every byte is read once and written once, and the
+// written tiles are consumed only after the denoiser has run, so loads and
+// stores carry the non-temporal hint (they do not displace other data in
+// L2 and the Infinity Cache).
+template <typename T>
+__device__ inline T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ inline void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
 
 // ---------------------------------------------------------------------------
-// Axis helpers
+// Axis helpers (closed-form split from plan_internal.h; no tables)
 // ---------------------------------------------------------------------------
 
-// Tiles of one axis that contain cell x, ascending; at most two under the
-// overlap guard.  Returns how many were found.
-__device__ inline int axis_covers(const AxisDev& ax, int x, int* ti, int* tl) {
-  int c = 0;
-  for (int i = 0; i < ax.n; ++i) {
-    const int l = x - ax.start[i];
-    if (l >= 0 && l < ax.size[i] && c < 2) {
-      ti[c] = i;
-      tl[c] = l;
-      ++c;
-    }
-  }
-  return c;
-}
-
-// 1-D trapezoid of tile i at local cell l: (l+1)/(o+1) on a left ramp,
-// (size-l)/(o+1) on a right ramp, 1 elsewhere.  IEEE division (the build
-// keeps fp32 division correctly rounded), so each value equals the host
-// plan's window bit for bit.
-__device__ inline float axis_weight(const AxisDev& ax, int i, int l) {
+// 1-D trapezoid of tile i (of `size` cells) at local cell l: (l+1)/(o+1) on
+// a left ramp, (size-l)/(o+1) on a right ramp, 1 elsewhere.  fp32 division
+// is built correctly rounded, so each value equals the host plan's window
+// bit for bit.
+__device__ inline float ramp_weight(const AxisSplit& ax, int i, int l, int size) {
   float w = 1.0f;
   const float den = (float)(ax.o + 1);
   if (i > 0 && l < ax.o) w = (float)(l + 1) / den;
-  if (i < ax.n - 1 && l >= ax.size[i] - ax.o) w *= (float)(ax.size[i] - l) / den;
+  if (i < ax.n - 1 && l >= size - ax.o) w *= (float)(size - l) / den;
   return w;
 }
 
-__device__ inline int pack_covers(int c, const int* ti) {
-  const int a = c > 0 ? ti[0] : kNoTile;
-  const int b = c > 1 ? ti[1] : kNoTile;
-  return a | (b << 8);
+struct TileBox {
+  int f0, h0, w0, sf, sh, sw;
+  TileSlot s;
+};
+
+__device__ inline TileBox tile_box(const PlanDev& p, int t) {
+  int i, j, k;
+  tile_grid(p, t, i, j, k);
+  TileBox tb;
+  tb.f0 = split_start(p.ax[0], i);
+  tb.h0 = split_start(p.ax[1], j);
+  tb.w0 = split_start(p.ax[2], k);
+  tb.sf = split_size(p.ax[0], i);
+  tb.sh = split_size(p.ax[1], j);
+  tb.sw = split_size(p.ax[2], k);
+  tb.s = tile_slot(p, i, j, k);
+  return tb;
+}
+
+// Frame x height covers of one (f, h) line: up to four (tile pair, local
+// cell) combos in ascending (i_f, i_h) order.
+struct LineCombos {
+  int n;                   // number of combos: 1, 2 or 4
+  int nh;                  // height covers
+  Covers cf, ch;
+  __device__ inline void init(const PlanDev& p, int f, int h) {
+    cf = split_covers(p.ax[0], f);
+    ch = split_covers(p.ax[1], h);
+    nh = ch.n;
+    n = cf.n * ch.n;
+  }
+  // combo -> (i, lf, sf, j, lh, sh)
+  __device__ inline void get(int combo, int f, int h, int& i, int& lf, int& sf, int& j, int& lh, int& sh) const {
+    const int a = nh == 2 ? combo >> 1 : combo, c = nh == 2 ? combo & 1 : 0;
+    i = a ? cf.t1 : cf.t0;
+    lf = f - (a ? cf.a1 : cf.a0);
+    sf = a ? cf.s1 : cf.s0;
+    j = c ? ch.t1 : ch.t0;
+    lh = h - (c ? ch.a1 : ch.a0);
+    sh = c ? ch.s1 : ch.s0;
+  }
+};
+
+// First row (in tile-slot rows) of width cell 0 of line (b, combo) in tile
+// (i, j, iw): row of cell w is this + w.
+__device__ inline int64_t line_row0(const PlanDev& p, int b, int i, int lf, int j, int lh, int sh, int iw) {
+  const TileSlot s = tile_slot(p, i, j, iw);
+  const int sw = split_size(p.ax[2], iw);
+  return s.row_base + (int64_t)b * s.cap + (int64_t)(lf * sh + lh) * sw - split_start(p.ax[2], iw);
 }
 
 // ---------------------------------------------------------------------------
@@ -78,36 +138,63 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-// Offset (minimum start) and extent end (maximum end) of tile t, batch b,
-// axis d, from the per-chunk partials written by extents_kernel.
-__device__ inline float2 tile_extent(const PlanDev& p, const float* __restrict__ part, int t, int b, int d) {
-  const float* q = part + ((int64_t)(t * p.B + b) * p.chunks) * 6 + d * 2;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int c = 0; c < p.chunks; ++c) {
-    lo = fminf(lo, q[c * 6]);
-    hi = fmaxf(hi, q[c * 6 + 1]);
+// Block-wide (min of a, max of b), returned to every thread.  `red` is
+// kWaves float2 of shared memory.
+__device__ inline float2 block_minmax(float a, float b, float2* red) {
+  a = wave_min(a);
+  b = wave_max(b);
+  __syncthreads();  // earlier readers of red are done
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(a, b);
+  __syncthreads();
+  float2 r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    r.x = fminf(r.x, red[w].x);
+    r.y = fmaxf(r.y, red[w].y);
   }
-  return make_float2(lo, hi);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Walking a tile's generated tokens line by line
+// ---------------------------------------------------------------------------
+//
+// A tile's generated tokens form sf*sh lines of sw consecutive tokens.
+// Threads split into `groups` groups of `lanes` (= min(sw, 256)) lanes; a
+// group takes every groups-th line, its lanes the tokens of that line.  The
+// line -> (frame, row) split advances incrementally (no divisions).
+struct LineWalk {
+  int lanes, groups, g, lane;  // lane < lanes; g < groups when active
+  bool active;
+  int dlf, dlh;                // line step `groups` as (frames, rows)
+
+  __device__ inline void init(int sw, int sh) {
+    lanes = sw < kBlock ? sw : kBlock;
+    groups = kBlock / lanes;
+    g = threadIdx.x / lanes;
+    lane = threadIdx.x - g * lanes;
+    active = g < groups;
+    dlf = groups / sh;
+    dlh = groups - dlf * sh;
+  }
+};
+
+// Source offset (token index within one batch element, < N <= INT32_MAX)
+// of the start of local line (lf, lh) of a tile.
+__device__ inline int line_source(const PlanDev& p, const TileBox& tb, int lf, int lh) {
+  return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0;
 }
 
 // ---------------------------------------------------------------------------
 // bf16 / f32 vectors
 // ---------------------------------------------------------------------------
 
-__device__ inline uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Unpack one 16-byte input vector into E floats.
 template <int IN>  // IN = TDP_BF16 or TDP_F32
 struct InVec;
 template <>
 struct InVec<TDP_BF16> {
   static constexpr int E = 8;
-  __device__ static inline void unpack(const uint4& v, float* x) {
+  __device__ static inline void unpack(const u32x4& v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -119,7 +206,7 @@ struct InVec<TDP_BF16> {
 template <>
 struct InVec<TDP_F32> {
   static constexpr int E = 4;
-  __device__ static inline void unpack(const uint4& v, float* x) {
+  __device__ static inline void unpack(const u32x4& v, float* x) {
     x[0] = __uint_as_float(v.x);
     x[1] = __uint_as_float(v.y);
     x[2] = __uint_as_float(v.z);
@@ -127,332 +214,438 @@ struct InVec<TDP_F32> {
   }
 };
 
+// fp32 -> bf16, round to nearest even: gfx950's packed conversion
+// (v_cvt_pk_bf16_f32) converts two values per instruction.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Store E accumulated floats as the output dtype at element offset `e`.
 template <int OUT, int E>
 __device__ inline void store_out(void* out, int64_t e, const float* acc);
 template <>
 __device__ inline void store_out<TDP_BF16, 8>(void* out, int64_t e, const float* a) {
-  uint4 v;
-  v.x = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-  v.y = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-  v.z = bf16_rne(a[4]) | (bf16_rne(a[5]) << 16);
-  v.w = bf16_rne(a[6]) | (bf16_rne(a[7]) << 16);
-  *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + e) = v;
+  u32x4 v;
+  v.x = pack_bf16x2(a[0], a[1]);
+  v.y = pack_bf16x2(a[2], a[3]);
+  v.z = pack_bf16x2(a[4], a[5]);
+  v.w = pack_bf16x2(a[6], a[7]);
+  st_nt(reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + e), v);
 }
 template <>
 __device__ inline void store_out<TDP_BF16, 4>(void* out, int64_t e, const float* a) {
-  uint2 v;
-  v.x = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
-  v.y = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
-  *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + e) = v;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 v;
+  v.x = pack_bf16x2(a[0], a[1]);
+  v.y = pack_bf16x2(a[2], a[3]);
+  st_nt(reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + e), v);
 }
 template <>
 __device__ inline void store_out<TDP_F32, 8>(void* out, int64_t e, const float* a) {
-  float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e);
-  o[0] = make_float4(a[0], a[1], a[2], a[3]);
-  o[1] = make_float4(a[4], a[5], a[6], a[7]);
+  f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e);
+  st_nt(o, f32x4{a[0], a[1], a[2], a[3]});
+  st_nt(o + 1, f32x4{a[4], a[5], a[6], a[7]});
 }
 template <>
 __device__ inline void store_out<TDP_F32, 4>(void* out, int64_t e, const float* a) {
-  *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e) = make_float4(a[0], a[1], a[2], a[3]);
+  st_nt(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e), f32x4{a[0], a[1], a[2], a[3]});
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: per-chunk extents of every tile's generated positions.
-// grid (chunks, B, T).  Writes part[(t, b, chunk)] = 3 x {min start, max end}.
+// extract
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void extents_kernel(const PlanDev p, const float2* __restrict__ pos,
-                                                         float* __restrict__ part) {
-  const int ch = blockIdx.x, b = blockIdx.y, t = blockIdx.z;
-  int i, j, k;
-  tile_grid(p, t, i, j, k);
-  const int f0 = p.ax[0].start[i], h0 = p.ax[1].start[j], w0 = p.ax[2].start[k];
-  const int sh = p.ax[1].size[j], sw = p.ax[2].size[k];
-  const int lines = p.ax[0].size[i] * sh;
-  const int per = (lines + p.chunks - 1) / p.chunks;
-  const int l0 = min(lines, ch * per), l1 = min(lines, l0 + per);
-  const int count = (l1 - l0) * sw;
+struct ExtractArgs {
+  const u32x4* latent;   // (B, rows, V) vectors
+  const f32x2* pos;      // (B, 3, rows) [start, end)
+  u32x4* tile_lat;
+  f32x2* tile_pos;
+  int32_t* tile_index;
+  int32_t* tile_count;
+  int32_t* cond_row;     // (T, Nc)
+  const float2* ext;      // (T, B, 3, chunks) partial [min start, max end)
+  int n_sel, n_pos, pos_parts;
+};
 
-  float lo[3] = {INFINITY, INFINITY, INFINITY};
-  float hi[3] = {-INFINITY, -INFINITY, -INFINITY};
-  const float2* pb = pos + (int64_t)b * 3 * p.rows;
-  for (int e = threadIdx.x; e < count; e += kBlock) {
-    const int line = l0 + e / sw;
-    const int w = w0 + e % sw;
-    const int f = f0 + line / sh, h = h0 + line % sh;
-    const int64_t n = ((int64_t)f * p.H + h) * p.W + w;
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      const float2 v = pb[(int64_t)d * p.rows + n];
-      lo[d] = fminf(lo[d], v.x);
-      hi[d] = fmaxf(hi[d], v.y);
-    }
+// [min start, max end) of plane (t, b, d) from its extent partials.
+__device__ inline float2 plane_extent(const PlanDev& p, const float2* __restrict__ ext, int t, int b, int d) {
+  const float2* q = ext + ((int64_t)(t * p.B + b) * 3 + d) * p.ext_chunks;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int c = 0; c < p.ext_chunks; ++c) {
+    const float2 v = q[c];
+    lo = fminf(lo, v.x);
+    hi = fmaxf(hi, v.y);
   }
-  __shared__ float red[kWaves][6];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    const float a = wave_min(lo[d]);
-    const float c = wave_max(hi[d]);
-    if (lane == 0) {
-      red[wave][2 * d] = a;
-      red[wave][2 * d + 1] = c;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < 6) {
-    const int m = threadIdx.x;
-    float v = red[0][m];
-    for (int wv = 1; wv < kWaves; ++wv) v = (m & 1) ? fmaxf(v, red[wv][m]) : fminf(v, red[wv][m]);
-    part[((int64_t)(t * p.B + b) * p.chunks + ch) * 6 + m] = v;
-  }
+  return make_float2(lo, hi);
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 2: conditioning-token selection, one workgroup per tile.
-// Keeps token c when, for some batch element, its [start, end) overlaps
-// the tile's extent on all three axes, or its time start is negative;
-// compacts the kept tokens in ascending order (wave ballot + prefix).
-// ---------------------------------------------------------------------------
+// Row tables hold vector offsets, not pointers: a pointer read back from
+// LDS loses its address space and turns every access into a flat one.
+struct LineShared {
+  int64_t rowoff[kMaxCombos][kMaxTiles];  // tile_lat vector of cell w: rowoff + w*V + lane
+};
+struct SelShared {
+  int wave_tot[kWaves];
+  int kept_c[kSelChunk];     // kept tokens of this chunk, ascending
+  int base;                  // kept tokens of this tile before this chunk
+};
+union ExtractShared {
+  LineShared line;
+  SelShared sel;
+};
 
-__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const float2* __restrict__ pos,
-                                                        const float* __restrict__ part,
-                                                        int32_t* __restrict__ tile_index,
-                                                        int32_t* __restrict__ tile_count,
-                                                        int32_t* __restrict__ cond_row) {
-  extern __shared__ float ext[];  // [B][3][2]: extent start, end
-  __shared__ int wave_tot[kWaves];
-  const int t = blockIdx.x;
-  int i, j, k;
-  tile_grid(p, t, i, j, k);
-  const TileSlot s = tile_slot(p, i, j, k);
+// Extent workgroup: lines [l0, l1) of plane (t, b, d) -> one partial
+// [min start, max end).  Launched before the extract kernel proper, whose
+// position and selection workgroups combine the partials of their tile.
+__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const f32x2* __restrict__ pos,
+                                                        float2* __restrict__ ext) {
+  __shared__ float2 red[kWaves];
+  const int chunk = blockIdx.x % p.ext_chunks;
+  const int plane = blockIdx.x / p.ext_chunks;  // (t * B + b) * 3 + d
+  const int d = plane % 3, b = (plane / 3) % p.B, t = plane / (3 * p.B);
+  const TileBox tb = tile_box(p, t);
+  const int lines = tb.sf * tb.sh;
+  const int per = (lines + p.ext_chunks - 1) / p.ext_chunks;
+  const int l_begin = min(lines, chunk * per), l_end = min(lines, l_begin + per);
+  LineWalk lw;
+  lw.init(tb.sw, tb.sh);
+  const f32x2* src = pos + ((int64_t)b * 3 + d) * p.rows;
+  float lo = INFINITY, hi = -INFINITY;
+  if (lw.active) {
+    const int l_first = l_begin + lw.g;
+    int lf = l_first / tb.sh, lh = l_first - (l_first / tb.sh) * tb.sh;
+    for (int l0 = l_first; l0 < l_end; l0 += kExtUnroll * lw.groups) {
+      int n0[kExtUnroll];
+      bool ok[kExtUnroll];
+#pragma unroll
+      for (int u = 0; u < kExtUnroll; ++u) {
+        ok[u] = l0 + u * lw.groups < l_end;
+        n0[u] = line_source(p, tb, ok[u] ? lf : 0, ok[u] ? lh : 0);
+        lh += lw.dlh;
+        lf += lw.dlf;
+        if (lh >= tb.sh) {
+          lh -= tb.sh;
+          ++lf;
+        }
+      }
+      for (int x = lw.lane; x < tb.sw; x += lw.lanes) {
+        f32x2 v[kExtUnroll];
+#pragma unroll
+        for (int u = 0; u < kExtUnroll; ++u) v[u] = src[n0[u] + x];
+#pragma unroll
+        for (int u = 0; u < kExtUnroll; ++u) {
+          lo = ok[u] ? fminf(lo, v[u].x) : lo;
+          hi = ok[u] ? fmaxf(hi, v[u].y) : hi;
+        }
+      }
+    }
+  }
+  const float2 r = block_minmax(lo, hi, red);
+  if (threadIdx.x == 0) ext[blockIdx.x] = r;
+}
+
+// Selection workgroup: tile t, conditioning tokens [c0, c0 + kSelChunk).
+__device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, float* ext,
+                                  int t, int chunk) {
+  const TileBox tb = tile_box(p, t);
+
+  // 1. extent [min start, max end) of the tile on every (batch, axis).
   for (int e = threadIdx.x; e < p.B * 3; e += kBlock) {
-    const float2 x = tile_extent(p, part, t, e / 3, e % 3);
+    const float2 x = plane_extent(p, a.ext, t, e / 3, e % 3);
     ext[2 * e] = x.x;
     ext[2 * e + 1] = x.y;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int running = 0;
-  for (int c0 = 0; c0 < p.Nc; c0 += kBlock) {
-    const int c = c0 + threadIdx.x;
+
+  // 2. keep test.  The kept tokens before this chunk are counted again here
+  //    (cheap compares) so that chunks compact independently.
+  auto keeps = [&](int c) -> bool {
     bool keep = false;
-    if (c < p.Nc) {
-      for (int b = 0; b < p.B && !keep; ++b) {
-        const float2* pc = pos + (int64_t)b * 3 * p.rows + p.N + c;
-        const float2 x0 = pc[0], x1 = pc[p.rows], x2 = pc[2 * (int64_t)p.rows];
-        const float* e = ext + b * 6;
-        const bool inside = x0.x < e[1] && x0.y > e[0] && x1.x < e[3] && x1.y > e[2] && x2.x < e[5] && x2.y > e[4];
-        keep = inside || x0.x < 0.0f;
-      }
+    for (int b = 0; b < p.B && !keep; ++b) {
+      const f32x2* pc = a.pos + (int64_t)b * 3 * p.rows + p.N + c;
+      const f32x2 x0 = pc[0], x1 = pc[p.rows], x2 = pc[2 * (int64_t)p.rows];
+      const float* e = ext + b * 6;
+      const bool inside =
+          x0.x < e[1] && x0.y > e[0] && x1.x < e[3] && x1.y > e[2] && x2.x < e[5] && x2.y > e[4];
+      keep = inside || x0.x < 0.0f;
     }
-    const uint64_t m = __ballot(keep);
-    const int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __popcll(m);
-    __syncthreads();
-    int base = running;
-    for (int wv = 0; wv < wave; ++wv) base += wave_tot[wv];
-    int total = 0;
-    for (int wv = 0; wv < kWaves; ++wv) total += wave_tot[wv];
-    if (c < p.Nc) {
-      const int slot_row = s.gen + base + before;
-      cond_row[(int64_t)t * p.Nc + c] = keep ? slot_row : -1;
-      if (keep) tile_index[s.index_base + slot_row] = p.N + c;
-    }
-    running += total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) tile_count[t] = s.gen + running;
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 3: gather.  Three kinds of workgroups in one launch:
-//   [0, n_line)                 one (b, f, h) line of the latent: read every
-//                               latent row once and write it to each tile
-//                               that covers it, with shifted positions and
-//                               the source index;
-//   [n_line, n_line + n_cond)   kept conditioning rows of one tile;
-//   [.., + n_k)                 k = number of tiles keeping each token.
-// ---------------------------------------------------------------------------
-
-struct LineTables {
-  int ncombo;
-  int64_t row[kMaxCombos][kMaxTiles];    // tile_lat row of cell w = row + w
-  int64_t pos2[kMaxCombos][kMaxTiles];   // tile_pos float2 of axis 0, cell w
-  int64_t idx[kMaxCombos][kMaxTiles];    // tile_index entry of cell w
-  int32_t cap[kMaxCombos][kMaxTiles];
-  float off[kMaxCombos][kMaxTiles][3];
-};
-
-__global__ __launch_bounds__(kBlock) void gather_kernel(const PlanDev p, const uint4* __restrict__ latent,
-                                                        const float2* __restrict__ pos,
-                                                        const float* __restrict__ part,
-                                                        uint4* __restrict__ tile_lat,
-                                                        float2* __restrict__ tile_pos,
-                                                        int32_t* __restrict__ tile_index,
-                                                        int32_t* __restrict__ tile_count,
-                                                        const int32_t* __restrict__ cond_row,
-                                                        int32_t* __restrict__ cond_k, int n_line, int n_cond) {
-  extern __shared__ int wcov[];  // [W] packed covering width tiles
-  __shared__ LineTables tb;
-  const int bid = blockIdx.x;
-  const int V = p.vin;
-  const int rpp = kBlock / V;  // rows per pass
-  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
-  const bool lane_on = r < rpp;
-
-  if (bid < n_line) {
-    if (bid == 0 && p.Nc == 0) {
-      for (int t = threadIdx.x; t < p.T; t += kBlock) {
-        int i, j, k;
-        tile_grid(p, t, i, j, k);
-        tile_count[t] = p.ax[0].size[i] * p.ax[1].size[j] * p.ax[2].size[k];
-      }
-    }
-    const int b = bid / (p.F * p.H);
-    const int fh = bid - b * (p.F * p.H);
-    const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
-    int fi[2], fl[2], hi[2], hl[2];
-    const int nf = axis_covers(p.ax[0], f, fi, fl);
-    const int nh = axis_covers(p.ax[1], h, hi, hl);
-    const int nw = p.ax[2].n;
-    for (int w = threadIdx.x; w < p.W; w += kBlock) {
-      int ti[2], tl[2];
-      const int c = axis_covers(p.ax[2], w, ti, tl);
-      wcov[w] = pack_covers(c, ti);
-    }
-    for (int e = threadIdx.x; e < nf * nh * nw; e += kBlock) {
-      const int combo = e / nw, iw = e - (e / nw) * nw;
-      const int cf = combo / nh, chh = combo - (combo / nh) * nh;
-      const int i = fi[cf], j = hi[chh];
-      const TileSlot s = tile_slot(p, i, j, iw);
-      const int64_t local = (int64_t)(fl[cf] * p.ax[1].size[j] + hl[chh]) * p.ax[2].size[iw] - p.ax[2].start[iw];
-      tb.row[combo][iw] = s.row_base + (int64_t)b * s.cap + local;
-      tb.pos2[combo][iw] = 3 * s.row_base + (int64_t)b * 3 * s.cap + local;
-      tb.idx[combo][iw] = s.index_base + local;
-      tb.cap[combo][iw] = s.cap;
-      const int t = (i * p.ax[1].n + j) * nw + iw;
-#pragma unroll
-      for (int d = 0; d < 3; ++d) tb.off[combo][iw][d] = p.normalize ? tile_extent(p, part, t, b, d).x : 0.0f;
-    }
-    if (threadIdx.x == 0) tb.ncombo = nf * nh;
-    __syncthreads();
-    const int ncombo = tb.ncombo;
-    const int64_t src0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
-
-    // latent rows
-    for (int wb = 0; wb < p.W; wb += rpp * kGatherUnroll) {
-      uint4 v[kGatherUnroll];
-      int w[kGatherUnroll];
-#pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        w[u] = wb + u * rpp + r;
-        if (lane_on && w[u] < p.W) v[u] = latent[(src0 + w[u]) * V + vv];
-      }
-#pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        if (!(lane_on && w[u] < p.W)) continue;
-        const int cov = wcov[w[u]];
-        for (int q = 0; q < 2; ++q) {
-          const int iw = (cov >> (8 * q)) & 0xFF;
-          if (iw == kNoTile) break;
-          for (int cb = 0; cb < ncombo; ++cb) tile_lat[(tb.row[cb][iw] + w[u]) * V + vv] = v[u];
-        }
-      }
-    }
-    // positions and source indices
-    const int64_t nline = ((int64_t)f * p.H + h) * p.W;
-    for (int e = threadIdx.x; e < 3 * p.W; e += kBlock) {
-      const int d = e / p.W, w = e - (e / p.W) * p.W;
-      const float2 pv = pos[((int64_t)b * 3 + d) * p.rows + nline + w];
-      const int cov = wcov[w];
-      for (int q = 0; q < 2; ++q) {
-        const int iw = (cov >> (8 * q)) & 0xFF;
-        if (iw == kNoTile) break;
-        for (int cb = 0; cb < ncombo; ++cb) {
-          const float o = tb.off[cb][iw][d];
-          tile_pos[tb.pos2[cb][iw] + (int64_t)d * tb.cap[cb][iw] + w] = make_float2(pv.x - o, pv.y - o);
-          if (b == 0 && d == 0) tile_index[tb.idx[cb][iw] + w] = (int32_t)(nline + w);
-        }
-      }
-    }
-    return;
-  }
-
-  if (bid < n_line + n_cond) {
-    // kept conditioning rows of one tile
-    const int per_tile = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
-    const int cid = bid - n_line;
-    const int t = cid / per_tile;
-    const int j0 = (cid - t * per_tile) * kCondRowsPerBlock;
-    int i, j, k;
-    tile_grid(p, t, i, j, k);
-    const TileSlot s = tile_slot(p, i, j, k);
-    const int kept = tile_count[t] - s.gen;
-    if (j0 >= kept) return;
-    const int nrows = min(kCondRowsPerBlock, kept - j0);
-    float* off = reinterpret_cast<float*>(wcov);  // [B][3]
-    for (int e = threadIdx.x; e < p.B * 3; e += kBlock)
-      off[e] = p.normalize ? tile_extent(p, part, t, e / 3, e % 3).x : 0.0f;
-    __syncthreads();
-    const int32_t* srcidx = tile_index + s.index_base + s.gen + j0;
-    // latent: rows (b, jj) flattened
-    const int total = p.B * nrows;
-    for (int e = r; e < total; e += rpp) {
-      if (!lane_on) break;
-      const int b = e / nrows, jj = e - (e / nrows) * nrows;
-      const int64_t src = (int64_t)b * p.rows + srcidx[jj];
-      const int64_t dst = s.row_base + (int64_t)b * s.cap + s.gen + j0 + jj;
-      tile_lat[dst * V + vv] = latent[src * V + vv];
-    }
-    for (int e = threadIdx.x; e < total * 3; e += kBlock) {
-      const int jj = e % nrows, bd = e / nrows;  // bd = b*3 + d
-      const int b = bd / 3, d = bd - (bd / 3) * 3;
-      const float2 pv = pos[(int64_t)bd * p.rows + srcidx[jj]];
-      const float o = off[b * 3 + d];
-      tile_pos[3 * s.row_base + ((int64_t)b * 3 + d) * s.cap + s.gen + j0 + jj] = make_float2(pv.x - o, pv.y - o);
-    }
-    return;
-  }
-
-  // k per conditioning token
-  const int c = (bid - n_line - n_cond) * kBlock + threadIdx.x;
+    return keep;
+  };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = chunk * kSelChunk;
+  int before = 0;
+  for (int c = threadIdx.x; c < c0; c += kBlock) before += keeps(c) ? 1 : 0;
+  for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
+  if (lane == 0) sm.sel.wave_tot[wave] = before;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm.sel.base = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
+  __syncthreads();
+  const int base = sm.sel.base;
+  const int c = c0 + threadIdx.x;
+  const bool keep = c < p.Nc && keeps(c);
+  const uint64_t mask = __ballot(keep);
+  const int in_wave = __popcll(mask & ((1ull << lane) - 1ull));
+  __syncthreads();  // wave_tot reuse
+  if (lane == 0) sm.sel.wave_tot[wave] = __popcll(mask);
+  __syncthreads();
+  int offset = 0;
+  for (int w = 0; w < wave; ++w) offset += sm.sel.wave_tot[w];
+  const int n_kept = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
+  const int idx = offset + in_wave;  // rank of c among this chunk's kept tokens
   if (c < p.Nc) {
-    int kc = 0;
-    for (int t = 0; t < p.T; ++t) kc += cond_row[(int64_t)t * p.Nc + c] >= 0;
-    cond_k[c] = kc;
+    const int row = tb.s.gen + base + idx;
+    a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
+    if (keep) {
+      a.tile_index[tb.s.index_base + row] = p.N + c;
+      sm.sel.kept_c[idx] = c;
+    }
+  }
+  const bool last_chunk = c0 + kSelChunk >= p.Nc;
+  if (last_chunk && threadIdx.x == 0) a.tile_count[t] = tb.s.gen + base + n_kept;
+  __syncthreads();
+
+  // 3. copy the kept rows: latent vectors, then shifted positions.
+  const int V = p.vin;
+  const int rpp = kBlock / V;
+  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int total = n_kept * p.B;
+  if (r < rpp) {
+    for (int e = r; e < total; e += rpp) {
+      const int b = e / n_kept, j = e - (e / n_kept) * n_kept;
+      const int cc = sm.sel.kept_c[j];
+      const int64_t src = (int64_t)b * p.rows + p.N + cc;
+      const int64_t dst = tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + j;
+      st_nt(a.tile_lat + dst * V + vv, ld_nt(a.latent + src * V + vv));
+    }
+  }
+  for (int e = threadIdx.x; e < total * 3; e += kBlock) {
+    const int j = e % n_kept, bd = e / n_kept;  // bd = b * 3 + d
+    const int cc = sm.sel.kept_c[j];
+    const f32x2 v = a.pos[(int64_t)bd * p.rows + p.N + cc];
+    const float o = p.normalize ? ext[bd * 2] : 0.0f;
+    const int b = bd / 3, d = bd - (bd / 3) * 3;
+    st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v - o);
   }
 }
 
-// ---------------------------------------------------------------------------
-// Kernel 4: blend.  Owner computes: each output row sums its covering tiles
-// in ascending tile order, fp32 accumulation, one store.
-//   [0, n_line)   one (b, f, h) line of generated tokens;
-//   [n_line, ..)  kCondRowsPerBlock conditioning rows of one batch element.
-// ---------------------------------------------------------------------------
+// Positions workgroup: tile t, batch b, axis d, part `part` of the lines:
+// the shifted [start, end) pairs and source indices of those lines.  The
+// shift is the tile's minimum start on this plane, from the extent partials.
+__device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t, int b, int d, int part) {
+  const TileBox tb = tile_box(p, t);
+  const int lines = tb.sf * tb.sh;
+  LineWalk lw;
+  lw.init(tb.sw, tb.sh);
+  const f32x2* src = a.pos + ((int64_t)b * 3 + d) * p.rows;
+  const float off = p.normalize ? plane_extent(p, a.ext, t, b, d).x : 0.0f;
 
-struct BlendTables {
-  int ncombo;
-  float wfh[kMaxCombos];                 // frames x height weight of the combo
-  int64_t row[kMaxCombos][kMaxTiles];    // tile_out row of cell w = row + w
-};
+  // pass 2: shifted positions (and source indices) of this part's lines
+  const int per = (lines + a.pos_parts - 1) / a.pos_parts;
+  const int l_begin = min(lines, part * per), l_end = min(lines, l_begin + per);
+  if (part == 0 && b == 0 && d == 0 && p.Nc == 0 && threadIdx.x == 0) a.tile_count[t] = tb.s.gen;
+  if (!lw.active) return;
+  f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
+  int32_t* idx = a.tile_index + tb.s.index_base;
+  const bool write_index = (b == 0 && d == 0);
+  const int l_first = l_begin + lw.g;
+  int lf = l_first / tb.sh, lh = l_first - (l_first / tb.sh) * tb.sh;
+  for (int l0 = l_first; l0 < l_end; l0 += kPosUnroll * lw.groups) {
+    int n0[kPosUnroll];
+    bool ok[kPosUnroll];
+#pragma unroll
+    for (int u = 0; u < kPosUnroll; ++u) {
+      ok[u] = l0 + u * lw.groups < l_end;
+      n0[u] = line_source(p, tb, ok[u] ? lf : 0, ok[u] ? lh : 0);
+      lh += lw.dlh;
+      lf += lw.dlf;
+      if (lh >= tb.sh) {
+        lh -= tb.sh;
+        ++lf;
+      }
+    }
+    for (int x = lw.lane; x < tb.sw; x += lw.lanes) {
+      f32x2 v[kPosUnroll];
+#pragma unroll
+      for (int u = 0; u < kPosUnroll; ++u) v[u] = ld_nt(src + n0[u] + x);
+#pragma unroll
+      for (int u = 0; u < kPosUnroll; ++u) {
+        if (ok[u]) {
+          const int row = (l0 + u * lw.groups) * tb.sw + x;
+          st_nt(dst + row, v[u] - off);
+          if (write_index) st_nt(idx + row, (int32_t)(n0[u] + x));
+        }
+      }
+    }
+  }
+}
 
-template <int IN, int OUT, int NCM>
-__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const uint4* __restrict__ tile_out,
-                                                       const int32_t* __restrict__ cond_row,
-                                                       const int32_t* __restrict__ cond_k, void* __restrict__ out,
-                                                       int n_line) {
-  constexpr int E = InVec<IN>::E;
-  // Rows in flight per lane: keeps (rows x covering tiles) loads near 16.
-  constexpr int U = NCM >= 4 ? 2 : 4;
-  extern __shared__ int smem[];  // wcov[W] then wgt[W] (float2)
-  __shared__ BlendTables tb;
-  const int bid = blockIdx.x;
+// Latent workgroup: one (b, f, h) line, every row read once and written to
+// each covering tile.  Source addresses need no tables, so the first pass's
+// loads are issued before the cover and row tables are built: the table
+// setup runs while those loads are in flight.
+__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int* wcov, int line) {
+  const int b = line / (p.F * p.H);
+  const int fh = line - b * (p.F * p.H);
+  const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
   const int V = p.vin;
   const int rpp = kBlock / V;
   const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
   const bool lane_on = r < rpp;
+  const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W) * V + vv;
+
+  u32x4 v[kLatUnroll];
+  int wv[kLatUnroll];
+  bool ok[kLatUnroll];
+#pragma unroll
+  for (int u = 0; u < kLatUnroll; ++u) {
+    const int w = u * rpp + r;
+    ok[u] = lane_on && w < p.W;
+    wv[u] = ok[u] ? w : 0;
+    v[u] = ld_nt(src + wv[u] * V);
+  }
+
+  LineCombos lc;
+  lc.init(p, f, h);
+  const int nw = p.ax[2].n;
+  for (int w = threadIdx.x; w < p.W; w += kBlock) {
+    const Covers c = split_covers(p.ax[2], w);
+    wcov[w] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
+  }
+  for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
+    const int combo = e / nw, iw = e - (e / nw) * nw;
+    int i, lf, sf, j, lh, sh;
+    lc.get(combo, f, h, i, lf, sf, j, lh, sh);
+    sm.line.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
+  }
+  __syncthreads();
+  const int ncombo = lc.n;
+  for (int wb = 0;;) {
+    int cov[kLatUnroll];
+#pragma unroll
+    for (int u = 0; u < kLatUnroll; ++u) cov[u] = wcov[wv[u]];
+    for (int cb = 0; cb < ncombo; ++cb) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int u = 0; u < kLatUnroll; ++u) {
+          const int iw = (cov[u] >> (8 * q)) & 0xFF;
+          if (ok[u] && iw != kNoTile) st_nt(a.tile_lat + sm.line.rowoff[cb][iw] + wv[u] * V + vv, v[u]);
+        }
+      }
+    }
+    wb += rpp * kLatUnroll;
+    if (wb >= p.W) break;
+#pragma unroll
+    for (int u = 0; u < kLatUnroll; ++u) {
+      const int w = wb + u * rpp + r;
+      ok[u] = lane_on && w < p.W;
+      wv[u] = ok[u] ? w : 0;
+      v[u] = ld_nt(src + wv[u] * V);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
+  extern __shared__ float dyn[];  // selection: ext[B][3][2]; latent: wcov[W]
+  __shared__ ExtractShared sm;
+  int bid = blockIdx.x;
+  if (bid < a.n_sel) {
+    const int per_tile = (p.Nc + kSelChunk - 1) / kSelChunk;
+    extract_selection(p, a, sm, dyn, bid / per_tile, bid - (bid / per_tile) * per_tile);
+    return;
+  }
+  bid -= a.n_sel;
+  if (bid < a.n_pos) {
+    const int part = bid % a.pos_parts;
+    int rest = bid / a.pos_parts;
+    const int d = rest % 3;
+    rest /= 3;
+    const int b = rest % p.B;
+    const int t = rest / p.B;
+    extract_positions(p, a, t, b, d, part);
+    return;
+  }
+  extract_latent(p, a, sm, reinterpret_cast<int*>(dyn), bid - a.n_pos);
+}
+
+// ---------------------------------------------------------------------------
+// blend
+// ---------------------------------------------------------------------------
+
+struct BlendShared {
+  int64_t rowoff[kMaxCombos][kMaxTiles];  // tile_out vector of cell w: rowoff + w*V + lane
+  float wfh[kMaxCombos];                  // frames x height weight of the combo
+};
+
+// One (b, f, h) line of generated tokens with exactly NC frame x height
+// combos.  Width covers: the first always exists; a missing second one
+// re-reads the first row and is masked out of the sum.
+template <int IN, int OUT, int NC>
+__device__ void blend_line_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
+                                const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0) {
+  constexpr int E = InVec<IN>::E;
+  // rows per pass: 8 loads in flight per lane (2 per combo and row)
+  constexpr int U = 4 / NC;
+  const int V = p.vin;
+  const int rpp = kBlock / V;
+  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const bool lane_on = r < rpp;
+  for (int wb = 0; wb < p.W; wb += rpp * U) {
+    u32x4 y0[U][NC], y1[U][NC];
+    int wv[U];
+    bool ok[U], has1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = wb + u * rpp + r;
+      ok[u] = lane_on && w < p.W;
+      wv[u] = ok[u] ? w : 0;
+      const int cov = wcov[wv[u]];
+      const int iw0 = cov & 0xFF, iw1 = (cov >> 8) & 0xFF;
+      has1[u] = iw1 != kNoTile;
+      const int iw1s = has1[u] ? iw1 : iw0;
+      const int64_t off = (int64_t)wv[u] * V + vv;
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        y0[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw0] + off);
+        y1[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw1s] + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float2 ww = wgt[wv[u]];
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+      // ascending tile index: combos ascend in (i_f, i_h), then i_w
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        const float w0 = sm.wfh[cb] * ww.x;
+        const float w1 = sm.wfh[cb] * ww.y;
+        float x0[E], x1[E];
+        InVec<IN>::unpack(y0[u][cb], x0);
+        InVec<IN>::unpack(y1[u][cb], x1);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(w0, x0[e], acc[e]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = has1[u] ? fmaf(w1, x1[e], acc[e]) : acc[e];
+      }
+      if (ok[u]) store_out<OUT, E>(out, ((dst0 + wv[u]) * V + vv) * (int64_t)E, acc);
+    }
+  }
+}
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
+                                                       const int32_t* __restrict__ cond_row,
+                                                       void* __restrict__ out, int n_line) {
+  constexpr int E = InVec<IN>::E;
+  extern __shared__ int smem[];  // wcov[W] then wgt[W] (float2)
+  __shared__ BlendShared sm;
+  const int bid = blockIdx.x;
+  const int V = p.vin;
 
   if (bid < n_line) {
     int* wcov = smem;
@@ -460,88 +653,47 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const ui
     const int b = bid / (p.F * p.H);
     const int fh = bid - b * (p.F * p.H);
     const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
-    int fi[2], fl[2], hi[2], hl[2];
-    const int nf = axis_covers(p.ax[0], f, fi, fl);
-    const int nh = axis_covers(p.ax[1], h, hi, hl);
+    LineCombos lc;
+    lc.init(p, f, h);
     const int nw = p.ax[2].n;
     for (int w = threadIdx.x; w < p.W; w += kBlock) {
-      int ti[2], tl[2];
-      const int c = axis_covers(p.ax[2], w, ti, tl);
-      wcov[w] = pack_covers(c, ti);
-      wgt[w] = make_float2(c > 0 ? axis_weight(p.ax[2], ti[0], tl[0]) : 0.0f,
-                           c > 1 ? axis_weight(p.ax[2], ti[1], tl[1]) : 0.0f);
+      const Covers c = split_covers(p.ax[2], w);
+      wcov[w] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
+      wgt[w] = make_float2(ramp_weight(p.ax[2], c.t0, w - c.a0, c.s0),
+                           c.n > 1 ? ramp_weight(p.ax[2], c.t1, w - c.a1, c.s1) : 0.0f);
     }
-    for (int e = threadIdx.x; e < nf * nh * nw; e += kBlock) {
+    for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
       const int combo = e / nw, iw = e - (e / nw) * nw;
-      const int cf = combo / nh, chh = combo - (combo / nh) * nh;
-      const int i = fi[cf], j = hi[chh];
-      const TileSlot s = tile_slot(p, i, j, iw);
-      const int64_t local = (int64_t)(fl[cf] * p.ax[1].size[j] + hl[chh]) * p.ax[2].size[iw] - p.ax[2].start[iw];
-      tb.row[combo][iw] = s.row_base + (int64_t)b * s.cap + local;
-      if (iw == 0) tb.wfh[combo] = axis_weight(p.ax[0], i, fl[cf]) * axis_weight(p.ax[1], j, hl[chh]);
+      int i, lf, sf, j, lh, sh;
+      lc.get(combo, f, h, i, lf, sf, j, lh, sh);
+      sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
+      if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
     }
-    if (threadIdx.x == 0) tb.ncombo = nf * nh;
     __syncthreads();
-    const int ncombo = tb.ncombo;
     const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
-    for (int wb = 0; wb < p.W; wb += rpp * U) {
-      // All loads of U rows first, then the arithmetic in ascending tile
-      // order: combos ascend in (i_f, i_h), width covers in i_w.
-      uint4 y[U][2 * NCM];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int w = wb + u * rpp + r;
-        if (!(lane_on && w < p.W)) continue;
-        const int cov = wcov[w];
-#pragma unroll
-        for (int cb = 0; cb < NCM; ++cb) {
-          if (cb >= ncombo) break;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int iw = (cov >> (8 * q)) & 0xFF;
-            if (iw != kNoTile) y[u][2 * cb + q] = tile_out[(tb.row[cb][iw] + w) * V + vv];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int w = wb + u * rpp + r;
-        if (!(lane_on && w < p.W)) continue;
-        const int cov = wcov[w];
-        const float2 ww = wgt[w];
-        float acc[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-#pragma unroll
-        for (int cb = 0; cb < NCM; ++cb) {
-          if (cb >= ncombo) break;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int iw = (cov >> (8 * q)) & 0xFF;
-            if (iw == kNoTile) continue;
-            const float wt = tb.wfh[cb] * (q == 0 ? ww.x : ww.y);
-            float x[E];
-            InVec<IN>::unpack(y[u][2 * cb + q], x);
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
-          }
-        }
-        store_out<OUT, E>(out, ((dst0 + w) * V + vv) * (int64_t)E, acc);
-      }
-    }
+    const int nc = lc.n;
+    if (nc == 1)
+      blend_line_rows<IN, OUT, 1>(p, sm, wcov, wgt, tile_out, out, dst0);
+    else if (nc == 2)
+      blend_line_rows<IN, OUT, 2>(p, sm, wcov, wgt, tile_out, out, dst0);
+    else
+      blend_line_rows<IN, OUT, 4>(p, sm, wcov, wgt, tile_out, out, dst0);
     return;
   }
 
-  // conditioning rows: (1/k) * sum over the tiles that keep the token
+  // conditioning rows: (1/k) * sum over the k tiles that keep the token
+  const int rpp = kBlock / V;
+  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  if (r >= rpp) return;
   const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
   const int cid = bid - n_line;
   const int b = cid / per_b;
   const int c0 = (cid - b * per_b) * kCondRowsPerBlock;
   const int nrows = min(kCondRowsPerBlock, p.Nc - c0);
   for (int jj = r; jj < nrows; jj += rpp) {
-    if (!lane_on) break;
     const int c = c0 + jj;
-    const int kc = cond_k[c];
+    int kc = 0;
+    for (int t = 0; t < p.T; ++t) kc += cond_row[(int64_t)t * p.Nc + c] >= 0;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
@@ -554,7 +706,7 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const ui
         tile_grid(p, t, i, j, k);
         const TileSlot s = tile_slot(p, i, j, k);
         if (row >= s.cap) continue;  // not a row tdp_extract could have written
-        const uint4 yv = tile_out[(s.row_base + (int64_t)b * s.cap + row) * V + vv];
+        const u32x4 yv = ld_nt(tile_out + (s.row_base + (int64_t)b * s.cap + row) * V + vv);
         float x[E];
         InVec<IN>::unpack(yv, x);
 #pragma unroll
@@ -566,20 +718,12 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const ui
 }
 
 template <int IN, int OUT>
-hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
-                        void* out, hipStream_t s) {
+hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
   const int n_line = p.B * p.F * p.H;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
   const size_t lds = (size_t)((p.W + 1) & ~1) * sizeof(int) + (size_t)p.W * sizeof(float2);
-  const int ncm = (p.ax[0].n > 1 ? 2 : 1) * (p.ax[1].n > 1 ? 2 : 1);
-  const dim3 grid(n_line + n_cond), block(kBlock);
-  const uint4* y = reinterpret_cast<const uint4*>(tile_out);
-  if (ncm == 1)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, 1>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_line);
-  else if (ncm == 2)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, 2>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_line);
-  else
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, 4>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_line);
+  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_line + n_cond), dim3(kBlock), lds, s, p,
+                     reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_line);
   return hipGetLastError();
 }
 
@@ -593,67 +737,66 @@ using namespace tdp;
 extern "C" {
 
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
-                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, void* workspace,
-                void* stream) {
+                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, void* workspace, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_extract: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_extract: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (!latent || !pos || !tile_lat || !tile_pos || !tile_index || !tile_count)
     return fail(TDP_EINVAL, "tdp_extract: null device pointer");
-  if (p.Nc > 0 && (!cond_row || !cond_k))
-    return fail(TDP_EINVAL, "tdp_extract: cond_row and cond_k are required when num_cond > 0");
+  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_extract: cond_row is required when num_cond > 0");
   const bool need_ext = p.normalize || p.Nc > 0;
   if (need_ext && !workspace) return fail(TDP_EINVAL, "tdp_extract: null workspace");
+  if (!aligned(workspace, 8)) return fail(TDP_EINVAL, "tdp_extract: workspace must be 8-byte aligned");
   if (!aligned(latent, 16) || !aligned(tile_lat, 16))
     return fail(TDP_EINVAL, "tdp_extract: latent and tile_lat must be 16-byte aligned");
-  if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(workspace, 4) || !aligned(tile_index, 4) ||
-      !aligned(tile_count, 4) || !aligned(cond_row, 4) || !aligned(cond_k, 4))
-    return fail(TDP_EINVAL, "tdp_extract: pos/tile_pos need 8-byte and int/float buffers 4-byte alignment");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const float2* pos2 = reinterpret_cast<const float2*>(pos);
-  float* part = reinterpret_cast<float*>(workspace);
-  if (need_ext) {
-    hipLaunchKernelGGL(extents_kernel, dim3(p.chunks, p.B, p.T), dim3(kBlock), 0, s, p, pos2, part);
-  }
-  if (p.Nc > 0) {
-    hipLaunchKernelGGL(select_kernel, dim3(p.T), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s, p, pos2, part,
-                       tile_index, tile_count, cond_row);
-  }
+  if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
+      !aligned(cond_row, 4))
+    return fail(TDP_EINVAL, "tdp_extract: pos/tile_pos need 8-byte and int buffers 4-byte alignment");
+  ExtractArgs a;
+  a.latent = reinterpret_cast<const u32x4*>(latent);
+  a.pos = reinterpret_cast<const f32x2*>(pos);
+  a.tile_lat = reinterpret_cast<u32x4*>(tile_lat);
+  a.tile_pos = reinterpret_cast<f32x2*>(tile_pos);
+  a.tile_index = tile_index;
+  a.tile_count = tile_count;
+  a.cond_row = cond_row;
+  a.ext = reinterpret_cast<const float2*>(workspace);
+  a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
+  a.pos_parts = p.pos_parts;
+  a.n_pos = p.T * p.B * 3 * p.pos_parts;
   const int n_line = p.B * p.F * p.H;
-  const int n_cond = p.Nc > 0 ? p.T * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
-  const int n_k = p.Nc > 0 ? (p.Nc + kBlock - 1) / kBlock : 0;
   size_t lds = (size_t)p.W * sizeof(int);
-  const size_t lds_cond = (size_t)p.B * 3 * sizeof(float);
-  if (lds_cond > lds) lds = lds_cond;
-  hipLaunchKernelGGL(gather_kernel, dim3(n_line + n_cond + n_k), dim3(kBlock), lds, s, p,
-                     reinterpret_cast<const uint4*>(latent), pos2, part, reinterpret_cast<uint4*>(tile_lat),
-                     reinterpret_cast<float2*>(tile_pos), tile_index, tile_count, cond_row, cond_k, n_line, n_cond);
+  const size_t lds_sel = (size_t)p.B * 6 * sizeof(float);
+  if (lds_sel > lds) lds = lds_sel;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (need_ext)
+    hipLaunchKernelGGL(extent_kernel, dim3(p.T * p.B * 3 * p.ext_chunks), dim3(kBlock), 0, s, p, a.pos,
+                       reinterpret_cast<float2*>(workspace));
+  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_line), dim3(kBlock), lds, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
 }
 
-int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k, void* out,
-              void* stream) {
+int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, void* out, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_blend: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (!tile_out || !out) return fail(TDP_EINVAL, "tdp_blend: null device pointer");
-  if (p.Nc > 0 && (!cond_row || !cond_k))
-    return fail(TDP_EINVAL, "tdp_blend: cond_row and cond_k are required when num_cond > 0");
+  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend: cond_row is required when num_cond > 0");
   if (!aligned(tile_out, 16) || !aligned(out, 16))
     return fail(TDP_EINVAL, "tdp_blend: tile_out and out must be 16-byte aligned");
-  if (!aligned(cond_row, 4) || !aligned(cond_k, 4)) return fail(TDP_EINVAL, "tdp_blend: misaligned int buffers");
+  if (!aligned(cond_row, 4)) return fail(TDP_EINVAL, "tdp_blend: misaligned cond_row");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
-    e = launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, out, s);
   else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, out, s);
   else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, out, s);
   else
-    e = launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, out, s);
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
 }

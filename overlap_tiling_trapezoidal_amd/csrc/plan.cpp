@@ -42,15 +42,16 @@ int dtype_bytes(int32_t dtype) {
 
 static const char* kAxisName[3] = {"frames", "height", "width"};
 
-// Validate one axis and fill its intervals.  The split: a_i =
-// floor(i*(dim-o)/n), tile i = [a_i, a_{i+1} + o), so neighbours overlap by
-// exactly o cells and the last tile ends at dim.
-static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisDev* ax) {
+// Validate one axis.  The split itself (a_i = floor(i*(dim-o)/n), tile i =
+// [a_i, a_{i+1} + o)) is the closed form in plan_internal.h, shared with the
+// kernels: neighbours overlap by exactly o cells and the last tile ends at dim.
+static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisSplit* ax) {
   const char* name = kAxisName[d];
   if (t.num_tiles < 1) return fail(TDP_EINVAL, "%s: num_tiles must be >= 1 (got %d)", name, t.num_tiles);
   if (t.overlap < 0) return fail(TDP_EINVAL, "%s: overlap must be >= 0 (got %d)", name, t.overlap);
-  if (t.num_tiles > kMaxTiles)
-    return fail(TDP_ESHAPE, "%s: %d tiles exceed the limit of %d per axis", name, t.num_tiles, kMaxTiles);
+  if (t.num_tiles > TDP_MAX_TILES_PER_AXIS)
+    return fail(TDP_ESHAPE, "%s: %d tiles exceed the limit of %d per axis", name, t.num_tiles,
+                TDP_MAX_TILES_PER_AXIS);
   if (t.num_tiles == 1 && t.overlap != 0)
     return fail(TDP_EGUARD, "%s: an untiled axis (1 tile) must request overlap 0 (got %d)", name, t.overlap);
   const int64_t free_len = (int64_t)dim - t.overlap;
@@ -64,22 +65,13 @@ static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisD
                 "%s: overlap %d exceeds dim/(n+1) = %d/%d, so three windows would stack; "
                 "reduce overlap on %s to <= %d or use fewer tiles",
                 name, t.overlap, dim, t.num_tiles + 1, name, dim / (t.num_tiles + 1));
+  if (dim > TDP_MAX_AXIS)
+    return fail(TDP_ESHAPE, "%s: %d cells exceed the limit of %d per axis", name, dim, TDP_MAX_AXIS);
   ax->dim = dim;
   ax->n = t.num_tiles;
   ax->o = t.overlap;
-  ax->pre[0] = 0;
-  for (int i = 0; i < t.num_tiles; ++i) {
-    const int64_t a = (int64_t)i * free_len / t.num_tiles;
-    const int64_t a_next = (int64_t)(i + 1) * free_len / t.num_tiles;
-    ax->start[i] = (int32_t)a;
-    ax->size[i] = (int32_t)(a_next + t.overlap - a);
-    ax->pre[i + 1] = ax->pre[i] + ax->size[i];
-  }
-  for (int i = t.num_tiles; i < kMaxTiles; ++i) {
-    ax->start[i] = 0;
-    ax->size[i] = 0;
-    ax->pre[i + 1] = ax->pre[i];
-  }
+  ax->by_n = make_fastdiv((uint32_t)t.num_tiles);
+  ax->by_s = make_fastdiv((uint32_t)free_len);
   return TDP_OK;
 }
 
@@ -138,24 +130,31 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
 
   // Tile slots: sum over tiles of capacity = (sum of gen) + T * Nc.
   const int64_t total_gen =
-      (int64_t)dev.ax[0].pre[dev.ax[0].n] * dev.ax[1].pre[dev.ax[1].n] * dev.ax[2].pre[dev.ax[2].n];
+      (int64_t)split_total(dev.ax[0]) * split_total(dev.ax[1]) * split_total(dev.ax[2]);
   const int64_t total_index = total_gen + (int64_t)dev.T * c.num_cond;
   if (total_index * c.batch > INT32_MAX)
     return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
                 (long long)(total_index * c.batch));
 
-  // Extent partials: enough chunks that each covers about 2048 tokens.
+  // Position workgroups: each shifts about 2048 tokens of one (tile, batch
+  // element, axis).
   int64_t max_gen = 0;
   for (int i = 0; i < dev.ax[0].n; ++i)
     for (int j = 0; j < dev.ax[1].n; ++j)
       for (int k = 0; k < dev.ax[2].n; ++k) {
-        const int64_t g = (int64_t)dev.ax[0].size[i] * dev.ax[1].size[j] * dev.ax[2].size[k];
+        const int64_t g =
+            (int64_t)split_size(dev.ax[0], i) * split_size(dev.ax[1], j) * split_size(dev.ax[2], k);
         if (g > max_gen) max_gen = g;
       }
-  int64_t chunks = (max_gen + 2047) / 2048;
+  int64_t parts = (max_gen + 2047) / 2048;
+  if (parts < 1) parts = 1;
+  if (parts > 32) parts = 32;
+  dev.pos_parts = (int32_t)parts;
+  // Extent partials: each reduces about 1024 tokens of one plane.
+  int64_t chunks = (max_gen + 1023) / 1024;
   if (chunks < 1) chunks = 1;
   if (chunks > 64) chunks = 64;
-  dev.chunks = (int32_t)chunks;
+  dev.ext_chunks = (int32_t)chunks;
 
   tdp_plan* p = new (std::nothrow) tdp_plan;
   if (!p) return fail(TDP_EINVAL, "out of host memory");
@@ -178,10 +177,10 @@ int tdp_plan_num_tiles(const tdp_plan* plan, int32_t* num_tiles) {
 int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t* ends) {
   if (!plan || !starts || !ends) return fail(TDP_EINVAL, "tdp_plan_intervals: null argument");
   if (axis < 0 || axis > 2) return fail(TDP_EINVAL, "axis must be 0, 1 or 2 (got %d)", axis);
-  const AxisDev& ax = plan->dev.ax[axis];
+  const AxisSplit& ax = plan->dev.ax[axis];
   for (int i = 0; i < ax.n; ++i) {
-    starts[i] = ax.start[i];
-    ends[i] = ax.start[i] + ax.size[i];
+    starts[i] = split_start(ax, i);
+    ends[i] = split_start(ax, i) + split_size(ax, i);
   }
   return TDP_OK;
 }
@@ -189,9 +188,9 @@ int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t*
 int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w) {
   if (!plan || !w) return fail(TDP_EINVAL, "tdp_plan_window: null argument");
   if (axis < 0 || axis > 2) return fail(TDP_EINVAL, "axis must be 0, 1 or 2 (got %d)", axis);
-  const AxisDev& ax = plan->dev.ax[axis];
+  const AxisSplit& ax = plan->dev.ax[axis];
   if (i < 0 || i >= ax.n) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", i, ax.n);
-  const int size = ax.size[i], o = ax.o;
+  const int size = split_size(ax, i), o = ax.o;
   for (int j = 0; j < size; ++j) {
     // Exact ratios are formed in double (numerator and denominator are
     // small integers, so each ratio is one rounding) and the product of the
@@ -201,6 +200,19 @@ int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w) {
     if (i < ax.n - 1 && j >= size - o) v *= (double)(size - j) / (double)(o + 1);
     w[j] = (float)v;
   }
+  return TDP_OK;
+}
+
+int tdp_plan_cell_tiles(const tdp_plan* plan, int axis, int32_t x, int32_t* tiles, int32_t* count) {
+  if (!plan || !tiles || !count) return fail(TDP_EINVAL, "tdp_plan_cell_tiles: null argument");
+  if (axis < 0 || axis > 2) return fail(TDP_EINVAL, "axis must be 0, 1 or 2 (got %d)", axis);
+  if (!plan->guarded) return fail(TDP_EGUARD, "tdp_plan_cell_tiles: plan was built with TDP_UNGUARDED");
+  const AxisSplit& ax = plan->dev.ax[axis];
+  if (x < 0 || x >= ax.dim) return fail(TDP_EINVAL, "cell %d out of range [0, %d)", x, ax.dim);
+  const Covers c = split_covers(ax, x);
+  tiles[0] = c.t0;
+  tiles[1] = c.t1;
+  *count = c.n;
   return TDP_OK;
 }
 
@@ -217,8 +229,8 @@ int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info) {
   info->grid[2] = k;
   const int g[3] = {i, j, k};
   for (int d = 0; d < 3; ++d) {
-    info->origin[d] = p.ax[d].start[g[d]];
-    info->shape[d] = p.ax[d].size[g[d]];
+    info->origin[d] = split_start(p.ax[d], g[d]);
+    info->shape[d] = split_size(p.ax[d], g[d]);
   }
   info->gen_tokens = s.gen;
   info->capacity = s.cap;
@@ -237,8 +249,8 @@ int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes) {
   sizes->tile_index_ints = plan->total_index;
   sizes->cond_row_ints = (int64_t)p.T * p.Nc;
   sizes->out_elems = (int64_t)p.B * p.rows * p.C;
-  // extent partials: (T, B, chunks, 3 axes, {min start, max end}) floats
-  sizes->workspace_bytes = (int64_t)p.T * p.B * p.chunks * 6 * (int64_t)sizeof(float);
+  // extent partials: (T, B, 3, chunks) x {min start, max end} floats
+  sizes->workspace_bytes = (int64_t)p.T * p.B * 3 * p.ext_chunks * 2 * (int64_t)sizeof(float);
   return TDP_OK;
 }
 

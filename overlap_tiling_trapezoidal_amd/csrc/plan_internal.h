@@ -1,4 +1,14 @@
 // Internal plan representation shared by the host planner and the kernels.
+//
+// The split of an axis is a closed form (mold issue #673, "A bug found
+// while porting", and TDP docs, "API": n tiles per axis overlapping by o
+// cells): with s = dim - o,
+//   start a_i = floor(i * s / n)           i = 0..n   (a_n = s)
+//   tile  i   = [a_i, a_{i+1} + o)
+//   size      = a_{i+1} + o - a_i
+//   prefix    = a_i + i * o                 (sizes of tiles 0..i-1)
+// so kernels and host compute every interval quantity from (dim, n, o) with
+// the same functions below, instead of reading tables.
 #pragma once
 
 #include <stdint.h>
@@ -14,21 +24,83 @@
 
 namespace tdp {
 
-constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
-
-// One axis of the split: n intervals [start[i], start[i] + size[i]).
-struct AxisDev {
-  int32_t dim;
-  int32_t n;
-  int32_t o;
-  int32_t start[kMaxTiles];
-  int32_t size[kMaxTiles];
-  int32_t pre[kMaxTiles + 1];  // pre[i] = size[0] + ... + size[i-1]
+// Unsigned division by an invariant d >= 1 for numerators below 2^31, by
+// multiplication (Granlund & Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 * (2^l - d) / d) + 1, q = (mulhi(m, x) + x) >> l.
+struct FastDiv {
+  uint32_t m;
+  uint32_t l;
 };
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.l = l;
+  return f;
+}
+TDP_HD uint32_t fastdiv(uint32_t x, const FastDiv& f) {
+  const uint32_t hi = (uint32_t)(((uint64_t)f.m * x) >> 32);
+  return (hi + x) >> f.l;
+}
+
+struct AxisSplit {
+  int32_t dim;  // cells on the axis (<= TDP_MAX_AXIS, so products stay below 2^31)
+  int32_t n;    // tiles on the axis
+  int32_t o;    // overlap in cells
+  FastDiv by_n; // division by n
+  FastDiv by_s; // division by s = dim - o
+};
+
+TDP_HD int split_start(const AxisSplit& a, int i) {
+  return (int)fastdiv((uint32_t)(i * (a.dim - a.o)), a.by_n);
+}
+TDP_HD int split_size(const AxisSplit& a, int i) { return split_start(a, i + 1) + a.o - split_start(a, i); }
+TDP_HD int split_prefix(const AxisSplit& a, int i) { return split_start(a, i) + i * a.o; }
+TDP_HD int split_total(const AxisSplit& a) { return a.dim + (a.n - 1) * a.o; }
+
+// The last tile that contains cell x: the largest i with a_i <= x.
+// a_i <= x  <=>  i * s < (x + 1) * n  <=>  i <= ((x + 1) * n - 1) / s.
+TDP_HD int split_last_cover(const AxisSplit& a, int x) {
+  const int i = (int)fastdiv((uint32_t)((x + 1) * a.n - 1), a.by_s);
+  return i < a.n - 1 ? i : a.n - 1;
+}
+
+// Tiles containing cell x, ascending (at most two when o*(n+1) <= dim):
+// the last cover i always contains x; tile i-1 also does iff x < a_i + o.
+struct Covers {
+  int n;       // 1 or 2
+  int t0, t1;  // tile indices, t0 < t1 when n == 2
+  int a0, a1;  // their starts
+  int s0, s1;  // their sizes
+};
+TDP_HD Covers split_covers(const AxisSplit& a, int x) {
+  Covers c;
+  const int i = split_last_cover(a, x);
+  const int ai = split_start(a, i);
+  const int si = split_start(a, i + 1) + a.o - ai;
+  if (i > 0 && x < ai + a.o) {
+    const int ap = split_start(a, i - 1);
+    c.n = 2;
+    c.t0 = i - 1;
+    c.a0 = ap;
+    c.s0 = ai + a.o - ap;
+    c.t1 = i;
+    c.a1 = ai;
+    c.s1 = si;
+  } else {
+    c.n = 1;
+    c.t0 = c.t1 = i;
+    c.a0 = c.a1 = ai;
+    c.s0 = c.s1 = si;
+  }
+  return c;
+}
 
 // Everything a kernel needs about a plan; passed by value (kernel argument).
 struct PlanDev {
-  AxisDev ax[3];
+  AxisSplit ax[3];
   int32_t B, C, F, H, W;
   int32_t N;          // F * H * W generated tokens
   int32_t Nc;         // appended conditioning tokens
@@ -38,10 +110,11 @@ struct PlanDev {
   int32_t in_dtype;
   int32_t out_dtype;
   int32_t normalize;  // subtract the per-tile offsets
-  int32_t chunks;     // extent partials per (tile, batch element)
+  int32_t pos_parts;  // position workgroups per (tile, batch element, axis)
+  int32_t ext_chunks; // extent partials per (tile, batch element, axis)
 };
 
-// Tile t -> per-axis tile index.
+// Tile t -> per-axis tile index (row-major, width fastest).
 TDP_HD void tile_grid(const PlanDev& p, int t, int& i, int& j, int& k) {
   const int nh = p.ax[1].n, nw = p.ax[2].n;
   k = t % nw;
@@ -52,9 +125,10 @@ TDP_HD void tile_grid(const PlanDev& p, int t, int& i, int& j, int& k) {
 // Generated tokens held by all tiles that precede tile (i, j, k) in
 // row-major order: sum of sf*sh*sw over lexicographically smaller triples.
 TDP_HD int64_t gen_before(const PlanDev& p, int i, int j, int k) {
-  const int64_t SH = p.ax[1].pre[p.ax[1].n], SW = p.ax[2].pre[p.ax[2].n];
-  return (int64_t)p.ax[0].pre[i] * SH * SW +
-         (int64_t)p.ax[0].size[i] * ((int64_t)p.ax[1].pre[j] * SW + (int64_t)p.ax[1].size[j] * p.ax[2].pre[k]);
+  const int64_t SH = split_total(p.ax[1]), SW = split_total(p.ax[2]);
+  return (int64_t)split_prefix(p.ax[0], i) * SH * SW +
+         (int64_t)split_size(p.ax[0], i) *
+             ((int64_t)split_prefix(p.ax[1], j) * SW + (int64_t)split_size(p.ax[1], j) * split_prefix(p.ax[2], k));
 }
 
 struct TileSlot {
@@ -67,7 +141,7 @@ struct TileSlot {
 TDP_HD TileSlot tile_slot(const PlanDev& p, int i, int j, int k) {
   const int t = (i * p.ax[1].n + j) * p.ax[2].n + k;
   TileSlot s;
-  s.gen = p.ax[0].size[i] * p.ax[1].size[j] * p.ax[2].size[k];
+  s.gen = split_size(p.ax[0], i) * split_size(p.ax[1], j) * split_size(p.ax[2], k);
   s.cap = s.gen + p.Nc;
   s.index_base = gen_before(p, i, j, k) + (int64_t)t * p.Nc;
   s.row_base = s.index_base * p.B;

@@ -51,7 +51,7 @@ def poisoned_buffers(plan, device):
     bufs = tdp.allocate_extract_outputs(plan, device)
     bufs["tile_lat"].view(torch.int16 if bufs["tile_lat"].dtype == torch.bfloat16 else torch.int32).fill_(POISON)
     bufs["tile_pos"].fill_(float("nan"))
-    for k in ("tile_index", "tile_count", "cond_row", "cond_k"):
+    for k in ("tile_index", "tile_count", "cond_row"):
         bufs[k].fill_(POISON)
     bufs["workspace"].fill_(0xAB)
     return bufs
@@ -88,7 +88,8 @@ def check_extract(plan, bufs, ex, num_cond):
         for t, et in enumerate(ex["tiles"]):
             want[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
         assert np.array_equal(cond_row, want)
-        assert np.array_equal(bufs["cond_k"][:num_cond].cpu().numpy(), ex["k"].astype(np.int32))
+        k = tdp.cond_keep_counts(plan, bufs["cond_row"]).cpu().numpy()
+        assert np.array_equal(k, ex["k"])
 
 
 def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
@@ -115,7 +116,7 @@ def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
     return buf
 
 
-def gpu_blend(plan, tile_out_np, cond_row, cond_k, device, label=""):
+def gpu_blend(plan, tile_out_np, cond_row, device, label=""):
     c = plan.cfg
     if tile_out_np.dtype == np.uint16:
         y = torch.from_numpy(tile_out_np.view(np.int16)).view(torch.bfloat16).to(device)
@@ -124,19 +125,18 @@ def gpu_blend(plan, tile_out_np, cond_row, cond_k, device, label=""):
     out = tdp.allocate_output(plan, device)
     out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32).fill_(POISON)
     note(f"blend {label}")
-    tdp.tdp_blend(plan, y, cond_row, cond_k, out)
+    tdp.tdp_blend(plan, y, cond_row, out)
     torch.cuda.synchronize()
     return out
 
 
 def cond_tables(plan, ex, num_cond, device):
-    """The oracle's selection in the library's (cond_row, cond_k) format."""
+    """The oracle's selection in the library's cond_row format."""
     T = len(ex["tiles"])
     cond_row = np.full((T, max(num_cond, 1)), -1, np.int32)
     for t, et in enumerate(ex["tiles"]):
         cond_row[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
-    k = ex["k"].astype(np.int32) if num_cond else np.zeros(1, np.int32)
-    return (torch.from_numpy(cond_row.reshape(-1)).to(device), torch.from_numpy(k).to(device))
+    return torch.from_numpy(cond_row.reshape(-1)).to(device)
 
 
 def check_blend(out: torch.Tensor, ref: np.ndarray, mag: np.ndarray, out_dtype: int):

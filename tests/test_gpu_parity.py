@@ -46,8 +46,8 @@ def test_blend_random_tiles(name, out_dtype, cuda):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    cond_row, cond_k = cond_tables(plan, ex, wl.num_cond, cuda)
-    out = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"{name} {out_dtype}")
+    cond_row = cond_tables(plan, ex, wl.num_cond, cuda)
+    out = gpu_blend(plan, buf, cond_row, cuda, f"{name} {out_dtype}")
     check_blend(out, ref, mag, plan.cfg.out_dtype)
 
 
@@ -70,7 +70,7 @@ def test_end_to_end_stand_in_denoiser(name, cuda):
         out_views[t]["lat"].copy_(torch.add(torch.mul(x, float(a[t])), float(b[t])).to(tile_out.dtype))
     out = tdp.allocate_output(plan, cuda)
     note(f"blend e2e {name}")
-    tdp.tdp_blend(plan, tile_out, bufs["cond_row"], bufs["cond_k"], out)
+    tdp.tdp_blend(plan, tile_out, bufs["cond_row"], out)
     torch.cuda.synchronize()
 
     ex = oracle_extract(wl, inp)
@@ -92,7 +92,7 @@ def test_identity_round_trip(name, cuda):
     lat, _, bufs = gpu_extract(plan, inp, cuda, name)
     out = tdp.allocate_output(plan, cuda)
     note(f"blend identity {name}")
-    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
+    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
     torch.cuda.synchronize()
     if wl.dtype == "bf16":
         assert torch.equal(out.float(), lat.float())   # -0.0 may come back as +0.0
@@ -109,7 +109,7 @@ def test_deterministic_repeat(cuda):
         _, _, bufs = gpu_extract(plan, inp, cuda, f"conditioned rep {rep}")
         out = tdp.allocate_output(plan, cuda)
         note(f"blend conditioned rep {rep}")
-        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
         torch.cuda.synchronize()
         counts = bufs["tile_count"].cpu().numpy()
         views = tdp.tile_views(plan, bufs, counts)
@@ -175,7 +175,7 @@ def test_edge_cases(case, cuda):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    out = gpu_blend(plan, buf, bufs["cond_row"], bufs["cond_k"], cuda, case)
+    out = gpu_blend(plan, buf, bufs["cond_row"], cuda, case)
     check_blend(out, ref, mag, tdp.TDP_F32)
 
 
@@ -195,7 +195,7 @@ def test_cond_tokens_kept_by_no_tile(cuda):
     check_extract(plan, bufs, ex, wl.num_cond)
     out = tdp.allocate_output(plan, cuda)
     note("blend k0")
-    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
+    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
     torch.cuda.synchronize()
     assert torch.all(out[:, N:] == 0)
 
@@ -210,8 +210,8 @@ def test_mixed_dtypes(cuda):
         buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
         ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
         ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, 0)
-        cond_row, cond_k = cond_tables(plan, ex, 0, cuda)
-        out = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"{in_dtype}->{out_dtype}")
+        cond_row = cond_tables(plan, ex, 0, cuda)
+        out = gpu_blend(plan, buf, cond_row, cuda, f"{in_dtype}->{out_dtype}")
         check_blend(out, ref, mag, plan.cfg.out_dtype)
 
 
@@ -222,7 +222,7 @@ def test_window_weights_bit_exact(cuda):
     plan = plan_for(wl, out_dtype="f32")
     ex = oracle_extract(wl, inp)
     tiles = [np.ones((1, len(et["rows"]), 16), np.float32) for et in ex["tiles"]]
-    out = gpu_blend(plan, slot_buffer_from_tiles(plan, tiles, tdp.TDP_F32), *cond_tables(plan, ex, 0, cuda),
+    out = gpu_blend(plan, slot_buffer_from_tiles(plan, tiles, tdp.TDP_F32), cond_tables(plan, ex, 0, cuda),
                     cuda, "onehot")
     got = out.cpu().numpy()[0, :, 0]
     # expected: fp32 sum over covering tiles of fl(fl(wF*wH)*wW) with plan windows
@@ -236,3 +236,26 @@ def test_window_weights_bit_exact(cuda):
             wt = np.float32(np.float32(wins[0][i][f - f0] * wins[1][j][h - h0]) * wins[2][k][w - w0])
             want[n] = np.float32(want[n] + wt)
     assert np.array_equal(got, want)
+
+
+def test_bf16_output_rounding_bit_exact(cuda):
+    """One tile, no overlap: out = RNE_bf16(y) exactly, compared with the oracle's rounding."""
+    rng = np.random.default_rng(21)
+    C, W = 64, 64
+    y = rng.standard_normal((1, W, C)).astype(np.float32)
+    u = y.view(np.uint32)
+    u[0, :8, :] = (u[0, :8, :] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exact ties
+    u[0, 8, :] = np.arange(C, dtype=np.uint32) << np.uint32(16) | np.uint32(0x8000)  # ties, both parities
+    y[0, 9, :4] = [0.0, -0.0, 3.3895314e38, -3.3895314e38]                    # zeros, near overflow
+    y[0, 10, :] = rng.standard_normal(C).astype(np.float32) * np.float32(1e-30)  # tiny normals
+    wl = Workload("round", 1, C, (1, 1, W), ((1, 0), (1, 0), (1, 0)), dtype="f32", seed=0)
+    plan = plan_for(wl, out_dtype="bf16")
+    ex = O.extract(y, grid_positions(1, (1, 1, W), (1, 1, 1)), wl.shape, wl.tiling, 0)
+    out = gpu_blend(plan, slot_buffer_from_tiles(plan, [y], tdp.TDP_F32), cond_tables(plan, ex, 0, cuda),
+                    cuda, "rounding")
+    ref, _ = O.blend([y], ex, wl.shape, wl.tiling, 0)   # one term: exact in fp32 (-0.0 sums to +0.0)
+    want = O.f32_to_bf16_bits(ref.astype(np.float32))
+    got = latent_bits(out)
+    bad = np.argwhere(got != want)
+    assert len(bad) == 0, [(tuple(i), hex(int(y[tuple(i)].view(np.uint32))), hex(int(got[tuple(i)])),
+                            hex(int(want[tuple(i)]))) for i in bad[:5]]

@@ -173,24 +173,63 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
     cfg = tdp.make_config(1, 8, (1, 1, 21), ((1, 0), (1, 0), (3, 8)), unguarded=True)
     plan = tdp.tdp_plan_create(cfg)
     null = ctypes.c_void_p(None)
-    assert lib.tdp_extract(plan.handle, *([null] * 10)) == tdp.TDP_EGUARD
-    assert lib.tdp_blend(plan.handle, *([null] * 5)) == tdp.TDP_EGUARD
+    assert lib.tdp_extract(plan.handle, *([null] * 9)) == tdp.TDP_EGUARD
+    assert lib.tdp_blend(plan.handle, *([null] * 4)) == tdp.TDP_EGUARD
     good = tdp.tdp_plan_create(tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2))))
-    assert lib.tdp_extract(good.handle, *([null] * 10)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, *([null] * 9)) == tdp.TDP_EINVAL
     assert "null" in tdp.tdp_last_error()
-    assert lib.tdp_blend(good.handle, *([null] * 5)) == tdp.TDP_EINVAL
-    assert lib.tdp_extract(None, *([null] * 10)) == tdp.TDP_EINVAL
+    assert lib.tdp_blend(good.handle, *([null] * 4)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(None, *([null] * 9)) == tdp.TDP_EINVAL
     # misaligned pointers are refused too
     odd = ctypes.c_void_p(0x1002)
     al = ctypes.c_void_p(0x1000)
-    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, null, al, null) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, al, null) == tdp.TDP_EINVAL
     assert "aligned" in tdp.tdp_last_error()
 
 
-def test_workspace_and_chunks_sizes():
+def test_4k_sizes():
     plan = plan_for(WORKLOADS["4k"])
     s = tdp.tdp_plan_sizes(plan)
     assert s.num_tiles == 16
     assert s.tile_index_ints == 247296
     assert s.tile_lat_elems == 247296 * 128
-    assert s.workspace_bytes > 0 and s.workspace_bytes % 24 == 0
+    assert s.tile_pos_floats == 247296 * 6
+    assert s.cond_row_ints == 0
+    assert s.workspace_bytes == 16 * 3 * 16 * 8   # 16 partials per plane
+
+
+def _brute_cover(ivs, x):
+    return [i for i, (a, b) in enumerate(ivs) if a <= x < b]
+
+
+def test_cell_tiles_match_brute_force():
+    rng = np.random.default_rng(5)
+    checked = 0
+    for _ in range(400):
+        dim = int(rng.integers(1, 300))
+        n = int(rng.integers(1, min(32, dim) + 1))
+        o = 0 if n == 1 else int(rng.integers(0, dim // (n + 1) + 1))
+        if dim - o < n:
+            continue
+        plan = tdp.tdp_plan_create(tdp.make_config(1, 8, (1, 1, dim), ((1, 0), (1, 0), (n, o))))
+        ivs = O.split_by_count(dim, n, o)
+        for x in range(dim):
+            assert tdp.tdp_plan_cell_tiles(plan, 2, x) == _brute_cover(ivs, x), (dim, n, o, x)
+        checked += 1
+    assert checked > 300
+
+
+def test_large_axes_near_limit():
+    # Products i*(dim-o) and (x+1)*n stay below 2^31 up to TDP_MAX_AXIS cells.
+    limit = 1 << 26
+    rng = np.random.default_rng(9)
+    for dim, n in [(limit, 32), (limit - 7, 31), (limit // 3 + 1, 17), (123457, 32)]:
+        o = int(rng.integers(0, dim // (n + 1) + 1))
+        plan = tdp.tdp_plan_create(tdp.make_config(1, 8, (dim, 1, 1), ((n, o), (1, 0), (1, 0))))
+        ivs = O.split_by_count(dim, n, o)
+        assert tdp.tdp_plan_intervals(plan, 0) == ivs
+        for x in list(rng.integers(0, dim, 200)) + [0, dim - 1] + [a for a, _ in ivs] + [b - 1 for _, b in ivs]:
+            assert tdp.tdp_plan_cell_tiles(plan, 0, int(x)) == _brute_cover(ivs, int(x))
+    with pytest.raises(tdp.TdpError) as ei:
+        tdp.tdp_plan_create(tdp.make_config(1, 8, (limit + 1, 1, 1), ((1, 0),) * 3))
+    assert ei.value.status == tdp.TDP_ESHAPE
