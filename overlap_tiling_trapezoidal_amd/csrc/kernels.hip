@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kLatUnroll = 8;      // latent rows in flight per thread (extract)
+constexpr int kLatRows = 4;        // latent rows per lane in one extract workgroup
 constexpr int kPosUnroll = 4;      // position lines in flight per thread
 constexpr int kExtUnroll = 4;      // extent-reduction lines in flight per thread
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
@@ -40,6 +40,7 @@ constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kNoTile = 0xFF;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kCondRowsPerBlock = 64;
+constexpr int kBlendRows = 4;      // generated rows per lane in one blend workgroup
 
 // 16-byte vector as a native clang vector: HIP's uint4 wrapper (a union)
 // keeps arrays of it out of registers, which would serialize the loads.
@@ -482,74 +483,74 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t,
   }
 }
 
-// Latent workgroup: one (b, f, h) line, every row read once and written to
-// each covering tile.  Source addresses need no tables, so the first pass's
-// loads are issued before the cover and row tables are built: the table
-// setup runs while those loads are in flight.
-__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int* wcov, int line) {
+// Latent workgroup: rows [w0, w0 + rpp * kLatRows) of one (b, f, h) line,
+// every row read once and written to each covering tile.  Source addresses
+// need no tables, so the loads are issued before the cover and row tables
+// are built: the table setup runs while those loads are in flight.
+__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int* wcov, int blk) {
+  const int V = p.vin;
+  const int rpp = kBlock / V;
+  const int rows = rpp * kLatRows;
+  const int nchunk = (p.W + rows - 1) / rows;
+  const int line = blk / nchunk;
+  const int w0 = (blk - line * nchunk) * rows;
+  const int nrow = min(rows, p.W - w0);
   const int b = line / (p.F * p.H);
   const int fh = line - b * (p.F * p.H);
   const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
-  const int V = p.vin;
-  const int rpp = kBlock / V;
   const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
   const bool lane_on = r < rpp;
-  const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W) * V + vv;
+  const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w0) * V + vv;
 
-  u32x4 v[kLatUnroll];
-  int wv[kLatUnroll];
-  bool ok[kLatUnroll];
+  u32x4 v[kLatRows];
+  int kv[kLatRows];
+  bool ok[kLatRows];
 #pragma unroll
-  for (int u = 0; u < kLatUnroll; ++u) {
-    const int w = u * rpp + r;
-    ok[u] = lane_on && w < p.W;
-    wv[u] = ok[u] ? w : 0;
-    v[u] = ld_nt(src + wv[u] * V);
+  for (int u = 0; u < kLatRows; ++u) {
+    const int k = u * rpp + r;  // row within the chunk
+    ok[u] = lane_on && k < nrow;
+    kv[u] = ok[u] ? k : 0;
+    v[u] = ld_nt(src + kv[u] * V);
   }
 
   LineCombos lc;
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
-  for (int w = threadIdx.x; w < p.W; w += kBlock) {
-    const Covers c = split_covers(p.ax[2], w);
-    wcov[w] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
+  for (int k = threadIdx.x; k < nrow; k += kBlock) {
+    const Covers c = split_covers(p.ax[2], w0 + k);
+    wcov[k] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
   }
   for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
     const int combo = e / nw, iw = e - (e / nw) * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    sm.line.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
+    sm.line.rowoff[combo][iw] = (line_row0(p, b, i, lf, j, lh, sh, iw) + w0) * V;
   }
   __syncthreads();
   const int ncombo = lc.n;
-  for (int wb = 0;;) {
-    int cov[kLatUnroll];
+  int cov[kLatRows];
 #pragma unroll
-    for (int u = 0; u < kLatUnroll; ++u) cov[u] = wcov[wv[u]];
-    for (int cb = 0; cb < ncombo; ++cb) {
+  for (int u = 0; u < kLatRows; ++u) cov[u] = wcov[kv[u]];
+  for (int cb = 0; cb < ncombo; ++cb) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
 #pragma unroll
-        for (int u = 0; u < kLatUnroll; ++u) {
-          const int iw = (cov[u] >> (8 * q)) & 0xFF;
-          if (ok[u] && iw != kNoTile) st_nt(a.tile_lat + sm.line.rowoff[cb][iw] + wv[u] * V + vv, v[u]);
-        }
+      for (int u = 0; u < kLatRows; ++u) {
+        const int iw = (cov[u] >> (8 * q)) & 0xFF;
+        if (ok[u] && iw != kNoTile) st_nt(a.tile_lat + sm.line.rowoff[cb][iw] + kv[u] * V + vv, v[u]);
       }
-    }
-    wb += rpp * kLatUnroll;
-    if (wb >= p.W) break;
-#pragma unroll
-    for (int u = 0; u < kLatUnroll; ++u) {
-      const int w = wb + u * rpp + r;
-      ok[u] = lane_on && w < p.W;
-      wv[u] = ok[u] ? w : 0;
-      v[u] = ld_nt(src + wv[u] * V);
     }
   }
 }
 
+// One launch, three kinds of workgroups (independent, disjoint outputs):
+//   [0, n_sel)                 conditioning selection per (tile, chunk);
+//   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
+//   [.., + row blocks)         generated latent rows per (line, chunk).
+// Selection and position workgroups come first so that they are dispatched
+// early; they read the extent partials written by extent_kernel.
 __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
-  extern __shared__ float dyn[];  // selection: ext[B][3][2]; latent: wcov[W]
+  extern __shared__ float dyn[];  // selection: ext[B][3][2]; latent: wcov[chunk rows]
   __shared__ ExtractShared sm;
   int bid = blockIdx.x;
   if (bid < a.n_sel) {
@@ -580,86 +581,130 @@ struct BlendShared {
   float wfh[kMaxCombos];                  // frames x height weight of the combo
 };
 
-// One (b, f, h) line of generated tokens with exactly NC frame x height
-// combos.  Width covers: the first always exists; a missing second one
-// re-reads the first row and is masked out of the sum.
-template <int IN, int OUT, int NC>
-__device__ void blend_line_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
-                                const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0) {
+// SU rows of one lane (rows k = (sub + u) * rpp + r of the chunk), NC frame
+// x height combos.  TWO: some row of this wave has a second width cover;
+// then every row loads both covers (a missing second one re-reads the
+// first row and is masked out of the sum).  Without TWO only the first
+// cover is loaded.
+template <int IN, int OUT, int NC, int SU, bool TWO>
+__device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
+                                  const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0, int w0,
+                                  const int* kv, const bool* ok, int vv) {
   constexpr int E = InVec<IN>::E;
-  // rows per pass: 8 loads in flight per lane (2 per combo and row)
-  constexpr int U = 4 / NC;
   const int V = p.vin;
-  const int rpp = kBlock / V;
-  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
-  const bool lane_on = r < rpp;
-  for (int wb = 0; wb < p.W; wb += rpp * U) {
-    u32x4 y0[U][NC], y1[U][NC];
-    int wv[U];
-    bool ok[U], has1[U];
+  u32x4 y0[SU][NC], y1[SU][TWO ? NC : 1];
+  bool has1[SU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int w = wb + u * rpp + r;
-      ok[u] = lane_on && w < p.W;
-      wv[u] = ok[u] ? w : 0;
-      const int cov = wcov[wv[u]];
-      const int iw0 = cov & 0xFF, iw1 = (cov >> 8) & 0xFF;
-      has1[u] = iw1 != kNoTile;
-      const int iw1s = has1[u] ? iw1 : iw0;
-      const int64_t off = (int64_t)wv[u] * V + vv;
+  for (int u = 0; u < SU; ++u) {
+    const int cov = wcov[kv[u]];
+    const int iw0 = cov & 0xFF, iw1 = (cov >> 8) & 0xFF;
+    has1[u] = iw1 != kNoTile;
+    const int iw1s = has1[u] ? iw1 : iw0;
+    const int64_t off = (int64_t)(w0 + kv[u]) * V + vv;
 #pragma unroll
-      for (int cb = 0; cb < NC; ++cb) {
-        y0[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw0] + off);
-        y1[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw1s] + off);
+    for (int cb = 0; cb < NC; ++cb) {
+      y0[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw0] + off);
+      if (TWO) y1[u][TWO ? cb : 0] = ld_nt(tile_out + sm.rowoff[cb][iw1s] + off);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const float2 ww = wgt[kv[u]];
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+    // ascending tile index: combos ascend in (i_f, i_h), then i_w
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const float wa = sm.wfh[cb] * ww.x;
+      float x0[E];
+      InVec<IN>::unpack(y0[u][cb], x0);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(wa, x0[e], acc[e]);
+      if (TWO) {
+        const float wb = sm.wfh[cb] * ww.y;
+        float x1[E];
+        InVec<IN>::unpack(y1[u][TWO ? cb : 0], x1);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = has1[u] ? fmaf(wb, x1[e], acc[e]) : acc[e];
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float2 ww = wgt[wv[u]];
-      float acc[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-      // ascending tile index: combos ascend in (i_f, i_h), then i_w
-#pragma unroll
-      for (int cb = 0; cb < NC; ++cb) {
-        const float w0 = sm.wfh[cb] * ww.x;
-        const float w1 = sm.wfh[cb] * ww.y;
-        float x0[E], x1[E];
-        InVec<IN>::unpack(y0[u][cb], x0);
-        InVec<IN>::unpack(y1[u][cb], x1);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(w0, x0[e], acc[e]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = has1[u] ? fmaf(w1, x1[e], acc[e]) : acc[e];
-      }
-      if (ok[u]) store_out<OUT, E>(out, ((dst0 + wv[u]) * V + vv) * (int64_t)E, acc);
-    }
+    if (ok[u]) store_out<OUT, E>(out, ((dst0 + w0 + kv[u]) * V + vv) * (int64_t)E, acc);
   }
 }
 
+// Rows [w0, w0 + blend_chunk_rows(V)) of one (b, f, h) line, with exactly
+// NC frame x height combos.  Each wave owns consecutive rows: in sub-pass
+// `sub` its lanes hold rows sub*4*rw*SU + wave*rw*SU + u*rw + lane/V,
+// u < SU (rw = 64/V rows per wave instruction), so a wave usually lies
+// inside one width tile and takes the single-cover path.  SU rows at a
+// time keep at most 8 loads in flight (2 per combo and row).  `wcov` /
+// `wgt` are indexed by w - w0.
+template <int IN, int OUT, int NC>
+__device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
+                                 const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0,
+                                 int w0) {
+  constexpr int SU = 4 / NC;
+  const int V = p.vin;
+  const int rw = 64 / V;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane / V, vv = lane - lr * V;
+  const bool lane_on = lr < rw;
+#pragma unroll
+  for (int sub = 0; sub < kBlendRows; sub += SU) {
+    int kv[SU];
+    bool ok[SU];
+    bool two = false;
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int k = (sub * kWaves + wave * SU + u) * rw + lr;  // row within the chunk
+      ok[u] = lane_on && w0 + k < p.W;
+      kv[u] = ok[u] ? k : 0;
+      two |= ok[u] && ((wcov[kv[u]] >> 8) & 0xFF) != kNoTile;
+    }
+    // wave-uniform: most waves lie inside one width tile
+    if (__any(two))
+      blend_rows<IN, OUT, NC, SU, true>(p, sm, wcov, wgt, tile_out, out, dst0, w0, kv, ok, vv);
+    else
+      blend_rows<IN, OUT, NC, SU, false>(p, sm, wcov, wgt, tile_out, out, dst0, w0, kv, ok, vv);
+  }
+}
+
+// Rows per blend workgroup: 4 waves x (64 / V) rows x kBlendRows.
+__host__ __device__ inline int blend_chunk_rows_for(int V) { return kWaves * (64 / V) * kBlendRows; }
+
+// Generated rows: one workgroup per (b, f, h, chunk of rpp * kBlendRows
+// rows), one pass each; many short workgroups let the dispatcher overlap
+// the tail of one with the start of the next.
 template <int IN, int OUT>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
                                                        const int32_t* __restrict__ cond_row,
-                                                       void* __restrict__ out, int n_line) {
+                                                       void* __restrict__ out, int n_gen_blocks) {
   constexpr int E = InVec<IN>::E;
-  extern __shared__ int smem[];  // wcov[W] then wgt[W] (float2)
+  extern __shared__ int smem[];  // wcov[chunk] then wgt[chunk] (float2)
   __shared__ BlendShared sm;
   const int bid = blockIdx.x;
   const int V = p.vin;
 
-  if (bid < n_line) {
+  if (bid < n_gen_blocks) {
+    const int rows = blend_chunk_rows_for(V);  // rows per chunk
+    const int nchunk = (p.W + rows - 1) / rows;
+    const int line = bid / nchunk;
+    const int w0 = (bid - line * nchunk) * rows;
+    const int nrow = min(rows, p.W - w0);
     int* wcov = smem;
-    float2* wgt = reinterpret_cast<float2*>(smem + ((p.W + 1) & ~1));
-    const int b = bid / (p.F * p.H);
-    const int fh = bid - b * (p.F * p.H);
+    float2* wgt = reinterpret_cast<float2*>(smem + ((rows + 1) & ~1));
+    const int b = line / (p.F * p.H);
+    const int fh = line - b * (p.F * p.H);
     const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
     LineCombos lc;
     lc.init(p, f, h);
     const int nw = p.ax[2].n;
-    for (int w = threadIdx.x; w < p.W; w += kBlock) {
+    for (int k = threadIdx.x; k < nrow; k += kBlock) {
+      const int w = w0 + k;
       const Covers c = split_covers(p.ax[2], w);
-      wcov[w] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
-      wgt[w] = make_float2(ramp_weight(p.ax[2], c.t0, w - c.a0, c.s0),
+      wcov[k] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
+      wgt[k] = make_float2(ramp_weight(p.ax[2], c.t0, w - c.a0, c.s0),
                            c.n > 1 ? ramp_weight(p.ax[2], c.t1, w - c.a1, c.s1) : 0.0f);
     }
     for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
@@ -673,11 +718,11 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
     const int nc = lc.n;
     if (nc == 1)
-      blend_line_rows<IN, OUT, 1>(p, sm, wcov, wgt, tile_out, out, dst0);
+      blend_chunk_rows<IN, OUT, 1>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
     else if (nc == 2)
-      blend_line_rows<IN, OUT, 2>(p, sm, wcov, wgt, tile_out, out, dst0);
+      blend_chunk_rows<IN, OUT, 2>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
     else
-      blend_line_rows<IN, OUT, 4>(p, sm, wcov, wgt, tile_out, out, dst0);
+      blend_chunk_rows<IN, OUT, 4>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
     return;
   }
 
@@ -686,7 +731,7 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
   if (r >= rpp) return;
   const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
-  const int cid = bid - n_line;
+  const int cid = bid - n_gen_blocks;
   const int b = cid / per_b;
   const int c0 = (cid - b * per_b) * kCondRowsPerBlock;
   const int nrows = min(kCondRowsPerBlock, p.Nc - c0);
@@ -719,11 +764,12 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
 
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
-  const int n_line = p.B * p.F * p.H;
+  const int rows = blend_chunk_rows_for(p.vin);
+  const int n_gen = p.B * p.F * p.H * ((p.W + rows - 1) / rows);
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
-  const size_t lds = (size_t)((p.W + 1) & ~1) * sizeof(int) + (size_t)p.W * sizeof(float2);
-  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_line + n_cond), dim3(kBlock), lds, s, p,
-                     reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_line);
+  const size_t lds = (size_t)((rows + 1) & ~1) * sizeof(int) + (size_t)rows * sizeof(float2);
+  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
+                     reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
   return hipGetLastError();
 }
 
@@ -764,15 +810,16 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T * p.B * 3 * p.pos_parts;
-  const int n_line = p.B * p.F * p.H;
-  size_t lds = (size_t)p.W * sizeof(int);
+  const int lat_rows = (kBlock / p.vin) * kLatRows;
+  const int n_rows_blocks = p.B * p.F * p.H * ((p.W + lat_rows - 1) / lat_rows);
+  size_t lds = (size_t)lat_rows * sizeof(int);
   const size_t lds_sel = (size_t)p.B * 6 * sizeof(float);
   if (lds_sel > lds) lds = lds_sel;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (need_ext)
     hipLaunchKernelGGL(extent_kernel, dim3(p.T * p.B * 3 * p.ext_chunks), dim3(kBlock), 0, s, p, a.pos,
                        reinterpret_cast<float2*>(workspace));
-  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_line), dim3(kBlock), lds, s, p, a);
+  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_rows_blocks), dim3(kBlock), lds, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
