@@ -12,15 +12,20 @@
 // lanes re-read a valid row and discard it), so the compiler keeps all of a
 // thread's loads in flight instead of waiting before each one.
 //
-// extract is ONE launch with three kinds of workgroups:
-//   selection  (tile, chunk of conditioning tokens): tile extents, keep
-//              test, ordered compaction, copy of the kept rows;
-//   positions  (tile, batch, axis, part): minimum start over the tile's
-//              generated tokens, then the shifted positions of one part of
-//              the tile and its source indices;
-//   latent     (batch, frame, row): every latent row of one (f, h) line is
-//              read once and written to each tile that covers it.
-// The kinds are independent, so they overlap in one grid.
+// extract is two launches.  The first holds the bulk of the bytes and the
+// reduction that the second depends on:
+//   extent     (tile, batch, axis, chunk of rows): partial [min start,
+//              max end) of the tile's generated positions;
+//   latent     (batch, frame, row, chunk of rows): every latent row is read
+//              once and written to each tile that covers it.
+// The second reads the finished extents:
+//   selection  (tile, chunk of conditioning tokens): keep test, ordered
+//              compaction, copy of the kept rows;
+//   positions  (tile, batch, axis, part): shifted positions of one part of
+//              the tile and its source indices.
+// The extent reduction thus runs under the latent copy instead of before
+// it.  (Splitting the latent copy across both launches, to hide the
+// positions too, measured no faster.)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -32,15 +37,14 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kLatRows = 4;        // latent rows per lane in one extract workgroup
+constexpr int kLatRows = 1;        // latent rows per lane in one extract workgroup
 constexpr int kPosUnroll = 4;      // position lines in flight per thread
 constexpr int kExtUnroll = 4;      // extent-reduction lines in flight per thread
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
-constexpr int kNoTile = 0xFF;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kCondRowsPerBlock = 64;
-constexpr int kBlendRows = 4;      // generated rows per lane in one blend workgroup
+constexpr int kBlendRows = 2;      // generated rows per lane in one blend workgroup
 
 // 16-byte vector as a native clang vector: HIP's uint4 wrapper (a union)
 // keeps arrays of it out of registers, which would serialize the loads.
@@ -157,36 +161,6 @@ __device__ inline float2 block_minmax(float a, float b, float2* red) {
 }
 
 // ---------------------------------------------------------------------------
-// Walking a tile's generated tokens line by line
-// ---------------------------------------------------------------------------
-//
-// A tile's generated tokens form sf*sh lines of sw consecutive tokens.
-// Threads split into `groups` groups of `lanes` (= min(sw, 256)) lanes; a
-// group takes every groups-th line, its lanes the tokens of that line.  The
-// line -> (frame, row) split advances incrementally (no divisions).
-struct LineWalk {
-  int lanes, groups, g, lane;  // lane < lanes; g < groups when active
-  bool active;
-  int dlf, dlh;                // line step `groups` as (frames, rows)
-
-  __device__ inline void init(int sw, int sh) {
-    lanes = sw < kBlock ? sw : kBlock;
-    groups = kBlock / lanes;
-    g = threadIdx.x / lanes;
-    lane = threadIdx.x - g * lanes;
-    active = g < groups;
-    dlf = groups / sh;
-    dlh = groups - dlf * sh;
-  }
-};
-
-// Source offset (token index within one batch element, < N <= INT32_MAX)
-// of the start of local line (lf, lh) of a tile.
-__device__ inline int line_source(const PlanDev& p, const TileBox& tb, int lf, int lh) {
-  return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0;
-}
-
-// ---------------------------------------------------------------------------
 // bf16 / f32 vectors
 // ---------------------------------------------------------------------------
 
@@ -266,20 +240,30 @@ struct ExtractArgs {
   int32_t* tile_index;
   int32_t* tile_count;
   int32_t* cond_row;     // (T, Nc)
-  const float2* ext;      // (T, B, 3, chunks) partial [min start, max end)
-  int n_sel, n_pos, pos_parts;
+  float2* ext;           // (T, B, 3, chunks) partial [min start, max end)
+  int n_ext, n_sel, n_pos, pos_parts;
 };
 
-// [min start, max end) of plane (t, b, d) from its extent partials.
-__device__ inline float2 plane_extent(const PlanDev& p, const float2* __restrict__ ext, int t, int b, int d) {
+// Extent partials of plane (t, b, d): lane l of a wave loads partial l
+// (clamped; ext_chunks <= 64, and a repeated partial does not change a min
+// or a max).  Load first, reduce later, so the load overlaps other loads.
+__device__ inline float2 load_extent_partial(const PlanDev& p, const float2* __restrict__ ext, int t, int b,
+                                             int d) {
   const float2* q = ext + ((int64_t)(t * p.B + b) * 3 + d) * p.ext_chunks;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int c = 0; c < p.ext_chunks; ++c) {
-    const float2 v = q[c];
-    lo = fminf(lo, v.x);
-    hi = fmaxf(hi, v.y);
-  }
-  return make_float2(lo, hi);
+  const int lane = threadIdx.x & 63;
+  return q[lane < p.ext_chunks ? lane : p.ext_chunks - 1];
+}
+// [min start, max end) of the plane; every lane of the wave must call it.
+__device__ inline float2 reduce_extent(float2 v) { return make_float2(wave_min(v.x), wave_max(v.y)); }
+
+// Source token (within one batch element) of generated row r of a tile:
+// r = (lf * sh + lh) * sw + x.
+__device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r) {
+  const int line = (int)div_by_size(p.ax[2], (uint32_t)r, tb.sw);
+  const int x = r - line * tb.sw;
+  const int lf = (int)div_by_size(p.ax[1], (uint32_t)line, tb.sh);
+  const int lh = line - lf * tb.sh;
+  return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + x;
 }
 
 // Row tables hold vector offsets, not pointers: a pointer read back from
@@ -295,56 +279,38 @@ struct SelShared {
 union ExtractShared {
   LineShared line;
   SelShared sel;
+  float2 red[kWaves];
 };
 
-// Extent workgroup: lines [l0, l1) of plane (t, b, d) -> one partial
-// [min start, max end).  Launched before the extract kernel proper, whose
-// position and selection workgroups combine the partials of their tile.
-__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const f32x2* __restrict__ pos,
-                                                        float2* __restrict__ ext) {
-  __shared__ float2 red[kWaves];
-  const int chunk = blockIdx.x % p.ext_chunks;
-  const int plane = blockIdx.x / p.ext_chunks;  // (t * B + b) * 3 + d
+// Extent workgroup `blk`: one chunk of the lines of plane (t, b, d) -> one
+// partial [min start, max end).  The selection and position workgroups of
+// the second extract launch combine the partials of their tile.
+__device__ void extent_partial(const PlanDev& p, const f32x2* __restrict__ pos, float2* __restrict__ ext,
+                               float2* red, int blk) {
+  const int chunk = blk % p.ext_chunks;
+  const int plane = blk / p.ext_chunks;  // (t * B + b) * 3 + d
   const int d = plane % 3, b = (plane / 3) % p.B, t = plane / (3 * p.B);
   const TileBox tb = tile_box(p, t);
-  const int lines = tb.sf * tb.sh;
-  const int per = (lines + p.ext_chunks - 1) / p.ext_chunks;
-  const int l_begin = min(lines, chunk * per), l_end = min(lines, l_begin + per);
-  LineWalk lw;
-  lw.init(tb.sw, tb.sh);
+  const int per = (tb.s.gen + p.ext_chunks - 1) / p.ext_chunks;
+  const int r_begin = min(tb.s.gen, chunk * per), r_end = min(tb.s.gen, r_begin + per);
   const f32x2* src = pos + ((int64_t)b * 3 + d) * p.rows;
   float lo = INFINITY, hi = -INFINITY;
-  if (lw.active) {
-    const int l_first = l_begin + lw.g;
-    int lf = l_first / tb.sh, lh = l_first - (l_first / tb.sh) * tb.sh;
-    for (int l0 = l_first; l0 < l_end; l0 += kExtUnroll * lw.groups) {
-      int n0[kExtUnroll];
-      bool ok[kExtUnroll];
+  // Rows past r_end re-read row r_begin: a repeat does not change the result.
+  for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kExtUnroll) {
+    f32x2 v[kExtUnroll];
 #pragma unroll
-      for (int u = 0; u < kExtUnroll; ++u) {
-        ok[u] = l0 + u * lw.groups < l_end;
-        n0[u] = line_source(p, tb, ok[u] ? lf : 0, ok[u] ? lh : 0);
-        lh += lw.dlh;
-        lf += lw.dlf;
-        if (lh >= tb.sh) {
-          lh -= tb.sh;
-          ++lf;
-        }
-      }
-      for (int x = lw.lane; x < tb.sw; x += lw.lanes) {
-        f32x2 v[kExtUnroll];
+    for (int u = 0; u < kExtUnroll; ++u) {
+      const int r = r0 + u * kBlock + (int)threadIdx.x;
+      v[u] = ld_nt(src + tile_row_source(p, tb, r < r_end ? r : r_begin));
+    }
 #pragma unroll
-        for (int u = 0; u < kExtUnroll; ++u) v[u] = src[n0[u] + x];
-#pragma unroll
-        for (int u = 0; u < kExtUnroll; ++u) {
-          lo = ok[u] ? fminf(lo, v[u].x) : lo;
-          hi = ok[u] ? fmaxf(hi, v[u].y) : hi;
-        }
-      }
+    for (int u = 0; u < kExtUnroll; ++u) {
+      lo = fminf(lo, v[u].x);
+      hi = fmaxf(hi, v[u].y);
     }
   }
   const float2 r = block_minmax(lo, hi, red);
-  if (threadIdx.x == 0) ext[blockIdx.x] = r;
+  if (threadIdx.x == 0) ext[blk] = r;
 }
 
 // Selection workgroup: tile t, conditioning tokens [c0, c0 + kSelChunk).
@@ -352,11 +318,14 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
                                   int t, int chunk) {
   const TileBox tb = tile_box(p, t);
 
-  // 1. extent [min start, max end) of the tile on every (batch, axis).
-  for (int e = threadIdx.x; e < p.B * 3; e += kBlock) {
-    const float2 x = plane_extent(p, a.ext, t, e / 3, e % 3);
-    ext[2 * e] = x.x;
-    ext[2 * e + 1] = x.y;
+  // 1. extent [min start, max end) of the tile on every (batch, axis), one
+  //    plane per wave at a time.
+  for (int e = threadIdx.x >> 6; e < p.B * 3; e += kWaves) {
+    const float2 x = reduce_extent(load_extent_partial(p, a.ext, t, e / 3, e % 3));
+    if ((threadIdx.x & 63) == 0) {
+      ext[2 * e] = x.x;
+      ext[2 * e + 1] = x.y;
+    }
   }
   __syncthreads();
 
@@ -432,52 +401,43 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
   }
 }
 
-// Positions workgroup: tile t, batch b, axis d, part `part` of the lines:
-// the shifted [start, end) pairs and source indices of those lines.  The
-// shift is the tile's minimum start on this plane, from the extent partials.
+// Positions workgroup: tile t, batch b, axis d, part `part` of the tile's
+// generated rows: the shifted [start, end) pairs and the source indices.
+// The shift is the tile's minimum start on this plane; its partials are
+// loaded before the positions and reduced after, so the two loads overlap.
 __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t, int b, int d, int part) {
   const TileBox tb = tile_box(p, t);
-  const int lines = tb.sf * tb.sh;
-  LineWalk lw;
-  lw.init(tb.sw, tb.sh);
+  const int gen = tb.s.gen;
+  const int per = (gen + a.pos_parts - 1) / a.pos_parts;
+  const int r_begin = min(gen, part * per), r_end = min(gen, r_begin + per);
+  if (part == 0 && b == 0 && d == 0 && p.Nc == 0 && threadIdx.x == 0) a.tile_count[t] = gen;
   const f32x2* src = a.pos + ((int64_t)b * 3 + d) * p.rows;
-  const float off = p.normalize ? plane_extent(p, a.ext, t, b, d).x : 0.0f;
-
-  // pass 2: shifted positions (and source indices) of this part's lines
-  const int per = (lines + a.pos_parts - 1) / a.pos_parts;
-  const int l_begin = min(lines, part * per), l_end = min(lines, l_begin + per);
-  if (part == 0 && b == 0 && d == 0 && p.Nc == 0 && threadIdx.x == 0) a.tile_count[t] = tb.s.gen;
-  if (!lw.active) return;
   f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
   int32_t* idx = a.tile_index + tb.s.index_base;
   const bool write_index = (b == 0 && d == 0);
-  const int l_first = l_begin + lw.g;
-  int lf = l_first / tb.sh, lh = l_first - (l_first / tb.sh) * tb.sh;
-  for (int l0 = l_first; l0 < l_end; l0 += kPosUnroll * lw.groups) {
-    int n0[kPosUnroll];
-    bool ok[kPosUnroll];
+  const float2 partial = p.normalize ? load_extent_partial(p, a.ext, t, b, d) : make_float2(0.0f, 0.0f);
+  float off = 0.0f;
+  bool have_off = false;
+  // The loop bounds are uniform, so every lane takes part in the reduction.
+  for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
+    int n[kPosUnroll];
+    f32x2 v[kPosUnroll];
 #pragma unroll
     for (int u = 0; u < kPosUnroll; ++u) {
-      ok[u] = l0 + u * lw.groups < l_end;
-      n0[u] = line_source(p, tb, ok[u] ? lf : 0, ok[u] ? lh : 0);
-      lh += lw.dlh;
-      lf += lw.dlf;
-      if (lh >= tb.sh) {
-        lh -= tb.sh;
-        ++lf;
-      }
+      const int r = r0 + u * kBlock + (int)threadIdx.x;
+      n[u] = tile_row_source(p, tb, r < r_end ? r : r_begin);
+      v[u] = ld_nt(src + n[u]);
     }
-    for (int x = lw.lane; x < tb.sw; x += lw.lanes) {
-      f32x2 v[kPosUnroll];
+    if (!have_off) {
+      off = p.normalize ? reduce_extent(partial).x : 0.0f;
+      have_off = true;
+    }
 #pragma unroll
-      for (int u = 0; u < kPosUnroll; ++u) v[u] = ld_nt(src + n0[u] + x);
-#pragma unroll
-      for (int u = 0; u < kPosUnroll; ++u) {
-        if (ok[u]) {
-          const int row = (l0 + u * lw.groups) * tb.sw + x;
-          st_nt(dst + row, v[u] - off);
-          if (write_index) st_nt(idx + row, (int32_t)(n0[u] + x));
-        }
+    for (int u = 0; u < kPosUnroll; ++u) {
+      const int r = r0 + u * kBlock + (int)threadIdx.x;
+      if (r < r_end) {
+        st_nt(dst + r, v[u] - off);
+        if (write_index) st_nt(idx + r, (int32_t)n[u]);
       }
     }
   }
@@ -487,7 +447,7 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t,
 // every row read once and written to each covering tile.  Source addresses
 // need no tables, so the loads are issued before the cover and row tables
 // are built: the table setup runs while those loads are in flight.
-__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int* wcov, int blk) {
+__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int blk) {
   const int V = p.vin;
   const int rpp = kBlock / V;
   const int rows = rpp * kLatRows;
@@ -516,10 +476,6 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   LineCombos lc;
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
-  for (int k = threadIdx.x; k < nrow; k += kBlock) {
-    const Covers c = split_covers(p.ax[2], w0 + k);
-    wcov[k] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
-  }
   for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
     const int combo = e / nw, iw = e - (e / nw) * nw;
     int i, lf, sf, j, lh, sh;
@@ -528,29 +484,37 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   }
   __syncthreads();
   const int ncombo = lc.n;
-  int cov[kLatRows];
+  Covers cw[kLatRows];
 #pragma unroll
-  for (int u = 0; u < kLatRows; ++u) cov[u] = wcov[kv[u]];
+  for (int u = 0; u < kLatRows; ++u) cw[u] = split_covers(p.ax[2], w0 + kv[u]);
   for (int cb = 0; cb < ncombo; ++cb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int u = 0; u < kLatRows; ++u) {
-        const int iw = (cov[u] >> (8 * q)) & 0xFF;
-        if (ok[u] && iw != kNoTile) st_nt(a.tile_lat + sm.line.rowoff[cb][iw] + kv[u] * V + vv, v[u]);
-      }
+    for (int u = 0; u < kLatRows; ++u) {
+      if (ok[u]) st_nt(a.tile_lat + sm.line.rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
+      if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + sm.line.rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
     }
   }
 }
 
-// One launch, three kinds of workgroups (independent, disjoint outputs):
-//   [0, n_sel)                 conditioning selection per (tile, chunk);
-//   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
-//   [.., + row blocks)         generated latent rows per (line, chunk).
-// Selection and position workgroups come first so that they are dispatched
-// early; they read the extent partials written by extent_kernel.
-__global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
-  extern __shared__ float dyn[];  // selection: ext[B][3][2]; latent: wcov[chunk rows]
+// First extract launch (disjoint outputs):
+//   [0, n_ext)      extent partials per (tile, batch, axis, chunk), first so
+//                   that they are dispatched early;
+//   [n_ext, ..)     generated latent rows per (line, chunk of rows).
+__global__ __launch_bounds__(kBlock) void extract_rows_kernel(const PlanDev p, const ExtractArgs a) {
+  __shared__ ExtractShared sm;
+  const int bid = blockIdx.x;
+  if (bid < a.n_ext) {
+    extent_partial(p, a.pos, a.ext, sm.red, bid);
+    return;
+  }
+  extract_latent(p, a, sm, bid - a.n_ext);
+}
+
+// Second extract launch, after every extent partial is written:
+//   [0, n_sel)             conditioning selection per (tile, chunk);
+//   [n_sel, n_sel + n_pos) positions per (tile, batch, axis, part).
+__global__ __launch_bounds__(kBlock) void extract_tail_kernel(const PlanDev p, const ExtractArgs a) {
+  extern __shared__ float dyn[];  // selection: ext[B][3][2]
   __shared__ ExtractShared sm;
   int bid = blockIdx.x;
   if (bid < a.n_sel) {
@@ -559,17 +523,13 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
     return;
   }
   bid -= a.n_sel;
-  if (bid < a.n_pos) {
-    const int part = bid % a.pos_parts;
-    int rest = bid / a.pos_parts;
-    const int d = rest % 3;
-    rest /= 3;
-    const int b = rest % p.B;
-    const int t = rest / p.B;
-    extract_positions(p, a, t, b, d, part);
-    return;
-  }
-  extract_latent(p, a, sm, reinterpret_cast<int*>(dyn), bid - a.n_pos);
+  const int part = bid % a.pos_parts;
+  int rest = bid / a.pos_parts;
+  const int d = rest % 3;
+  rest /= 3;
+  const int b = rest % p.B;
+  const int t = rest / p.B;
+  extract_positions(p, a, t, b, d, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -581,25 +541,22 @@ struct BlendShared {
   float wfh[kMaxCombos];                  // frames x height weight of the combo
 };
 
-// SU rows of one lane (rows k = (sub + u) * rpp + r of the chunk), NC frame
-// x height combos.  TWO: some row of this wave has a second width cover;
-// then every row loads both covers (a missing second one re-reads the
-// first row and is masked out of the sum).  Without TWO only the first
-// cover is loaded.
+// SU rows of one lane, NC frame x height combos.  `cw[u]` are the width
+// covers of row w0 + kv[u].  TWO: some row of this wave has a second width
+// cover; then every row loads both covers (a missing second one re-reads
+// the first row and is masked out of the sum).  Without TWO only the first
+// cover is loaded.  The width weights are computed after the loads are
+// issued, while they are in flight.
 template <int IN, int OUT, int NC, int SU, bool TWO>
-__device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
+__device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const Covers* cw,
                                   const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0, int w0,
                                   const int* kv, const bool* ok, int vv) {
   constexpr int E = InVec<IN>::E;
   const int V = p.vin;
   u32x4 y0[SU][NC], y1[SU][TWO ? NC : 1];
-  bool has1[SU];
 #pragma unroll
   for (int u = 0; u < SU; ++u) {
-    const int cov = wcov[kv[u]];
-    const int iw0 = cov & 0xFF, iw1 = (cov >> 8) & 0xFF;
-    has1[u] = iw1 != kNoTile;
-    const int iw1s = has1[u] ? iw1 : iw0;
+    const int iw0 = cw[u].t0, iw1s = cw[u].t1;  // t1 == t0 with one cover
     const int64_t off = (int64_t)(w0 + kv[u]) * V + vv;
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
@@ -609,27 +566,30 @@ __device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const
   }
 #pragma unroll
   for (int u = 0; u < SU; ++u) {
-    const float2 ww = wgt[kv[u]];
+    const int w = w0 + kv[u];
+    const bool has1 = cw[u].n > 1;
+    const float wx = ramp_weight(p.ax[2], cw[u].t0, w - cw[u].a0, cw[u].s0);
+    const float wy = TWO && has1 ? ramp_weight(p.ax[2], cw[u].t1, w - cw[u].a1, cw[u].s1) : 0.0f;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
     // ascending tile index: combos ascend in (i_f, i_h), then i_w
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      const float wa = sm.wfh[cb] * ww.x;
+      const float wa = sm.wfh[cb] * wx;
       float x0[E];
       InVec<IN>::unpack(y0[u][cb], x0);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(wa, x0[e], acc[e]);
       if (TWO) {
-        const float wb = sm.wfh[cb] * ww.y;
+        const float wb = sm.wfh[cb] * wy;
         float x1[E];
         InVec<IN>::unpack(y1[u][TWO ? cb : 0], x1);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = has1[u] ? fmaf(wb, x1[e], acc[e]) : acc[e];
+        for (int e = 0; e < E; ++e) acc[e] = has1 ? fmaf(wb, x1[e], acc[e]) : acc[e];
       }
     }
-    if (ok[u]) store_out<OUT, E>(out, ((dst0 + w0 + kv[u]) * V + vv) * (int64_t)E, acc);
+    if (ok[u]) store_out<OUT, E>(out, ((dst0 + w) * V + vv) * (int64_t)E, acc);
   }
 }
 
@@ -638,13 +598,11 @@ __device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const
 // `sub` its lanes hold rows sub*4*rw*SU + wave*rw*SU + u*rw + lane/V,
 // u < SU (rw = 64/V rows per wave instruction), so a wave usually lies
 // inside one width tile and takes the single-cover path.  SU rows at a
-// time keep at most 8 loads in flight (2 per combo and row).  `wcov` /
-// `wgt` are indexed by w - w0.
+// time keep at most 8 loads in flight (2 per combo and row).
 template <int IN, int OUT, int NC>
-__device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const int* wcov, const float2* wgt,
-                                 const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0,
-                                 int w0) {
-  constexpr int SU = 4 / NC;
+__device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const u32x4* __restrict__ tile_out,
+                                 void* __restrict__ out, int64_t dst0, int w0) {
+  constexpr int SU = 4 / NC < kBlendRows ? 4 / NC : kBlendRows;
   const int V = p.vin;
   const int rw = 64 / V;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -654,19 +612,21 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
   for (int sub = 0; sub < kBlendRows; sub += SU) {
     int kv[SU];
     bool ok[SU];
+    Covers cw[SU];
     bool two = false;
 #pragma unroll
     for (int u = 0; u < SU; ++u) {
       const int k = (sub * kWaves + wave * SU + u) * rw + lr;  // row within the chunk
       ok[u] = lane_on && w0 + k < p.W;
       kv[u] = ok[u] ? k : 0;
-      two |= ok[u] && ((wcov[kv[u]] >> 8) & 0xFF) != kNoTile;
+      cw[u] = split_covers(p.ax[2], w0 + kv[u]);
+      two |= ok[u] && cw[u].n > 1;
     }
     // wave-uniform: most waves lie inside one width tile
     if (__any(two))
-      blend_rows<IN, OUT, NC, SU, true>(p, sm, wcov, wgt, tile_out, out, dst0, w0, kv, ok, vv);
+      blend_rows<IN, OUT, NC, SU, true>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
     else
-      blend_rows<IN, OUT, NC, SU, false>(p, sm, wcov, wgt, tile_out, out, dst0, w0, kv, ok, vv);
+      blend_rows<IN, OUT, NC, SU, false>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
   }
 }
 
@@ -681,7 +641,6 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
                                                        const int32_t* __restrict__ cond_row,
                                                        void* __restrict__ out, int n_gen_blocks) {
   constexpr int E = InVec<IN>::E;
-  extern __shared__ int smem[];  // wcov[chunk] then wgt[chunk] (float2)
   __shared__ BlendShared sm;
   const int bid = blockIdx.x;
   const int V = p.vin;
@@ -691,22 +650,12 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     const int nchunk = (p.W + rows - 1) / rows;
     const int line = bid / nchunk;
     const int w0 = (bid - line * nchunk) * rows;
-    const int nrow = min(rows, p.W - w0);
-    int* wcov = smem;
-    float2* wgt = reinterpret_cast<float2*>(smem + ((rows + 1) & ~1));
     const int b = line / (p.F * p.H);
     const int fh = line - b * (p.F * p.H);
     const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
     LineCombos lc;
     lc.init(p, f, h);
     const int nw = p.ax[2].n;
-    for (int k = threadIdx.x; k < nrow; k += kBlock) {
-      const int w = w0 + k;
-      const Covers c = split_covers(p.ax[2], w);
-      wcov[k] = c.t0 | ((c.n > 1 ? c.t1 : kNoTile) << 8);
-      wgt[k] = make_float2(ramp_weight(p.ax[2], c.t0, w - c.a0, c.s0),
-                           c.n > 1 ? ramp_weight(p.ax[2], c.t1, w - c.a1, c.s1) : 0.0f);
-    }
     for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
       const int combo = e / nw, iw = e - (e / nw) * nw;
       int i, lf, sf, j, lh, sh;
@@ -718,11 +667,11 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
     const int nc = lc.n;
     if (nc == 1)
-      blend_chunk_rows<IN, OUT, 1>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
+      blend_chunk_rows<IN, OUT, 1>(p, sm, tile_out, out, dst0, w0);
     else if (nc == 2)
-      blend_chunk_rows<IN, OUT, 2>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
+      blend_chunk_rows<IN, OUT, 2>(p, sm, tile_out, out, dst0, w0);
     else
-      blend_chunk_rows<IN, OUT, 4>(p, sm, wcov, wgt, tile_out, out, dst0, w0);
+      blend_chunk_rows<IN, OUT, 4>(p, sm, tile_out, out, dst0, w0);
     return;
   }
 
@@ -767,8 +716,7 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
   const int rows = blend_chunk_rows_for(p.vin);
   const int n_gen = p.B * p.F * p.H * ((p.W + rows - 1) / rows);
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
-  const size_t lds = (size_t)((rows + 1) & ~1) * sizeof(int) + (size_t)rows * sizeof(float2);
-  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
+  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), 0, s, p,
                      reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
   return hipGetLastError();
 }
@@ -806,20 +754,17 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.tile_index = tile_index;
   a.tile_count = tile_count;
   a.cond_row = cond_row;
-  a.ext = reinterpret_cast<const float2*>(workspace);
+  a.ext = reinterpret_cast<float2*>(workspace);
+  a.n_ext = need_ext ? p.T * p.B * 3 * p.ext_chunks : 0;
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T * p.B * 3 * p.pos_parts;
   const int lat_rows = (kBlock / p.vin) * kLatRows;
-  const int n_rows_blocks = p.B * p.F * p.H * ((p.W + lat_rows - 1) / lat_rows);
-  size_t lds = (size_t)lat_rows * sizeof(int);
-  const size_t lds_sel = (size_t)p.B * 6 * sizeof(float);
-  if (lds_sel > lds) lds = lds_sel;
+  const int n_lat = p.B * p.F * p.H * ((p.W + lat_rows - 1) / lat_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (need_ext)
-    hipLaunchKernelGGL(extent_kernel, dim3(p.T * p.B * 3 * p.ext_chunks), dim3(kBlock), 0, s, p, a.pos,
-                       reinterpret_cast<float2*>(workspace));
-  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_rows_blocks), dim3(kBlock), lds, s, p, a);
+  hipLaunchKernelGGL(extract_rows_kernel, dim3(a.n_ext + n_lat), dim3(kBlock), 0, s, p, a);
+  hipLaunchKernelGGL(extract_tail_kernel, dim3(a.n_sel + a.n_pos), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s,
+                     p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;

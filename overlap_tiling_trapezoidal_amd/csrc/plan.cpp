@@ -71,7 +71,16 @@ static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisS
   ax->n = t.num_tiles;
   ax->o = t.overlap;
   ax->by_n = make_fastdiv((uint32_t)t.num_tiles);
+  ax->size_min = (int32_t)(free_len / t.num_tiles) + t.overlap;
+  ax->by_size[0] = make_fastdiv((uint32_t)ax->size_min);
+  ax->by_size[1] = make_fastdiv((uint32_t)ax->size_min + 1);
   ax->by_s = make_fastdiv((uint32_t)free_len);
+  for (int i = 0; i < ax->n; ++i) {
+    const int sz = split_size(*ax, i);
+    if (sz != ax->size_min && sz != ax->size_min + 1)
+      return fail(TDP_ESHAPE, "%s: internal error: tile %d has size %d outside {%d, %d}", name, i, sz,
+                  ax->size_min, ax->size_min + 1);
+  }
   return TDP_OK;
 }
 
@@ -136,7 +145,7 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
     return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
                 (long long)(total_index * c.batch));
 
-  // Position workgroups: each shifts about 2048 tokens of one (tile, batch
+  // Position workgroups: each shifts about 1024 tokens of one (tile, batch
   // element, axis).
   int64_t max_gen = 0;
   for (int i = 0; i < dev.ax[0].n; ++i)
@@ -146,9 +155,9 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
             (int64_t)split_size(dev.ax[0], i) * split_size(dev.ax[1], j) * split_size(dev.ax[2], k);
         if (g > max_gen) max_gen = g;
       }
-  int64_t parts = (max_gen + 2047) / 2048;
+  int64_t parts = (max_gen + 1023) / 1024;
   if (parts < 1) parts = 1;
-  if (parts > 32) parts = 32;
+  if (parts > 64) parts = 64;
   dev.pos_parts = (int32_t)parts;
   // Extent partials: each reduces about 1024 tokens of one plane.
   int64_t chunks = (max_gen + 1023) / 1024;

@@ -46,11 +46,13 @@ TDP_HD uint32_t fastdiv(uint32_t x, const FastDiv& f) {
 }
 
 struct AxisSplit {
-  int32_t dim;  // cells on the axis (<= TDP_MAX_AXIS, so products stay below 2^31)
-  int32_t n;    // tiles on the axis
-  int32_t o;    // overlap in cells
-  FastDiv by_n; // division by n
-  FastDiv by_s; // division by s = dim - o
+  int32_t dim;         // cells on the axis (<= TDP_MAX_AXIS, so products stay below 2^31)
+  int32_t n;           // tiles on the axis
+  int32_t o;           // overlap in cells
+  int32_t size_min;    // floor(s / n) + o: every tile size is size_min or size_min + 1
+  FastDiv by_n;        // division by n
+  FastDiv by_s;        // division by s = dim - o
+  FastDiv by_size[2];  // division by size_min and size_min + 1
 };
 
 TDP_HD int split_start(const AxisSplit& a, int i) {
@@ -59,6 +61,11 @@ TDP_HD int split_start(const AxisSplit& a, int i) {
 TDP_HD int split_size(const AxisSplit& a, int i) { return split_start(a, i + 1) + a.o - split_start(a, i); }
 TDP_HD int split_prefix(const AxisSplit& a, int i) { return split_start(a, i) + i * a.o; }
 TDP_HD int split_total(const AxisSplit& a) { return a.dim + (a.n - 1) * a.o; }
+
+// Division by the size of a tile on this axis (x < 2^31).
+TDP_HD uint32_t div_by_size(const AxisSplit& a, uint32_t x, int size) {
+  return fastdiv(x, size == a.size_min ? a.by_size[0] : a.by_size[1]);
+}
 
 // The last tile that contains cell x: the largest i with a_i <= x.
 // a_i <= x  <=>  i * s < (x + 1) * n  <=>  i <= ((x + 1) * n - 1) / s.
