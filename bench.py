@@ -138,7 +138,7 @@ def main():
     def extract(s):
         b = s["bufs"]
         tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
-                        b["tile_count"], b["cond_row"], b["workspace"], stream)
+                        b["tile_count"], b["cond_row"], stream)
 
     def blend(s):
         b = s["bufs"]

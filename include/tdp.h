@@ -82,6 +82,7 @@ extern "C" {
 #define TDP_MAX_WIDTH 4096
 #define TDP_MAX_BATCH 1024
 #define TDP_MAX_AXIS (1 << 26) /* cells per axis */
+#define TDP_MAX_ROWS (1 << 29) /* tokens + conditioning per batch element (below) */
 
 /* One axis of the tiling: a tile COUNT and an overlap in latent grid cells
  * (TDP docs, "API": DimensionTilingConfig(num_tiles, overlap)). */
@@ -97,7 +98,8 @@ typedef struct {
   int32_t frames;       /* 1 <= F <= TDP_MAX_AXIS latent grid                 */
   int32_t height;       /* 1 <= H <= TDP_MAX_AXIS                             */
   int32_t width;        /* 1 <= W <= TDP_MAX_WIDTH                            */
-  int32_t num_cond;     /* Nc >= 0 conditioning tokens after the N generated  */
+  int32_t num_cond;     /* Nc >= 0 conditioning tokens after the N generated; */
+                        /* F*H*W + Nc < TDP_MAX_ROWS                          */
   tdp_axis_tiling axis[3]; /* frames, height, width (TDP docs, "API":       */
                            /* TileCountConfig)                                */
   int32_t in_dtype;     /* latent / tile dtype: TDP_F32 or TDP_BF16           */
@@ -126,7 +128,6 @@ typedef struct {
   int64_t tile_index_ints;  /* int32 entries of tile_index                    */
   int64_t cond_row_ints;    /* int32 entries of cond_row: T * Nc              */
   int64_t out_elems;        /* elements of out: B * (N + Nc) * C              */
-  int64_t workspace_bytes;  /* device scratch of tdp_extract (extent partials) */
 } tdp_sizes;
 
 /* ---- plan (host only; no GPU needed) ------------------------------------ */
@@ -178,9 +179,8 @@ int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* 
 
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
 
-/* Gather all tiles, every latent row read once.  Two launches: a short
- * reduction of each tile's position extent into `workspace`, then one
- * kernel for rows, positions and selection.
+/* Gather all tiles, every latent row read once, in one launch that needs
+ * no scratch memory.
  *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
  *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
  *        tile_count (T) int32: gen_t + kept_t.
@@ -202,15 +202,11 @@ int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* 
  * All pointers are device pointers except `plan`; latent/tile_lat 16-byte
  * aligned, pos/tile_pos 8-byte aligned; buffers must not overlap and hold
  * the sizes tdp_plan_sizes() reports (the library cannot check sizes).
- * workspace: tdp_sizes.workspace_bytes of device scratch, 8-byte aligned;
- *   its contents on entry do not matter and on return are unspecified.  It
- *   may be NULL only when the plan neither normalizes nor has Nc > 0.
- *   Calls that share a workspace must not overlap in time.
- * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
+  * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
  * pointers, TDP_EHIP on launch failure. */
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 void* tile_lat, float* tile_pos, int32_t* tile_index,
-                int32_t* tile_count, int32_t* cond_row, void* workspace, void* stream);
+                int32_t* tile_count, int32_t* cond_row, void* stream);
 
 /* Blend tile outputs (tile-major slots with tile_lat's layout and dtype,
  * rows as tdp_extract placed them) into out (B, N+Nc, C) out_dtype:

@@ -74,7 +74,6 @@ class tdp_sizes(ctypes.Structure):
         ("tile_index_ints", ctypes.c_int64),
         ("cond_row_ints", ctypes.c_int64),
         ("out_elems", ctypes.c_int64),
-        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -107,7 +106,7 @@ def load_library(path: str = LIB_PATH):
         "tdp_plan_cell_tiles": (ctypes.c_int, [vp, ctypes.c_int, i32, i32p, i32p]),
         "tdp_plan_sizes": (ctypes.c_int, [vp, ctypes.POINTER(tdp_sizes)]),
         "tdp_plan_tile_rank": (ctypes.c_int, [vp, i32, i32, i32p]),
-        "tdp_extract": (ctypes.c_int, [vp] * 10),
+        "tdp_extract": (ctypes.c_int, [vp] * 9),
         "tdp_blend": (ctypes.c_int, [vp] * 5),
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tdp_last_error": (ctypes.c_char_p, []),
@@ -288,7 +287,6 @@ def allocate_extract_outputs(plan: Plan, device="cuda"):
         "tile_index": torch.empty(s.tile_index_ints, dtype=torch.int32, device=dev),
         "tile_count": torch.empty(s.num_tiles, dtype=torch.int32, device=dev),
         "cond_row": torch.empty(max(s.cond_row_ints, 1), dtype=torch.int32, device=dev),
-        "workspace": torch.empty(max(s.workspace_bytes, 16), dtype=torch.uint8, device=dev),
     }
 
 
@@ -308,7 +306,7 @@ def _stream_handle(stream, device):
 
 
 def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
-                cond_row=None, workspace=None, stream=None):
+                cond_row=None, stream=None):
     """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
     import torch
     c = plan.cfg
@@ -324,8 +322,6 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
         _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
         _ptr(tile_count, "tile_count", torch.int32, s.num_tiles, dev),
         _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
-        _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes
-        else ctypes.c_void_p(None),
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_extract(*args))

@@ -38,8 +38,8 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kLatRows = 1;        // latent rows per lane in one extract workgroup
-constexpr int kPosUnroll = 4;      // position lines in flight per thread
-constexpr int kExtUnroll = 4;      // extent-reduction lines in flight per thread
+constexpr int kPosUnroll = 4;      // position rows in flight per thread (copy pass)
+constexpr int kExtUnroll = 8;      // position rows in flight per thread (extent pass)
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
@@ -240,21 +240,8 @@ struct ExtractArgs {
   int32_t* tile_index;
   int32_t* tile_count;
   int32_t* cond_row;     // (T, Nc)
-  float2* ext;           // (T, B, 3, chunks) partial [min start, max end)
-  int n_ext, n_sel, n_pos, pos_parts;
+  int n_sel, n_pos, pos_parts;
 };
-
-// Extent partials of plane (t, b, d): lane l of a wave loads partial l
-// (clamped; ext_chunks <= 64, and a repeated partial does not change a min
-// or a max).  Load first, reduce later, so the load overlaps other loads.
-__device__ inline float2 load_extent_partial(const PlanDev& p, const float2* __restrict__ ext, int t, int b,
-                                             int d) {
-  const float2* q = ext + ((int64_t)(t * p.B + b) * 3 + d) * p.ext_chunks;
-  const int lane = threadIdx.x & 63;
-  return q[lane < p.ext_chunks ? lane : p.ext_chunks - 1];
-}
-// [min start, max end) of the plane; every lane of the wave must call it.
-__device__ inline float2 reduce_extent(float2 v) { return make_float2(wave_min(v.x), wave_max(v.y)); }
 
 // Source token (within one batch element) of generated row r of a tile:
 // r = (lf * sh + lh) * sw + x.
@@ -282,26 +269,25 @@ union ExtractShared {
   float2 red[kWaves];
 };
 
-// Extent workgroup `blk`: one chunk of the lines of plane (t, b, d) -> one
-// partial [min start, max end).  The selection and position workgroups of
-// the second extract launch combine the partials of their tile.
-__device__ void extent_partial(const PlanDev& p, const f32x2* __restrict__ pos, float2* __restrict__ ext,
-                               float2* red, int blk) {
-  const int chunk = blk % p.ext_chunks;
-  const int plane = blk / p.ext_chunks;  // (t * B + b) * 3 + d
-  const int d = plane % 3, b = (plane / 3) % p.B, t = plane / (3 * p.B);
-  const TileBox tb = tile_box(p, t);
-  const int per = (tb.s.gen + p.ext_chunks - 1) / p.ext_chunks;
-  const int r_begin = min(tb.s.gen, chunk * per), r_end = min(tb.s.gen, r_begin + per);
-  const f32x2* src = pos + ((int64_t)b * 3 + d) * p.rows;
+// Token n of a position plane (n < 2^29, which the plan enforces): a 32-bit
+// byte offset lets the load take a scalar base plus one vector register.
+__device__ inline f32x2 ld_plane(const f32x2* plane, int n) {
+  return *reinterpret_cast<const f32x2*>(reinterpret_cast<const char*>(plane) + ((uint32_t)n << 3));
+}
+
+// [min start, max end) over a tile's generated tokens of one position plane
+// (`src` = pos of one (batch, axis)), reduced by the whole workgroup.  Rows
+// past the end re-read row 0: a repeat does not change a min or a max.
+__device__ float2 tile_plane_extent(const PlanDev& p, const TileBox& tb, const f32x2* __restrict__ src,
+                                    float2* red) {
+  const int gen = tb.s.gen;
   float lo = INFINITY, hi = -INFINITY;
-  // Rows past r_end re-read row r_begin: a repeat does not change the result.
-  for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kExtUnroll) {
+  for (int r0 = 0; r0 < gen; r0 += kBlock * kExtUnroll) {
     f32x2 v[kExtUnroll];
 #pragma unroll
     for (int u = 0; u < kExtUnroll; ++u) {
       const int r = r0 + u * kBlock + (int)threadIdx.x;
-      v[u] = ld_nt(src + tile_row_source(p, tb, r < r_end ? r : r_begin));
+      v[u] = ld_plane(src, tile_row_source(p, tb, r < gen ? r : 0));
     }
 #pragma unroll
     for (int u = 0; u < kExtUnroll; ++u) {
@@ -309,8 +295,7 @@ __device__ void extent_partial(const PlanDev& p, const f32x2* __restrict__ pos, 
       hi = fmaxf(hi, v[u].y);
     }
   }
-  const float2 r = block_minmax(lo, hi, red);
-  if (threadIdx.x == 0) ext[blk] = r;
+  return block_minmax(lo, hi, red);
 }
 
 // Selection workgroup: tile t, conditioning tokens [c0, c0 + kSelChunk).
@@ -318,11 +303,10 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
                                   int t, int chunk) {
   const TileBox tb = tile_box(p, t);
 
-  // 1. extent [min start, max end) of the tile on every (batch, axis), one
-  //    plane per wave at a time.
-  for (int e = threadIdx.x >> 6; e < p.B * 3; e += kWaves) {
-    const float2 x = reduce_extent(load_extent_partial(p, a.ext, t, e / 3, e % 3));
-    if ((threadIdx.x & 63) == 0) {
+  // 1. extent [min start, max end) of the tile on every (batch, axis).
+  for (int e = 0; e < p.B * 3; ++e) {
+    const float2 x = tile_plane_extent(p, tb, a.pos + (int64_t)e * p.rows, sm.red);
+    if (threadIdx.x == 0) {
       ext[2 * e] = x.x;
       ext[2 * e + 1] = x.y;
     }
@@ -403,9 +387,12 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
 
 // Positions workgroup: tile t, batch b, axis d, part `part` of the tile's
 // generated rows: the shifted [start, end) pairs and the source indices.
-// The shift is the tile's minimum start on this plane; its partials are
-// loaded before the positions and reduced after, so the two loads overlap.
-__device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t, int b, int d, int part) {
+// The shift is the tile's minimum start on this plane, which the workgroup
+// reduces itself over the whole plane (the parts of a plane repeat that
+// pass, so no workgroup waits on another); the copy pass then re-reads its
+// own rows from L2.
+__device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int t, int b, int d,
+                                  int part) {
   const TileBox tb = tile_box(p, t);
   const int gen = tb.s.gen;
   const int per = (gen + a.pos_parts - 1) / a.pos_parts;
@@ -415,10 +402,7 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t,
   f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
   int32_t* idx = a.tile_index + tb.s.index_base;
   const bool write_index = (b == 0 && d == 0);
-  const float2 partial = p.normalize ? load_extent_partial(p, a.ext, t, b, d) : make_float2(0.0f, 0.0f);
-  float off = 0.0f;
-  bool have_off = false;
-  // The loop bounds are uniform, so every lane takes part in the reduction.
+  const float off = p.normalize ? tile_plane_extent(p, tb, src, sm.red).x : 0.0f;
   for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
     int n[kPosUnroll];
     f32x2 v[kPosUnroll];
@@ -426,11 +410,7 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, int t,
     for (int u = 0; u < kPosUnroll; ++u) {
       const int r = r0 + u * kBlock + (int)threadIdx.x;
       n[u] = tile_row_source(p, tb, r < r_end ? r : r_begin);
-      v[u] = ld_nt(src + n[u]);
-    }
-    if (!have_off) {
-      off = p.normalize ? reduce_extent(partial).x : 0.0f;
-      have_off = true;
+      v[u] = ld_plane(src, n[u]);
     }
 #pragma unroll
     for (int u = 0; u < kPosUnroll; ++u) {
@@ -496,24 +476,13 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   }
 }
 
-// First extract launch (disjoint outputs):
-//   [0, n_ext)      extent partials per (tile, batch, axis, chunk), first so
-//                   that they are dispatched early;
-//   [n_ext, ..)     generated latent rows per (line, chunk of rows).
-__global__ __launch_bounds__(kBlock) void extract_rows_kernel(const PlanDev p, const ExtractArgs a) {
-  __shared__ ExtractShared sm;
-  const int bid = blockIdx.x;
-  if (bid < a.n_ext) {
-    extent_partial(p, a.pos, a.ext, sm.red, bid);
-    return;
-  }
-  extract_latent(p, a, sm, bid - a.n_ext);
-}
-
-// Second extract launch, after every extent partial is written:
-//   [0, n_sel)             conditioning selection per (tile, chunk);
-//   [n_sel, n_sel + n_pos) positions per (tile, batch, axis, part).
-__global__ __launch_bounds__(kBlock) void extract_tail_kernel(const PlanDev p, const ExtractArgs a) {
+// One launch, three kinds of workgroups (independent, disjoint outputs):
+//   [0, n_sel)                 conditioning selection per (tile, chunk);
+//   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
+//   [.., + latent blocks)      generated latent rows per (line, chunk).
+// Selection and position workgroups are few and long (each reduces a whole
+// tile plane), so they come first and run under the latent copy.
+__global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
   extern __shared__ float dyn[];  // selection: ext[B][3][2]
   __shared__ ExtractShared sm;
   int bid = blockIdx.x;
@@ -523,13 +492,17 @@ __global__ __launch_bounds__(kBlock) void extract_tail_kernel(const PlanDev p, c
     return;
   }
   bid -= a.n_sel;
-  const int part = bid % a.pos_parts;
-  int rest = bid / a.pos_parts;
-  const int d = rest % 3;
-  rest /= 3;
-  const int b = rest % p.B;
-  const int t = rest / p.B;
-  extract_positions(p, a, t, b, d, part);
+  if (bid < a.n_pos) {
+    const int part = bid % a.pos_parts;
+    int rest = bid / a.pos_parts;
+    const int d = rest % 3;
+    rest /= 3;
+    const int b = rest % p.B;
+    const int t = rest / p.B;
+    extract_positions(p, a, sm, t, b, d, part);
+    return;
+  }
+  extract_latent(p, a, sm, bid - a.n_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -731,16 +704,13 @@ using namespace tdp;
 extern "C" {
 
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
-                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, void* workspace, void* stream) {
+                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_extract: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_extract: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (!latent || !pos || !tile_lat || !tile_pos || !tile_index || !tile_count)
     return fail(TDP_EINVAL, "tdp_extract: null device pointer");
   if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_extract: cond_row is required when num_cond > 0");
-  const bool need_ext = p.normalize || p.Nc > 0;
-  if (need_ext && !workspace) return fail(TDP_EINVAL, "tdp_extract: null workspace");
-  if (!aligned(workspace, 8)) return fail(TDP_EINVAL, "tdp_extract: workspace must be 8-byte aligned");
   if (!aligned(latent, 16) || !aligned(tile_lat, 16))
     return fail(TDP_EINVAL, "tdp_extract: latent and tile_lat must be 16-byte aligned");
   if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
@@ -754,16 +724,13 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.tile_index = tile_index;
   a.tile_count = tile_count;
   a.cond_row = cond_row;
-  a.ext = reinterpret_cast<float2*>(workspace);
-  a.n_ext = need_ext ? p.T * p.B * 3 * p.ext_chunks : 0;
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
-  a.n_pos = p.T * p.B * 3 * p.pos_parts;
+  a.n_pos = p.T * p.B * 3 * a.pos_parts;
   const int lat_rows = (kBlock / p.vin) * kLatRows;
   const int n_lat = p.B * p.F * p.H * ((p.W + lat_rows - 1) / lat_rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(extract_rows_kernel, dim3(a.n_ext + n_lat), dim3(kBlock), 0, s, p, a);
-  hipLaunchKernelGGL(extract_tail_kernel, dim3(a.n_sel + a.n_pos), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s,
+  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_lat), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s,
                      p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));

@@ -114,6 +114,9 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
   if ((int64_t)c.batch * rows > INT32_MAX || N > INT32_MAX)
     return fail(TDP_ESHAPE, "batch * (tokens + conditioning) = %lld exceeds the int32 range",
                 (long long)((int64_t)c.batch * rows));
+  if (rows >= TDP_MAX_ROWS)
+    return fail(TDP_ESHAPE, "tokens + conditioning = %lld per batch element exceed the limit of %d",
+                (long long)rows, TDP_MAX_ROWS);
 
   const bool guarded = !(c.flags & TDP_UNGUARDED);
   PlanDev dev;
@@ -145,8 +148,8 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
     return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
                 (long long)(total_index * c.batch));
 
-  // Position workgroups: each shifts about 1024 tokens of one (tile, batch
-  // element, axis).
+  // Position workgroups: each reduces the extent of a whole (tile, batch
+  // element, axis) plane and shifts about 4096 of its tokens.
   int64_t max_gen = 0;
   for (int i = 0; i < dev.ax[0].n; ++i)
     for (int j = 0; j < dev.ax[1].n; ++j)
@@ -155,15 +158,10 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
             (int64_t)split_size(dev.ax[0], i) * split_size(dev.ax[1], j) * split_size(dev.ax[2], k);
         if (g > max_gen) max_gen = g;
       }
-  int64_t parts = (max_gen + 1023) / 1024;
+  int64_t parts = (max_gen + 4095) / 4096;
   if (parts < 1) parts = 1;
   if (parts > 64) parts = 64;
   dev.pos_parts = (int32_t)parts;
-  // Extent partials: each reduces about 1024 tokens of one plane.
-  int64_t chunks = (max_gen + 1023) / 1024;
-  if (chunks < 1) chunks = 1;
-  if (chunks > 64) chunks = 64;
-  dev.ext_chunks = (int32_t)chunks;
 
   tdp_plan* p = new (std::nothrow) tdp_plan;
   if (!p) return fail(TDP_EINVAL, "out of host memory");
@@ -259,7 +257,6 @@ int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes) {
   sizes->cond_row_ints = (int64_t)p.T * p.Nc;
   sizes->out_elems = (int64_t)p.B * p.rows * p.C;
   // extent partials: (T, B, 3, chunks) x {min start, max end} floats
-  sizes->workspace_bytes = (int64_t)p.T * p.B * 3 * p.ext_chunks * 2 * (int64_t)sizeof(float);
   return TDP_OK;
 }
 

@@ -118,7 +118,6 @@ struct PlanDev {
   int32_t out_dtype;
   int32_t normalize;  // subtract the per-tile offsets
   int32_t pos_parts;  // position workgroups per (tile, batch element, axis)
-  int32_t ext_chunks; // extent partials per (tile, batch element, axis)
 };
 
 // Tile t -> per-axis tile index (row-major, width fastest).

@@ -53,7 +53,6 @@ def poisoned_buffers(plan, device):
     bufs["tile_pos"].fill_(float("nan"))
     for k in ("tile_index", "tile_count", "cond_row"):
         bufs[k].fill_(POISON)
-    bufs["workspace"].fill_(0xAB)
     return bufs
 
 

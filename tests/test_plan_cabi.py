@@ -173,17 +173,17 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
     cfg = tdp.make_config(1, 8, (1, 1, 21), ((1, 0), (1, 0), (3, 8)), unguarded=True)
     plan = tdp.tdp_plan_create(cfg)
     null = ctypes.c_void_p(None)
-    assert lib.tdp_extract(plan.handle, *([null] * 9)) == tdp.TDP_EGUARD
+    assert lib.tdp_extract(plan.handle, *([null] * 8)) == tdp.TDP_EGUARD
     assert lib.tdp_blend(plan.handle, *([null] * 4)) == tdp.TDP_EGUARD
     good = tdp.tdp_plan_create(tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2))))
-    assert lib.tdp_extract(good.handle, *([null] * 9)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, *([null] * 8)) == tdp.TDP_EINVAL
     assert "null" in tdp.tdp_last_error()
     assert lib.tdp_blend(good.handle, *([null] * 4)) == tdp.TDP_EINVAL
-    assert lib.tdp_extract(None, *([null] * 9)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(None, *([null] * 8)) == tdp.TDP_EINVAL
     # misaligned pointers are refused too
     odd = ctypes.c_void_p(0x1002)
     al = ctypes.c_void_p(0x1000)
-    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, al, null) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, null) == tdp.TDP_EINVAL
     assert "aligned" in tdp.tdp_last_error()
 
 
@@ -195,7 +195,6 @@ def test_4k_sizes():
     assert s.tile_lat_elems == 247296 * 128
     assert s.tile_pos_floats == 247296 * 6
     assert s.cond_row_ints == 0
-    assert s.workspace_bytes == 16 * 3 * 16 * 8   # 16 partials per plane
 
 
 def _brute_cover(ivs, x):
@@ -233,3 +232,9 @@ def test_large_axes_near_limit():
     with pytest.raises(tdp.TdpError) as ei:
         tdp.tdp_plan_create(tdp.make_config(1, 8, (limit + 1, 1, 1), ((1, 0),) * 3))
     assert ei.value.status == tdp.TDP_ESHAPE
+    # positions are addressed with 32-bit byte offsets: fewer than 2^29 rows
+    tdp.tdp_plan_create(tdp.make_config(1, 8, (limit, 7, 1), ((1, 0),) * 3, num_cond=limit - 1))
+    with pytest.raises(tdp.TdpError) as ei:
+        tdp.tdp_plan_create(tdp.make_config(1, 8, (limit, 7, 1), ((1, 0),) * 3, num_cond=limit))
+    assert ei.value.status == tdp.TDP_ESHAPE
+    assert "2^29" in str(ei.value) or str(1 << 29) in str(ei.value)
