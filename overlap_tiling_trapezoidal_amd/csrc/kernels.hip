@@ -45,6 +45,7 @@ constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kCondRowsPerBlock = 64;
 constexpr int kBlendRows = 2;      // generated rows per lane in one blend workgroup
+constexpr int kXcds = 8;           // accelerator dies; workgroups are dealt to them round-robin
 
 // 16-byte vector as a native clang vector: HIP's uint4 wrapper (a union)
 // keeps arrays of it out of registers, which would serialize the loads.
@@ -493,12 +494,22 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
   }
   bid -= a.n_sel;
   if (bid < a.n_pos) {
-    const int part = bid % a.pos_parts;
-    int rest = bid / a.pos_parts;
-    const int d = rest % 3;
-    rest /= 3;
-    const int b = rest % p.B;
-    const int t = rest / p.B;
+    // Workgroups go to the 8 XCDs round-robin by index, and every part of a
+    // plane reads the whole plane: give the parts of one plane indices that
+    // are equal mod 8, so that they share one L2.  Planes past the last full
+    // group of 8 keep the plain order.
+    int plane, part;
+    const int grouped = (a.n_pos / a.pos_parts) / kXcds * kXcds * a.pos_parts;
+    if (bid < grouped) {
+      part = (bid / kXcds) % a.pos_parts;
+      plane = bid / (kXcds * a.pos_parts) * kXcds + bid % kXcds;
+    } else {
+      part = (bid - grouped) % a.pos_parts;
+      plane = grouped / a.pos_parts + (bid - grouped) / a.pos_parts;
+    }
+    const int d = plane % 3;
+    const int b = (plane / 3) % p.B;
+    const int t = plane / (3 * p.B);
     extract_positions(p, a, sm, t, b, d, part);
     return;
   }
