@@ -17,6 +17,7 @@ from .tdp_oracle import (  # noqa: F401
     split_by_count,
     tile_generated_tokens,
     tile_weights,
+    tiling_quality,
     window_exact,
     window_f64,
     window_sums_exact,

@@ -323,6 +323,59 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 # Geometry helpers used by checks
 # --------------------------------------------------------------------------
 
+def tiling_quality(dims, intervals, world: int) -> dict:
+    """Plan-quality figures of a tiling, exact (integers and Fractions).
+
+    Source: DistVAE docs, "Choosing a tile window": section "The two axes
+    cost differently" (a tiling decodes more than the latent's area because
+    tiles repeat their overlaps; tiles hold a share of the activations; each
+    pair of neighbouring tiles leaves a seam), "Clipping unbalances a grid,
+    not the tile count" (ranks that get the same number of tiles can get
+    different amounts of work; imbalance is the heaviest rank against an
+    even split) and "The tile count caps the GPU count".
+
+    ``dims`` are the axis lengths; ``intervals[d]`` the half-open intervals
+    of axis d.  Tiles are the Cartesian product in row-major order, and on
+    ``world`` ranks tile t goes to rank t mod world (TDP docs, "What it
+    is").  Readings: a tile's work is its cell count; a seam is a pair of
+    tiles whose grid indices differ by one on exactly one axis; the even
+    split divides the total work by ``world`` (idle ranks included).
+    """
+    grid_cells = 1
+    for d in dims:
+        grid_cells *= int(d)
+    counts = [len(v) for v in intervals]
+    cells = []
+    for grid in itertools.product(*[range(c) for c in counts]):
+        c = 1
+        for d, i in enumerate(grid):
+            a, b = intervals[d][i]
+            c *= int(b) - int(a)
+        cells.append(c)
+    seams = 0
+    grids = list(itertools.product(*[range(c) for c in counts]))
+    for x in range(len(grids)):
+        for y in range(x + 1, len(grids)):
+            diff = [abs(p - q) for p, q in zip(grids[x], grids[y])]
+            if sorted(diff)[-1] == 1 and sum(diff) == 1:
+                seams += 1
+    rank_cells = [0] * world
+    for t, c in enumerate(cells):
+        rank_cells[round_robin_rank(t, world)] += c
+    total = sum(cells)
+    return {
+        "total_cells": total,
+        "grid_cells": grid_cells,
+        "largest_cells": max(cells),
+        "seams": seams,
+        "rank_cells": rank_cells,
+        "max_rank_cells": max(rank_cells),
+        "area_ratio": Fraction(total, grid_cells),
+        "largest_fraction": Fraction(max(cells), grid_cells),
+        "imbalance": Fraction(max(rank_cells) * world, total) - 1,
+    }
+
+
 def decoded_area_ratio(shape, tiling) -> float:
     """Total generated tokens over all tiles divided by N (tiles re-process overlaps)."""
     tiles = enumerate_tiles(shape, tiling)

@@ -440,3 +440,75 @@ def test_mutant_blend_dropped_term_fails_identity():
     out, _ = O.blend(ys, ex, wl.shape, wl.tiling, 0)
     got = O.bf16_bits_to_f32(O.f32_to_bf16_bits(out.astype(np.float32)))
     assert not np.array_equal(got, O.bf16_bits_to_f32(inp["latent"]))
+
+
+# --------------------------------------------------------------------------
+# Plan-quality figures (DistVAE docs, "Choosing a tile window")
+# --------------------------------------------------------------------------
+
+def _read_fixture(name):
+    vals = {}
+    for line in open(GOLDEN / name):
+        line = line.split("#", 1)[0].split()
+        if line:
+            vals[line[0]] = [float(x) if "." in x else int(x) for x in line[1:]]
+    return vals
+
+
+def _strips_from_fixture(fx):
+    h, w = fx["latent"]
+    rows = fx["strip_rows"]
+    full, last = rows[0], rows[-1]
+    stride = (h - last) // (len(rows) - 1)
+    starts = [i * stride for i in range(len(rows))]
+    ivs = [(a, min(a + full, h)) for a in starts]
+    assert [b - a for a, b in ivs] == rows          # the printed row counts
+    assert full - last == full - stride             # last strip shorter by exactly the overlap
+    return (h, w), [ivs, [(0, w)]]
+
+
+def test_quality_distvae_strips():
+    fx = _read_fixture("distvae_strips.txt")
+    dims, ivs = _strips_from_fixture(fx)
+    q = O.tiling_quality(dims, ivs, fx["ranks"][0])
+    assert q["area_ratio"] == Fraction(161, 128)
+    assert round(float(q["area_ratio"]), 2) == fx["area_ratio"][0]
+    assert round(float(q["largest_fraction"]), 2) == fx["activations_fraction"][0]
+    assert q["seams"] == fx["strip_seams"][0]
+    assert q["rank_cells"] == [r * dims[1] for r in fx["strip_rows"]]
+    assert q["imbalance"] == Fraction(11, 161)
+    assert round(100 * float(q["imbalance"]), 1) == fx["imbalance_percent"][0]
+
+
+def test_quality_grid_seams_and_closed_form():
+    fx = _read_fixture("distvae_strips.txt")
+    nh, nw = fx["grid"]
+    q = O.tiling_quality((128, 128), [O.split_by_count(128, nh, 8), O.split_by_count(128, nw, 8)], 4)
+    assert q["seams"] == fx["grid_seams"][0]
+    # seams = sum over axes of (n_d - 1) * prod of the other counts
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        counts = [int(x) for x in rng.integers(1, 5, 3)]
+        ivs = [O.split_by_count(64, n, 0) for n in counts]
+        expect = sum((counts[d] - 1) * int(np.prod([counts[e] for e in range(3) if e != d])) for d in range(3))
+        assert O.tiling_quality((64, 64, 64), ivs, 3)["seams"] == expect
+
+
+def test_quality_ratio_matches_geometry_and_balance():
+    # area ratio = prod (dim + (n-1) o) / dim for count-based splits
+    for shape, tiling in [((16, 68, 120), ((1, 0), (4, 8), (4, 16))), ((16, 32, 48), ((2, 2), (3, 6), (3, 8)))]:
+        ivs = [O.split_by_count(d, n, o) for d, (n, o) in zip(shape, tiling)]
+        q = O.tiling_quality(shape, ivs, 4)
+        assert q["area_ratio"] == Fraction(int(np.prod([d + (n - 1) * o for d, (n, o) in zip(shape, tiling)])),
+                                           int(np.prod(shape)))
+        assert sum(q["rank_cells"]) == q["total_cells"]
+    # the 4K grid on 4 ranks: rank r gets the column i_w = r, all equal
+    q = O.tiling_quality((16, 68, 120), [O.split_by_count(16, 1, 0), O.split_by_count(68, 4, 8),
+                                         O.split_by_count(120, 4, 16)], 4)
+    assert q["imbalance"] == 0
+    # more ranks than tiles: idle ranks count in the even split
+    fx = _read_fixture("distvae_strips.txt")
+    dims, ivs = _strips_from_fixture(fx)
+    q = O.tiling_quality(dims, ivs, 8)
+    assert q["rank_cells"][4:] == [0, 0, 0, 0]
+    assert q["imbalance"] == Fraction(43 * 8, 161) - 1
