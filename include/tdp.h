@@ -177,6 +177,38 @@ int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes);
  * "What it is").  On one GPU every tile is local. */
 int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* rank);
 
+/* ---- plan quality (host only) -------------------------------------------- */
+
+/* Cost figures of a tiling (DistVAE docs, "Choosing a tile window":
+ * sections "The two axes cost differently", "Clipping unbalances a grid,
+ * not the tile count" and "The tile count caps the GPU count").  A tile's
+ * work is its cell count; tiles go to ranks round-robin, t mod world. */
+typedef struct {
+  int64_t total_cells;     /* sum over tiles of their cells (decoded work)    */
+  int64_t grid_cells;      /* product of the axis lengths                     */
+  int64_t largest_cells;   /* cells of the largest tile                       */
+  int64_t seams;           /* pairs of tiles whose grid indices differ by one */
+                           /* on exactly one axis                             */
+  int64_t max_rank_cells;  /* cells of the heaviest rank                      */
+  double area_ratio;       /* total_cells / grid_cells                        */
+  double largest_fraction; /* largest_cells / grid_cells (activations held)   */
+  double imbalance;        /* max_rank_cells / (total_cells / world) - 1;     */
+                           /* idle ranks (world > tiles) count in the split   */
+} tdp_quality;
+
+/* Figures of any tiling given as per-axis intervals: ndim axes (1..8) of
+ * lengths dims[d], counts[d] >= 1 intervals each, listed axis after axis in
+ * starts/ends (sum of counts entries, 0 <= start < end <= dims[d]); tiles
+ * are their Cartesian product in row-major order (at most 2^20 tiles).
+ * rank_cells: NULL or `world` int64 entries, the cells of each rank.
+ * Returns TDP_EINVAL for null or malformed arguments or world < 1. */
+int tdp_tiling_quality(int32_t ndim, const int32_t* dims, const int32_t* counts, const int32_t* starts,
+                       const int32_t* ends, int32_t world, tdp_quality* out, int64_t* rank_cells);
+
+/* The same figures for a plan's generated-token tiles (frames, height,
+ * width), e.g. to choose tile counts and overlaps before running. */
+int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int64_t* rank_cells);
+
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
 
 /* Gather all tiles, every latent row read once, in one launch that needs

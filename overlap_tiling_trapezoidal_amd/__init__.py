@@ -77,6 +77,19 @@ class tdp_sizes(ctypes.Structure):
     ]
 
 
+class tdp_quality(ctypes.Structure):
+    _fields_ = [
+        ("total_cells", ctypes.c_int64),
+        ("grid_cells", ctypes.c_int64),
+        ("largest_cells", ctypes.c_int64),
+        ("seams", ctypes.c_int64),
+        ("max_rank_cells", ctypes.c_int64),
+        ("area_ratio", ctypes.c_double),
+        ("largest_fraction", ctypes.c_double),
+        ("imbalance", ctypes.c_double),
+    ]
+
+
 class TdpError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} [{status}]")
@@ -106,6 +119,9 @@ def load_library(path: str = LIB_PATH):
         "tdp_plan_cell_tiles": (ctypes.c_int, [vp, ctypes.c_int, i32, i32p, i32p]),
         "tdp_plan_sizes": (ctypes.c_int, [vp, ctypes.POINTER(tdp_sizes)]),
         "tdp_plan_tile_rank": (ctypes.c_int, [vp, i32, i32, i32p]),
+        "tdp_tiling_quality": (ctypes.c_int, [i32, i32p, i32p, i32p, i32p, i32, ctypes.POINTER(tdp_quality),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+        "tdp_plan_quality": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_quality), ctypes.POINTER(ctypes.c_int64)]),
         "tdp_extract": (ctypes.c_int, [vp] * 9),
         "tdp_blend": (ctypes.c_int, [vp] * 5),
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -274,6 +290,33 @@ def _ptr(t, name, dtype, numel, device):
     if t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _quality_dict(q: tdp_quality, ranks) -> dict:
+    d = {name: getattr(q, name) for name, _ in tdp_quality._fields_}
+    d["rank_cells"] = list(ranks)
+    return d
+
+
+def tdp_tiling_quality(dims, intervals, world: int) -> dict:
+    """Cost figures of a tiling given per-axis [start, end) intervals."""
+    nd = len(dims)
+    arr = lambda xs: (ctypes.c_int32 * max(1, len(xs)))(*xs)  # noqa: E731
+    starts = [a for ivs in intervals for a, _ in ivs]
+    ends = [b for ivs in intervals for _, b in ivs]
+    q = tdp_quality()
+    ranks = (ctypes.c_int64 * max(1, world))()
+    _check(load_library().tdp_tiling_quality(nd, arr(list(dims)), arr([len(v) for v in intervals]), arr(starts),
+                                              arr(ends), world, ctypes.byref(q), ranks))
+    return _quality_dict(q, ranks[:world])
+
+
+def tdp_plan_quality(plan: Plan, world: int) -> dict:
+    """Cost figures of a plan's tiles on ``world`` round-robin ranks."""
+    q = tdp_quality()
+    ranks = (ctypes.c_int64 * max(1, world))()
+    _check(load_library().tdp_plan_quality(plan.handle, world, ctypes.byref(q), ranks))
+    return _quality_dict(q, ranks[:world])
 
 
 def allocate_extract_outputs(plan: Plan, device="cuda"):

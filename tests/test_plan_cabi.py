@@ -238,3 +238,61 @@ def test_large_axes_near_limit():
         tdp.tdp_plan_create(tdp.make_config(1, 8, (limit, 7, 1), ((1, 0),) * 3, num_cond=limit))
     assert ei.value.status == tdp.TDP_ESHAPE
     assert "2^29" in str(ei.value) or str(1 << 29) in str(ei.value)
+
+
+# --------------------------------------------------------------------------
+# Plan quality: library figures against the oracle's
+# --------------------------------------------------------------------------
+
+def _same_quality(lib_q, ref):
+    for k in ("total_cells", "grid_cells", "largest_cells", "seams", "max_rank_cells", "rank_cells"):
+        assert lib_q[k] == ref[k], k
+    for k in ("area_ratio", "largest_fraction", "imbalance"):
+        assert lib_q[k] == pytest.approx(float(ref[k]), rel=1e-15, abs=1e-15), k
+
+
+def test_quality_distvae_strips_matches_oracle():
+    dims, ivs = (128, 128), [[(0, 43), (32, 75), (64, 107), (96, 128)], [(0, 128)]]
+    for world in (1, 2, 3, 4, 5, 8):
+        _same_quality(tdp.tdp_tiling_quality(dims, ivs, world), O.tiling_quality(dims, ivs, world))
+    q = tdp.tdp_tiling_quality(dims, ivs, 4)
+    assert (q["seams"], round(q["area_ratio"], 2), round(100 * q["imbalance"], 1)) == (3, 1.26, 6.8)
+
+
+def test_quality_random_tilings_match_oracle():
+    rng = np.random.default_rng(21)
+    for _ in range(60):
+        nd = int(rng.integers(1, 4))
+        dims = [int(x) for x in rng.integers(1, 40, nd)]
+        ivs = []
+        for d in dims:
+            k = int(rng.integers(1, 5))
+            a = sorted(int(x) for x in rng.integers(0, d, k))
+            ivs.append([(s, int(rng.integers(s + 1, d + 1))) for s in a])   # arbitrary, may overlap or leave gaps
+        world = int(rng.integers(1, 9))
+        _same_quality(tdp.tdp_tiling_quality(dims, ivs, world), O.tiling_quality(dims, ivs, world))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_quality_matches_oracle(name):
+    wl = WORKLOADS[name]
+    plan = tdp.tdp_plan_create(tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond,
+                                               in_dtype=wl.dtype))
+    ivs = [O.split_by_count(d, n, o) for d, (n, o) in zip(wl.shape, wl.tiling)]
+    for world in (1, 2, 4, 8):
+        _same_quality(tdp.tdp_plan_quality(plan, world), O.tiling_quality(wl.shape, ivs, world))
+    assert tdp.tdp_plan_quality(plan, 1)["area_ratio"] == pytest.approx(O.decoded_area_ratio(wl.shape, wl.tiling))
+
+
+def test_quality_errors():
+    with pytest.raises(tdp.TdpError):
+        tdp.tdp_tiling_quality((10,), [[(3, 3)]], 1)          # empty interval
+    with pytest.raises(tdp.TdpError):
+        tdp.tdp_tiling_quality((10,), [[(0, 11)]], 1)         # past the axis
+    with pytest.raises(tdp.TdpError):
+        tdp.tdp_tiling_quality((10,), [[(0, 5)]], 0)          # no ranks
+    with pytest.raises(tdp.TdpError):
+        tdp.tdp_tiling_quality((10,) * 9, [[(0, 5)]] * 9, 1)  # too many axes
+    lib = tdp.load_library()
+    q = tdp.tdp_quality()
+    assert lib.tdp_plan_quality(None, 1, ctypes.byref(q), None) == tdp.TDP_EINVAL
