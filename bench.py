@@ -67,6 +67,18 @@ def compulsory_bytes(wl, counts, num_tiles, e_in, e_out):
     return extract, blend, S
 
 
+def stream_bytes(wl, S, e_in, e_out):
+    """Algorithmic bytes of the streaming blend of all tiles plus the rounding:
+    tile rows read once, the fp32 accumulator written for every tile row and
+    read for every row but a voxel's first, then read once and rounded."""
+    B, C = wl.batch, wl.channels
+    rows = wl.tokens + wl.num_cond
+    tiles = S * B * C * e_in
+    acc = S * B * C * 4 + (S - rows) * B * C * 4
+    finish = rows * B * C * 4 + rows * B * C * e_out
+    return tiles + acc + finish
+
+
 def sources_hash():
     """First 16 hex digits of the SHA-256 over the kernel sources, in order."""
     h = hashlib.sha256()
@@ -250,6 +262,23 @@ def main():
     ex_ms = graph_time_ms(torch, gstream, extract_g, reps)
     bl_ms = graph_time_ms(torch, gstream, blend_g, reps)
 
+    # streaming blend: tile by tile into an fp32 accumulator, then rounding
+    accs = [tdp.allocate_accumulator(plan, dev) for _ in range(2)]
+    infos = [tdp.tdp_plan_tile(plan, t) for t in range(T)]
+    tile_elems = [wl.batch * inf.capacity * wl.channels for inf in infos]
+    views = [[s["bufs"]["tile_lat"][inf.lat_offset: inf.lat_offset + n] for inf, n in zip(infos, tile_elems)]
+             for s in sets]
+
+    def stream_g(i):
+        s = sets[i % R]
+        acc = accs[i % 2]
+        for t in range(T):
+            tdp.tdp_blend_tile(plan, t, views[i % R][t], s["bufs"]["cond_row"], acc, gstream)
+        tdp.tdp_blend_finish(plan, acc, s["out"], gstream)
+
+    st_ms = graph_time_ms(torch, gstream, stream_g, max(8, reps // 4))
+    st_bytes = stream_bytes(wl, S, e_in, e_in)
+
     # plain device copy of the same size as a practical ceiling
     nbytes = 256 << 20
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -299,6 +328,8 @@ def main():
             "blend_ms": round(bl_ms, 5), "blend_bytes": bl_bytes,
             "blend_gbs": round(bl_bytes / (bl_ms * 1e-3) / 1e9, 1),
             "graph_launches": reps,
+            "stream_blend_ms": round(st_ms, 5), "stream_blend_bytes": st_bytes,
+            "stream_blend_gbs": round(st_bytes / (st_ms * 1e-3) / 1e9, 1),
         },
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "roofline": {

@@ -253,6 +253,29 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
 int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row,
               void* out, void* stream);
 
+/* Streaming blend, for schedules that produce one tile output at a time
+ * (TDP docs, "What it is": a rank runs its tiles in turn and their blended
+ * outputs are accumulated in place).  Adds tile t's outputs into the fp32
+ * accumulator acc (B, N+Nc, C): generated rows weighted (wF*wH)*wW, kept
+ * conditioning rows weighted 1/k.  tile_out is tile t's slot alone,
+ * (B, capacity_t, C) in_dtype with the rows tdp_extract placed there
+ * (tdp_tile_info.capacity, .gen_tokens), so it may live in its own buffer.
+ * A voxel's first covering tile and a token's first keeping tile (smallest
+ * index) overwrite acc instead of adding, so acc needs no clearing; tokens
+ * no tile keeps are set to 0 at t = 0.  Call for t = 0, 1, ..., T-1 in this
+ * order on one stream: acc then holds tdp_blend's fp32 sums bit for bit.
+ * Any other order gives wrong sums.  Calls that share acc must not overlap.
+ * tile_out/acc 16-byte aligned device pointers; cond_row as for tdp_blend.
+ * Returns TDP_EINVAL for a bad tile index or pointer. */
+int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
+                   float* acc, void* stream);
+
+/* Round the accumulator (B, N+Nc, C) fp32 to the plan's out_dtype into out
+ * (round to nearest even for bf16; a copy for fp32, nothing when out == acc).
+ * After tdp_blend_tile for every tile in order, out equals tdp_blend's
+ * output bit for bit.  16-byte aligned device pointers. */
+int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* stream);
+
 /* ---- errors ------------------------------------------------------------ */
 const char* tdp_status_string(int status);
 const char* tdp_last_error(void); /* thread-local, never NULL */

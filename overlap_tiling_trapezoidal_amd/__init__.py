@@ -124,6 +124,8 @@ def load_library(path: str = LIB_PATH):
         "tdp_plan_quality": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_quality), ctypes.POINTER(ctypes.c_int64)]),
         "tdp_extract": (ctypes.c_int, [vp] * 9),
         "tdp_blend": (ctypes.c_int, [vp] * 5),
+        "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp]),
+        "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tdp_last_error": (ctypes.c_char_p, []),
     }
@@ -384,6 +386,41 @@ def tdp_blend(plan: Plan, tile_out, cond_row, out, stream=None):
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_blend(*args))
+
+
+def allocate_accumulator(plan: Plan, device="cuda"):
+    """fp32 (B, N+Nc, C) accumulator for the streaming blend."""
+    import torch
+    c = plan.cfg
+    return torch.empty((c.batch, plan.tokens + c.num_cond, c.channels), dtype=torch.float32,
+                       device=torch.device(device))
+
+
+def tdp_blend_tile(plan: Plan, t: int, tile_out, cond_row, acc, stream=None):
+    """Enqueue the streaming blend of tile t's slot ``tile_out`` into ``acc``."""
+    import torch
+    c = plan.cfg
+    info = tdp_plan_tile(plan, t)
+    dev = acc.device
+    rows = plan.tokens + c.num_cond
+    _check(load_library().tdp_blend_tile(
+        plan.handle, t,
+        _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), c.batch * info.capacity * c.channels, dev),
+        _ptr(cond_row, "cond_row", torch.int32, c.num_cond * tdp_plan_num_tiles(plan), dev) if c.num_cond
+        else ctypes.c_void_p(None),
+        _ptr(acc, "acc", torch.float32, c.batch * rows * c.channels, dev),
+        _stream_handle(stream, dev)))
+
+
+def tdp_blend_finish(plan: Plan, acc, out, stream=None):
+    """Enqueue the rounding of ``acc`` to the output dtype into ``out``."""
+    import torch
+    c = plan.cfg
+    n = c.batch * (plan.tokens + c.num_cond) * c.channels
+    dev = acc.device
+    _check(load_library().tdp_blend_finish(plan.handle, _ptr(acc, "acc", torch.float32, n, dev),
+                                           _ptr(out, "out", _torch_dtype(c.out_dtype), n, dev),
+                                           _stream_handle(stream, dev)))
 
 
 def cond_keep_counts(plan: Plan, cond_row):

@@ -705,6 +705,139 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// streaming blend: one tile at a time into an fp32 accumulator
+// ---------------------------------------------------------------------------
+
+constexpr int kStreamRows = 2;  // generated rows per lane in one streaming workgroup
+
+// Generated rows of tile t, batch element b, one lane per 16-byte vector.
+// The weight is (wF * wH) * wW, as in blend_kernel.  A voxel's first
+// covering tile (smallest index: on every axis, not inside the previous
+// tile's overlap) writes fmaf(w, y, +0) without reading the accumulator;
+// later tiles add with fmaf.  Run for t = 0, 1, ..., T-1 in order, this is
+// blend_kernel's fp32 sum, term by term.
+template <int IN>
+__device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int j, int k, int b, int blk,
+                                const u32x4* __restrict__ tile_out, float* __restrict__ acc) {
+  constexpr int E = InVec<IN>::E;
+  const int V = p.vin;
+  const int rpp = kBlock / V;
+  const int lr = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  if (lr >= rpp) return;
+#pragma unroll
+  for (int u = 0; u < kStreamRows; ++u) {
+    const int r = (blk * kStreamRows + u) * rpp + lr;
+    if (r >= tb.s.gen) return;
+    const int line = (int)div_by_size(p.ax[2], (uint32_t)r, tb.sw);
+    const int lw = r - line * tb.sw;
+    const int lf = (int)div_by_size(p.ax[1], (uint32_t)line, tb.sh);
+    const int lh = line - lf * tb.sh;
+    const float wa = ramp_weight(p.ax[0], i, lf, tb.sf) * ramp_weight(p.ax[1], j, lh, tb.sh) *
+                     ramp_weight(p.ax[2], k, lw, tb.sw);
+    const bool first = !(i > 0 && lf < p.ax[0].o) && !(j > 0 && lh < p.ax[1].o) && !(k > 0 && lw < p.ax[2].o);
+    const u32x4 yv = ld_nt(tile_out + ((int64_t)b * tb.s.cap + r) * V + vv);
+    const int64_t voxel = (int64_t)b * p.rows + ((int64_t)(tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + lw;
+    f32x4* a4 = reinterpret_cast<f32x4*>(acc + (voxel * V + vv) * E);
+    float x[E], old[E];
+    InVec<IN>::unpack(yv, x);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      const f32x4 o = first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : a4[q];
+      old[4 * q] = o.x;
+      old[4 * q + 1] = o.y;
+      old[4 * q + 2] = o.z;
+      old[4 * q + 3] = o.w;
+    }
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q)
+      a4[q] = f32x4{fmaf(wa, x[4 * q], old[4 * q]), fmaf(wa, x[4 * q + 1], old[4 * q + 1]),
+                    fmaf(wa, x[4 * q + 2], old[4 * q + 2]), fmaf(wa, x[4 * q + 3], old[4 * q + 3])};
+  }
+}
+
+// Conditioning tokens [c0, c0 + kCondRowsPerBlock) of batch element b for
+// tile t: (1/k) * y added in tile order, the first keeping tile
+// overwriting.  Tokens no tile keeps (blend_kernel's sum of nothing) are
+// set to 0 when t == 0.
+template <int IN>
+__device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u32x4* __restrict__ tile_out,
+                                 const int32_t* __restrict__ cond_row, float* __restrict__ acc, int cap_t) {
+  constexpr int E = InVec<IN>::E;
+  const int V = p.vin;
+  const int rpp = kBlock / V;
+  const int lr = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  if (lr >= rpp) return;
+  const int nrows = min(kCondRowsPerBlock, p.Nc - c0);
+  for (int jj = lr; jj < nrows; jj += rpp) {
+    const int c = c0 + jj;
+    const int row = cond_row[(int64_t)t * p.Nc + c];
+    int kc = 0;
+    bool first = true, any = false;  // any: some tile holds a row blend_kernel sums
+    for (int u = 0; u < p.T; ++u) {
+      const int ru = cond_row[(int64_t)u * p.Nc + c];
+      kc += ru >= 0;
+      if (ru >= 0) {
+        int iu, ju, ku;
+        tile_grid(p, u, iu, ju, ku);
+        if (ru < tile_slot(p, iu, ju, ku).cap) {
+          any = true;
+          if (u < t) first = false;
+        }
+      }
+    }
+    f32x4* a4 = reinterpret_cast<f32x4*>(acc + (((int64_t)b * p.rows + p.N + c) * V + vv) * E);
+    if (row < 0 || row >= cap_t) {
+      if (t == 0 && !any)
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) a4[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      continue;
+    }
+    const float inv = 1.0f / (float)kc;
+    const u32x4 yv = ld_nt(tile_out + ((int64_t)b * cap_t + row) * V + vv);
+    float x[E];
+    InVec<IN>::unpack(yv, x);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      const f32x4 o = first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : a4[q];
+      a4[q] = f32x4{fmaf(inv, x[4 * q], o.x), fmaf(inv, x[4 * q + 1], o.y), fmaf(inv, x[4 * q + 2], o.z),
+                    fmaf(inv, x[4 * q + 3], o.w)};
+    }
+  }
+}
+
+// One launch per tile: [0, n_gen) generated-row workgroups (B of them per
+// row chunk), then conditioning workgroups per (batch element, chunk).
+template <int IN>
+__global__ __launch_bounds__(kBlock) void blend_tile_kernel(const PlanDev p, int t, const u32x4* __restrict__ tile_out,
+                                                            const int32_t* __restrict__ cond_row,
+                                                            float* __restrict__ acc, int gen_per_b, int n_gen) {
+  int i, j, k;
+  tile_grid(p, t, i, j, k);
+  const TileBox tb = tile_box(p, t);
+  const int bid = blockIdx.x;
+  if (bid < n_gen) {
+    const int b = bid / gen_per_b;
+    stream_gen_rows<IN>(p, tb, i, j, k, b, bid - b * gen_per_b, tile_out, acc);
+    return;
+  }
+  const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
+  const int cid = bid - n_gen;
+  const int b = cid / per_b;
+  stream_cond_rows<IN>(p, t, b, (cid - b * per_b) * kCondRowsPerBlock, tile_out, cond_row, acc, tb.s.cap);
+}
+
+// acc (fp32) -> out (OUT), four values per thread.
+template <int OUT>
+__global__ __launch_bounds__(kBlock) void blend_finish_kernel(const f32x4* __restrict__ acc, void* __restrict__ out,
+                                                              int64_t n4) {
+  const int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (q >= n4) return;
+  const f32x4 v = ld_nt(acc + q);
+  const float a[4] = {v.x, v.y, v.z, v.w};
+  store_out<OUT, 4>(out, q * 4, a);
+}
+
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
 }  // namespace
@@ -745,6 +878,55 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
                      p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
+  return TDP_OK;
+}
+
+int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row, float* acc,
+                   void* stream) {
+  if (!plan) return fail(TDP_EINVAL, "tdp_blend_tile: null plan");
+  if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend_tile: plan was built with TDP_UNGUARDED");
+  const PlanDev& p = plan->dev;
+  if (t < 0 || t >= p.T) return fail(TDP_EINVAL, "tdp_blend_tile: tile index %d out of range [0, %d)", t, p.T);
+  if (!tile_out || !acc) return fail(TDP_EINVAL, "tdp_blend_tile: null device pointer");
+  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend_tile: cond_row is required when num_cond > 0");
+  if (!aligned(tile_out, 16) || !aligned(acc, 16) || !aligned(cond_row, 4))
+    return fail(TDP_EINVAL, "tdp_blend_tile: tile_out and acc must be 16-byte aligned");
+  int i, j, k;
+  tile_grid(p, t, i, j, k);
+  const TileSlot slot = tile_slot(p, i, j, k);
+  const int rows_per_block = (kBlock / p.vin) * kStreamRows;
+  const int gen_per_b = (slot.gen + rows_per_block - 1) / rows_per_block;
+  const int n_gen = p.B * gen_per_b;
+  const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
+  if (p.in_dtype == TDP_BF16)
+    hipLaunchKernelGGL(blend_tile_kernel<TDP_BF16>, dim3(n_gen + n_cond), dim3(kBlock), 0, s, p, (int)t, y, cond_row,
+                       acc, gen_per_b, n_gen);
+  else
+    hipLaunchKernelGGL(blend_tile_kernel<TDP_F32>, dim3(n_gen + n_cond), dim3(kBlock), 0, s, p, (int)t, y, cond_row,
+                       acc, gen_per_b, n_gen);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend_tile: kernel launch failed: %s", hipGetErrorString(e));
+  return TDP_OK;
+}
+
+int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* stream) {
+  if (!plan) return fail(TDP_EINVAL, "tdp_blend_finish: null plan");
+  const PlanDev& p = plan->dev;
+  if (!acc || !out) return fail(TDP_EINVAL, "tdp_blend_finish: null device pointer");
+  if (!aligned(acc, 16) || !aligned(out, 16)) return fail(TDP_EINVAL, "tdp_blend_finish: misaligned pointer");
+  if (p.out_dtype == TDP_F32 && static_cast<const void*>(acc) == out) return TDP_OK;
+  const int64_t n4 = (int64_t)p.B * p.rows * p.C / 4;  // C * 4 bytes is a multiple of 16
+  const int64_t blocks = (n4 + kBlock - 1) / kBlock;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const f32x4* a4 = reinterpret_cast<const f32x4*>(acc);
+  if (p.out_dtype == TDP_BF16)
+    hipLaunchKernelGGL(blend_finish_kernel<TDP_BF16>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a4, out, n4);
+  else
+    hipLaunchKernelGGL(blend_finish_kernel<TDP_F32>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a4, out, n4);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend_finish: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
 }
 
