@@ -13,6 +13,8 @@ from .tdp_oracle import (  # noqa: F401
     extract,
     f32_to_bf16_bits,
     guard_holds,
+    pixel_blend,
+    pixel_intervals,
     round_robin_rank,
     split_by_count,
     tile_generated_tokens,

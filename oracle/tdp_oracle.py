@@ -301,6 +301,49 @@ def blend(tile_outputs, extracted, shape, tiling, num_cond: int):
 
 
 # --------------------------------------------------------------------------
+# Spatial blend of decoded pixel tiles
+# --------------------------------------------------------------------------
+
+def pixel_intervals(dim: int, num_tiles: int, overlap: int, scale: int) -> list[tuple[int, int]]:
+    """Pixel rows (or columns) that the decode of each latent tile covers.
+
+    Source: mold #673, "Scope" (the VAE decode is tiled spatially so that a
+    large frame need not be decoded whole) and DistVAE docs, "Choosing a tile
+    window" (tiles and overlaps are set per spatial axis).  Reading: a latent
+    cell decodes to ``scale`` pixels on the axis, so latent tile [a, b)
+    decodes to pixels [scale*a, scale*b) and neighbours overlap by
+    scale*overlap pixels.
+    """
+    return [(scale * a, scale * b) for a, b in split_by_count(dim, num_tiles, overlap)]
+
+
+def pixel_blend(tiles, latent_hw, tiling_hw, scale_hw):
+    """Recombine decoded pixel tiles (fp64).
+
+    ``tiles[t]``: (B, C, frames, h_t, w_t) arrays, tile t = i_h * n_w + i_w;
+    ``latent_hw`` = (H, W) latent cells, ``tiling_hw`` = ((n_h, o_h),
+    (n_w, o_w)), ``scale_hw`` = pixels per cell.  Source: TDP docs, "What it
+    is" (overlaps are blended with trapezoidal masks that sum to one) and
+    mold #673, "Scope" (spatial VAE decode tiling).  Reading: the windows are
+    those of the latent blend taken in pixel units, ramps over the
+    scale*overlap overlapping pixels; frames are not tiled; the sum runs over
+    tiles in ascending index from zero.  Returns ``(out, magnitude)``.
+    """
+    ivs = [pixel_intervals(d, n, o, s) for d, (n, o), s in zip(latent_hw, tiling_hw, scale_hw)]
+    ovl = [o * s for (_, o), s in zip(tiling_hw, scale_hw)]
+    B, C, Fo = tiles[0].shape[:3]
+    out = np.zeros((B, C, Fo, latent_hw[0] * scale_hw[0], latent_hw[1] * scale_hw[1]), dtype=np.float64)
+    mag = np.zeros_like(out)
+    for t, (i, j) in enumerate(itertools.product(range(len(ivs[0])), range(len(ivs[1])))):
+        (y0, y1), (x0, x1) = ivs[0][i], ivs[1][j]
+        w = np.outer(window_f64(ivs[0], i, ovl[0]), window_f64(ivs[1], j, ovl[1]))
+        term = w * np.asarray(tiles[t], dtype=np.float64)
+        out[:, :, :, y0:y1, x0:x1] += term
+        mag[:, :, :, y0:y1, x0:x1] += np.abs(term)
+    return out, mag
+
+
+# --------------------------------------------------------------------------
 # bf16 storage
 # --------------------------------------------------------------------------
 

@@ -512,3 +512,61 @@ def test_quality_ratio_matches_geometry_and_balance():
     q = O.tiling_quality(dims, ivs, 8)
     assert q["rank_cells"][4:] == [0, 0, 0, 0]
     assert q["imbalance"] == Fraction(43 * 8, 161) - 1
+
+
+# --------------------------------------------------------------------------
+# Spatial blend of decoded pixel tiles (mold #673, "Scope")
+# --------------------------------------------------------------------------
+
+def test_pixel_windows_partition_of_unity_exact():
+    rng = np.random.default_rng(41)
+    for _ in range(40):
+        dim = int(rng.integers(2, 30))
+        n = int(rng.integers(1, 5))
+        o = 0 if n == 1 else int(rng.integers(0, dim // (n + 1) + 1))
+        if dim - o < n:
+            continue
+        s = int(rng.integers(1, 9))
+        ivs = O.pixel_intervals(dim, n, o, s)
+        assert ivs[0][0] == 0 and ivs[-1][1] == dim * s
+        sums = [Fraction(0)] * (dim * s)
+        for i, (a, _) in enumerate(ivs):
+            for jj, w in enumerate(OT.window_exact(ivs, i, o * s)):
+                sums[a + jj] += w
+        assert all(x == 1 for x in sums), (dim, n, o, s)
+
+
+def test_pixel_blend_reassembles_an_image():
+    """Tiles cut from one image blend back to it: the windows sum to one."""
+    rng = np.random.default_rng(42)
+    for hw, tiling, scale in [((6, 10), ((2, 2), (3, 2)), (4, 8)), ((5, 7), ((1, 0), (2, 1)), (3, 2)),
+                              ((9, 9), ((3, 2), (3, 2)), (2, 2))]:
+        B, C, Fo = 2, 3, 2
+        img = rng.standard_normal((B, C, Fo, hw[0] * scale[0], hw[1] * scale[1]))
+        ivs = [O.pixel_intervals(d, n, o, s) for d, (n, o), s in zip(hw, tiling, scale)]
+        tiles = [img[:, :, :, y0:y1, x0:x1] for (y0, y1) in ivs[0] for (x0, x1) in ivs[1]]
+        out, mag = O.pixel_blend(tiles, hw, tiling, scale)
+        assert np.allclose(out, img, rtol=0, atol=1e-14 * np.abs(img).max() * 4)
+        assert np.all(mag >= np.abs(out) - 1e-12)
+
+
+def test_pixel_blend_scale_one_is_the_latent_blend():
+    """At one pixel per cell the pixel blend is the latent blend of a one-frame grid."""
+    rng = np.random.default_rng(43)
+    hw, tiling = (8, 12), ((2, 2), (3, 2))
+    shape, tiling3 = (1,) + hw, ((1, 0),) + tiling
+    N = int(np.prod(shape))
+    ex = O.extract(np.zeros((1, N, 4), np.float32), OT_grid(shape), shape, tiling3, 0)
+    ys, tiles = [], []
+    for et in ex["tiles"]:
+        y = rng.standard_normal((1, len(et["rows"]), 4))
+        ys.append(y)
+        _, sh, sw = et["tile"]["size"]
+        tiles.append(y.reshape(1, sh, sw, 4).transpose(0, 3, 1, 2)[:, :, None])   # (B, C, 1, h, w)
+    ref, _ = O.blend(ys, ex, shape, tiling3, 0)
+    out, _ = O.pixel_blend(tiles, hw, tiling, (1, 1))
+    assert np.array_equal(out[:, :, 0].transpose(0, 2, 3, 1).reshape(1, N, 4), ref)
+
+
+def OT_grid(shape):
+    return grid_positions(1, shape, (1, 1, 1))
