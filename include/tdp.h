@@ -276,6 +276,57 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
  * output bit for bit.  16-byte aligned device pointers. */
 int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* stream);
 
+/* ---- spatial blend of decoded pixel tiles --------------------------------- */
+
+/* The VAE decode of a large frame is tiled too (mold #673, "Scope"; DistVAE
+ * docs, "Choosing a tile window"): latent tile [a, b) on an axis decodes to
+ * pixels [scale*a, scale*b), so neighbouring pixel tiles overlap by
+ * scale*overlap pixels and are recombined with the same trapezoids in pixel
+ * units (ramps over the overlapping pixels; TDP docs, "What it is").  Height
+ * and width are tiled; frames are not. */
+typedef struct tdp_pixel_plan tdp_pixel_plan;
+
+typedef struct {
+  int32_t batch;           /* B >= 1                                            */
+  int32_t channels;        /* C >= 1 decoded channels (3 for RGB)               */
+  int32_t frames;          /* decoded frames, >= 1 (not tiled)                  */
+  int32_t height, width;   /* latent cells H, W (<= TDP_MAX_AXIS)               */
+  int32_t scale[2];        /* pixels per latent cell on height and width; the   */
+                           /* width scale times the element size is a multiple  */
+                           /* of 16 bytes                                       */
+  tdp_axis_tiling axis[2]; /* latent tiling of height and width (guarded)       */
+  int32_t in_dtype;        /* decoded tiles: TDP_F32 or TDP_BF16                */
+  int32_t out_dtype;       /* blended frame: TDP_F32 or TDP_BF16 (RNE)          */
+} tdp_pixel_config;
+
+typedef struct {
+  int32_t index;           /* t = i_h * n_w + i_w                              */
+  int32_t grid[2];         /* (i_h, i_w)                                       */
+  int32_t origin[2];       /* first pixel row and column                       */
+  int32_t shape[2];        /* pixel rows and columns                           */
+  int64_t offset;          /* element offset of the tile in the tile buffer    */
+  int64_t elems;           /* B * C * frames * rows * columns                  */
+} tdp_pixel_tile;
+
+/* Validate and build (host only).  TDP_EINVAL for a null argument, a bad
+ * dtype or a scale below one; TDP_EGUARD as tdp_plan_create; TDP_ESHAPE when
+ * the width scale does not fill 16-byte vectors or sizes leave int32 range
+ * (B*C*frames*H*scale_h rows). */
+int tdp_pixel_plan_create(const tdp_pixel_config* cfg, tdp_pixel_plan** out);
+void tdp_pixel_plan_destroy(tdp_pixel_plan* plan);
+/* Tile t's place: tiles are packed back to back in index order, each a
+ * (B, C, frames, rows, columns) array of in_dtype. */
+int tdp_pixel_plan_tile(const tdp_pixel_plan* plan, int32_t t, tdp_pixel_tile* out);
+/* Elements of the tile buffer and of the output (B, C, frames, H*scale_h,
+ * W*scale_w); tile count. */
+int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_t* out_elems,
+                         int32_t* num_tiles);
+
+/* out = sum over the tiles covering each pixel, ascending t, of
+ * (wH * wW) * tile, fp32 accumulation from zero, rounded once to out_dtype.
+ * Device pointers, 16-byte aligned; tiles holds every tile as packed above. */
+int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream);
+
 /* ---- errors ------------------------------------------------------------ */
 const char* tdp_status_string(int status);
 const char* tdp_last_error(void); /* thread-local, never NULL */

@@ -77,6 +77,31 @@ class tdp_sizes(ctypes.Structure):
     ]
 
 
+class tdp_pixel_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("frames", ctypes.c_int32),
+        ("height", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("scale", ctypes.c_int32 * 2),
+        ("axis", tdp_axis_tiling * 2),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
+class tdp_pixel_tile(ctypes.Structure):
+    _fields_ = [
+        ("index", ctypes.c_int32),
+        ("grid", ctypes.c_int32 * 2),
+        ("origin", ctypes.c_int32 * 2),
+        ("shape", ctypes.c_int32 * 2),
+        ("offset", ctypes.c_int64),
+        ("elems", ctypes.c_int64),
+    ]
+
+
 class tdp_quality(ctypes.Structure):
     _fields_ = [
         ("total_cells", ctypes.c_int64),
@@ -126,6 +151,12 @@ def load_library(path: str = LIB_PATH):
         "tdp_blend": (ctypes.c_int, [vp] * 5),
         "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
+        "tdp_pixel_plan_create": (ctypes.c_int, [ctypes.POINTER(tdp_pixel_config), ctypes.POINTER(vp)]),
+        "tdp_pixel_plan_destroy": (None, [vp]),
+        "tdp_pixel_plan_tile": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_pixel_tile)]),
+        "tdp_pixel_plan_sizes": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                                i32p]),
+        "tdp_pixel_blend": (ctypes.c_int, [vp] * 4),
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tdp_last_error": (ctypes.c_char_p, []),
     }
@@ -453,3 +484,63 @@ def tile_views(plan: Plan, buffers, counts=None):
             "info": info,
         })
     return views
+
+
+# ---------------------------------------------------------------------------
+# Spatial blend of decoded pixel tiles
+# ---------------------------------------------------------------------------
+
+def make_pixel_config(batch, channels, frames, latent_hw, scale_hw, tiling_hw, in_dtype="bf16",
+                      out_dtype=None) -> tdp_pixel_config:
+    """Fill a tdp_pixel_config; ``tiling_hw`` = ((n_h, o_h), (n_w, o_w)) in latent cells."""
+    cfg = tdp_pixel_config()
+    cfg.batch, cfg.channels, cfg.frames = batch, channels, frames
+    cfg.height, cfg.width = latent_hw
+    for a in range(2):
+        cfg.scale[a] = scale_hw[a]
+        cfg.axis[a].num_tiles, cfg.axis[a].overlap = tiling_hw[a]
+    code = lambda d: _DTYPES[d] if isinstance(d, str) else d  # noqa: E731
+    cfg.in_dtype = code(in_dtype)
+    cfg.out_dtype = code(in_dtype if out_dtype is None else out_dtype)
+    return cfg
+
+
+class PixelPlan:
+    """Owning handle of a tdp_pixel_plan."""
+
+    def __init__(self, handle, cfg):
+        self.handle, self.cfg = handle, cfg
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.tdp_pixel_plan_destroy(self.handle)
+            self.handle = None
+
+
+def tdp_pixel_plan_create(cfg: tdp_pixel_config) -> PixelPlan:
+    h = ctypes.c_void_p()
+    _check(load_library().tdp_pixel_plan_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return PixelPlan(h, cfg)
+
+
+def tdp_pixel_plan_tile(plan: PixelPlan, t: int) -> tdp_pixel_tile:
+    info = tdp_pixel_tile()
+    _check(load_library().tdp_pixel_plan_tile(plan.handle, t, ctypes.byref(info)))
+    return info
+
+
+def tdp_pixel_plan_sizes(plan: PixelPlan):
+    """(tile buffer elements, output elements, tile count)."""
+    a, b, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(load_library().tdp_pixel_plan_sizes(plan.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
+    return a.value, b.value, n.value
+
+
+def tdp_pixel_blend(plan: PixelPlan, tiles, out, stream=None):
+    """Enqueue the blend of packed pixel tiles into ``out`` (B, C, frames, H*s_h, W*s_w)."""
+    c = plan.cfg
+    tile_elems, out_elems, _ = tdp_pixel_plan_sizes(plan)
+    dev = out.device
+    _check(load_library().tdp_pixel_blend(plan.handle, _ptr(tiles, "tiles", _torch_dtype(c.in_dtype), tile_elems, dev),
+                                          _ptr(out, "out", _torch_dtype(c.out_dtype), out_elems, dev),
+                                          _stream_handle(stream, dev)))

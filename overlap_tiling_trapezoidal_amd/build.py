@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtdp.so")
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("plan.cpp", "quality.cpp", "kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("plan.cpp", "quality.cpp", "kernels.hip", "pixel.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,248 @@
+// Spatial blend of decoded pixel tiles on gfx950.
+//
+// Sources: mold issue #673, "Scope" (the VAE decode of a large frame is
+// tiled spatially as well); DistVAE docs, "Choosing a tile window" (tiles
+// and overlaps are set per spatial axis); LTX-2 docs, "Tiled Data
+// Parallelism (TDP)", "What it is" (overlaps are blended with trapezoidal
+// masks that sum to one).
+//
+// Latent tile [a, b) on an axis decodes to pixels [s*a, s*b), so the pixel
+// tiling is the latent split scaled by s and neighbours overlap by s*o
+// pixels; the windows are the latent trapezoids in pixel units.  Frames
+// are not tiled.  Tiles (B, C, frames, rows, cols) are packed back to back
+// in tile order; the output is (B, C, frames, H*s_h, W*s_w).
+//
+// The kernel is bound by HBM bandwidth (a fan-in of at most four tile
+// reads per output element).  A workgroup owns a strip of 64 * E output
+// columns (E = elements per 16-byte vector) and kPixRows output rows; each
+// lane computes its columns' width covers and weights once and reuses them
+// for every row, each wave takes consecutive rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "device_common.h"
+#include "plan_internal.h"
+
+namespace tdp {
+
+struct PixelDev {
+  AxisSplit ax[2];   // latent split of height and width
+  int32_t s[2];      // pixels per cell
+  int32_t o[2];      // pixel overlaps s * overlap
+  int32_t B, C, Fo;
+  int32_t Hp, Wp;    // output pixel rows and columns
+  int32_t rows;      // B * C * Fo * Hp output rows
+  int32_t in_dtype, out_dtype;
+  FastDiv by_s[2];   // pixel -> cell
+  FastDiv by_hp;     // output row -> (b, c, f)
+};
+
+// Element offset of tile (i, j): B*C*Fo*s_h*s_w times the latent cells of
+// the tiles before it in row-major order.
+TDP_HD int64_t pixel_tile_offset(const PixelDev& p, int i, int j) {
+  const int64_t cells = (int64_t)split_prefix(p.ax[0], i) * split_total(p.ax[1]) +
+                        (int64_t)split_size(p.ax[0], i) * split_prefix(p.ax[1], j);
+  return (int64_t)p.B * p.C * p.Fo * p.s[0] * p.s[1] * cells;
+}
+
+}  // namespace tdp
+
+struct tdp_pixel_plan {
+  tdp_pixel_config cfg;
+  tdp::PixelDev dev;
+  int64_t tile_elems, out_elems;
+};
+
+namespace tdp {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kPixRows = 16;  // output rows per workgroup (4 consecutive per wave)
+
+template <int IN, int OUT>
+__global__ __launch_bounds__(kBlock) void pixel_blend_kernel(const PixelDev p, const u32x4* __restrict__ tiles,
+                                                             void* __restrict__ out, int n_strips) {
+  constexpr int E = InVec<IN>::E;
+  const int strip = blockIdx.x % n_strips;
+  const int group = blockIdx.x / n_strips;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // Columns x .. x+E-1 of this lane share their covers: s_w is a multiple
+  // of E, so tile edges fall on vector boundaries.
+  const int x = (strip * 64 + lane) * E;
+  const bool col_ok = x < p.Wp;
+  const int xc = col_ok ? x : 0;
+  const Covers cw = split_covers(p.ax[1], (int)fastdiv((uint32_t)xc, p.by_s[1]));
+  const int pw0 = p.s[1] * cw.s0, pw1 = p.s[1] * cw.s1;
+  const int lx0 = xc - p.s[1] * cw.a0, lx1 = xc - p.s[1] * cw.a1;
+  const bool two_w = cw.n > 1;
+  const bool wave_two = __any(two_w);  // else every lane of the wave has one width cover
+  float w0[E], w1[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    w0[e] = ramp(p.ax[1].n, p.o[1], cw.t0, lx0 + e, pw0);
+    w1[e] = two_w ? ramp(p.ax[1].n, p.o[1], cw.t1, lx1 + e, pw1) : 0.0f;
+  }
+
+  constexpr int kPerWave = kPixRows / 4;
+  for (int k = 0; k < kPerWave; ++k) {
+    const int r = group * kPixRows + wave * kPerWave + k;  // wave-uniform
+    if (r >= p.rows) break;
+    const int bcf = (int)fastdiv((uint32_t)r, p.by_hp);
+    const int y = r - bcf * p.Hp;
+    const Covers ch = split_covers(p.ax[0], (int)fastdiv((uint32_t)y, p.by_s[0]));
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+    // ascending tile index: (i0, j0), (i0, j1), (i1, j0), (i1, j1)
+    for (int hi = 0; hi < ch.n; ++hi) {
+      const int i = hi ? ch.t1 : ch.t0;
+      const int ph = p.s[0] * (hi ? ch.s1 : ch.s0);
+      const int ly = y - p.s[0] * (hi ? ch.a1 : ch.a0);
+      const float wy = ramp(p.ax[0].n, p.o[0], i, ly, ph);
+      const int64_t row0 = (int64_t)bcf * ph + ly;
+      // unconditional loads; a missing second width cover re-reads the first
+      const int j1 = two_w ? cw.t1 : cw.t0;
+      const int64_t e0 = pixel_tile_offset(p, i, cw.t0) + row0 * pw0 + lx0;
+      const int64_t e1 = pixel_tile_offset(p, i, j1) + row0 * (two_w ? pw1 : pw0) + (two_w ? lx1 : lx0);
+      const u32x4 v0 = ld_nt(tiles + e0 / E);
+      u32x4 v1 = v0;
+      if (wave_two) v1 = ld_nt(tiles + e1 / E);
+      float a0[E], a1[E];
+      InVec<IN>::unpack(v0, a0);
+      InVec<IN>::unpack(v1, a1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        acc[e] = fmaf(wy * w0[e], a0[e], acc[e]);
+        acc[e] = two_w ? fmaf(wy * w1[e], a1[e], acc[e]) : acc[e];
+      }
+    }
+    if (col_ok) store_out<OUT, E>(out, (int64_t)r * p.Wp + x, acc);
+  }
+}
+
+template <int IN, int OUT>
+hipError_t launch_pixel(const PixelDev& p, const void* tiles, void* out, hipStream_t s) {
+  constexpr int E = InVec<IN>::E;
+  const int n_strips = (p.Wp + 64 * E - 1) / (64 * E);
+  const int64_t groups = ((int64_t)p.rows + kPixRows - 1) / kPixRows;
+  hipLaunchKernelGGL((pixel_blend_kernel<IN, OUT>), dim3((unsigned)(groups * n_strips)), dim3(kBlock), 0, s, p,
+                     reinterpret_cast<const u32x4*>(tiles), out, n_strips);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+}  // namespace
+}  // namespace tdp
+
+using namespace tdp;
+
+extern "C" {
+
+int tdp_pixel_plan_create(const tdp_pixel_config* cfg, tdp_pixel_plan** out) {
+  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_pixel_plan_create: null argument");
+  *out = nullptr;
+  const tdp_pixel_config c = *cfg;
+  if (c.batch < 1 || c.channels < 1 || c.frames < 1)
+    return fail(TDP_EINVAL, "batch, channels and frames must be >= 1 (got %d, %d, %d)", c.batch, c.channels,
+                c.frames);
+  if (c.height < 1 || c.width < 1) return fail(TDP_EINVAL, "latent height and width must be >= 1");
+  if (c.scale[0] < 1 || c.scale[1] < 1)
+    return fail(TDP_EINVAL, "scale must be >= 1 pixel per cell (got %d, %d)", c.scale[0], c.scale[1]);
+  const int ein = dtype_bytes(c.in_dtype), eout = dtype_bytes(c.out_dtype);
+  if (!ein || !eout) return fail(TDP_EINVAL, "dtypes must be TDP_F32 or TDP_BF16");
+  PixelDev d;
+  memset(&d, 0, sizeof d);
+  const int32_t dims[2] = {c.height, c.width};
+  for (int a = 0; a < 2; ++a) {
+    const int st = build_axis(1 + a, dims[a], c.axis[a], true, &d.ax[a]);
+    if (st != TDP_OK) return st;
+  }
+  const int vec = 16 / ein;
+  if (c.scale[1] % vec != 0)
+    return fail(TDP_ESHAPE,
+                "width scale %d: pixel tiles must start and end on 16-byte vectors, so it must be a multiple of "
+                "%d for this input dtype",
+                c.scale[1], vec);
+  const int64_t hp = (int64_t)c.height * c.scale[0], wp = (int64_t)c.width * c.scale[1];
+  const int64_t rows = (int64_t)c.batch * c.channels * c.frames * hp;
+  if (hp > INT32_MAX || wp > INT32_MAX || rows > INT32_MAX)
+    return fail(TDP_ESHAPE, "%lld output rows of %lld pixels exceed the int32 range", (long long)rows,
+                (long long)wp);
+  for (int a = 0; a < 2; ++a) {
+    d.s[a] = c.scale[a];
+    d.o[a] = c.axis[a].overlap * c.scale[a];
+    d.by_s[a] = make_fastdiv((uint32_t)c.scale[a]);
+  }
+  d.B = c.batch;
+  d.C = c.channels;
+  d.Fo = c.frames;
+  d.Hp = (int32_t)hp;
+  d.Wp = (int32_t)wp;
+  d.rows = (int32_t)rows;
+  d.in_dtype = c.in_dtype;
+  d.out_dtype = c.out_dtype;
+  d.by_hp = make_fastdiv((uint32_t)hp);
+  tdp_pixel_plan* p = new (std::nothrow) tdp_pixel_plan;
+  if (!p) return fail(TDP_EINVAL, "out of host memory");
+  p->cfg = c;
+  p->dev = d;
+  p->tile_elems = (int64_t)c.batch * c.channels * c.frames * c.scale[0] * c.scale[1] *
+                  ((int64_t)split_total(d.ax[0]) * split_total(d.ax[1]));
+  p->out_elems = rows * wp;
+  *out = p;
+  return TDP_OK;
+}
+
+void tdp_pixel_plan_destroy(tdp_pixel_plan* plan) { delete plan; }
+
+int tdp_pixel_plan_tile(const tdp_pixel_plan* plan, int32_t t, tdp_pixel_tile* out) {
+  if (!plan || !out) return fail(TDP_EINVAL, "tdp_pixel_plan_tile: null argument");
+  const PixelDev& d = plan->dev;
+  const int T = d.ax[0].n * d.ax[1].n;
+  if (t < 0 || t >= T) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", t, T);
+  const int i = t / d.ax[1].n, j = t % d.ax[1].n;
+  tdp_pixel_tile r;
+  r.index = t;
+  r.grid[0] = i;
+  r.grid[1] = j;
+  r.origin[0] = d.s[0] * split_start(d.ax[0], i);
+  r.origin[1] = d.s[1] * split_start(d.ax[1], j);
+  r.shape[0] = d.s[0] * split_size(d.ax[0], i);
+  r.shape[1] = d.s[1] * split_size(d.ax[1], j);
+  r.offset = pixel_tile_offset(d, i, j);
+  r.elems = (int64_t)d.B * d.C * d.Fo * r.shape[0] * r.shape[1];
+  *out = r;
+  return TDP_OK;
+}
+
+int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_t* out_elems, int32_t* num_tiles) {
+  if (!plan || !tile_elems || !out_elems || !num_tiles) return fail(TDP_EINVAL, "tdp_pixel_plan_sizes: null argument");
+  *tile_elems = plan->tile_elems;
+  *out_elems = plan->out_elems;
+  *num_tiles = plan->dev.ax[0].n * plan->dev.ax[1].n;
+  return TDP_OK;
+}
+
+int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream) {
+  if (!plan) return fail(TDP_EINVAL, "tdp_pixel_blend: null plan");
+  if (!tiles || !out) return fail(TDP_EINVAL, "tdp_pixel_blend: null device pointer");
+  if (!aligned16(tiles) || !aligned16(out)) return fail(TDP_EINVAL, "tdp_pixel_blend: tiles and out must be 16-byte aligned");
+  const PixelDev& p = plan->dev;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p.in_dtype == TDP_BF16)
+    e = p.out_dtype == TDP_BF16 ? launch_pixel<TDP_BF16, TDP_BF16>(p, tiles, out, s)
+                                : launch_pixel<TDP_BF16, TDP_F32>(p, tiles, out, s);
+  else
+    e = p.out_dtype == TDP_BF16 ? launch_pixel<TDP_F32, TDP_BF16>(p, tiles, out, s)
+                                : launch_pixel<TDP_F32, TDP_F32>(p, tiles, out, s);
+  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_pixel_blend: kernel launch failed: %s", hipGetErrorString(e));
+  return TDP_OK;
+}
+
+}  // extern "C"

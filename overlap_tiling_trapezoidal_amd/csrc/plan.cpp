@@ -45,7 +45,7 @@ static const char* kAxisName[3] = {"frames", "height", "width"};
 // Validate one axis.  The split itself (a_i = floor(i*(dim-o)/n), tile i =
 // [a_i, a_{i+1} + o)) is the closed form in plan_internal.h, shared with the
 // kernels: neighbours overlap by exactly o cells and the last tile ends at dim.
-static int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisSplit* ax) {
+int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisSplit* ax) {
   const char* name = kAxisName[d];
   if (t.num_tiles < 1) return fail(TDP_EINVAL, "%s: num_tiles must be >= 1 (got %d)", name, t.num_tiles);
   if (t.overlap < 0) return fail(TDP_EINVAL, "%s: overlap must be >= 0 (got %d)", name, t.overlap);

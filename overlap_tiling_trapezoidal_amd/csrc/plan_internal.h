@@ -165,6 +165,8 @@ struct tdp_plan {
 };
 
 namespace tdp {
+// Validate axis d (0 frames, 1 height, 2 width) of length dim and fill *ax.
+int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisSplit* ax);
 void set_error(const char* fmt, ...);
 int fail(int status, const char* fmt, ...);
 int dtype_bytes(int32_t dtype);
