@@ -36,16 +36,14 @@
 namespace tdp {
 namespace {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = kThreads;
 constexpr int kWaves = kBlock / 64;
-constexpr int kLatRows = 1;        // latent rows per lane in one extract workgroup
 constexpr int kPosUnroll = 4;      // position rows in flight per thread (copy pass)
 constexpr int kExtUnroll = 8;      // position rows in flight per thread (extent pass)
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kCondRowsPerBlock = 64;
-constexpr int kBlendRows = 2;      // generated rows per lane in one blend workgroup
 constexpr int kXcds = 8;           // accelerator dies; workgroups are dealt to them round-robin
 
 // ---------------------------------------------------------------------------
@@ -270,8 +268,8 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
 
   // 3. copy the kept rows: latent vectors, then shifted positions.
   const int V = p.vin;
-  const int rpp = kBlock / V;
-  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int rpp = p.rpp;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   const int total = n_kept * p.B;
   if (r < rpp) {
     for (int e = r; e < total; e += rpp) {
@@ -336,16 +334,15 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
 // are built: the table setup runs while those loads are in flight.
 __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int blk) {
   const int V = p.vin;
-  const int rpp = kBlock / V;
-  const int rows = rpp * kLatRows;
-  const int nchunk = (p.W + rows - 1) / rows;
-  const int line = blk / nchunk;
-  const int w0 = (blk - line * nchunk) * rows;
+  const int rpp = p.rpp;
+  const int rows = p.lat_rows;
+  const int line = (int)fastdiv((uint32_t)blk, p.by_lat_chunks);
+  const int w0 = (blk - line * p.lat_chunks) * rows;
   const int nrow = min(rows, p.W - w0);
-  const int b = line / (p.F * p.H);
+  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
   const int fh = line - b * (p.F * p.H);
-  const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
-  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   const bool lane_on = r < rpp;
   const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w0) * V + vv;
 
@@ -364,7 +361,7 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
   for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
-    const int combo = e / nw, iw = e - (e / nw) * nw;
+    const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
     sm.line.rowoff[combo][iw] = (line_row0(p, b, i, lf, j, lh, sh, iw) + w0) * V;
@@ -494,9 +491,9 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
                                  void* __restrict__ out, int64_t dst0, int w0) {
   constexpr int SU = 4 / NC < kBlendRows ? 4 / NC : kBlendRows;
   const int V = p.vin;
-  const int rw = 64 / V;
+  const int rw = p.rw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane / V, vv = lane - lr * V;
+  const int lr = (int)fastdiv((uint32_t)lane, p.by_vin), vv = lane - lr * V;
   const bool lane_on = lr < rw;
 #pragma unroll
   for (int sub = 0; sub < kBlendRows; sub += SU) {
@@ -520,8 +517,6 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
   }
 }
 
-// Rows per blend workgroup: 4 waves x (64 / V) rows x kBlendRows.
-__host__ __device__ inline int blend_chunk_rows_for(int V) { return kWaves * (64 / V) * kBlendRows; }
 
 // Generated rows: one workgroup per (b, f, h, chunk of rpp * kBlendRows
 // rows), one pass each; many short workgroups let the dispatcher overlap
@@ -536,18 +531,17 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   const int V = p.vin;
 
   if (bid < n_gen_blocks) {
-    const int rows = blend_chunk_rows_for(V);  // rows per chunk
-    const int nchunk = (p.W + rows - 1) / rows;
-    const int line = bid / nchunk;
-    const int w0 = (bid - line * nchunk) * rows;
-    const int b = line / (p.F * p.H);
+    const int rows = p.blend_rows;  // rows per chunk
+    const int line = (int)fastdiv((uint32_t)bid, p.by_blend_chunks);
+    const int w0 = (bid - line * p.blend_chunks) * rows;
+    const int b = (int)fastdiv((uint32_t)line, p.by_FH);
     const int fh = line - b * (p.F * p.H);
-    const int f = fh / p.H, h = fh - (fh / p.H) * p.H;
+    const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
     LineCombos lc;
     lc.init(p, f, h);
     const int nw = p.ax[2].n;
     for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
-      const int combo = e / nw, iw = e - (e / nw) * nw;
+      const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
       int i, lf, sf, j, lh, sh;
       lc.get(combo, f, h, i, lf, sf, j, lh, sh);
       sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
@@ -566,8 +560,8 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   }
 
   // conditioning rows: (1/k) * sum over the k tiles that keep the token
-  const int rpp = kBlock / V;
-  const int r = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int rpp = p.rpp;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   if (r >= rpp) return;
   const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
   const int cid = bid - n_gen_blocks;
@@ -603,8 +597,7 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
 
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
-  const int rows = blend_chunk_rows_for(p.vin);
-  const int n_gen = p.B * p.F * p.H * ((p.W + rows - 1) / rows);
+  const int n_gen = p.B * p.F * p.H * p.blend_chunks;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
   hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), 0, s, p,
                      reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
@@ -628,8 +621,8 @@ __device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int 
                                 const u32x4* __restrict__ tile_out, float* __restrict__ acc) {
   constexpr int E = InVec<IN>::E;
   const int V = p.vin;
-  const int rpp = kBlock / V;
-  const int lr = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int rpp = p.rpp;
+  const int lr = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - lr * V;
   if (lr >= rpp) return;
 #pragma unroll
   for (int u = 0; u < kStreamRows; ++u) {
@@ -671,8 +664,8 @@ __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u
                                  const int32_t* __restrict__ cond_row, float* __restrict__ acc, int cap_t) {
   constexpr int E = InVec<IN>::E;
   const int V = p.vin;
-  const int rpp = kBlock / V;
-  const int lr = threadIdx.x / V, vv = threadIdx.x - (threadIdx.x / V) * V;
+  const int rpp = p.rpp;
+  const int lr = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - lr * V;
   if (lr >= rpp) return;
   const int nrows = min(kCondRowsPerBlock, p.Nc - c0);
   for (int jj = lr; jj < nrows; jj += rpp) {
@@ -777,8 +770,7 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T * p.B * 3 * a.pos_parts;
-  const int lat_rows = (kBlock / p.vin) * kLatRows;
-  const int n_lat = p.B * p.F * p.H * ((p.W + lat_rows - 1) / lat_rows);
+  const int n_lat = p.B * p.F * p.H * p.lat_chunks;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_lat), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s,
                      p, a);

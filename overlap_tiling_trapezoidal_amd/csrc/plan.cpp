@@ -162,6 +162,18 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
   if (parts < 1) parts = 1;
   if (parts > 64) parts = 64;
   dev.pos_parts = (int32_t)parts;
+  dev.rpp = kThreads / dev.vin;
+  dev.rw = 64 / dev.vin;
+  dev.lat_rows = dev.rpp * kLatRows;
+  dev.lat_chunks = (dev.W + dev.lat_rows - 1) / dev.lat_rows;
+  dev.blend_rows = (kThreads / 64) * dev.rw * kBlendRows;
+  dev.blend_chunks = (dev.W + dev.blend_rows - 1) / dev.blend_rows;
+  dev.by_vin = make_fastdiv((uint32_t)dev.vin);
+  dev.by_H = make_fastdiv((uint32_t)dev.H);
+  dev.by_FH = make_fastdiv((uint32_t)(dev.F * dev.H));
+  dev.by_nw = make_fastdiv((uint32_t)dev.ax[2].n);
+  dev.by_lat_chunks = make_fastdiv((uint32_t)dev.lat_chunks);
+  dev.by_blend_chunks = make_fastdiv((uint32_t)dev.blend_chunks);
 
   tdp_plan* p = new (std::nothrow) tdp_plan;
   if (!p) return fail(TDP_EINVAL, "out of host memory");

@@ -105,6 +105,11 @@ TDP_HD Covers split_covers(const AxisSplit& a, int x) {
   return c;
 }
 
+// Launch shape shared by the host planner and the kernels.
+constexpr int kThreads = 256;   // threads per workgroup
+constexpr int kLatRows = 1;     // latent rows per lane in one extract workgroup
+constexpr int kBlendRows = 2;   // generated rows per lane in one blend workgroup
+
 // Everything a kernel needs about a plan; passed by value (kernel argument).
 struct PlanDev {
   AxisSplit ax[3];
@@ -118,6 +123,12 @@ struct PlanDev {
   int32_t out_dtype;
   int32_t normalize;  // subtract the per-tile offsets
   int32_t pos_parts;  // position workgroups per (tile, batch element, axis)
+  // Launch geometry and invariant divisors (multiply-shift), from the host:
+  int32_t rpp;        // rows per workgroup pass: kThreads / vin
+  int32_t rw;         // rows per wave instruction: 64 / vin
+  int32_t lat_rows, lat_chunks;      // extract: rows per latent workgroup, chunks per line
+  int32_t blend_rows, blend_chunks;  // blend: rows per workgroup, chunks per line
+  FastDiv by_vin, by_H, by_FH, by_nw, by_lat_chunks, by_blend_chunks;
 };
 
 // Tile t -> per-axis tile index (row-major, width fastest).
