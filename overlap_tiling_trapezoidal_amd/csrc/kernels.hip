@@ -43,7 +43,13 @@ constexpr int kExtUnroll = 8;      // position rows in flight per thread (extent
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
-constexpr int kCondRowsPerBlock = 64;
+constexpr int kSelPlanes = 6;      // position planes reduced per pass by a selection workgroup
+constexpr int kSelRows = 2;        // rows per thread per pass of that reduction
+constexpr int kCopyBatch = 8;      // kept conditioning rows in flight per lane
+constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
+constexpr int kCondTokens = 16;        // conditioning tokens per blend workgroup
+constexpr int kCondTiles = 256;        // plans up to this many tiles cache cond_row and slots in LDS
+constexpr int kCondBatch = 8;          // tile rows in flight per lane
 constexpr int kXcds = 8;           // accelerator dies; workgroups are dealt to them round-robin
 
 // ---------------------------------------------------------------------------
@@ -208,33 +214,67 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
                                   int t, int chunk) {
   const TileBox tb = tile_box(p, t);
 
-  // 1. extent [min start, max end) of the tile on every (batch, axis).
-  for (int e = 0; e < p.B * 3; ++e) {
-    const float2 x = tile_plane_extent(p, tb, a.pos + (int64_t)e * p.rows, sm.red);
-    if (threadIdx.x == 0) {
-      ext[2 * e] = x.x;
-      ext[2 * e + 1] = x.y;
+  // 1. extent [min start, max end) of the tile on every (batch, axis): six
+  //    planes per pass, each row's source index shared by the planes.
+  for (int e0 = 0; e0 < p.B * 3; e0 += kSelPlanes) {
+    float lo[kSelPlanes], hi[kSelPlanes];
+#pragma unroll
+    for (int q = 0; q < kSelPlanes; ++q) {
+      lo[q] = INFINITY;
+      hi[q] = -INFINITY;
+    }
+    for (int r0 = 0; r0 < tb.s.gen; r0 += kBlock * kSelRows) {
+      f32x2 v[kSelRows][kSelPlanes];
+#pragma unroll
+      for (int u = 0; u < kSelRows; ++u) {
+        const int r = r0 + u * kBlock + (int)threadIdx.x;
+        const int n = tile_row_source(p, tb, r < tb.s.gen ? r : 0);  // a repeat keeps min and max
+#pragma unroll
+        for (int q = 0; q < kSelPlanes; ++q) {
+          const int e = min(e0 + q, p.B * 3 - 1);                     // so does a repeated plane
+          v[u][q] = ld_plane(a.pos + (int64_t)e * p.rows, n);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSelRows; ++u)
+#pragma unroll
+        for (int q = 0; q < kSelPlanes; ++q) {
+          lo[q] = fminf(lo[q], v[u][q].x);
+          hi[q] = fmaxf(hi[q], v[u][q].y);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kSelPlanes; ++q) {
+      const float2 x = block_minmax(lo[q], hi[q], sm.red);
+      if (threadIdx.x == 0 && e0 + q < p.B * 3) {
+        ext[2 * (e0 + q)] = x.x;
+        ext[2 * (e0 + q) + 1] = x.y;
+      }
     }
   }
   __syncthreads();
 
   // 2. keep test.  The kept tokens before this chunk are counted again here
   //    (cheap compares) so that chunks compact independently.
+  // Every batch element is tested (no early exit), so the loads of all of
+  // them can be in flight together.
   auto keeps = [&](int c) -> bool {
     bool keep = false;
-    for (int b = 0; b < p.B && !keep; ++b) {
+#pragma unroll 4
+    for (int b = 0; b < p.B; ++b) {
       const f32x2* pc = a.pos + (int64_t)b * 3 * p.rows + p.N + c;
       const f32x2 x0 = pc[0], x1 = pc[p.rows], x2 = pc[2 * (int64_t)p.rows];
       const float* e = ext + b * 6;
       const bool inside =
           x0.x < e[1] && x0.y > e[0] && x1.x < e[3] && x1.y > e[2] && x2.x < e[5] && x2.y > e[4];
-      keep = inside || x0.x < 0.0f;
+      keep = keep || inside || x0.x < 0.0f;
     }
     return keep;
   };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = chunk * kSelChunk;
   int before = 0;
+#pragma unroll 4
   for (int c = threadIdx.x; c < c0; c += kBlock) before += keeps(c) ? 1 : 0;
   for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
   if (lane == 0) sm.sel.wave_tot[wave] = before;
@@ -266,27 +306,50 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
   if (last_chunk && threadIdx.x == 0) a.tile_count[t] = tb.s.gen + base + n_kept;
   __syncthreads();
 
-  // 3. copy the kept rows: latent vectors, then shifted positions.
+  // 3. copy the kept rows: latent vectors, then shifted positions.  Loads
+  //    go out in batches (then their stores), not one round trip per row.
   const int V = p.vin;
   const int rpp = p.rpp;
   const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
-  const int total = n_kept * p.B;
   if (r < rpp) {
-    for (int e = r; e < total; e += rpp) {
-      const int b = e / n_kept, j = e - (e / n_kept) * n_kept;
-      const int cc = sm.sel.kept_c[j];
-      const int64_t src = (int64_t)b * p.rows + p.N + cc;
-      const int64_t dst = tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + j;
-      st_nt(a.tile_lat + dst * V + vv, ld_nt(a.latent + src * V + vv));
+    for (int b = 0; b < p.B; ++b) {
+      const u32x4* src = a.latent + ((int64_t)b * p.rows + p.N) * V + vv;
+      u32x4* dst = a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base) * V + vv;
+      for (int j0 = r; j0 < n_kept; j0 += rpp * kCopyBatch) {
+        u32x4 v[kCopyBatch];
+#pragma unroll
+        for (int q = 0; q < kCopyBatch; ++q) {
+          const int j = j0 + q * rpp;
+          v[q] = ld_nt(src + (int64_t)sm.sel.kept_c[j < n_kept ? j : j0] * V);
+        }
+#pragma unroll
+        for (int q = 0; q < kCopyBatch; ++q) {
+          const int j = j0 + q * rpp;
+          if (j < n_kept) st_nt(dst + (int64_t)j * V, v[q]);
+        }
+      }
     }
   }
-  for (int e = threadIdx.x; e < total * 3; e += kBlock) {
-    const int j = e % n_kept, bd = e / n_kept;  // bd = b * 3 + d
-    const int cc = sm.sel.kept_c[j];
-    const f32x2 v = a.pos[(int64_t)bd * p.rows + p.N + cc];
-    const float o = p.normalize ? ext[bd * 2] : 0.0f;
-    const int b = bd / 3, d = bd - (bd / 3) * 3;
-    st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v - o);
+  // n_kept <= kSelChunk == kBlock: thread j copies token j on every plane
+  static_assert(kSelChunk == kBlock, "one kept token per thread");
+  const int j = threadIdx.x;
+  const int cj = j < n_kept ? sm.sel.kept_c[j] : 0;  // token 0 exists whenever selection runs
+  for (int bd0 = 0; bd0 < p.B * 3; bd0 += kSelPlanes) {  // bd = b * 3 + d
+    f32x2 v[kSelPlanes];
+#pragma unroll
+    for (int q = 0; q < kSelPlanes; ++q) {
+      const int bd = min(bd0 + q, p.B * 3 - 1);
+      v[q] = a.pos[(int64_t)bd * p.rows + p.N + cj];
+    }
+#pragma unroll
+    for (int q = 0; q < kSelPlanes; ++q) {
+      const int bd = bd0 + q;
+      if (bd < p.B * 3 && j < n_kept) {
+        const float o = p.normalize ? ext[bd * 2] : 0.0f;
+        const int b = bd / 3, d = bd - b * 3;
+        st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v[q] - o);
+      }
+    }
   }
 }
 
@@ -380,6 +443,21 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   }
 }
 
+// Workgroups are dealt to the XCDs round-robin by index.  Index `bid` of
+// `items * parts` workgroups -> (item, part) such that the parts of one item
+// get indices equal mod kXcds and so share one L2; items past the last full
+// group of kXcds keep the plain order.
+__device__ inline void xcd_group(int bid, int items, int parts, int& item, int& part) {
+  const int grouped = items / kXcds * kXcds * parts;
+  if (bid < grouped) {
+    part = (bid / kXcds) % parts;
+    item = bid / (kXcds * parts) * kXcds + bid % kXcds;
+  } else {
+    part = (bid - grouped) % parts;
+    item = grouped / parts + (bid - grouped) / parts;
+  }
+}
+
 // One launch, three kinds of workgroups (independent, disjoint outputs):
 //   [0, n_sel)                 conditioning selection per (tile, chunk);
 //   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
@@ -391,25 +469,18 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
   __shared__ ExtractShared sm;
   int bid = blockIdx.x;
   if (bid < a.n_sel) {
+    // every chunk of a tile reduces the tile's position planes: keep them on one XCD
     const int per_tile = (p.Nc + kSelChunk - 1) / kSelChunk;
-    extract_selection(p, a, sm, dyn, bid / per_tile, bid - (bid / per_tile) * per_tile);
+    int t, chunk;
+    xcd_group(bid, p.T, per_tile, t, chunk);
+    extract_selection(p, a, sm, dyn, t, chunk);
     return;
   }
   bid -= a.n_sel;
   if (bid < a.n_pos) {
-    // Workgroups go to the 8 XCDs round-robin by index, and every part of a
-    // plane reads the whole plane: give the parts of one plane indices that
-    // are equal mod 8, so that they share one L2.  Planes past the last full
-    // group of 8 keep the plain order.
+    // every part of a plane reads the whole plane: keep them on one XCD
     int plane, part;
-    const int grouped = (a.n_pos / a.pos_parts) / kXcds * kXcds * a.pos_parts;
-    if (bid < grouped) {
-      part = (bid / kXcds) % a.pos_parts;
-      plane = bid / (kXcds * a.pos_parts) * kXcds + bid % kXcds;
-    } else {
-      part = (bid - grouped) % a.pos_parts;
-      plane = grouped / a.pos_parts + (bid - grouped) / a.pos_parts;
-    }
+    xcd_group(bid, a.n_pos / a.pos_parts, a.pos_parts, plane, part);
     const int d = plane % 3;
     const int b = (plane / 3) % p.B;
     const int t = plane / (3 * p.B);
@@ -521,54 +592,87 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
 // Generated rows: one workgroup per (b, f, h, chunk of rpp * kBlendRows
 // rows), one pass each; many short workgroups let the dispatcher overlap
 // the tail of one with the start of the next.
+// Conditioning rows: (1/k) * sum, ascending t, over the k tiles that keep
+// the token (k = non-negative entries of its cond_row column; 0 when k = 0).
+// Workgroup `cid` = (batch element, chunk of kCondTokens tokens).  The
+// chunk's cond_row entries and every tile's slot go to LDS in one parallel
+// pass, then each lane keeps kCondBatch tile rows in flight.
 template <int IN, int OUT>
-__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
-                                                       const int32_t* __restrict__ cond_row,
-                                                       void* __restrict__ out, int n_gen_blocks) {
+__device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ tile_out,
+                                  const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
   constexpr int E = InVec<IN>::E;
-  __shared__ BlendShared sm;
-  const int bid = blockIdx.x;
-  const int V = p.vin;
-
-  if (bid < n_gen_blocks) {
-    const int rows = p.blend_rows;  // rows per chunk
-    const int line = (int)fastdiv((uint32_t)bid, p.by_blend_chunks);
-    const int w0 = (bid - line * p.blend_chunks) * rows;
-    const int b = (int)fastdiv((uint32_t)line, p.by_FH);
-    const int fh = line - b * (p.F * p.H);
-    const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
-    LineCombos lc;
-    lc.init(p, f, h);
-    const int nw = p.ax[2].n;
-    for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
-      const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
-      int i, lf, sf, j, lh, sh;
-      lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-      sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
-      if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
-    }
-    __syncthreads();
-    const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
-    const int nc = lc.n;
-    if (nc == 1)
-      blend_chunk_rows<IN, OUT, 1>(p, sm, tile_out, out, dst0, w0);
-    else if (nc == 2)
-      blend_chunk_rows<IN, OUT, 2>(p, sm, tile_out, out, dst0, w0);
-    else
-      blend_chunk_rows<IN, OUT, 4>(p, sm, tile_out, out, dst0, w0);
-    return;
-  }
-
-  // conditioning rows: (1/k) * sum over the k tiles that keep the token
-  const int rpp = p.rpp;
-  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
-  if (r >= rpp) return;
-  const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
-  const int cid = bid - n_gen_blocks;
+  extern __shared__ int cond_lds[];  // rowtab[T][kCondTokens], cap[T], k[kCondTokens], base[T] (int64)
+  int* rowtab = cond_lds;
+  int* cap = rowtab + p.T * kCondTokens;
+  int* kcount = cap + p.T;
+  int64_t* base = reinterpret_cast<int64_t*>(kcount + kCondTokens + 1) ;
+  base = reinterpret_cast<int64_t*>((reinterpret_cast<uintptr_t>(base) + 7) & ~uintptr_t(7));
+  const int per_b = (p.Nc + kCondTokens - 1) / kCondTokens;
   const int b = cid / per_b;
-  const int c0 = (cid - b * per_b) * kCondRowsPerBlock;
-  const int nrows = min(kCondRowsPerBlock, p.Nc - c0);
-  for (int jj = r; jj < nrows; jj += rpp) {
+  const int c0 = (cid - b * per_b) * kCondTokens;
+  const int ntok = min(kCondTokens, p.Nc - c0);
+  for (int t = threadIdx.x; t < p.T; t += kBlock) {
+    int i, j, k;
+    tile_grid(p, t, i, j, k);
+    const TileSlot sl = tile_slot(p, i, j, k);
+    cap[t] = sl.cap;
+    base[t] = sl.row_base + (int64_t)b * sl.cap;
+  }
+  for (int e = threadIdx.x; e < p.T * kCondTokens; e += kBlock) {
+    const int t = e / kCondTokens, jj = e - t * kCondTokens;
+    rowtab[e] = jj < ntok ? cond_row[(int64_t)t * p.Nc + c0 + jj] : -1;
+  }
+  __syncthreads();
+  if (threadIdx.x < kCondTokens) {
+    int kc = 0;
+    for (int t = 0; t < p.T; ++t) kc += rowtab[t * kCondTokens + threadIdx.x] >= 0;
+    kcount[threadIdx.x] = kc;
+  }
+  __syncthreads();
+  const int V = p.vin;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
+  if (r >= p.rpp) return;
+  for (int jj = r; jj < ntok; jj += p.rpp) {
+    const int kc = kcount[jj];
+    const float inv = kc > 0 ? 1.0f / (float)kc : 0.0f;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+    for (int t0 = 0; t0 < p.T; t0 += kCondBatch) {
+      u32x4 y[kCondBatch];
+      bool use[kCondBatch];
+#pragma unroll
+      for (int q = 0; q < kCondBatch; ++q) {
+        const int t = t0 + q;
+        const int row = t < p.T ? rowtab[t * kCondTokens + jj] : -1;
+        use[q] = row >= 0 && row < cap[t < p.T ? t : 0];  // rows tdp_extract could have written
+        y[q] = ld_nt(tile_out + (use[q] ? (base[t < p.T ? t : 0] + row) * V : 0) + vv);
+      }
+#pragma unroll
+      for (int q = 0; q < kCondBatch; ++q) {
+        float x[E];
+        InVec<IN>::unpack(y[q], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = use[q] ? fmaf(inv, x[e], acc[e]) : acc[e];
+      }
+    }
+    store_out<OUT, E>(out, (((int64_t)b * p.rows + p.N + c0 + jj) * V + vv) * (int64_t)E, acc);
+  }
+}
+
+// The same sum for plans with more than kCondTiles tiles, one tile at a time.
+template <int IN, int OUT>
+__device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ tile_out,
+                                  const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
+  constexpr int E = InVec<IN>::E;
+  const int V = p.vin;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
+  if (r >= p.rpp) return;
+  const int per_b = (p.Nc + kCondTokens - 1) / kCondTokens;
+  const int b = cid / per_b;
+  const int c0 = (cid - b * per_b) * kCondTokens;
+  const int ntok = min(kCondTokens, p.Nc - c0);
+  for (int jj = r; jj < ntok; jj += p.rpp) {
     const int c = c0 + jj;
     int kc = 0;
     for (int t = 0; t < p.T; ++t) kc += cond_row[(int64_t)t * p.Nc + c] >= 0;
@@ -582,9 +686,9 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
         if (row < 0) continue;
         int i, j, k;
         tile_grid(p, t, i, j, k);
-        const TileSlot s = tile_slot(p, i, j, k);
-        if (row >= s.cap) continue;  // not a row tdp_extract could have written
-        const u32x4 yv = ld_nt(tile_out + (s.row_base + (int64_t)b * s.cap + row) * V + vv);
+        const TileSlot sl = tile_slot(p, i, j, k);
+        if (row >= sl.cap) continue;  // not a row tdp_extract could have written
+        const u32x4 yv = ld_nt(tile_out + (sl.row_base + (int64_t)b * sl.cap + row) * V + vv);
         float x[E];
         InVec<IN>::unpack(yv, x);
 #pragma unroll
@@ -596,10 +700,58 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
 }
 
 template <int IN, int OUT>
+__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
+                                                       const int32_t* __restrict__ cond_row,
+                                                       void* __restrict__ out, int n_gen_blocks) {
+  __shared__ BlendShared sm;
+  const int V = p.vin;
+  // conditioning workgroups first: each is a short dependent chain, so they
+  // start early and run under the generated rows
+  const int n_cond = (int)gridDim.x - n_gen_blocks;
+  if ((int)blockIdx.x < n_cond) {
+    if (p.T <= kCondTiles)
+      blend_cond_cached<IN, OUT>(p, tile_out, cond_row, out, blockIdx.x);
+    else
+      blend_cond_direct<IN, OUT>(p, tile_out, cond_row, out, blockIdx.x);
+    return;
+  }
+  const int bid = blockIdx.x - n_cond;
+  const int rows = p.blend_rows;  // rows per chunk
+  const int line = (int)fastdiv((uint32_t)bid, p.by_blend_chunks);
+  const int w0 = (bid - line * p.blend_chunks) * rows;
+  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
+  const int fh = line - b * (p.F * p.H);
+  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+  LineCombos lc;
+  lc.init(p, f, h);
+  const int nw = p.ax[2].n;
+  for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
+    const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
+    int i, lf, sf, j, lh, sh;
+    lc.get(combo, f, h, i, lf, sf, j, lh, sh);
+    sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
+    if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
+  }
+  __syncthreads();
+  const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
+  const int nc = lc.n;
+  if (nc == 1)
+    blend_chunk_rows<IN, OUT, 1>(p, sm, tile_out, out, dst0, w0);
+  else if (nc == 2)
+    blend_chunk_rows<IN, OUT, 2>(p, sm, tile_out, out, dst0, w0);
+  else
+    blend_chunk_rows<IN, OUT, 4>(p, sm, tile_out, out, dst0, w0);
+}
+
+template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
   const int n_gen = p.B * p.F * p.H * p.blend_chunks;
-  const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
-  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), 0, s, p,
+  const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0;
+  // LDS for the cached conditioning path: rowtab, cap, k, then int64 bases
+  const size_t lds = p.Nc > 0 && p.T <= kCondTiles
+                         ? ((size_t)p.T * kCondTokens + p.T + kCondTokens + 1) * sizeof(int) + 8 + (size_t)p.T * 8
+                         : 0;
+  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
                      reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
   return hipGetLastError();
 }
