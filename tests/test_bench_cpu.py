@@ -1,0 +1,74 @@
+"""bench.py's host-side pieces, on the CPU: the algorithmic byte counts the
+metric divides by, the guard on the committed counter record, and the
+one-GPU contract."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle as O
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _oracle_counts(wl):
+    from synth import make_inputs
+    inp = make_inputs(wl)
+    ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    return np.array([len(et["rows"]) for et in ex["tiles"]]), len(ex["tiles"])
+
+
+def test_4k_compulsory_bytes():
+    wl = WORKLOADS["4k"]
+    counts, T = _oracle_counts(wl)
+    ex, bl, S = bench.compulsory_bytes(wl, counts, T, 2, 2)
+    # S = prod(dim + (n - 1) o) for a count-based split: 16 * 92 * 168
+    assert S == 16 * (68 + 3 * 8) * (120 + 3 * 16) == 247296
+    N, row = 16 * 68 * 120, 128 * 2
+    assert ex == N * row + N * 24 + S * row + S * 24 + 4 * S + 4 * T
+    assert bl == S * row + N * row
+    assert (ex, bl) == (106788928, 96731136)
+
+
+def test_conditioned_counts_kept_rows():
+    wl = WORKLOADS["conditioned"]
+    counts, T = _oracle_counts(wl)
+    ex, bl, S = bench.compulsory_bytes(wl, counts, T, 2, 2)
+    gen = int(np.prod([d + (n - 1) * o for d, (n, o) in zip(wl.shape, wl.tiling)]))
+    assert S > gen and S - gen >= 256 * T          # every reference token is kept by every tile
+    rows, row = wl.tokens + wl.num_cond, wl.batch * wl.channels * 2
+    sel = 4 * T * wl.num_cond + 4 * wl.num_cond
+    assert bl == S * row + rows * row + sel
+
+
+def test_stream_bytes_formula():
+    wl = WORKLOADS["4k"]
+    S, B, C, rows = 247296, 1, 128, 130560
+    got = bench.stream_bytes(wl, S, 2, 2)
+    assert got == S * B * C * 2 + (2 * S - rows) * B * C * 4 + rows * B * C * (4 + 2)
+
+
+def test_traffic_record_is_ignored_when_sources_change(monkeypatch):
+    path = os.path.join(ROOT, bench.PMC_SUMMARY)
+    rec = None
+    for line in open(path):
+        if line.strip().startswith("{") and '"traffic"' in line:
+            rec = json.loads(line)
+    assert rec is not None and rec["workload"] == "4k"
+    monkeypatch.setattr(bench, "sources_hash", lambda: rec["sources_sha256_16"])
+    t = bench.measured_traffic("4k", "extract_kernel")
+    assert t == rec["traffic"]["extract_kernel"]["fetch_bytes"] + rec["traffic"]["extract_kernel"]["write_bytes"]
+    assert bench.measured_traffic("fullres", "extract_kernel") is None
+    monkeypatch.setattr(bench, "sources_hash", lambda: "0" * 16)
+    assert bench.measured_traffic("4k", "extract_kernel") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
