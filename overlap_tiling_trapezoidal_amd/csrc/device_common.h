@@ -26,14 +26,13 @@ __device__ inline void st_nt(T* p, T v) { __builtin_nontemporal_store(v, p); }
 
 // 1-D trapezoid of tile i of n (`size` cells, overlap o) at local cell l:
 // (l+1)/(o+1) on a left ramp, (size-l)/(o+1) on a right ramp, 1 elsewhere.
-// fp32 division is built correctly rounded, so each value equals the host
-// plan's window bit for bit.
+// The kernels run guarded plans only (size >= 2o), where the two ramps never
+// meet, so one division with the numerator chosen per case gives every
+// value ((o+1)/(o+1) is exactly 1).  fp32 division is built correctly
+// rounded, so each value equals the host plan's window bit for bit.
 __device__ inline float ramp(int n, int o, int i, int l, int size) {
-  float w = 1.0f;
-  const float den = (float)(o + 1);
-  if (i > 0 && l < o) w = (float)(l + 1) / den;
-  if (i < n - 1 && l >= size - o) w *= (float)(size - l) / den;
-  return w;
+  const int num = (i > 0 && l < o) ? l + 1 : (i < n - 1 && l >= size - o) ? size - l : o + 1;
+  return (float)num / (float)(o + 1);
 }
 __device__ inline float ramp_weight(const AxisSplit& ax, int i, int l, int size) {
   return ramp(ax.n, ax.o, i, l, size);
