@@ -40,7 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 KERNEL_SOURCES = ("overlap_tiling_trapezoidal_amd/csrc/kernels.hip", "overlap_tiling_trapezoidal_amd/csrc/plan.cpp",
-                  "overlap_tiling_trapezoidal_amd/csrc/plan_internal.h", "include/tdp.h")
+                  "overlap_tiling_trapezoidal_amd/csrc/plan_internal.h",
+                  "overlap_tiling_trapezoidal_amd/csrc/device_common.h", "include/tdp.h")
 PMC_SUMMARY = "profiles/extract_kernel_4k_pmc.md"
 
 
