@@ -167,7 +167,7 @@ __device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r
 // Row tables hold vector offsets, not pointers: a pointer read back from
 // LDS loses its address space and turns every access into a flat one.
 struct LineShared {
-  int64_t rowoff[kMaxCombos][kMaxTiles];  // tile_lat vector of cell w: rowoff + w*V + lane
+  int64_t rowoff[kWaves][kMaxCombos][kMaxTiles];  // per wave: tile_lat vector of cell w = rowoff + w*V + lane
 };
 struct SelShared {
   int wave_tot[kWaves];
@@ -423,13 +423,17 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   LineCombos lc;
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
-  for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
+  // each wave builds its own copy of the row table (no workgroup barrier)
+  int64_t(*rowoff)[kMaxTiles] = sm.line.rowoff[threadIdx.x >> 6];
+  for (int e = threadIdx.x & 63; e < lc.n * nw; e += 64) {
     const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    sm.line.rowoff[combo][iw] = (line_row0(p, b, i, lf, j, lh, sh, iw) + w0) * V;
+    rowoff[combo][iw] = (line_row0(p, b, i, lf, j, lh, sh, iw) + w0) * V;
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int ncombo = lc.n;
   Covers cw[kLatRows];
 #pragma unroll
@@ -437,8 +441,8 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   for (int cb = 0; cb < ncombo; ++cb) {
 #pragma unroll
     for (int u = 0; u < kLatRows; ++u) {
-      if (ok[u]) st_nt(a.tile_lat + sm.line.rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
-      if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + sm.line.rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
+      if (ok[u]) st_nt(a.tile_lat + rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
+      if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
     }
   }
 }
@@ -703,7 +707,7 @@ template <int IN, int OUT>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
                                                        const int32_t* __restrict__ cond_row,
                                                        void* __restrict__ out, int n_gen_blocks) {
-  __shared__ BlendShared sm;
+  __shared__ BlendShared smw[kWaves];
   const int V = p.vin;
   // conditioning workgroups first: each is a short dependent chain, so they
   // start early and run under the generated rows
@@ -725,14 +729,19 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   LineCombos lc;
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
-  for (int e = threadIdx.x; e < lc.n * nw; e += kBlock) {
+  // Each wave builds its own copy of the row table, so no wave waits for
+  // another before issuing its loads.
+  BlendShared& sm = smw[threadIdx.x >> 6];
+  for (int e = threadIdx.x & 63; e < lc.n * nw; e += 64) {
     const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
     sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
     if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
   const int nc = lc.n;
   if (nc == 1)
