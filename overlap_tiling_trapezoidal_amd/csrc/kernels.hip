@@ -12,20 +12,20 @@
 // lanes re-read a valid row and discard it), so the compiler keeps all of a
 // thread's loads in flight instead of waiting before each one.
 //
-// extract is two launches.  The first holds the bulk of the bytes and the
-// reduction that the second depends on:
-//   extent     (tile, batch, axis, chunk of rows): partial [min start,
-//              max end) of the tile's generated positions;
+// extract is one launch with three kinds of workgroups, in grid order:
+//   selection  (tile, chunk of conditioning tokens): the tile's extents on
+//              every (batch, axis), keep test, ordered compaction, copy of
+//              the kept rows;
+//   positions  (tile, batch, axis, part): the plane's extent [min start,
+//              max end), reduced by the workgroup itself, then the shifted
+//              positions and source indices of one part of the tile;
 //   latent     (batch, frame, row, chunk of rows): every latent row is read
 //              once and written to each tile that covers it.
-// The second reads the finished extents:
-//   selection  (tile, chunk of conditioning tokens): keep test, ordered
-//              compaction, copy of the kept rows;
-//   positions  (tile, batch, axis, part): shifted positions of one part of
-//              the tile and its source indices.
-// The extent reduction thus runs under the latent copy instead of before
-// it.  (Splitting the latent copy across both launches, to hide the
-// positions too, measured no faster.)
+// The first two kinds are few and long; dispatched first, they run under
+// the latent copy, and no workgroup ever waits on another.  blend is one
+// launch too: conditioning workgroups first, then one workgroup per chunk
+// of a (batch, frame, row) line that gathers each output row from its
+// covering tile rows (owner computes: no atomics, fixed order).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
