@@ -44,7 +44,7 @@ constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on heigh
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kSelPlanes = 6;      // position planes reduced per pass by a selection workgroup
-constexpr int kSelRows = 2;        // rows per thread per pass of that reduction
+constexpr int kSelRows = 4;        // rows per thread per pass of that reduction
 constexpr int kCopyBatch = 8;      // kept conditioning rows in flight per lane
 constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
 constexpr int kCondTokens = 16;        // conditioning tokens per blend workgroup
