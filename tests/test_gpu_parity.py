@@ -159,6 +159,11 @@ EDGE = {
     "cond_random_pos": dict(shape=(4, 10, 12), tiling=((2, 1), (2, 3), (3, 3)), batch=2, num_cond=300,
                             random_pos=True),
     "wide_4096": dict(shape=(1, 2, 4096), tiling=((1, 0), (2, 0), (3, 512)), channels=16),
+    # more than 256 tiles with conditioning: the blend's per-tile conditioning path
+    "tiles272_cond": dict(shape=(1, 16, 17), tiling=((1, 0), (16, 0), (17, 0)), channels=16, num_cond=20, seed=6),
+    # twelve selection chunks: kept tokens counted across chunks
+    "many_cond": dict(shape=(2, 8, 12), tiling=((1, 0), (2, 2), (2, 3)), num_cond=3000, seed=7),
+    "batch64": dict(shape=(2, 4, 6), tiling=((1, 0), (2, 1), (2, 2)), batch=64, channels=16, seed=8),
 }
 
 

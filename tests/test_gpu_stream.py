@@ -22,6 +22,8 @@ EDGE = {
     "f32_ragged": Workload("f32_ragged", 1, 36, (3, 9, 13), ((1, 0), (2, 3), (3, 3)), dtype="f32", seed=33),
     "cond_frames": Workload("cond_frames", 2, 16, (6, 9, 10), ((2, 2), (2, 3), (2, 3)), num_cond=130, num_ref=20,
                             dtype="bf16", seed=34),
+    "tiles272_cond": Workload("tiles272_cond", 1, 16, (1, 16, 17), ((1, 0), (16, 0), (17, 0)), num_cond=20,
+                              num_ref=5, dtype="bf16", seed=35),
 }
 CASES = {**WORKLOADS, **EDGE}
 
