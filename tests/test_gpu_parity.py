@@ -264,3 +264,40 @@ def test_bf16_output_rounding_bit_exact(cuda):
     bad = np.argwhere(got != want)
     assert len(bad) == 0, [(tuple(i), hex(int(y[tuple(i)].view(np.uint32))), hex(int(got[tuple(i)])),
                             hex(int(want[tuple(i)]))) for i in bad[:5]]
+
+
+def _random_axis(rng, dim_max):
+    while True:
+        dim = int(rng.integers(1, dim_max + 1))
+        n = int(rng.integers(1, min(dim, 5) + 1))
+        o = 0 if n == 1 else int(rng.integers(0, dim // (n + 1) + 1))
+        if dim - o >= n:
+            return dim, (n, o)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configs(seed, cuda):
+    """Seeded random guarded plans: random tilings on all three axes, batch,
+    channel count, dtype, conditioning tokens and positions."""
+    rng = np.random.default_rng(1000 + seed)
+    axes = [_random_axis(rng, m) for m in (6, 14, 40)]
+    shape = tuple(d for d, _ in axes)
+    tiling = tuple(t for _, t in axes)
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    channels = int(rng.choice([4, 8, 12, 36]) if dtype == "f32" else rng.choice([8, 16, 24, 48, 128]))
+    batch = int(rng.integers(1, 4))
+    num_cond = int(rng.choice([0, 0, 5, 40, 300]))
+    wl, inp = _custom_case(shape, tiling, batch=batch, channels=channels, dtype=dtype, num_cond=num_cond,
+                           seed=seed, random_pos=bool(rng.random() < 0.5))
+    label = f"seed {seed}: {shape} {tiling} B{batch} C{channels} {dtype} Nc{num_cond}"
+    out_dtype = "bf16" if rng.random() < 0.5 else "f32"
+    plan = plan_for(wl, out_dtype=out_dtype)
+    _, _, bufs = gpu_extract(plan, inp, cuda, label)
+    ex = oracle_extract(wl, inp)
+    check_extract(plan, bufs, ex, wl.num_cond)
+    tiles = [random_tile_outputs(rng, wl.batch, len(et["rows"]), wl.channels, wl.dtype) for et in ex["tiles"]]
+    buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
+    ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
+    ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
+    out = gpu_blend(plan, buf, bufs["cond_row"], cuda, label)
+    check_blend(out, ref, mag, plan.cfg.out_dtype)
