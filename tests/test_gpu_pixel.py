@@ -74,3 +74,28 @@ def test_pixel_blend_reassembles_image_bit_exact(cfg, cuda):
     tdp.tdp_pixel_blend(plan, x, out)
     torch.cuda.synchronize()
     assert torch.equal(out.cpu().view(torch.int16), img.view(torch.int16))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pixel_blend_random_configs(seed, cuda):
+    from test_gpu_parity import _random_axis
+    rng = np.random.default_rng(4000 + seed)
+    (h, th), (w, tw) = _random_axis(rng, 10), _random_axis(rng, 14)
+    dt = "f32" if rng.random() < 0.4 else "bf16"
+    vec = 4 if dt == "f32" else 8
+    cfg = (int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 3)), (h, w),
+           (int(rng.integers(1, 6)), vec * int(rng.integers(1, 3))), (th, tw), dt)
+    out_dtype = "bf16" if rng.random() < 0.5 else "f32"
+    B, C, Fo, hw, s, tiling, _ = cfg
+    plan = make(cfg, out_dtype)
+    tiles = _tiles_random(cfg, rng)
+    ref, mag = O.pixel_blend(tiles, hw, tiling, s)
+    x = _pack(plan, tiles, dt).to(cuda)
+    out = torch.full(ref.shape, float("nan"), device=cuda,
+                     dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    note(f"pixel random {seed}: {cfg} -> {out_dtype}")
+    tdp.tdp_pixel_blend(plan, x, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    tol = 2e-6 * mag + (4e-3 * np.abs(ref) if out_dtype == "bf16" else 0.0)
+    assert not (np.abs(got - ref) > tol).any()

@@ -104,3 +104,21 @@ def test_stream_tokens_kept_by_no_tile(cuda):
     acc, out = stream_blend(plan, bufs["tile_lat"], bufs["cond_row"], cuda, label="k0s")
     assert torch.all(out[:, N:N + 10] == 0)
     assert torch.equal(_bits(out), _bits(whole))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_stream_random_configs(seed, cuda):
+    """Seeded random plans: streaming equals the fused blend bit for bit."""
+    from test_gpu_parity import _random_axis
+    rng = np.random.default_rng(2000 + seed)
+    axes = [_random_axis(rng, m) for m in (5, 12, 30)]
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    wl = Workload(f"rand{seed}", int(rng.integers(1, 3)), int(rng.choice([8, 16, 24]) if dtype == "bf16" else 8),
+                  tuple(d for d, _ in axes), tuple(t for _, t in axes), num_cond=int(rng.choice([0, 7, 64])),
+                  num_ref=2, dtype=dtype, seed=3000 + seed)
+    out_dtype = "bf16" if rng.random() < 0.5 else "f32"
+    plan, buf, y, cond_row, ref, mag = _setup(wl, out_dtype, cuda)
+    whole = gpu_blend(plan, buf, cond_row, cuda, f"rand {seed}")
+    _, out = stream_blend(plan, y, cond_row, cuda, label=f"rand {seed}")
+    assert torch.equal(_bits(out), _bits(whole))
+    check_blend(out, ref, mag, plan.cfg.out_dtype)
