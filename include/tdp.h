@@ -1,7 +1,7 @@
 /*
  * tdp.h — tiled-data-parallel (TDP) latent tiling on one MI355X (gfx950).
  *
- * Three operations, after the pages that describe TDP:
+ * The hot path is three operations, after the pages that describe TDP:
  *   plan    split a patchified (frames, height, width) latent into
  *           count-specified overlapping tiles, with trapezoidal windows
  *           (LTX-2 docs, "Tiled Data Parallelism (TDP)", sections "What it is"
@@ -17,13 +17,16 @@
  *
  * All tiles run on the calling GPU; what the multi-GPU form sums with one
  * all_reduce is accumulated in place here, with no GPU-to-GPU traffic.
+ * Around it: plan-quality figures (decoded area, seams, round-robin
+ * imbalance), a streaming blend that takes one tile at a time, and the blend
+ * of decoded pixel tiles for a tiled VAE decode.
  *
  * Conventions
  *   - Every function returns TDP_OK (0) or a negative status; the message of
  *     the last failure on the calling thread is in tdp_last_error().
  *   - The library owns only the host plan.  Every device buffer is allocated
  *     and freed by the caller; the library never allocates device memory.
- *   - tdp_extract and tdp_blend only enqueue work on `stream` (a hipStream_t,
+ *   - The device operations only enqueue work on `stream` (a hipStream_t,
  *     NULL = the null stream) and return without synchronizing.  All
  *     arguments are validated before anything is enqueued, so an error
  *     leaves every output untouched.
@@ -234,7 +237,7 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
  * All pointers are device pointers except `plan`; latent/tile_lat 16-byte
  * aligned, pos/tile_pos 8-byte aligned; buffers must not overlap and hold
  * the sizes tdp_plan_sizes() reports (the library cannot check sizes).
-  * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
+ * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
  * pointers, TDP_EHIP on launch failure. */
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 void* tile_lat, float* tile_pos, int32_t* tile_index,
