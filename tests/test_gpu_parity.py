@@ -289,11 +289,12 @@ def test_random_configs(seed, cuda):
     num_cond = int(rng.choice([0, 0, 5, 40, 300]))
     wl, inp = _custom_case(shape, tiling, batch=batch, channels=channels, dtype=dtype, num_cond=num_cond,
                            seed=seed, random_pos=bool(rng.random() < 0.5))
-    label = f"seed {seed}: {shape} {tiling} B{batch} C{channels} {dtype} Nc{num_cond}"
+    normalize = bool(rng.random() < 0.7)
+    label = f"seed {seed}: {shape} {tiling} B{batch} C{channels} {dtype} Nc{num_cond} normalize={normalize}"
     out_dtype = "bf16" if rng.random() < 0.5 else "f32"
-    plan = plan_for(wl, out_dtype=out_dtype)
+    plan = plan_for(wl, out_dtype=out_dtype, normalize=normalize)
     _, _, bufs = gpu_extract(plan, inp, cuda, label)
-    ex = oracle_extract(wl, inp)
+    ex = oracle_extract(wl, inp, normalize=normalize)
     check_extract(plan, bufs, ex, wl.num_cond)
     tiles = [random_tile_outputs(rng, wl.batch, len(et["rows"]), wl.channels, wl.dtype) for et in ex["tiles"]]
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
