@@ -73,6 +73,62 @@ def compulsory_bytes(wl, counts, num_tiles, e_in, e_out):
     return extract, blend, S
 
 
+def naive_bytes(wl, S, e_in):
+    """Bytes a per-tile gather moves on top of the compulsory ones: every
+    tile re-reads its own latent rows and positions, overlaps included."""
+    rows = wl.tokens + wl.num_cond
+    return (S - rows) * wl.batch * (wl.channels * e_in + 24)
+
+
+def rank_share_rate(torch, tdp, dev, sets, wl, world, rank, reps):
+    """One rank's round-robin share: extract of its tiles and its full-size
+    fp32 partial buffer (the all_reduce input), on the rotating input sets.
+    Algorithmic bytes: extract reads the latent rows and positions the
+    rank's tiles cover (each once) and writes its tile rows, positions and
+    index map; blend reads its tile rows and writes the whole fp32 buffer."""
+    import numpy as np
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond,
+                          in_dtype=wl.dtype, out_dtype="f32")
+    plan = tdp.tdp_plan_create_rank(cfg, world, rank)
+    held = tdp.held_tiles(plan)
+    cover = np.zeros(wl.shape, dtype=bool)
+    S_r = 0
+    for t in held:
+        inf = tdp.tdp_plan_tile(plan, t)
+        (f0, h0, w0), (sf, sh, sw) = tuple(inf.origin), tuple(inf.shape)
+        cover[f0:f0 + sf, h0:h0 + sh, w0:w0 + sw] = True
+        S_r += inf.gen_tokens
+    assert wl.num_cond == 0, "the rank-share figure is taken on workloads without conditioning"
+    e_in = 2 if wl.dtype == "bf16" else 4
+    B, C = wl.batch, wl.channels
+    U = int(cover.sum())
+    ex_bytes = U * B * (C * e_in + 24) + S_r * B * (C * e_in + 24) + 4 * S_r + 4 * len(held)
+    bl_bytes = S_r * B * C * e_in + B * wl.tokens * C * 4
+    rs = [{"bufs": tdp.allocate_extract_outputs(plan, dev), "out": tdp.allocate_output(plan, dev)}
+          for _ in range(len(sets))]
+    gstream = torch.cuda.Stream(dev)
+
+    def ex(i):
+        s, b = sets[i % len(sets)], rs[i % len(sets)]["bufs"]
+        tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
+                        b["tile_count"], b["cond_row"], gstream)
+
+    def bl(i):
+        r = rs[i % len(sets)]
+        tdp.tdp_blend(plan, r["bufs"]["tile_lat"], r["bufs"]["cond_row"], r["out"], gstream)
+
+    ex_ms = graph_time_ms(torch, gstream, ex, reps)
+    bl_ms = graph_time_ms(torch, gstream, bl, reps)
+    step = ex_ms + bl_ms
+    return {"world": world, "rank": rank, "tiles": held, "tile_rows": S_r, "covered_rows": U,
+            "extract_ms": round(ex_ms, 5), "extract_bytes": ex_bytes,
+            "extract_gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
+            "partial_blend_ms": round(bl_ms, 5), "partial_blend_bytes": bl_bytes,
+            "partial_blend_gbs": round(bl_bytes / (bl_ms * 1e-3) / 1e9, 1),
+            "gbs": round((ex_bytes + bl_bytes) / (step * 1e-3) / 1e9, 1),
+            "note": "partial buffer in fp32 over the whole latent; the all_reduce itself is not run"}
+
+
 def stream_bytes(wl, S, e_in, e_out):
     """Algorithmic bytes of the streaming blend of all tiles plus the rounding:
     tile rows read once, the fp32 accumulator written for every tile row and
@@ -328,6 +384,7 @@ def main():
     st_bytes = stream_bytes(wl, S, e_in, e_in)
     del accs, views
     pix = pixel_rate(torch, tdp, dev, gstream)
+    share = rank_share_rate(torch, tdp, dev, sets, wl, 4, 0, reps) if wl.num_cond == 0 else None
 
     # plain device copy of the same size as a practical ceiling
     nbytes = 256 << 20
@@ -368,6 +425,7 @@ def main():
             "tokens": wl.tokens,
             "tile_rows": S,
             "bytes_per_step": step_bytes,
+            "naive_bytes_per_step": step_bytes + naive_bytes(wl, S, e_in),
             "buffer_sets": R,
             "normalize_positions": not args.no_normalize,
         },
@@ -382,6 +440,7 @@ def main():
             "stream_blend_gbs": round(st_bytes / (st_ms * 1e-3) / 1e9, 1),
         },
         "pixel_blend": pix,
+        "rank_share": share,
         "copy_ceiling_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",

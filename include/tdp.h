@@ -16,7 +16,9 @@
  *           positions").
  *
  * All tiles run on the calling GPU; what the multi-GPU form sums with one
- * all_reduce is accumulated in place here, with no GPU-to-GPU traffic.
+ * all_reduce is accumulated in place here, with no GPU-to-GPU traffic.  A
+ * rank plan runs one rank's round-robin share instead and writes that
+ * rank's full-size partial sum, the input of the all_reduce.
  * Around it: plan-quality figures (decoded area, seams, round-robin
  * imbalance), a streaming blend that takes one tile at a time, and the blend
  * of decoded pixel tiles for a tiled VAE decode.
@@ -50,7 +52,9 @@
  *     tile_lat  + lat_offset   : (B, capacity_t, C)      dtype in_dtype
  *     tile_pos  + pos_offset   : (B, 3, capacity_t, 2)   float32
  *     tile_index+ index_offset : (capacity_t)            int32 source token
- *   Rows at and past tile_count[t] are not written.
+ *   Rows at and past tile_count[t] are not written.  A rank plan holds only
+ *   its own tiles, in uniform slots, and indexes tile_count by slot
+ *   (tdp_plan_create_rank).
  */
 #ifndef TDP_H
 #define TDP_H
@@ -122,10 +126,13 @@ typedef struct {
   int64_t lat_offset;    /* element offset of the slot in tile_lat/tile_out   */
   int64_t pos_offset;    /* float offset of the slot in tile_pos              */
   int64_t index_offset;  /* int32 offset of the slot in tile_index            */
+                         /* (the three offsets are -1 for a tile that a rank  */
+                         /* plan does not hold)                               */
 } tdp_tile_info;
 
 typedef struct {
-  int32_t num_tiles;        /* T                                              */
+  int32_t num_slots;        /* tiles the plan holds: T, or a rank's share;    */
+                            /* entries of tile_count                          */
   int64_t tile_lat_elems;   /* elements of tile_lat (and tile_out)            */
   int64_t tile_pos_floats;  /* floats of tile_pos                             */
   int64_t tile_index_ints;  /* int32 entries of tile_index                    */
@@ -180,6 +187,34 @@ int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes);
  * "What it is").  On one GPU every tile is local. */
 int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* rank);
 
+/* ---- rank share (host only) ---------------------------------------------- */
+
+/* The share of rank `rank` in a round-robin schedule of the plan's tiles over
+ * `world` ranks (TDP docs, "What it is": tile t runs on rank t mod world,
+ * every rank adds its tiles' weighted outputs into a full-size buffer and
+ * one all_reduce sums the buffers).  The plan holds tiles rank, rank + world,
+ * rank + 2*world, ...; local slot j = t / world.
+ *   tdp_extract  writes the held tiles only: slot j of tile_lat, tile_pos
+ *                and tile_index, and tile_count[j].  cond_row stays (T, Nc)
+ *                for every tile, since k counts the tiles of all ranks.
+ *   tdp_blend    writes the rank's partial sum over the whole output:
+ *                sum over held tiles of W_t * y_t on generated rows and of
+ *                (1/k) * y_t on conditioning rows, in ascending t; rows that
+ *                no held tile covers are 0.  Summed over the ranks (in fp32,
+ *                out_dtype TDP_F32), the partials give the whole plan's blend
+ *                up to the order of the rank sum.
+ *   tdp_blend_tile / tdp_blend_finish take whole plans only (TDP_EINVAL).
+ * Slots are uniform: max over tiles of gen_tokens, plus num_cond, rows per
+ * batch element; tdp_plan_tile gives each held tile's offsets.  A rank with
+ * no tiles (rank >= T) holds none: its extract writes cond_row only and its
+ * blend writes zeros.  world == 1 gives the whole plan.  Errors: TDP_EINVAL
+ * for world < 1 or rank outside [0, world), otherwise as tdp_plan_create. */
+int tdp_plan_create_rank(const tdp_config* cfg, int32_t world, int32_t rank, tdp_plan** out);
+
+/* The plan's round-robin world and rank (1 and 0 for a whole plan) and the
+ * number of tiles it holds. */
+int tdp_plan_local_tiles(const tdp_plan* plan, int32_t* world, int32_t* rank, int32_t* count);
+
 /* ---- plan quality (host only) -------------------------------------------- */
 
 /* Cost figures of a tiling (DistVAE docs, "Choosing a tile window":
@@ -218,7 +253,8 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
  * no scratch memory.
  *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
  *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
- *        tile_count (T) int32: gen_t + kept_t.
+ *        tile_count (one per slot: T, or a rank's share) int32:
+ *          gen_t + kept_t.
  *        cond_row (T * Nc) int32: row of conditioning token c inside tile
  *          t's slot, or -1 when t does not keep it; the number of
  *          non-negative entries in column c is k, the count of tiles that
@@ -269,7 +305,7 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * order on one stream: acc then holds tdp_blend's fp32 sums bit for bit.
  * Any other order gives wrong sums.  Calls that share acc must not overlap.
  * tile_out/acc 16-byte aligned device pointers; cond_row as for tdp_blend.
- * Returns TDP_EINVAL for a bad tile index or pointer. */
+ * Returns TDP_EINVAL for a bad tile index or pointer, or a rank plan. */
 int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
                    float* acc, void* stream);
 

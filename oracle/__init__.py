@@ -15,6 +15,7 @@ from .tdp_oracle import (  # noqa: F401
     guard_holds,
     pixel_blend,
     pixel_intervals,
+    rank_partial,
     round_robin_rank,
     split_by_count,
     tile_generated_tokens,

@@ -263,7 +263,7 @@ def tile_weights(tile, shape, tiling) -> np.ndarray:
     return w3.reshape(-1)
 
 
-def blend(tile_outputs, extracted, shape, tiling, num_cond: int):
+def blend(tile_outputs, extracted, shape, tiling, num_cond: int, tiles=None):
     """Recombine tile outputs into the full latent (fp64).
 
     ``tile_outputs[t]``: (B, N_t, C) floats, rows in the order ``extract``
@@ -272,6 +272,10 @@ def blend(tile_outputs, extracted, shape, tiling, num_cond: int):
     negative (reference) positions" (a token kept by k tiles is weighted
     1/k); mold #673, "A bug found while porting" (the blend has no
     normalization pass).
+
+    ``tiles``: the tile indices whose terms are added (default: every tile).
+    A subset gives the full-size partial buffer of the ranks that ran those
+    tiles; k still counts every tile that keeps the token.
 
     Readings: the sum runs over tiles in ascending tile index and starts
     from a zero buffer (so an all-zero sum is +0.0); a conditioning token
@@ -282,10 +286,14 @@ def blend(tile_outputs, extracted, shape, tiling, num_cond: int):
     """
     N = extracted["N"]
     k = extracted["k"]
-    B, _, C = tile_outputs[0].shape
+    T = len(extracted["tiles"])
+    chosen = sorted(set(range(T) if tiles is None else tiles))
+    B = extracted["tiles"][0]["latent"].shape[0]
+    C = extracted["tiles"][0]["latent"].shape[2]
     out = np.zeros((B, N + num_cond, C), dtype=np.float64)
     mag = np.zeros_like(out)
-    for t, et in enumerate(extracted["tiles"]):
+    for t in chosen:
+        et = extracted["tiles"][t]
         y = np.asarray(tile_outputs[t], dtype=np.float64)
         n_gen = et["n_gen"]
         gen_rows = et["rows"][:n_gen]
@@ -298,6 +306,21 @@ def blend(tile_outputs, extracted, shape, tiling, num_cond: int):
             out[:, N + c, :] += term
             mag[:, N + c, :] += np.abs(term)
     return out, mag
+
+
+def rank_partial(tile_outputs, extracted, shape, tiling, num_cond: int, world: int, rank: int):
+    """The buffer one rank contributes to the all_reduce (fp64).
+
+    Source: TDP docs, "What it is": tiles go to ranks round-robin, each rank
+    adds its tiles' masked outputs into a buffer of the full latent's shape,
+    and one all_reduce (a sum) over the ranks gives the blended latent.  So
+    rank r's buffer is the blend restricted to tiles t with t mod world == r;
+    rows no such tile covers stay zero, and the buffers of all ranks add up
+    to ``blend``.  Returns ``(partial, magnitude)`` like ``blend``.
+    """
+    T = len(extracted["tiles"])
+    mine = [t for t in range(T) if round_robin_rank(t, world) == rank]
+    return blend(tile_outputs, extracted, shape, tiling, num_cond, tiles=mine)
 
 
 # --------------------------------------------------------------------------

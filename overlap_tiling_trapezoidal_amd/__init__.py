@@ -68,7 +68,7 @@ class tdp_tile_info(ctypes.Structure):
 
 class tdp_sizes(ctypes.Structure):
     _fields_ = [
-        ("num_tiles", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32),
         ("tile_lat_elems", ctypes.c_int64),
         ("tile_pos_floats", ctypes.c_int64),
         ("tile_index_ints", ctypes.c_int64),
@@ -136,6 +136,8 @@ def load_library(path: str = LIB_PATH):
     vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
     sig = {
         "tdp_plan_create": (ctypes.c_int, [ctypes.POINTER(tdp_config), ctypes.POINTER(vp)]),
+        "tdp_plan_create_rank": (ctypes.c_int, [ctypes.POINTER(tdp_config), i32, i32, ctypes.POINTER(vp)]),
+        "tdp_plan_local_tiles": (ctypes.c_int, [vp, i32p, i32p, i32p]),
         "tdp_plan_destroy": (None, [vp]),
         "tdp_plan_num_tiles": (ctypes.c_int, [vp, i32p]),
         "tdp_plan_intervals": (ctypes.c_int, [vp, ctypes.c_int, i32p, i32p]),
@@ -239,6 +241,27 @@ def tdp_plan_create(cfg: tdp_config) -> Plan:
     h = ctypes.c_void_p()
     _check(lib.tdp_plan_create(ctypes.byref(cfg), ctypes.byref(h)))
     return Plan(h.value, cfg)
+
+
+def tdp_plan_create_rank(cfg: tdp_config, world: int, rank: int) -> Plan:
+    """Plan of rank ``rank``'s round-robin share of the tiles over ``world`` ranks."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.tdp_plan_create_rank(ctypes.byref(cfg), world, rank, ctypes.byref(h)))
+    return Plan(h.value, cfg)
+
+
+def tdp_plan_local_tiles(plan: Plan) -> tuple[int, int, int]:
+    """(world, rank, number of tiles the plan holds)."""
+    w, r, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().tdp_plan_local_tiles(plan.handle, ctypes.byref(w), ctypes.byref(r), ctypes.byref(n)))
+    return w.value, r.value, n.value
+
+
+def held_tiles(plan: Plan) -> list[int]:
+    """Tile indices the plan holds, in slot order (t = rank + slot * world)."""
+    world, rank, n = tdp_plan_local_tiles(plan)
+    return [rank + j * world for j in range(n)]
 
 
 def tdp_plan_destroy(plan: Plan):
@@ -361,7 +384,7 @@ def allocate_extract_outputs(plan: Plan, device="cuda"):
         "tile_lat": torch.empty(s.tile_lat_elems, dtype=_torch_dtype(plan.cfg.in_dtype), device=dev),
         "tile_pos": torch.empty(s.tile_pos_floats, dtype=torch.float32, device=dev),
         "tile_index": torch.empty(s.tile_index_ints, dtype=torch.int32, device=dev),
-        "tile_count": torch.empty(s.num_tiles, dtype=torch.int32, device=dev),
+        "tile_count": torch.empty(max(s.num_slots, 1), dtype=torch.int32, device=dev),
         "cond_row": torch.empty(max(s.cond_row_ints, 1), dtype=torch.int32, device=dev),
     }
 
@@ -396,7 +419,7 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
         _ptr(tile_lat, "tile_lat", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
         _ptr(tile_pos, "tile_pos", torch.float32, s.tile_pos_floats, dev),
         _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
-        _ptr(tile_count, "tile_count", torch.int32, s.num_tiles, dev),
+        _ptr(tile_count, "tile_count", torch.int32, s.num_slots, dev),
         _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
         _stream_handle(stream, dev),
     ]
@@ -462,18 +485,20 @@ def cond_keep_counts(plan: Plan, cond_row):
 
 
 def tile_views(plan: Plan, buffers, counts=None):
-    """Per-tile torch views into the tile-major buffers.
+    """Per-slot torch views into the tile-major buffers (every tile, or a
+    rank plan's own tiles in slot order).
 
     ``counts`` (host list of tile_count) trims each view to its used rows;
     without it the views span the whole slot.  Returns a list of dicts with
-    ``lat`` (B, rows, C), ``pos`` (B, 3, rows, 2) and ``index`` (rows,).
+    ``lat`` (B, rows, C), ``pos`` (B, 3, rows, 2), ``index`` (rows,) and
+    ``info`` (its ``index`` is the tile).
     """
     c = plan.cfg
     views = []
-    for t in range(tdp_plan_num_tiles(plan)):
+    for j, t in enumerate(held_tiles(plan)):
         info = tdp_plan_tile(plan, t)
         cap = info.capacity
-        used = cap if counts is None else int(counts[t])
+        used = cap if counts is None else int(counts[j])
         lat = buffers["tile_lat"][info.lat_offset: info.lat_offset + c.batch * cap * c.channels]
         pos = buffers["tile_pos"][info.pos_offset: info.pos_offset + c.batch * 6 * cap]
         idx = buffers["tile_index"][info.index_offset: info.index_offset + cap]

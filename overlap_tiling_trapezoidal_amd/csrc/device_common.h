@@ -106,4 +106,36 @@ __device__ inline void store_out<TDP_F32, 4>(void* out, int64_t e, const float* 
   st_nt(reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + e), f32x4{a[0], a[1], a[2], a[3]});
 }
 
+// Which elements of a row lane vv handles, for a kernel that reads a tile
+// row of IN and writes an output row of OUT, V 16-byte input vectors per
+// row.  By default lane vv takes input vector vv (elements [E*vv, E*vv+E)).
+// `idx` is the vector index of (row, vv) in `t`; `row` the output row.
+template <int IN, int OUT>
+struct LaneIO {
+  static constexpr int E = InVec<IN>::E;
+  __device__ static inline u32x4 load(const u32x4* t, int64_t idx, int vv, int V) { return ld_nt(t + idx); }
+  __device__ static inline void store(void* out, int64_t row, int vv, int V, const float* a) {
+    store_out<OUT, E>(out, (row * V + vv) * (int64_t)E, a);
+  }
+};
+// bf16 in, fp32 out: 32 output bytes per input vector.  Lane vv takes the
+// 8-byte pieces vv and V + vv instead (elements [4vv, 4vv+4) and
+// [4V+4vv, 4V+4vv+4)), so that each load and each fp32 store instruction of
+// a wave covers one contiguous span rather than every other 16 bytes.
+template <>
+struct LaneIO<TDP_BF16, TDP_F32> {
+  static constexpr int E = 8;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __device__ static inline u32x4 load(const u32x4* t, int64_t idx, int vv, int V) {
+    const u32x2* r = reinterpret_cast<const u32x2*>(t + (idx - vv));
+    const u32x2 a = ld_nt(r + vv), b = ld_nt(r + V + vv);
+    return u32x4{a.x, a.y, b.x, b.y};
+  }
+  __device__ static inline void store(void* out, int64_t row, int vv, int V, const float* a) {
+    f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + row * 8 * V);
+    st_nt(o + vv, f32x4{a[0], a[1], a[2], a[3]});
+    st_nt(o + V + vv, f32x4{a[4], a[5], a[6], a[7]});
+  }
+};
+
 }  // namespace tdp

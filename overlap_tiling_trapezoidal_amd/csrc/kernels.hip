@@ -26,6 +26,9 @@
 // launch too: conditioning workgroups first, then one workgroup per chunk
 // of a (batch, frame, row) line that gathers each output row from its
 // covering tile rows (owner computes: no atomics, fixed order).
+// A rank plan (one rank's round-robin share) runs the same kernels,
+// instantiated with R = true: they touch only the tiles the rank holds and
+// blend writes the rank's full-size partial sum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -39,7 +42,7 @@ namespace {
 constexpr int kBlock = kThreads;
 constexpr int kWaves = kBlock / 64;
 constexpr int kPosUnroll = 4;      // position rows in flight per thread (copy pass)
-constexpr int kExtUnroll = 8;      // position rows in flight per thread (extent pass)
+constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
@@ -56,11 +59,36 @@ constexpr int kXcds = 8;           // accelerator dies; workgroups are dealt to 
 // Axis helpers (closed-form split from plan_internal.h; no tables)
 // ---------------------------------------------------------------------------
 
+// R: the plan holds one rank's round-robin share (uniform slots, local
+// index t / world); otherwise every tile, packed.  A compile-time switch, so
+// the whole-plan kernels carry none of the share's checks.
+template <bool R>
+__device__ inline TileSlot slot_of(const PlanDev& p, int i, int j, int k) {
+  if constexpr (R)
+    return tile_slot_rank(p, i, j, k);
+  else
+    return tile_slot_whole(p, i, j, k);
+}
+
+// Row-table entry of a tile a rank plan does not hold.  Real entries can be
+// negative (the row of width cell 0 lies before a tile that starts past it),
+// so the mark is a value no entry reaches.
+constexpr int64_t kNotHeld = INT64_MIN;
+
+template <bool R>
+__device__ inline bool held(const PlanDev& p, int t) {
+  if constexpr (R)
+    return tile_is_local(p, t);
+  else
+    return true;
+}
+
 struct TileBox {
   int f0, h0, w0, sf, sh, sw;
   TileSlot s;
 };
 
+template <bool R>
 __device__ inline TileBox tile_box(const PlanDev& p, int t) {
   int i, j, k;
   tile_grid(p, t, i, j, k);
@@ -71,7 +99,7 @@ __device__ inline TileBox tile_box(const PlanDev& p, int t) {
   tb.sf = split_size(p.ax[0], i);
   tb.sh = split_size(p.ax[1], j);
   tb.sw = split_size(p.ax[2], k);
-  tb.s = tile_slot(p, i, j, k);
+  tb.s = slot_of<R>(p, i, j, k);
   return tb;
 }
 
@@ -101,8 +129,9 @@ struct LineCombos {
 
 // First row (in tile-slot rows) of width cell 0 of line (b, combo) in tile
 // (i, j, iw): row of cell w is this + w.
+template <bool R>
 __device__ inline int64_t line_row0(const PlanDev& p, int b, int i, int lf, int j, int lh, int sh, int iw) {
-  const TileSlot s = tile_slot(p, i, j, iw);
+  const TileSlot s = slot_of<R>(p, i, j, iw);
   const int sw = split_size(p.ax[2], iw);
   return s.row_base + (int64_t)b * s.cap + (int64_t)(lf * sh + lh) * sw - split_start(p.ax[2], iw);
 }
@@ -186,33 +215,38 @@ __device__ inline f32x2 ld_plane(const f32x2* plane, int n) {
   return *reinterpret_cast<const f32x2*>(reinterpret_cast<const char*>(plane) + ((uint32_t)n << 3));
 }
 
-// [min start, max end) over a tile's generated tokens of one position plane
-// (`src` = pos of one (batch, axis)), reduced by the whole workgroup.  Rows
-// past the end re-read row 0: a repeat does not change a min or a max.
-__device__ float2 tile_plane_extent(const PlanDev& p, const TileBox& tb, const f32x2* __restrict__ src,
-                                    float2* red) {
+// Minimum start over a tile's generated tokens of one position plane, the
+// offset that normalization subtracts.  Only the start of each interval is
+// loaded (4 bytes), so many rows fit in flight per thread, which keeps the
+// number of dependent passes over a large tile small.  Rows past the end
+// re-read row 0: a repeat does not change a minimum.
+__device__ float tile_plane_min_start(const PlanDev& p, const TileBox& tb, const f32x2* __restrict__ src,
+                                      float2* red) {
   const int gen = tb.s.gen;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int r0 = 0; r0 < gen; r0 += kBlock * kExtUnroll) {
-    f32x2 v[kExtUnroll];
+  const float* starts = reinterpret_cast<const float*>(src);
+  float lo = INFINITY;
+  for (int r0 = 0; r0 < gen; r0 += kBlock * kMinUnroll) {
+    float v[kMinUnroll];
 #pragma unroll
-    for (int u = 0; u < kExtUnroll; ++u) {
+    for (int u = 0; u < kMinUnroll; ++u) {
       const int r = r0 + u * kBlock + (int)threadIdx.x;
-      v[u] = ld_plane(src, tile_row_source(p, tb, r < gen ? r : 0));
+      const int n = tile_row_source(p, tb, r < gen ? r : 0);
+      v[u] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(starts) + ((uint32_t)n << 3));
     }
 #pragma unroll
-    for (int u = 0; u < kExtUnroll; ++u) {
-      lo = fminf(lo, v[u].x);
-      hi = fmaxf(hi, v[u].y);
-    }
+    for (int u = 0; u < kMinUnroll; ++u) lo = fminf(lo, v[u]);
   }
-  return block_minmax(lo, hi, red);
+  return block_minmax(lo, -INFINITY, red).x;
 }
 
 // Selection workgroup: tile t, conditioning tokens [c0, c0 + kSelChunk).
+// Every tile is tested, held or not, because k counts all of them; only a
+// held tile's rows are written.
+template <bool R>
 __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, float* ext,
                                   int t, int chunk) {
-  const TileBox tb = tile_box(p, t);
+  const TileBox tb = tile_box<R>(p, t);
+  const bool own = held<R>(p, t);
 
   // 1. extent [min start, max end) of the tile on every (batch, axis): six
   //    planes per pass, each row's source index shared by the planes.
@@ -298,12 +332,14 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
     const int row = tb.s.gen + base + idx;
     a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
     if (keep) {
-      a.tile_index[tb.s.index_base + row] = p.N + c;
+      if (own) a.tile_index[tb.s.index_base + row] = p.N + c;
       sm.sel.kept_c[idx] = c;
     }
   }
   const bool last_chunk = c0 + kSelChunk >= p.Nc;
-  if (last_chunk && threadIdx.x == 0) a.tile_count[t] = tb.s.gen + base + n_kept;
+  if (own && last_chunk && threadIdx.x == 0)
+    a.tile_count[R ? (int)fastdiv((uint32_t)t, p.by_world) : t] = tb.s.gen + base + n_kept;
+  if (!own) return;  // workgroup-uniform
   __syncthreads();
 
   // 3. copy the kept rows: latent vectors, then shifted positions.  Loads
@@ -359,18 +395,20 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
 // reduces itself over the whole plane (the parts of a plane repeat that
 // pass, so no workgroup waits on another); the copy pass then re-reads its
 // own rows from L2.
-__device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int t, int b, int d,
-                                  int part) {
-  const TileBox tb = tile_box(p, t);
+// `slot` is the tile's local index (t itself for a whole plan).
+template <bool R>
+__device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int t, int slot,
+                                  int b, int d, int part) {
+  const TileBox tb = tile_box<R>(p, t);
   const int gen = tb.s.gen;
   const int per = (gen + a.pos_parts - 1) / a.pos_parts;
   const int r_begin = min(gen, part * per), r_end = min(gen, r_begin + per);
-  if (part == 0 && b == 0 && d == 0 && p.Nc == 0 && threadIdx.x == 0) a.tile_count[t] = gen;
+  if (part == 0 && b == 0 && d == 0 && p.Nc == 0 && threadIdx.x == 0) a.tile_count[slot] = gen;
   const f32x2* src = a.pos + ((int64_t)b * 3 + d) * p.rows;
   f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
   int32_t* idx = a.tile_index + tb.s.index_base;
   const bool write_index = (b == 0 && d == 0);
-  const float off = p.normalize ? tile_plane_extent(p, tb, src, sm.red).x : 0.0f;
+  const float off = p.normalize ? tile_plane_min_start(p, tb, src, sm.red) : 0.0f;
   for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
     int n[kPosUnroll];
     f32x2 v[kPosUnroll];
@@ -394,17 +432,32 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
 // Latent workgroup: rows [w0, w0 + rpp * kLatRows) of one (b, f, h) line,
 // every row read once and written to each covering tile.  Source addresses
 // need no tables, so the loads are issued before the cover and row tables
-// are built: the table setup runs while those loads are in flight.
+// are built: the table setup runs while those loads are in flight.  A rank
+// plan reads only the rows that one of its tiles covers (table first,
+// kNotHeld for a tile it does not hold).
+template <bool R>
 __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int blk) {
   const int V = p.vin;
   const int rpp = p.rpp;
   const int rows = p.lat_rows;
-  const int line = (int)fastdiv((uint32_t)blk, p.by_lat_chunks);
-  const int w0 = (blk - line * p.lat_chunks) * rows;
+  int b, f, h, w0;
+  if constexpr (R) {  // workgroups tile the held tiles' bounding box only
+    const int line = (int)fastdiv((uint32_t)blk, p.by_box_c);
+    w0 = (p.box_c0 + blk - line * p.box_nc) * rows;
+    b = (int)fastdiv((uint32_t)line, p.by_box_fh);
+    const int fh = line - b * (p.box_nf * p.box_nh);
+    const int fb = (int)fastdiv((uint32_t)fh, p.by_box_h);
+    f = p.box_f0 + fb;
+    h = p.box_h0 + fh - fb * p.box_nh;
+  } else {
+    const int line = (int)fastdiv((uint32_t)blk, p.by_lat_chunks);
+    w0 = (blk - line * p.lat_chunks) * rows;
+    b = (int)fastdiv((uint32_t)line, p.by_FH);
+    const int fh = line - b * (p.F * p.H);
+    f = (int)fastdiv((uint32_t)fh, p.by_H);
+    h = fh - f * p.H;
+  }
   const int nrow = min(rows, p.W - w0);
-  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
-  const int fh = line - b * (p.F * p.H);
-  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
   const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   const bool lane_on = r < rpp;
   const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w0) * V + vv;
@@ -417,7 +470,7 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
     const int k = u * rpp + r;  // row within the chunk
     ok[u] = lane_on && k < nrow;
     kv[u] = ok[u] ? k : 0;
-    v[u] = ld_nt(src + kv[u] * V);
+    if constexpr (!R) v[u] = ld_nt(src + kv[u] * V);
   }
 
   LineCombos lc;
@@ -429,7 +482,8 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
     const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    rowoff[combo][iw] = (line_row0(p, b, i, lf, j, lh, sh, iw) + w0) * V;
+    const bool own = held<R>(p, (i * p.ax[1].n + j) * nw + iw);
+    rowoff[combo][iw] = own ? (line_row0<R>(p, b, i, lf, j, lh, sh, iw) + w0) * V : kNotHeld;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -438,11 +492,27 @@ __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractSh
   Covers cw[kLatRows];
 #pragma unroll
   for (int u = 0; u < kLatRows; ++u) cw[u] = split_covers(p.ax[2], w0 + kv[u]);
+  if constexpr (R) {
+#pragma unroll
+    for (int u = 0; u < kLatRows; ++u) {
+      bool any = false;
+      for (int cb = 0; cb < ncombo; ++cb)
+        any = any || rowoff[cb][cw[u].t0] != kNotHeld || (cw[u].n > 1 && rowoff[cb][cw[u].t1] != kNotHeld);
+      ok[u] = ok[u] && any;
+      v[u] = ok[u] ? ld_nt(src + kv[u] * V) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   for (int cb = 0; cb < ncombo; ++cb) {
 #pragma unroll
     for (int u = 0; u < kLatRows; ++u) {
-      if (ok[u]) st_nt(a.tile_lat + rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
-      if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
+      if constexpr (R) {
+        const int64_t o0 = rowoff[cb][cw[u].t0], o1 = rowoff[cb][cw[u].t1];
+        if (ok[u] && o0 != kNotHeld) st_nt(a.tile_lat + o0 + kv[u] * V + vv, v[u]);
+        if (ok[u] && cw[u].n > 1 && o1 != kNotHeld) st_nt(a.tile_lat + o1 + kv[u] * V + vv, v[u]);
+      } else {
+        if (ok[u]) st_nt(a.tile_lat + rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
+        if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
+      }
     }
   }
 }
@@ -468,6 +538,8 @@ __device__ inline void xcd_group(int bid, int items, int parts, int& item, int& 
 //   [.., + latent blocks)      generated latent rows per (line, chunk).
 // Selection and position workgroups are few and long (each reduces a whole
 // tile plane), so they come first and run under the latent copy.
+// Rank plans: selection over every tile, positions over the held tiles.
+template <bool R>
 __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
   extern __shared__ float dyn[];  // selection: ext[B][3][2]
   __shared__ ExtractShared sm;
@@ -477,7 +549,7 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
     const int per_tile = (p.Nc + kSelChunk - 1) / kSelChunk;
     int t, chunk;
     xcd_group(bid, p.T, per_tile, t, chunk);
-    extract_selection(p, a, sm, dyn, t, chunk);
+    extract_selection<R>(p, a, sm, dyn, t, chunk);
     return;
   }
   bid -= a.n_sel;
@@ -487,11 +559,11 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
     xcd_group(bid, a.n_pos / a.pos_parts, a.pos_parts, plane, part);
     const int d = plane % 3;
     const int b = (plane / 3) % p.B;
-    const int t = plane / (3 * p.B);
-    extract_positions(p, a, sm, t, b, d, part);
+    const int slot = plane / (3 * p.B);
+    extract_positions<R>(p, a, sm, R ? p.rank + slot * p.world : slot, slot, b, d, part);
     return;
   }
-  extract_latent(p, a, sm, bid - a.n_pos);
+  extract_latent<R>(p, a, sm, bid - a.n_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,22 +580,33 @@ struct BlendShared {
 // cover; then every row loads both covers (a missing second one re-reads
 // the first row and is masked out of the sum).  Without TWO only the first
 // cover is loaded.  The width weights are computed after the loads are
-// issued, while they are in flight.
-template <int IN, int OUT, int NC, int SU, bool TWO>
+// issued, while they are in flight.  R (rank plan): a tile the plan does not
+// hold has row offset kNotHeld; its load re-reads vector vv of slot 0 (there
+// is one: workgroups outside the held tiles' box never get here) and is
+// left out of the sum.
+template <int IN, int OUT, int NC, int SU, bool TWO, bool R>
 __device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const Covers* cw,
                                   const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0, int w0,
                                   const int* kv, const bool* ok, int vv) {
   constexpr int E = InVec<IN>::E;
+  using IO = LaneIO<IN, OUT>;
   const int V = p.vin;
   u32x4 y0[SU][NC], y1[SU][TWO ? NC : 1];
+  bool h0[SU][NC], h1[SU][TWO ? NC : 1];  // the term is held (always, for a whole plan)
 #pragma unroll
   for (int u = 0; u < SU; ++u) {
     const int iw0 = cw[u].t0, iw1s = cw[u].t1;  // t1 == t0 with one cover
     const int64_t off = (int64_t)(w0 + kv[u]) * V + vv;
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      y0[u][cb] = ld_nt(tile_out + sm.rowoff[cb][iw0] + off);
-      if (TWO) y1[u][TWO ? cb : 0] = ld_nt(tile_out + sm.rowoff[cb][iw1s] + off);
+      const int64_t o0 = sm.rowoff[cb][iw0];
+      h0[u][cb] = !R || o0 != kNotHeld;
+      y0[u][cb] = IO::load(tile_out, h0[u][cb] ? o0 + off : (int64_t)vv, vv, V);
+      if (TWO) {
+        const int64_t o1 = sm.rowoff[cb][iw1s];
+        h1[u][TWO ? cb : 0] = !R || o1 != kNotHeld;
+        y1[u][TWO ? cb : 0] = IO::load(tile_out, h1[u][TWO ? cb : 0] ? o1 + off : (int64_t)vv, vv, V);
+      }
     }
   }
 #pragma unroll
@@ -541,17 +624,19 @@ __device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const
       const float wa = sm.wfh[cb] * wx;
       float x0[E];
       InVec<IN>::unpack(y0[u][cb], x0);
+      const bool use0 = h0[u][cb];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(wa, x0[e], acc[e]);
+      for (int e = 0; e < E; ++e) acc[e] = use0 ? fmaf(wa, x0[e], acc[e]) : acc[e];
       if (TWO) {
         const float wb = sm.wfh[cb] * wy;
         float x1[E];
         InVec<IN>::unpack(y1[u][TWO ? cb : 0], x1);
+        const bool use1 = has1 && h1[u][TWO ? cb : 0];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = has1 ? fmaf(wb, x1[e], acc[e]) : acc[e];
+        for (int e = 0; e < E; ++e) acc[e] = use1 ? fmaf(wb, x1[e], acc[e]) : acc[e];
       }
     }
-    if (ok[u]) store_out<OUT, E>(out, ((dst0 + w) * V + vv) * (int64_t)E, acc);
+    if (ok[u]) IO::store(out, dst0 + w, vv, V, acc);
   }
 }
 
@@ -561,7 +646,7 @@ __device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const
 // u < SU (rw = 64/V rows per wave instruction), so a wave usually lies
 // inside one width tile and takes the single-cover path.  SU rows at a
 // time keep at most 8 loads in flight (2 per combo and row).
-template <int IN, int OUT, int NC>
+template <int IN, int OUT, int NC, bool R>
 __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const u32x4* __restrict__ tile_out,
                                  void* __restrict__ out, int64_t dst0, int w0) {
   constexpr int SU = 4 / NC < kBlendRows ? 4 / NC : kBlendRows;
@@ -586,9 +671,9 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
     }
     // wave-uniform: most waves lie inside one width tile
     if (__any(two))
-      blend_rows<IN, OUT, NC, SU, true>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
+      blend_rows<IN, OUT, NC, SU, true, R>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
     else
-      blend_rows<IN, OUT, NC, SU, false>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
+      blend_rows<IN, OUT, NC, SU, false, R>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
   }
 }
 
@@ -600,8 +685,10 @@ __device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const 
 // the token (k = non-negative entries of its cond_row column; 0 when k = 0).
 // Workgroup `cid` = (batch element, chunk of kCondTokens tokens).  The
 // chunk's cond_row entries and every tile's slot go to LDS in one parallel
-// pass, then each lane keeps kCondBatch tile rows in flight.
-template <int IN, int OUT>
+// pass, then each lane keeps kCondBatch tile rows in flight.  A rank plan
+// counts k over every tile but sums only the tiles it holds (capacity 0 for
+// the others).
+template <int IN, int OUT, bool R>
 __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ tile_out,
                                   const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
   constexpr int E = InVec<IN>::E;
@@ -618,8 +705,8 @@ __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ ti
   for (int t = threadIdx.x; t < p.T; t += kBlock) {
     int i, j, k;
     tile_grid(p, t, i, j, k);
-    const TileSlot sl = tile_slot(p, i, j, k);
-    cap[t] = sl.cap;
+    const TileSlot sl = slot_of<R>(p, i, j, k);
+    cap[t] = held<R>(p, t) ? sl.cap : 0;
     base[t] = sl.row_base + (int64_t)b * sl.cap;
   }
   for (int e = threadIdx.x; e < p.T * kCondTokens; e += kBlock) {
@@ -636,6 +723,14 @@ __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ ti
   const int V = p.vin;
   const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   if (r >= p.rpp) return;
+  if (R && p.T_local == 0) {  // a rank without tiles: zeros, and no slot 0 to re-read
+    float z[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) z[e] = 0.0f;
+    for (int jj = r; jj < ntok; jj += p.rpp)
+      store_out<OUT, E>(out, (((int64_t)b * p.rows + p.N + c0 + jj) * V + vv) * (int64_t)E, z);
+    return;
+  }
   for (int jj = r; jj < ntok; jj += p.rpp) {
     const int kc = kcount[jj];
     const float inv = kc > 0 ? 1.0f / (float)kc : 0.0f;
@@ -665,7 +760,7 @@ __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ ti
 }
 
 // The same sum for plans with more than kCondTiles tiles, one tile at a time.
-template <int IN, int OUT>
+template <int IN, int OUT, bool R>
 __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ tile_out,
                                   const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
   constexpr int E = InVec<IN>::E;
@@ -687,10 +782,10 @@ __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ ti
       const float inv = 1.0f / (float)kc;
       for (int t = 0; t < p.T; ++t) {
         const int row = cond_row[(int64_t)t * p.Nc + c];
-        if (row < 0) continue;
+        if (row < 0 || !held<R>(p, t)) continue;
         int i, j, k;
         tile_grid(p, t, i, j, k);
-        const TileSlot sl = tile_slot(p, i, j, k);
+        const TileSlot sl = slot_of<R>(p, i, j, k);
         if (row >= sl.cap) continue;  // not a row tdp_extract could have written
         const u32x4 yv = ld_nt(tile_out + (sl.row_base + (int64_t)b * sl.cap + row) * V + vv);
         float x[E];
@@ -703,7 +798,22 @@ __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ ti
   }
 }
 
+// Rank plans: rows [w0, w0 + rows) of a line outside the held tiles' box
+// are zero in the partial buffer; written without tables or loads.
 template <int IN, int OUT>
+__device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_t dst0, int w0, int rows) {
+  constexpr int E = InVec<IN>::E;
+  const int V = p.vin;
+  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
+  if (r >= p.rpp) return;
+  float z[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) z[e] = 0.0f;
+  const int nrow = min(rows, p.W - w0);
+  for (int k = r; k < nrow; k += p.rpp) LaneIO<IN, OUT>::store(out, dst0 + w0 + k, vv, V, z);
+}
+
+template <int IN, int OUT, bool R>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
                                                        const int32_t* __restrict__ cond_row,
                                                        void* __restrict__ out, int n_gen_blocks) {
@@ -714,9 +824,9 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   const int n_cond = (int)gridDim.x - n_gen_blocks;
   if ((int)blockIdx.x < n_cond) {
     if (p.T <= kCondTiles)
-      blend_cond_cached<IN, OUT>(p, tile_out, cond_row, out, blockIdx.x);
+      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, out, blockIdx.x);
     else
-      blend_cond_direct<IN, OUT>(p, tile_out, cond_row, out, blockIdx.x);
+      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, out, blockIdx.x);
     return;
   }
   const int bid = blockIdx.x - n_cond;
@@ -726,6 +836,13 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   const int b = (int)fastdiv((uint32_t)line, p.by_FH);
   const int fh = line - b * (p.F * p.H);
   const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+  if constexpr (R) {
+    if (f < p.box_f0 || f >= p.box_f0 + p.box_nf || h < p.box_h0 || h >= p.box_h0 + p.box_nh ||
+        w0 >= p.box_w0 + p.box_nw || w0 + rows <= p.box_w0) {
+      blend_zero_rows<IN, OUT>(p, out, (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W, w0, rows);
+      return;
+    }
+  }
   LineCombos lc;
   lc.init(p, f, h);
   const int nw = p.ax[2].n;
@@ -736,7 +853,8 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
     int i, lf, sf, j, lh, sh;
     lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    sm.rowoff[combo][iw] = line_row0(p, b, i, lf, j, lh, sh, iw) * V;
+    const bool own = held<R>(p, (i * p.ax[1].n + j) * nw + iw);
+    sm.rowoff[combo][iw] = own ? line_row0<R>(p, b, i, lf, j, lh, sh, iw) * V : kNotHeld;
     if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -745,11 +863,11 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
   const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
   const int nc = lc.n;
   if (nc == 1)
-    blend_chunk_rows<IN, OUT, 1>(p, sm, tile_out, out, dst0, w0);
+    blend_chunk_rows<IN, OUT, 1, R>(p, sm, tile_out, out, dst0, w0);
   else if (nc == 2)
-    blend_chunk_rows<IN, OUT, 2>(p, sm, tile_out, out, dst0, w0);
+    blend_chunk_rows<IN, OUT, 2, R>(p, sm, tile_out, out, dst0, w0);
   else
-    blend_chunk_rows<IN, OUT, 4>(p, sm, tile_out, out, dst0, w0);
+    blend_chunk_rows<IN, OUT, 4, R>(p, sm, tile_out, out, dst0, w0);
 }
 
 template <int IN, int OUT>
@@ -760,8 +878,12 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
   const size_t lds = p.Nc > 0 && p.T <= kCondTiles
                          ? ((size_t)p.T * kCondTokens + p.T + kCondTokens + 1) * sizeof(int) + 8 + (size_t)p.T * 8
                          : 0;
-  hipLaunchKernelGGL((blend_kernel<IN, OUT>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
-                     reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
+  if (p.world > 1)
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, true>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
+                       reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
+  else
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, false>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
+                       reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
   return hipGetLastError();
 }
 
@@ -840,7 +962,7 @@ __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u
       if (ru >= 0) {
         int iu, ju, ku;
         tile_grid(p, u, iu, ju, ku);
-        if (ru < tile_slot(p, iu, ju, ku).cap) {
+        if (ru < tile_slot_whole(p, iu, ju, ku).cap) {
           any = true;
           if (u < t) first = false;
         }
@@ -874,7 +996,7 @@ __global__ __launch_bounds__(kBlock) void blend_tile_kernel(const PlanDev p, int
                                                             float* __restrict__ acc, int gen_per_b, int n_gen) {
   int i, j, k;
   tile_grid(p, t, i, j, k);
-  const TileBox tb = tile_box(p, t);
+  const TileBox tb = tile_box<false>(p, t);
   const int bid = blockIdx.x;
   if (bid < n_gen) {
     const int b = bid / gen_per_b;
@@ -912,7 +1034,8 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   if (!plan) return fail(TDP_EINVAL, "tdp_extract: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_extract: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
-  if (!latent || !pos || !tile_lat || !tile_pos || !tile_index || !tile_count)
+  if (!latent || !pos) return fail(TDP_EINVAL, "tdp_extract: null device pointer");
+  if (p.T_local > 0 && (!tile_lat || !tile_pos || !tile_index || !tile_count))
     return fail(TDP_EINVAL, "tdp_extract: null device pointer");
   if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_extract: cond_row is required when num_cond > 0");
   if (!aligned(latent, 16) || !aligned(tile_lat, 16))
@@ -930,11 +1053,16 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.cond_row = cond_row;
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
-  a.n_pos = p.T * p.B * 3 * a.pos_parts;
-  const int n_lat = p.B * p.F * p.H * p.lat_chunks;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  const int n_lat = p.world > 1 ? p.B * p.box_nf * p.box_nh * p.box_nc : p.B * p.F * p.H * p.lat_chunks;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(extract_kernel, dim3(a.n_sel + a.n_pos + n_lat), dim3(kBlock), (size_t)p.B * 6 * sizeof(float), s,
-                     p, a);
+  const dim3 grid(a.n_sel + a.n_pos + n_lat);
+  if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
+  const size_t ext_lds = (size_t)p.B * 6 * sizeof(float);
+  if (p.world > 1)
+    hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), ext_lds, s, p, a);
+  else
+    hipLaunchKernelGGL(extract_kernel<false>, grid, dim3(kBlock), ext_lds, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
@@ -945,6 +1073,7 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
   if (!plan) return fail(TDP_EINVAL, "tdp_blend_tile: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend_tile: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
+  if (p.world > 1) return fail(TDP_EINVAL, "tdp_blend_tile: rank plans take tdp_blend (streaming is for whole plans)");
   if (t < 0 || t >= p.T) return fail(TDP_EINVAL, "tdp_blend_tile: tile index %d out of range [0, %d)", t, p.T);
   if (!tile_out || !acc) return fail(TDP_EINVAL, "tdp_blend_tile: null device pointer");
   if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend_tile: cond_row is required when num_cond > 0");
@@ -952,7 +1081,7 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
     return fail(TDP_EINVAL, "tdp_blend_tile: tile_out and acc must be 16-byte aligned");
   int i, j, k;
   tile_grid(p, t, i, j, k);
-  const TileSlot slot = tile_slot(p, i, j, k);
+  const TileSlot slot = tile_slot_whole(p, i, j, k);
   const int rows_per_block = (kBlock / p.vin) * kStreamRows;
   const int gen_per_b = (slot.gen + rows_per_block - 1) / rows_per_block;
   const int n_gen = p.B * gen_per_b;
@@ -973,6 +1102,7 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
 int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_blend_finish: null plan");
   const PlanDev& p = plan->dev;
+  if (p.world > 1) return fail(TDP_EINVAL, "tdp_blend_finish: rank plans take tdp_blend (streaming is for whole plans)");
   if (!acc || !out) return fail(TDP_EINVAL, "tdp_blend_finish: null device pointer");
   if (!aligned(acc, 16) || !aligned(out, 16)) return fail(TDP_EINVAL, "tdp_blend_finish: misaligned pointer");
   if (p.out_dtype == TDP_F32 && static_cast<const void*>(acc) == out) return TDP_OK;
@@ -993,7 +1123,7 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
   if (!plan) return fail(TDP_EINVAL, "tdp_blend: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
-  if (!tile_out || !out) return fail(TDP_EINVAL, "tdp_blend: null device pointer");
+  if (!out || (!tile_out && p.T_local > 0)) return fail(TDP_EINVAL, "tdp_blend: null device pointer");
   if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend: cond_row is required when num_cond > 0");
   if (!aligned(tile_out, 16) || !aligned(out, 16))
     return fail(TDP_EINVAL, "tdp_blend: tile_out and out must be 16-byte aligned");

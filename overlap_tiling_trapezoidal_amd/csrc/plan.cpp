@@ -88,11 +88,9 @@ int build_axis(int d, int32_t dim, tdp_axis_tiling t, bool guarded, AxisSplit* a
 
 using namespace tdp;
 
-extern "C" {
-
-int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
-  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_plan_create: null argument");
-  *out = nullptr;
+// A whole plan (world == 1) or the share of one rank of a round-robin
+// schedule over `world` ranks.
+static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_plan** out) {
   const tdp_config c = *cfg;
   if (c.batch < 1 || c.channels < 1 || c.frames < 1 || c.height < 1 || c.width < 1)
     return fail(TDP_EINVAL, "batch, channels, frames, height and width must all be >= 1");
@@ -140,16 +138,6 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
   dev.out_dtype = c.out_dtype;
   dev.normalize = (c.flags & TDP_NORMALIZE_POSITIONS) ? 1 : 0;
 
-  // Tile slots: sum over tiles of capacity = (sum of gen) + T * Nc.
-  const int64_t total_gen =
-      (int64_t)split_total(dev.ax[0]) * split_total(dev.ax[1]) * split_total(dev.ax[2]);
-  const int64_t total_index = total_gen + (int64_t)dev.T * c.num_cond;
-  if (total_index * c.batch > INT32_MAX)
-    return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
-                (long long)(total_index * c.batch));
-
-  // Position workgroups: each reduces the extent of a whole (tile, batch
-  // element, axis) plane and shifts about 4096 of its tokens.
   int64_t max_gen = 0;
   for (int i = 0; i < dev.ax[0].n; ++i)
     for (int j = 0; j < dev.ax[1].n; ++j)
@@ -158,6 +146,32 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
             (int64_t)split_size(dev.ax[0], i) * split_size(dev.ax[1], j) * split_size(dev.ax[2], k);
         if (g > max_gen) max_gen = g;
       }
+
+  // Tile slots.  Whole plan: capacities packed back to back, (sum of gen)
+  // + T * Nc.  Rank plan: its tiles t = rank, rank + world, ... in uniform
+  // slots of max gen + Nc rows.
+  dev.world = world;
+  dev.rank = rank;
+  dev.by_world = make_fastdiv((uint32_t)world);
+  dev.T_local = rank < dev.T ? (int32_t)(((int64_t)dev.T - rank + world - 1) / world) : 0;
+  int64_t total_index;
+  if (world == 1) {
+    dev.slot_cap = 0;
+    total_index = (int64_t)split_total(dev.ax[0]) * split_total(dev.ax[1]) * split_total(dev.ax[2]) +
+                  (int64_t)dev.T * c.num_cond;
+  } else {
+    if (max_gen + c.num_cond > INT32_MAX)
+      return fail(TDP_ESHAPE, "tile capacity of %lld rows exceeds the int32 range",
+                  (long long)(max_gen + c.num_cond));
+    dev.slot_cap = (int32_t)(max_gen + c.num_cond);
+    total_index = (int64_t)dev.T_local * dev.slot_cap;
+  }
+  if (total_index * c.batch > INT32_MAX)
+    return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
+                (long long)(total_index * c.batch));
+
+  // Position workgroups: each reduces the extent of a whole (tile, batch
+  // element, axis) plane and shifts about 4096 of its tokens.
   int64_t parts = (max_gen + 4095) / 4096;
   if (parts < 1) parts = 1;
   if (parts > 64) parts = 64;
@@ -175,6 +189,32 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
   dev.by_lat_chunks = make_fastdiv((uint32_t)dev.lat_chunks);
   dev.by_blend_chunks = make_fastdiv((uint32_t)dev.blend_chunks);
 
+  // Bounding box of the held tiles (rank plans launch the latent copy over
+  // it only; the blend writes zeros outside it without reading anything).
+  int lo[3] = {INT_MAX, INT_MAX, INT_MAX}, hi[3] = {0, 0, 0};
+  for (int64_t t = rank; t < dev.T; t += world) {
+    int g[3];
+    tile_grid(dev, (int)t, g[0], g[1], g[2]);
+    for (int d = 0; d < 3; ++d) {
+      const int a = split_start(dev.ax[d], g[d]);
+      if (a < lo[d]) lo[d] = a;
+      if (a + split_size(dev.ax[d], g[d]) > hi[d]) hi[d] = a + split_size(dev.ax[d], g[d]);
+    }
+  }
+  if (dev.T_local > 0) {
+    dev.box_f0 = lo[0];
+    dev.box_nf = hi[0] - lo[0];
+    dev.box_h0 = lo[1];
+    dev.box_nh = hi[1] - lo[1];
+    dev.box_w0 = lo[2];
+    dev.box_nw = hi[2] - lo[2];
+    dev.box_c0 = lo[2] / dev.lat_rows;
+    dev.box_nc = (hi[2] + dev.lat_rows - 1) / dev.lat_rows - dev.box_c0;
+  }
+  dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));
+  dev.by_box_fh = make_fastdiv((uint32_t)(dev.box_nf * dev.box_nh > 0 ? dev.box_nf * dev.box_nh : 1));
+  dev.by_box_c = make_fastdiv((uint32_t)(dev.box_nc > 0 ? dev.box_nc : 1));
+
   tdp_plan* p = new (std::nothrow) tdp_plan;
   if (!p) return fail(TDP_EINVAL, "out of host memory");
   p->cfg = c;
@@ -182,6 +222,30 @@ int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
   p->guarded = guarded;
   p->total_index = total_index;
   *out = p;
+  return TDP_OK;
+}
+
+extern "C" {
+
+int tdp_plan_create(const tdp_config* cfg, tdp_plan** out) {
+  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_plan_create: null argument");
+  *out = nullptr;
+  return create_plan(cfg, 1, 0, out);
+}
+
+int tdp_plan_create_rank(const tdp_config* cfg, int32_t world, int32_t rank, tdp_plan** out) {
+  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_plan_create_rank: null argument");
+  *out = nullptr;
+  if (world < 1) return fail(TDP_EINVAL, "world must be >= 1 (got %d)", world);
+  if (rank < 0 || rank >= world) return fail(TDP_EINVAL, "rank %d out of range [0, %d)", rank, world);
+  return create_plan(cfg, world, rank, out);
+}
+
+int tdp_plan_local_tiles(const tdp_plan* plan, int32_t* world, int32_t* rank, int32_t* count) {
+  if (!plan || !world || !rank || !count) return fail(TDP_EINVAL, "tdp_plan_local_tiles: null argument");
+  *world = plan->dev.world;
+  *rank = plan->dev.rank;
+  *count = plan->dev.T_local;
   return TDP_OK;
 }
 
@@ -253,22 +317,22 @@ int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info) {
   }
   info->gen_tokens = s.gen;
   info->capacity = s.cap;
-  info->lat_offset = s.row_base * p.C;
-  info->pos_offset = s.row_base * 6;
-  info->index_offset = s.index_base;
+  const bool held = tile_is_local(p, t);
+  info->lat_offset = held ? s.row_base * p.C : -1;
+  info->pos_offset = held ? s.row_base * 6 : -1;
+  info->index_offset = held ? s.index_base : -1;
   return TDP_OK;
 }
 
 int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes) {
   if (!plan || !sizes) return fail(TDP_EINVAL, "tdp_plan_sizes: null argument");
   const PlanDev& p = plan->dev;
-  sizes->num_tiles = p.T;
+  sizes->num_slots = p.T_local;
   sizes->tile_lat_elems = plan->total_index * p.B * p.C;
   sizes->tile_pos_floats = plan->total_index * p.B * 6;
   sizes->tile_index_ints = plan->total_index;
   sizes->cond_row_ints = (int64_t)p.T * p.Nc;
   sizes->out_elems = (int64_t)p.B * p.rows * p.C;
-  // extent partials: (T, B, 3, chunks) x {min start, max end} floats
   return TDP_OK;
 }
 

@@ -129,6 +129,20 @@ struct PlanDev {
   int32_t lat_rows, lat_chunks;      // extract: rows per latent workgroup, chunks per line
   int32_t blend_rows, blend_chunks;  // blend: rows per workgroup, chunks per line
   FastDiv by_vin, by_H, by_FH, by_nw, by_lat_chunks, by_blend_chunks;
+  // Round-robin share (TDP docs, "What it is": tile t runs on rank t mod
+  // world).  world == 1 is the whole plan.  A rank plan holds the tiles with
+  // t mod world == rank, local index t / world, in uniform slots of
+  // slot_cap rows per batch element.
+  int32_t world, rank;
+  int32_t T_local;    // tiles of this plan's rank (T when world == 1)
+  int32_t slot_cap;   // rank plans: largest tile's gen + Nc
+  FastDiv by_world;
+  // Rank plans: bounding box of the held tiles, [f0, f0+nf) x [h0, h0+nh)
+  // x [w0, w0+nw) cells; on width also as extract chunks [c0, c0+nc) (all
+  // zero without tiles).
+  int32_t box_f0, box_nf, box_h0, box_nh, box_c0, box_nc;
+  int32_t box_w0, box_nw;  // the same box on width, in cells
+  FastDiv by_box_h, by_box_fh, by_box_c;
 };
 
 // Tile t -> per-axis tile index (row-major, width fastest).
@@ -155,7 +169,8 @@ struct TileSlot {
   int32_t cap;         // gen + Nc
 };
 
-TDP_HD TileSlot tile_slot(const PlanDev& p, int i, int j, int k) {
+// Whole plan: tiles packed back to back in index order.
+TDP_HD TileSlot tile_slot_whole(const PlanDev& p, int i, int j, int k) {
   const int t = (i * p.ax[1].n + j) * p.ax[2].n + k;
   TileSlot s;
   s.gen = split_size(p.ax[0], i) * split_size(p.ax[1], j) * split_size(p.ax[2], k);
@@ -165,6 +180,26 @@ TDP_HD TileSlot tile_slot(const PlanDev& p, int i, int j, int k) {
   return s;
 }
 
+TDP_HD bool tile_is_local(const PlanDev& p, int t) {
+  return (int)((uint32_t)t - fastdiv((uint32_t)t, p.by_world) * (uint32_t)p.world) == p.rank;
+}
+
+// Rank plan: local tile t / world in a slot of slot_cap rows per batch
+// element (meaningful for the rank's own tiles only).
+TDP_HD TileSlot tile_slot_rank(const PlanDev& p, int i, int j, int k) {
+  const int t = (i * p.ax[1].n + j) * p.ax[2].n + k;
+  TileSlot s;
+  s.gen = split_size(p.ax[0], i) * split_size(p.ax[1], j) * split_size(p.ax[2], k);
+  s.cap = s.gen + p.Nc;
+  s.index_base = (int64_t)fastdiv((uint32_t)t, p.by_world) * p.slot_cap;
+  s.row_base = s.index_base * p.B;
+  return s;
+}
+
+TDP_HD TileSlot tile_slot(const PlanDev& p, int i, int j, int k) {
+  return p.world > 1 ? tile_slot_rank(p, i, j, k) : tile_slot_whole(p, i, j, k);
+}
+
 }  // namespace tdp
 
 // The opaque handle of the public API.
@@ -172,7 +207,7 @@ struct tdp_plan {
   tdp_config cfg;
   tdp::PlanDev dev;
   bool guarded;
-  int64_t total_index;  // sum over tiles of capacity
+  int64_t total_index;  // tile_index entries: sum of the slots' capacities
 };
 
 namespace tdp {

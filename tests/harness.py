@@ -69,12 +69,14 @@ def gpu_extract(plan, inp, device, label=""):
 def check_extract(plan, bufs, ex, num_cond):
     """Bit-exact comparison of the GPU extract with the oracle's."""
     counts = bufs["tile_count"].cpu().numpy()
-    views = tdp.tile_views(plan, bufs, counts)
+    views = tdp.tile_views(plan, bufs, counts)   # the tiles the plan holds, in slot order
     T = len(ex["tiles"])
-    assert len(views) == T
-    for t, (v, et) in enumerate(zip(views, ex["tiles"])):
+    assert [v["info"].index for v in views] == tdp.held_tiles(plan)
+    for j, v in enumerate(views):
+        t = v["info"].index
+        et = ex["tiles"][t]
         n_t = len(et["rows"])
-        assert counts[t] == n_t, (t, counts[t], n_t)
+        assert counts[j] == n_t, (t, counts[j], n_t)
         assert np.array_equal(v["index"].cpu().numpy(), et["rows"].astype(np.int32)), t
         got_lat = latent_bits(v["lat"])
         want_lat = et["latent"] if et["latent"].dtype == np.uint16 else et["latent"].view(np.uint32)
@@ -92,7 +94,9 @@ def check_extract(plan, bufs, ex, num_cond):
 
 
 def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
-    """Pack per-tile (B, N_t, C) arrays into a tile-major slot buffer (numpy).
+    """Pack per-tile (B, N_t, C) arrays (one per tile of the plan's grid) into
+    its tile-major slot buffer (numpy); tiles a rank plan does not hold are
+    skipped.
 
     Unused slot rows get random garbage (when ``rng`` is given) so a blend
     that reads them would be caught.
@@ -109,6 +113,8 @@ def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
             buf[:] = rng.standard_normal(buf.size).astype(np.float32) * 1e30
     for t, arr in enumerate(tile_arrays):
         info = tdp.tdp_plan_tile(plan, t)
+        if info.lat_offset < 0:   # a rank plan holds only its own tiles
+            continue
         slot = buf[info.lat_offset: info.lat_offset + c.batch * info.capacity * c.channels]
         slot = slot.reshape(c.batch, info.capacity, c.channels)
         slot[:, :arr.shape[1], :] = arr

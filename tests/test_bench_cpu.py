@@ -34,6 +34,16 @@ def test_4k_compulsory_bytes():
     assert (ex, bl) == (106788928, 96731136)
 
 
+def test_4k_naive_bytes():
+    # Per-tile gathers re-read the overlaps: 236.2 MB against 203.5 MB.
+    wl = WORKLOADS["4k"]
+    counts, T = _oracle_counts(wl)
+    ex, bl, S = bench.compulsory_bytes(wl, counts, T, 2, 2)
+    extra = bench.naive_bytes(wl, S, 2)
+    assert extra == (247296 - 130560) * (256 + 24)
+    assert round((ex + bl) / 1e6, 1) == 203.5 and round((ex + bl + extra) / 1e6, 1) == 236.2
+
+
 def test_conditioned_counts_kept_rows():
     wl = WORKLOADS["conditioned"]
     counts, T = _oracle_counts(wl)

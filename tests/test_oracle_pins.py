@@ -361,6 +361,106 @@ def test_blend_per_tile_affine_voxelwise():
         np.testing.assert_allclose(out[0, n], x[0, n] * float(sa) + float(sb), rtol=1e-12, atol=1e-12)
 
 
+# --- rank partials (round-robin share of the all_reduce) ------------------
+
+def _affine_outputs(wl, ex):
+    a, b = denoiser_params(wl.seed, len(ex["tiles"]), "affine")
+    return [a[t] * O.bf16_bits_to_f32(et["latent"]).astype(np.float64) + b[t]
+            for t, et in enumerate(ex["tiles"])], a, b
+
+
+def test_rank_partials_add_up_to_blend():
+    # The all_reduce sums the ranks' buffers: for any world size the
+    # partials add up to the whole blend, and one rank is the whole blend.
+    wl = WORKLOADS["conditioned"]
+    inp = make_inputs(wl)
+    ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    ys, _, _ = _affine_outputs(wl, ex)
+    full, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
+    one, _ = O.rank_partial(ys, ex, wl.shape, wl.tiling, wl.num_cond, 1, 0)
+    assert np.array_equal(one, full)
+    for world in (2, 4, 5, 18, 25):
+        total = sum(O.rank_partial(ys, ex, wl.shape, wl.tiling, wl.num_cond, world, r)[0] for r in range(world))
+        assert np.all(np.abs(total - full) <= 1e-12 * mag + 1e-300), world
+
+
+def test_rank_partial_voxelwise():
+    # Rank 1 of 3 on the LTX-like grid, restated per voxel with exact
+    # windows: the sum over the rank's tiles (t mod 3 == 1) that contain
+    # the voxel, zero where none does.
+    wl = WORKLOADS["ltx"]
+    inp = make_inputs(wl)
+    x = O.bf16_bits_to_f32(inp["latent"]).astype(np.float64)
+    ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, 0)
+    ys, a, b = _affine_outputs(wl, ex)
+    world, rank = 3, 1
+    part, _ = O.rank_partial(ys, ex, wl.shape, wl.tiling, 0, world, rank)
+    F, H, W = wl.shape
+    ivs = [O.split_by_count(d, n, o) for d, (n, o) in zip(wl.shape, wl.tiling)]
+    wins = [[O.window_exact(ivs[d], i, wl.tiling[d][1]) for i in range(len(ivs[d]))] for d in range(3)]
+    rng = np.random.default_rng(5)
+    zeros = 0
+    for n in rng.choice(F * H * W, size=400, replace=False):
+        cells = (n // (H * W), (n // W) % H, n % W)
+        sa = sb = Fraction(0)
+        covered = False
+        for t, idx in enumerate(itertools.product(*[range(len(v)) for v in ivs])):
+            if t % world != rank:
+                continue
+            if all(ivs[d][idx[d]][0] <= cells[d] < ivs[d][idx[d]][1] for d in range(3)):
+                covered = True
+                wt = Fraction(1)
+                for d in range(3):
+                    wt *= wins[d][idx[d]][cells[d] - ivs[d][idx[d]][0]]
+                sa += wt * Fraction(float(a[t]))
+                sb += wt * Fraction(float(b[t]))
+        if not covered:
+            zeros += 1
+            assert np.all(part[0, n] == 0.0)
+        np.testing.assert_allclose(part[0, n], x[0, n] * float(sa) + float(sb), rtol=1e-12, atol=1e-12)
+    assert zeros > 0   # the sample meets voxels outside the rank's tiles
+
+
+def test_rank_partial_conditioning_uses_global_k():
+    # All-ones tile outputs: a conditioning row of rank r's buffer is
+    # (tiles of rank r that keep c) / (tiles that keep c), so the ranks'
+    # rows add up to one for every kept token.
+    wl = WORKLOADS["conditioned"]
+    inp = make_inputs(wl)
+    ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    ones = [np.ones(et["latent"].shape) for et in ex["tiles"]]
+    keep = ex["keep"]
+    T = keep.shape[0]
+    world = 4
+    total = np.zeros(wl.num_cond)
+    for r in range(world):
+        part, _ = O.rank_partial(ones, ex, wl.shape, wl.tiling, wl.num_cond, world, r)
+        mine = keep[[t for t in range(T) if t % world == r]].sum(axis=0)
+        want = mine / keep.sum(axis=0)
+        np.testing.assert_allclose(part[:, wl.tokens:, :], np.broadcast_to(want[None, :, None], part[:, wl.tokens:, :].shape),
+                                   rtol=1e-15, atol=0)
+        total += part[0, wl.tokens:, 0]
+    np.testing.assert_allclose(total, 1.0, rtol=1e-15)
+
+
+def test_mutant_rank_local_k_fails_pin():
+    # Planted mistake: each rank divides by the number of its own tiles that
+    # keep the token.  The ranks' conditioning rows then no longer add to one.
+    wl = WORKLOADS["conditioned"]
+    inp = make_inputs(wl)
+    ex = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    ones = [np.ones(et["latent"].shape) for et in ex["tiles"]]
+    keep = ex["keep"]
+    T, world = keep.shape[0], 4
+    total = np.zeros(wl.num_cond)
+    for r in range(world):
+        mine = [t for t in range(T) if t % world == r]
+        wrong = dict(ex, k=keep[mine].sum(axis=0))
+        part, _ = O.blend(ones, wrong, wl.shape, wl.tiling, wl.num_cond, tiles=mine)
+        total += part[0, wl.tokens:, 0]
+    assert not np.allclose(total, 1.0, rtol=1e-15)
+
+
 # --- bf16 storage --------------------------------------------------------
 
 def test_bf16_rounding_matches_torch():

@@ -190,11 +190,80 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
 def test_4k_sizes():
     plan = plan_for(WORKLOADS["4k"])
     s = tdp.tdp_plan_sizes(plan)
-    assert s.num_tiles == 16
+    assert s.num_slots == 16
     assert s.tile_index_ints == 247296
     assert s.tile_lat_elems == 247296 * 128
     assert s.tile_pos_floats == 247296 * 6
     assert s.cond_row_ints == 0
+
+
+# --- rank plans: one rank's round-robin share -----------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "conditioned", "4k"])
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 7, 40])
+def test_rank_plan_layout(name, world):
+    wl = WORKLOADS[name]
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond, in_dtype=wl.dtype)
+    tiles = O.enumerate_tiles(wl.shape, wl.tiling)
+    T = len(tiles)
+    whole = tdp.tdp_plan_create(cfg)
+    gen_max = max(int(np.prod(t["size"])) for t in tiles)
+    for rank in range(world):
+        plan = tdp.tdp_plan_create_rank(cfg, world, rank)
+        mine = [t for t in range(T) if O.round_robin_rank(t, world) == rank]
+        assert tdp.tdp_plan_local_tiles(plan) == (world, rank, len(mine))
+        assert tdp.held_tiles(plan) == mine
+        assert tdp.tdp_plan_num_tiles(plan) == T
+        s = tdp.tdp_plan_sizes(plan)
+        assert s.num_slots == len(mine)
+        assert s.cond_row_ints == T * wl.num_cond          # k counts every rank's tiles
+        assert s.out_elems == wl.batch * (wl.tokens + wl.num_cond) * wl.channels
+        if world == 1:
+            sw = tdp.tdp_plan_sizes(whole)
+            assert (s.tile_lat_elems, s.tile_pos_floats, s.tile_index_ints) == \
+                   (sw.tile_lat_elems, sw.tile_pos_floats, sw.tile_index_ints)
+            for t in range(T):
+                a, b = tdp.tdp_plan_tile(plan, t), tdp.tdp_plan_tile(whole, t)
+                assert (a.lat_offset, a.pos_offset, a.index_offset) == (b.lat_offset, b.pos_offset, b.index_offset)
+            continue
+        cap = gen_max + wl.num_cond                        # uniform slots
+        assert s.tile_index_ints == len(mine) * cap
+        assert s.tile_lat_elems == len(mine) * cap * wl.batch * wl.channels
+        assert s.tile_pos_floats == len(mine) * cap * wl.batch * 6
+        for t in range(T):
+            info = tdp.tdp_plan_tile(plan, t)
+            assert tuple(info.origin) == tiles[t]["origin"] and tuple(info.shape) == tiles[t]["size"]
+            assert info.capacity == int(np.prod(tiles[t]["size"])) + wl.num_cond
+            if t in mine:
+                j = mine.index(t)
+                assert info.index_offset == j * cap
+                assert info.lat_offset == j * cap * wl.batch * wl.channels
+                assert info.pos_offset == j * cap * wl.batch * 6
+            else:
+                assert (info.lat_offset, info.pos_offset, info.index_offset) == (-1, -1, -1)
+
+
+def test_rank_plan_errors(lib):
+    cfg = tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2)))
+    for world, rank in [(0, 0), (-1, 0), (2, 2), (2, -1), (3, 5)]:
+        with pytest.raises(tdp.TdpError) as ei:
+            tdp.tdp_plan_create_rank(cfg, world, rank)
+        assert ei.value.status == tdp.TDP_EINVAL
+    assert lib.tdp_plan_create_rank(None, 2, 0, None) == tdp.TDP_EINVAL
+    bad = tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 5), (2, 2)))   # guard: 5 * 3 > 8
+    with pytest.raises(tdp.TdpError) as ei:
+        tdp.tdp_plan_create_rank(bad, 2, 0)
+    assert ei.value.status == tdp.TDP_EGUARD
+    # the streaming blend is for whole plans; refused before any launch
+    plan = tdp.tdp_plan_create_rank(cfg, 2, 1)
+    al = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(None)
+    assert lib.tdp_blend_tile(plan.handle, 1, al, null, al, null) == tdp.TDP_EINVAL
+    assert "rank plans" in tdp.tdp_last_error()
+    assert lib.tdp_blend_finish(plan.handle, al, al, null) == tdp.TDP_EINVAL
+    # a rank that holds tiles still needs its tile buffers
+    assert lib.tdp_extract(plan.handle, al, al, null, null, null, null, null, null) == tdp.TDP_EINVAL
+    assert lib.tdp_blend(plan.handle, null, null, al, null) == tdp.TDP_EINVAL
 
 
 def _brute_cover(ivs, x):
