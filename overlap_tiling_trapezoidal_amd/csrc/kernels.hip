@@ -16,9 +16,9 @@
 //   selection  (tile, chunk of conditioning tokens): the tile's extents on
 //              every (batch, axis), keep test, ordered compaction, copy of
 //              the kept rows;
-//   positions  (tile, batch, axis, part): the plane's extent [min start,
-//              max end), reduced by the workgroup itself, then the shifted
-//              positions and source indices of one part of the tile;
+//   positions  (tile, batch, axis, part): the plane's minimum start,
+//              reduced by the workgroup itself, then the shifted positions
+//              and source indices of one part of the tile;
 //   latent     (batch, frame, row, chunk of rows): every latent row is read
 //              once and written to each tile that covers it.
 // The first two kinds are few and long; dispatched first, they run under

@@ -170,12 +170,6 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
     return fail(TDP_ESHAPE, "tile buffers of %lld rows exceed the int32 range",
                 (long long)(total_index * c.batch));
 
-  // Position workgroups: each reduces the extent of a whole (tile, batch
-  // element, axis) plane and shifts about 4096 of its tokens.
-  int64_t parts = (max_gen + 4095) / 4096;
-  if (parts < 1) parts = 1;
-  if (parts > 64) parts = 64;
-  dev.pos_parts = (int32_t)parts;
   dev.rpp = kThreads / dev.vin;
   dev.rw = 64 / dev.vin;
   dev.lat_rows = dev.rpp * kLatRows;
@@ -210,6 +204,23 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
     dev.box_nw = hi[2] - lo[2];
     dev.box_c0 = lo[2] / dev.lat_rows;
     dev.box_nc = (hi[2] + dev.lat_rows - 1) / dev.lat_rows - dev.box_c0;
+  }
+  // Position workgroups per (tile, batch element, axis) plane: each reduces
+  // the whole plane's minimum start, then shifts its part of the tokens.
+  // More parts shorten each workgroup's copy pass (at most 1024 rows each),
+  // but every part re-reads the plane; those re-reads are kept below 3/4 of
+  // the latent bytes the plan reads, so that on large latents they do not
+  // compete with the latent copy (measured: 4 parts beat 8 and 16 on the
+  // 4K-class latent, while small latents gain from the shorter chain).
+  {
+    const int64_t cells = world == 1 ? N : (int64_t)dev.box_nf * dev.box_nh * dev.box_nw;
+    const int64_t latent_bytes = (int64_t)c.batch * cells * row_bytes;
+    const int64_t plane_bytes = (int64_t)dev.T_local * c.batch * 3 * max_gen * 8;
+    int64_t parts = (max_gen + 1023) / 1024;
+    if (plane_bytes > 0 && parts * plane_bytes * 4 > latent_bytes * 3) parts = latent_bytes * 3 / (plane_bytes * 4);
+    if (parts < 1) parts = 1;
+    if (parts > 64) parts = 64;
+    dev.pos_parts = (int32_t)parts;
   }
   dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));
   dev.by_box_fh = make_fastdiv((uint32_t)(dev.box_nf * dev.box_nh > 0 ? dev.box_nf * dev.box_nh : 1));
