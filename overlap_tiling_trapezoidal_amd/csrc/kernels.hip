@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kBlock = kThreads;
 constexpr int kWaves = kBlock / 64;
-constexpr int kPosUnroll = 4;      // position rows in flight per thread (copy pass)
+constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy pass)
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
