@@ -117,6 +117,10 @@ struct LaneIO {
   __device__ static inline void store(void* out, int64_t row, int vv, int V, const float* a) {
     store_out<OUT, E>(out, (row * V + vv) * (int64_t)E, a);
   }
+  // The q-th 4-float group of the lane's elements in an fp32 row buffer.
+  __device__ static inline f32x4* quad(float* acc, int64_t row, int vv, int V, int q) {
+    return reinterpret_cast<f32x4*>(acc + (row * V + vv) * (int64_t)E) + q;
+  }
 };
 // bf16 in, fp32 out: 32 output bytes per input vector.  Lane vv takes the
 // 8-byte pieces vv and V + vv instead (elements [4vv, 4vv+4) and
@@ -135,6 +139,9 @@ struct LaneIO<TDP_BF16, TDP_F32> {
     f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + row * 8 * V);
     st_nt(o + vv, f32x4{a[0], a[1], a[2], a[3]});
     st_nt(o + V + vv, f32x4{a[4], a[5], a[6], a[7]});
+  }
+  __device__ static inline f32x4* quad(float* acc, int64_t row, int vv, int V, int q) {
+    return reinterpret_cast<f32x4*>(acc + row * 8 * V) + (q ? V : 0) + vv;
   }
 };
 

@@ -891,14 +891,16 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
 // streaming blend: one tile at a time into an fp32 accumulator
 // ---------------------------------------------------------------------------
 
-constexpr int kStreamRows = 2;  // generated rows per lane in one streaming workgroup
+constexpr int kStreamRows = 1;  // generated rows per lane in one streaming workgroup (1 measured best: more workgroups per tile launch)
 
 // Generated rows of tile t, batch element b, one lane per 16-byte vector.
 // The weight is (wF * wH) * wW, as in blend_kernel.  A voxel's first
 // covering tile (smallest index: on every axis, not inside the previous
 // tile's overlap) writes fmaf(w, y, +0) without reading the accumulator;
 // later tiles add with fmaf.  Run for t = 0, 1, ..., T-1 in order, this is
-// blend_kernel's fp32 sum, term by term.
+// blend_kernel's fp32 sum, term by term.  Lanes take their elements as
+// blend_kernel does for an fp32 output (LaneIO), so that each accumulator
+// load and store instruction covers a contiguous span.
 template <int IN>
 __device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int j, int k, int b, int blk,
                                 const u32x4* __restrict__ tile_out, float* __restrict__ acc) {
@@ -918,14 +920,14 @@ __device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int 
     const float wa = ramp_weight(p.ax[0], i, lf, tb.sf) * ramp_weight(p.ax[1], j, lh, tb.sh) *
                      ramp_weight(p.ax[2], k, lw, tb.sw);
     const bool first = !(i > 0 && lf < p.ax[0].o) && !(j > 0 && lh < p.ax[1].o) && !(k > 0 && lw < p.ax[2].o);
-    const u32x4 yv = ld_nt(tile_out + ((int64_t)b * tb.s.cap + r) * V + vv);
+    using IO = LaneIO<IN, TDP_F32>;
+    const u32x4 yv = IO::load(tile_out, ((int64_t)b * tb.s.cap + r) * V + vv, vv, V);
     const int64_t voxel = (int64_t)b * p.rows + ((int64_t)(tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + lw;
-    f32x4* a4 = reinterpret_cast<f32x4*>(acc + (voxel * V + vv) * E);
     float x[E], old[E];
     InVec<IN>::unpack(yv, x);
 #pragma unroll
     for (int q = 0; q < E / 4; ++q) {
-      const f32x4 o = first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : a4[q];
+      const f32x4 o = first ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *IO::quad(acc, voxel, vv, V, q);
       old[4 * q] = o.x;
       old[4 * q + 1] = o.y;
       old[4 * q + 2] = o.z;
@@ -933,8 +935,9 @@ __device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int 
     }
 #pragma unroll
     for (int q = 0; q < E / 4; ++q)
-      a4[q] = f32x4{fmaf(wa, x[4 * q], old[4 * q]), fmaf(wa, x[4 * q + 1], old[4 * q + 1]),
-                    fmaf(wa, x[4 * q + 2], old[4 * q + 2]), fmaf(wa, x[4 * q + 3], old[4 * q + 3])};
+      *IO::quad(acc, voxel, vv, V, q) =
+          f32x4{fmaf(wa, x[4 * q], old[4 * q]), fmaf(wa, x[4 * q + 1], old[4 * q + 1]),
+                fmaf(wa, x[4 * q + 2], old[4 * q + 2]), fmaf(wa, x[4 * q + 3], old[4 * q + 3])};
   }
 }
 
