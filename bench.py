@@ -327,6 +327,17 @@ def main():
     torch.cuda.synchronize()
     eager_ms_per_step = start.elapsed_time(stop) / K
 
+    # spread over steps: K more eager steps, each between events of its own
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record(stream)
+    for i in range(K):
+        extract(sets[i % R])
+        blend(sets[(i - D) % R])
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
+    pct = {f"p{q}": round(per_step[min(K - 1, round(q / 100 * (K - 1)))], 5) for q in (10, 50, 90)}
+
     # timed region: the same K steps captured once in a HIP graph (the form a
     # serving loop runs), replayed once untimed, then replayed between two
     # events on the capture stream
@@ -457,6 +468,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "timing": "HIP graph of the K steps, replayed between two events",
         "eager_ms_per_step": round(eager_ms_per_step, 5),
+        "eager_step_ms_percentiles": pct,
         "eager_value": round(step_bytes / (eager_ms_per_step * 1e-3) / 1e9, 2),
         "eager_enqueue_s": round(enqueue, 4),
         "sources_sha256_16": sources_hash(),

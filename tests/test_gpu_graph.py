@@ -76,3 +76,49 @@ def test_graph_replays_match_eager(name, cuda):
         for k, v in (("out", out), ("out_s", out_s), ("tile_lat", bufs["tile_lat"]),
                      ("tile_pos", bufs["tile_pos"]), ("cond_row", bufs["cond_row"])):
             assert torch.equal(_bits(v), ref[k]), (rep, k)
+
+
+@pytest.mark.parametrize("world,rank", [(4, 1), (3, 2)])
+def test_rank_plan_graph_replays_match_eager(world, rank, cuda):
+    """A rank plan's extract and partial blend under capture, replayed
+    three times with eager work in between, equal the eager run."""
+    wl = WORKLOADS["conditioned"]
+    inp = make_inputs(wl)
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond, in_dtype=wl.dtype,
+                          out_dtype="f32")
+    plan = tdp.tdp_plan_create_rank(cfg, world, rank)
+    lat = to_device_latent(inp["latent"], cuda)
+    pos = torch.from_numpy(inp["pos"]).to(cuda)
+    bufs = tdp.allocate_extract_outputs(plan, cuda)
+    out = tdp.allocate_output(plan, cuda)
+    s = torch.cuda.Stream(cuda)
+
+    def step():
+        tdp.tdp_extract(plan, lat, pos, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"],
+                        bufs["tile_count"], bufs["cond_row"], s)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out, s)
+
+    outputs = (out, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"], bufs["cond_row"])
+
+    def scramble():
+        for t in outputs:
+            t.view(torch.uint8).fill_(0x5A)
+
+    note(f"rank graph eager {world}/{rank}")
+    scramble()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    ref = [_bits(v) for v in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        scramble()
+        torch.cuda.synchronize()
+        note(f"rank graph replay {world}/{rank} #{rep}")
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        for i, v in enumerate(outputs):
+            assert torch.equal(_bits(v), ref[i]), (rep, i)
