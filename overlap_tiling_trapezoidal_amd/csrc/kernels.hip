@@ -7,7 +7,12 @@
 //
 // Both operations are bound by HBM bandwidth: nothing is a contraction, so
 // no MFMA is used.  Latent rows move as 16-byte vectors (global_load /
-// global_store_dwordx4), V lanes per row, 256 / V rows per workgroup pass.
+// global_store_dwordx4).  Generated rows go two vectors per lane, so
+// ceil(V / 2) lanes share a row and each wave instruction covers 16 *
+// ceil(V / 2) contiguous bytes of every row it touches (a full 128-byte
+// line at C = 128 bf16).  The unit of work is one wave's rows of one
+// (batch, frame, row) line; tile rows come in closed form from the lane's
+// width covers and the line's frame x height combos, with no tables.
 // Hot loops are straight-line: every load is unconditional (out-of-range
 // lanes re-read a valid row and discard it), so the compiler keeps all of a
 // thread's loads in flight instead of waiting before each one.
@@ -19,13 +24,14 @@
 //   positions  (tile, batch, axis, part): the plane's minimum start,
 //              reduced by the workgroup itself, then the shifted positions
 //              and source indices of one part of the tile;
-//   latent     (batch, frame, row, chunk of rows): every latent row is read
-//              once and written to each tile that covers it.
+//   latent     four wave units of (batch, frame, row) line rows each: every
+//              latent row is read once and written to each tile that
+//              covers it.
 // The first two kinds are few and long; dispatched first, they run under
 // the latent copy, and no workgroup ever waits on another.  blend is one
-// launch too: conditioning workgroups first, then one workgroup per chunk
-// of a (batch, frame, row) line that gathers each output row from its
-// covering tile rows (owner computes: no atomics, fixed order).
+// launch too: conditioning workgroups first, then workgroups of four wave
+// units that gather each output row from its covering tile rows (owner
+// computes: no atomics, fixed order).
 // A rank plan (one rank's round-robin share) runs the same kernels,
 // instantiated with R = true: they touch only the tiles the rank holds and
 // blend writes the rank's full-size partial sum.
@@ -127,13 +133,43 @@ struct LineCombos {
   }
 };
 
-// First row (in tile-slot rows) of width cell 0 of line (b, combo) in tile
-// (i, j, iw): row of cell w is this + w.
+// Rows of one (f, h) line in the tiles of one frame x height combo (i, j).
+// In tile t = tbase + k (width tile k, start a_k, size sw_k), batch element
+// b, the row of width cell w is
+//   whole plan: base + sfsh * (B * PW_k + b * sw_k) + Nc * (B * k + b)
+//                    + L * sw_k + (w - a_k),   PW_k = a_k + k * o (cells of
+//               width tiles before k), base = B * (rows of every tile before
+//               (i, j, 0), i.e. gen_before(i, j, 0) + tbase * Nc);
+//   rank plan:  (t / world) * slot_cap * B + b * (sfsh * sw_k + Nc)
+//                    + L * sw_k + (w - a_k),
+// the slot layout of tile_slot_whole / tile_slot_rank written out by width
+// tile.  The plan keeps every tile row below 2^31, so rows are int32.
+struct ComboRows {
+  int base;   // whole plan: rows of the tiles before (i, j, 0), all batch elements
+  int tbase;  // (i * nH + j) * nW
+  int sfsh;   // sf * sh: width rows per tile row of this combo's tiles
+  int L;      // lf * sh + lh: the line's row within a width-row of the tile
+};
 template <bool R>
-__device__ inline int64_t line_row0(const PlanDev& p, int b, int i, int lf, int j, int lh, int sh, int iw) {
-  const TileSlot s = slot_of<R>(p, i, j, iw);
-  const int sw = split_size(p.ax[2], iw);
-  return s.row_base + (int64_t)b * s.cap + (int64_t)(lf * sh + lh) * sw - split_start(p.ax[2], iw);
+__device__ inline ComboRows combo_rows(const PlanDev& p, int i, int lf, int sf, int j, int lh, int sh) {
+  ComboRows c;
+  c.tbase = (i * p.ax[1].n + j) * p.ax[2].n;
+  c.sfsh = sf * sh;
+  c.L = lf * sh + lh;
+  c.base = R ? 0
+             : p.B * ((split_prefix(p.ax[0], i) * split_total(p.ax[1]) + sf * split_prefix(p.ax[1], j)) *
+                          split_total(p.ax[2]) +
+                      p.Nc * c.tbase);
+  return c;
+}
+// Row of width cell w in width tile k (start a, size s) of combo c.
+template <bool R>
+__device__ inline int cover_row(const PlanDev& p, const ComboRows& c, int b, int k, int a, int s, int w) {
+  if constexpr (R)
+    return (int)fastdiv((uint32_t)(c.tbase + k), p.by_world) * p.slot_cap * p.B + b * (c.sfsh * s + p.Nc) +
+           c.L * s + (w - a);
+  else
+    return c.base + c.sfsh * (p.B * (a + k * p.ax[2].o) + b * s) + p.Nc * (p.B * k + b) + c.L * s + (w - a);
 }
 
 // ---------------------------------------------------------------------------
@@ -193,18 +229,12 @@ __device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r
   return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + x;
 }
 
-// Row tables hold vector offsets, not pointers: a pointer read back from
-// LDS loses its address space and turns every access into a flat one.
-struct LineShared {
-  int64_t rowoff[kWaves][kMaxCombos][kMaxTiles];  // per wave: tile_lat vector of cell w = rowoff + w*V + lane
-};
 struct SelShared {
   int wave_tot[kWaves];
   int kept_c[kSelChunk];     // kept tokens of this chunk, ascending
   int base;                  // kept tokens of this tile before this chunk
 };
 union ExtractShared {
-  LineShared line;
   SelShared sel;
   float2 red[kWaves];
 };
@@ -429,91 +459,80 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
   }
 }
 
-// Latent workgroup: rows [w0, w0 + rpp * kLatRows) of one (b, f, h) line,
-// every row read once and written to each covering tile.  Source addresses
-// need no tables, so the loads are issued before the cover and row tables
-// are built: the table setup runs while those loads are in flight.  A rank
-// plan reads only the rows that one of its tiles covers (table first,
-// kNotHeld for a tile it does not hold).
+// Latent wave unit: rows [w0, w0 + rwv) of one (b, f, h) line, every row
+// read once and written to each covering tile.  Lane (r, q) of the wave
+// moves vectors q and lpr + q of row w0 + r, so each load and
+// store instruction covers 16 * lpr contiguous bytes of every row it
+// touches.  Tile rows come in closed form from the lane's width covers and
+// the line's frame x height combos (workgroup-uniform), with no tables and
+// no barrier; the loads are issued before any of that is computed.  A rank
+// plan reads only the rows that one of its tiles covers.
 template <bool R>
-__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int blk) {
-  const int V = p.vin;
-  const int rpp = p.rpp;
+__device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, int blk) {
+  const int V = p.vin, LPR = p.lpr;
   const int rows = p.lat_rows;
+  // this wave's unit: the waves of a workgroup take consecutive units
+  const int unit = __builtin_amdgcn_readfirstlane(blk * kWaves + (int)(threadIdx.x >> 6));
+  if (unit >= p.lat_units) return;
   int b, f, h, w0;
-  if constexpr (R) {  // workgroups tile the held tiles' bounding box only
-    const int line = (int)fastdiv((uint32_t)blk, p.by_box_c);
-    w0 = (p.box_c0 + blk - line * p.box_nc) * rows;
+  if constexpr (R) {  // units tile the held tiles' bounding box only
+    const int line = (int)fastdiv((uint32_t)unit, p.by_box_c);
+    w0 = (p.box_c0 + unit - line * p.box_nc) * rows;
     b = (int)fastdiv((uint32_t)line, p.by_box_fh);
     const int fh = line - b * (p.box_nf * p.box_nh);
     const int fb = (int)fastdiv((uint32_t)fh, p.by_box_h);
     f = p.box_f0 + fb;
     h = p.box_h0 + fh - fb * p.box_nh;
   } else {
-    const int line = (int)fastdiv((uint32_t)blk, p.by_lat_chunks);
-    w0 = (blk - line * p.lat_chunks) * rows;
+    const int line = (int)fastdiv((uint32_t)unit, p.by_lat_chunks);
+    w0 = (unit - line * p.lat_chunks) * rows;
     b = (int)fastdiv((uint32_t)line, p.by_FH);
     const int fh = line - b * (p.F * p.H);
     f = (int)fastdiv((uint32_t)fh, p.by_H);
     h = fh - f * p.H;
   }
-  const int nrow = min(rows, p.W - w0);
-  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
-  const bool lane_on = r < rpp;
-  const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w0) * V + vv;
-
-  u32x4 v[kLatRows];
-  int kv[kLatRows];
-  bool ok[kLatRows];
-#pragma unroll
-  for (int u = 0; u < kLatRows; ++u) {
-    const int k = u * rpp + r;  // row within the chunk
-    ok[u] = lane_on && k < nrow;
-    kv[u] = ok[u] ? k : 0;
-    if constexpr (!R) v[u] = ld_nt(src + kv[u] * V);
+  const int lane = threadIdx.x & 63;
+  const int r = (int)fastdiv((uint32_t)lane, p.by_lpr), q = lane - r * LPR;
+  const int wr = w0 + r;
+  bool ok = r < p.rwv && wr < p.W;
+  const int w = ok ? wr : w0;  // w0 < W: an unused lane re-reads a row of this line
+  const int v1 = LPR + q;
+  const bool ok1 = v1 < V;
+  const int v1l = ok1 ? v1 : q;
+  const u32x4* src = a.latent + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w) * V;
+  u32x4 x0, x1;
+  if constexpr (!R) {
+    x0 = ld_nt(src + q);
+    x1 = ld_nt(src + v1l);
   }
-
   LineCombos lc;
   lc.init(p, f, h);
-  const int nw = p.ax[2].n;
-  // each wave builds its own copy of the row table (no workgroup barrier)
-  int64_t(*rowoff)[kMaxTiles] = sm.line.rowoff[threadIdx.x >> 6];
-  for (int e = threadIdx.x & 63; e < lc.n * nw; e += 64) {
-    const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
-    int i, lf, sf, j, lh, sh;
-    lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    const bool own = held<R>(p, (i * p.ax[1].n + j) * nw + iw);
-    rowoff[combo][iw] = own ? (line_row0<R>(p, b, i, lf, j, lh, sh, iw) + w0) * V : kNotHeld;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int ncombo = lc.n;
-  Covers cw[kLatRows];
-#pragma unroll
-  for (int u = 0; u < kLatRows; ++u) cw[u] = split_covers(p.ax[2], w0 + kv[u]);
+  const Covers cw = split_covers(p.ax[2], w);
   if constexpr (R) {
-#pragma unroll
-    for (int u = 0; u < kLatRows; ++u) {
-      bool any = false;
-      for (int cb = 0; cb < ncombo; ++cb)
-        any = any || rowoff[cb][cw[u].t0] != kNotHeld || (cw[u].n > 1 && rowoff[cb][cw[u].t1] != kNotHeld);
-      ok[u] = ok[u] && any;
-      v[u] = ok[u] ? ld_nt(src + kv[u] * V) : u32x4{0u, 0u, 0u, 0u};
+    bool any = false;
+    for (int cb = 0; cb < lc.n; ++cb) {
+      int i, lf, sf, j, lh, sh;
+      lc.get(cb, f, h, i, lf, sf, j, lh, sh);
+      const int tb = (i * p.ax[1].n + j) * p.ax[2].n;
+      any = any || tile_is_local(p, tb + cw.t0) || (cw.n > 1 && tile_is_local(p, tb + cw.t1));
     }
+    ok = ok && any;
+    x0 = ok ? ld_nt(src + q) : u32x4{0u, 0u, 0u, 0u};
+    x1 = ok ? ld_nt(src + v1l) : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int cb = 0; cb < ncombo; ++cb) {
-#pragma unroll
-    for (int u = 0; u < kLatRows; ++u) {
-      if constexpr (R) {
-        const int64_t o0 = rowoff[cb][cw[u].t0], o1 = rowoff[cb][cw[u].t1];
-        if (ok[u] && o0 != kNotHeld) st_nt(a.tile_lat + o0 + kv[u] * V + vv, v[u]);
-        if (ok[u] && cw[u].n > 1 && o1 != kNotHeld) st_nt(a.tile_lat + o1 + kv[u] * V + vv, v[u]);
-      } else {
-        if (ok[u]) st_nt(a.tile_lat + rowoff[cb][cw[u].t0] + kv[u] * V + vv, v[u]);
-        if (ok[u] && cw[u].n > 1) st_nt(a.tile_lat + rowoff[cb][cw[u].t1] + kv[u] * V + vv, v[u]);
-      }
-    }
+  for (int cb = 0; cb < lc.n; ++cb) {
+    int i, lf, sf, j, lh, sh;
+    lc.get(cb, f, h, i, lf, sf, j, lh, sh);
+    const ComboRows c = combo_rows<R>(p, i, lf, sf, j, lh, sh);
+    const bool s0 = ok && held<R>(p, c.tbase + cw.t0);
+    const bool s1 = ok && cw.n > 1 && held<R>(p, c.tbase + cw.t1);
+    // (a rank plan computes rows of the tiles it holds only)
+    u32x4* d0 = a.tile_lat + (int64_t)(!R || s0 ? cover_row<R>(p, c, b, cw.t0, cw.a0, cw.s0, w) : 0) * V;
+    u32x4* d1 = a.tile_lat + (int64_t)(!R || s1 ? cover_row<R>(p, c, b, cw.t1, cw.a1, cw.s1, w) : 0) * V;
+    if (s0) st_nt(d0 + q, x0);
+    if (s0 && ok1) st_nt(d0 + v1, x1);
+    if (s1) st_nt(d1 + q, x0);
+    if (s1 && ok1) st_nt(d1 + v1, x1);
   }
 }
 
@@ -563,124 +582,136 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
     extract_positions<R>(p, a, sm, R ? p.rank + slot * p.world : slot, slot, b, d, part);
     return;
   }
-  extract_latent<R>(p, a, sm, bid - a.n_pos);
+  extract_latent<R>(p, a, bid - a.n_pos);
 }
 
 // ---------------------------------------------------------------------------
 // blend
 // ---------------------------------------------------------------------------
 
-struct BlendShared {
-  int64_t rowoff[kMaxCombos][kMaxTiles];  // tile_out vector of cell w: rowoff + w*V + lane
-  float wfh[kMaxCombos];                  // frames x height weight of the combo
-};
-
-// SU rows of one lane, NC frame x height combos.  `cw[u]` are the width
-// covers of row w0 + kv[u].  TWO: some row of this wave has a second width
-// cover; then every row loads both covers (a missing second one re-reads
-// the first row and is masked out of the sum).  Without TWO only the first
-// cover is loaded.  The width weights are computed after the loads are
-// issued, while they are in flight.  R (rank plan): a tile the plan does not
-// hold has row offset kNotHeld; its load re-reads vector vv of slot 0 (there
-// is one: workgroups outside the held tiles' box never get here) and is
-// left out of the sum.
-template <int IN, int OUT, int NC, int SU, bool TWO, bool R>
-__device__ inline void blend_rows(const PlanDev& p, const BlendShared& sm, const Covers* cw,
-                                  const u32x4* __restrict__ tile_out, void* __restrict__ out, int64_t dst0, int w0,
-                                  const int* kv, const bool* ok, int vv) {
+// Terms of NC frame x height combos (cr, wfh) for the lane's row w and its
+// NV vectors vs[], added into acc[k] in ascending tile order: combos ascend
+// in (i_f, i_h), then the width covers.  TWO: some row of the wave has a
+// second width cover; then every lane loads both covers (a missing second
+// one re-reads the first row and is left out of the sum).  Without TWO only
+// the first cover is loaded.  R (rank plan): a term of a tile the plan does
+// not hold re-reads a vector of slot 0 (there is one: workgroups outside
+// the held tiles' box never get here) and is left out.
+template <int IN, int OUT, int NC, int NV, bool TWO, bool R>
+__device__ inline void blend_terms(const PlanDev& p, const ComboRows* cr, const float* wfh, const Covers& cw,
+                                   float wx, float wy, int b, int w, const int* vs,
+                                   const u32x4* __restrict__ tile_out, float (&acc)[NV][InVec<IN>::E]) {
   constexpr int E = InVec<IN>::E;
   using IO = LaneIO<IN, OUT>;
   const int V = p.vin;
-  u32x4 y0[SU][NC], y1[SU][TWO ? NC : 1];
-  bool h0[SU][NC], h1[SU][TWO ? NC : 1];  // the term is held (always, for a whole plan)
+  u32x4 y0[NC][NV], y1[NC][NV];
+  bool h0[NC], h1[NC];  // the term is held (always, for a whole plan)
 #pragma unroll
-  for (int u = 0; u < SU; ++u) {
-    const int iw0 = cw[u].t0, iw1s = cw[u].t1;  // t1 == t0 with one cover
-    const int64_t off = (int64_t)(w0 + kv[u]) * V + vv;
+  for (int cb = 0; cb < NC; ++cb) {
+    h0[cb] = held<R>(p, cr[cb].tbase + cw.t0);
+    const int64_t r0 = h0[cb] ? (int64_t)cover_row<R>(p, cr[cb], b, cw.t0, cw.a0, cw.s0, w) * V : 0;
 #pragma unroll
-    for (int cb = 0; cb < NC; ++cb) {
-      const int64_t o0 = sm.rowoff[cb][iw0];
-      h0[u][cb] = !R || o0 != kNotHeld;
-      y0[u][cb] = IO::load(tile_out, h0[u][cb] ? o0 + off : (int64_t)vv, vv, V);
-      if (TWO) {
-        const int64_t o1 = sm.rowoff[cb][iw1s];
-        h1[u][TWO ? cb : 0] = !R || o1 != kNotHeld;
-        y1[u][TWO ? cb : 0] = IO::load(tile_out, h1[u][TWO ? cb : 0] ? o1 + off : (int64_t)vv, vv, V);
-      }
+    for (int k = 0; k < NV; ++k) y0[cb][k] = IO::load(tile_out, r0 + vs[k], vs[k], V);
+    if (TWO) {
+      h1[cb] = held<R>(p, cr[cb].tbase + cw.t1);
+      const int64_t r1 = h1[cb] ? (int64_t)cover_row<R>(p, cr[cb], b, cw.t1, cw.a1, cw.s1, w) * V : 0;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) y1[cb][k] = IO::load(tile_out, r1 + vs[k], vs[k], V);
     }
   }
+  const bool has1 = cw.n > 1;
 #pragma unroll
-  for (int u = 0; u < SU; ++u) {
-    const int w = w0 + kv[u];
-    const bool has1 = cw[u].n > 1;
-    const float wx = ramp_weight(p.ax[2], cw[u].t0, w - cw[u].a0, cw[u].s0);
-    const float wy = TWO && has1 ? ramp_weight(p.ax[2], cw[u].t1, w - cw[u].a1, cw[u].s1) : 0.0f;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    // ascending tile index: combos ascend in (i_f, i_h), then i_w
+  for (int k = 0; k < NV; ++k) {
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-      const float wa = sm.wfh[cb] * wx;
+      const float wa = wfh[cb] * wx;
       float x0[E];
-      InVec<IN>::unpack(y0[u][cb], x0);
-      const bool use0 = h0[u][cb];
+      InVec<IN>::unpack(y0[cb][k], x0);
+      const bool use0 = h0[cb];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = use0 ? fmaf(wa, x0[e], acc[e]) : acc[e];
+      for (int e = 0; e < E; ++e) acc[k][e] = use0 ? fmaf(wa, x0[e], acc[k][e]) : acc[k][e];
       if (TWO) {
-        const float wb = sm.wfh[cb] * wy;
+        const float wb = wfh[cb] * wy;
         float x1[E];
-        InVec<IN>::unpack(y1[u][TWO ? cb : 0], x1);
-        const bool use1 = has1 && h1[u][TWO ? cb : 0];
+        InVec<IN>::unpack(y1[cb][k], x1);
+        const bool use1 = has1 && h1[cb];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = use1 ? fmaf(wb, x1[e], acc[e]) : acc[e];
+        for (int e = 0; e < E; ++e) acc[k][e] = use1 ? fmaf(wb, x1[e], acc[k][e]) : acc[k][e];
       }
     }
-    if (ok[u]) IO::store(out, dst0 + w, vv, V, acc);
   }
 }
 
-// Rows [w0, w0 + blend_chunk_rows(V)) of one (b, f, h) line, with exactly
-// NC frame x height combos.  Each wave owns consecutive rows: in sub-pass
-// `sub` its lanes hold rows sub*4*rw*SU + wave*rw*SU + u*rw + lane/V,
-// u < SU (rw = 64/V rows per wave instruction), so a wave usually lies
-// inside one width tile and takes the single-cover path.  SU rows at a
-// time keep at most 8 loads in flight (2 per combo and row).
-template <int IN, int OUT, int NC, bool R>
-__device__ void blend_chunk_rows(const PlanDev& p, const BlendShared& sm, const u32x4* __restrict__ tile_out,
-                                 void* __restrict__ out, int64_t dst0, int w0) {
-  constexpr int SU = 4 / NC < kBlendRows ? 4 / NC : kBlendRows;
-  const int V = p.vin;
-  const int rw = p.rw;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = (int)fastdiv((uint32_t)lane, p.by_vin), vv = lane - lr * V;
-  const bool lane_on = lr < rw;
+// Lane (r, q) owns row w = w0 + r of its wave's unit and its vectors q and
+// lpr + q; it sums the row's covering tile rows in fp32 and rounds once.
+// With up to two combos both vectors are in flight together; four combos (a
+// tiled frame axis) take one vector at a time, so a lane never holds more
+// than eight loads.
+template <int IN, int OUT, int NC, bool TWO, bool R>
+__device__ inline void blend_lane(const PlanDev& p, const LineCombos& lc, int f, int h, const Covers& cw, int b,
+                                  int w, bool ok, int q, const u32x4* __restrict__ tile_out,
+                                  void* __restrict__ out, int64_t dst_row) {
+  constexpr int E = InVec<IN>::E;
+  using IO = LaneIO<IN, OUT>;
+  ComboRows cr[NC];
+  float wfh[NC];
 #pragma unroll
-  for (int sub = 0; sub < kBlendRows; sub += SU) {
-    int kv[SU];
-    bool ok[SU];
-    Covers cw[SU];
-    bool two = false;
+  for (int cb = 0; cb < NC; ++cb) {
+    int i, lf, sf, j, lh, sh;
+    lc.get(cb, f, h, i, lf, sf, j, lh, sh);
+    cr[cb] = combo_rows<R>(p, i, lf, sf, j, lh, sh);
+    wfh[cb] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
+  }
+  const int v1 = p.lpr + q;
+  const bool ok1 = v1 < p.vin;
+  const int vs[2] = {q, ok1 ? v1 : q};
+  const float wx = ramp_weight(p.ax[2], cw.t0, w - cw.a0, cw.s0);
+  const float wy = TWO && cw.n > 1 ? ramp_weight(p.ax[2], cw.t1, w - cw.a1, cw.s1) : 0.0f;
+  if constexpr (NC <= 2) {
+    float acc[2][E];
 #pragma unroll
-    for (int u = 0; u < SU; ++u) {
-      const int k = (sub * kWaves + wave * SU + u) * rw + lr;  // row within the chunk
-      ok[u] = lane_on && w0 + k < p.W;
-      kv[u] = ok[u] ? k : 0;
-      cw[u] = split_covers(p.ax[2], w0 + kv[u]);
-      two |= ok[u] && cw[u].n > 1;
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[k][e] = 0.0f;
+    blend_terms<IN, OUT, NC, 2, TWO, R>(p, cr, wfh, cw, wx, wy, b, w, vs, tile_out, acc);
+    if (ok) IO::store(out, dst_row, q, p.vin, acc[0]);
+    if (ok && ok1) IO::store(out, dst_row, v1, p.vin, acc[1]);
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) {
+      float acc[1][E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[0][e] = 0.0f;
+      blend_terms<IN, OUT, NC, 1, TWO, R>(p, cr, wfh, cw, wx, wy, b, w, vs + k, tile_out, acc);
+      if (ok && (k == 0 || ok1)) IO::store(out, dst_row, vs[k], p.vin, acc[0]);
     }
-    // wave-uniform: most waves lie inside one width tile
-    if (__any(two))
-      blend_rows<IN, OUT, NC, SU, true, R>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
-    else
-      blend_rows<IN, OUT, NC, SU, false, R>(p, sm, cw, tile_out, out, dst0, w0, kv, ok, vv);
   }
 }
 
+// Rows [w0, w0 + rwv) of one (b, f, h) line, one wave, with exactly NC
+// frame x height combos (wave-uniform row bases and weights); the wave takes
+// the single-cover path unless one of its rows lies in two width tiles.
+template <int IN, int OUT, int NC, bool R>
+__device__ void blend_line(const PlanDev& p, const LineCombos& lc, int b, int f, int h, int w0,
+                           const u32x4* __restrict__ tile_out, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = (int)fastdiv((uint32_t)lane, p.by_lpr), q = lane - r * p.lpr;
+  const int wr = w0 + r;
+  const bool ok = r < p.rwv && wr < p.W;
+  const int w = ok ? wr : w0;  // w0 < W
+  const Covers cw = split_covers(p.ax[2], w);
+  const int64_t dst_row = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W + w;
+  // wave-uniform: most waves lie inside one width tile
+  if (__any(ok && cw.n > 1))
+    blend_lane<IN, OUT, NC, true, R>(p, lc, f, h, cw, b, w, ok, q, tile_out, out, dst_row);
+  else
+    blend_lane<IN, OUT, NC, false, R>(p, lc, f, h, cw, b, w, ok, q, tile_out, out, dst_row);
+}
 
-// Generated rows: one workgroup per (b, f, h, chunk of rpp * kBlendRows
-// rows), one pass each; many short workgroups let the dispatcher overlap
-// the tail of one with the start of the next.
+// Generated rows: one wave per unit of rwv rows of one (b, f, h) line, the
+// waves of a workgroup on consecutive units, one pass each; many short
+// workgroups let the dispatcher overlap the tail of one with the start of
+// the next, and no lane idles at the end of a line unless W % rwv != 0.
 // Conditioning rows: (1/k) * sum, ascending t, over the k tiles that keep
 // the token (k = non-negative entries of its cond_row column; 0 when k = 0).
 // Workgroup `cid` = (batch element, chunk of kCondTokens tokens).  The
@@ -798,27 +829,28 @@ __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ ti
   }
 }
 
-// Rank plans: rows [w0, w0 + rows) of a line outside the held tiles' box
-// are zero in the partial buffer; written without tables or loads.
+// Rank plans: a wave unit (rows [w0, w0 + rwv) of a line) outside the held
+// tiles' box is zero in the partial buffer; written without loads.
 template <int IN, int OUT>
-__device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_t dst0, int w0, int rows) {
+__device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_t dst0, int w0) {
   constexpr int E = InVec<IN>::E;
-  const int V = p.vin;
-  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
-  if (r >= p.rpp) return;
+  const int lane = threadIdx.x & 63;
+  const int r = (int)fastdiv((uint32_t)lane, p.by_lpr), q = lane - r * p.lpr;
+  if (r >= p.rwv || w0 + r >= p.W) return;
   float z[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) z[e] = 0.0f;
-  const int nrow = min(rows, p.W - w0);
-  for (int k = r; k < nrow; k += p.rpp) LaneIO<IN, OUT>::store(out, dst0 + w0 + k, vv, V, z);
+  LaneIO<IN, OUT>::store(out, dst0 + w0 + r, q, p.vin, z);
+  if (p.lpr + q < p.vin) LaneIO<IN, OUT>::store(out, dst0 + w0 + r, p.lpr + q, p.vin, z);
 }
 
-template <int IN, int OUT, bool R>
+// F2: the frame axis is tiled, so a line can have four frame x height
+// combos; only plans with a tiled frame axis carry that path (and its
+// registers).
+template <int IN, int OUT, bool R, bool F2>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
                                                        const int32_t* __restrict__ cond_row,
                                                        void* __restrict__ out, int n_gen_blocks) {
-  __shared__ BlendShared smw[kWaves];
-  const int V = p.vin;
   // conditioning workgroups first: each is a short dependent chain, so they
   // start early and run under the generated rows
   const int n_cond = (int)gridDim.x - n_gen_blocks;
@@ -829,61 +861,52 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
       blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, out, blockIdx.x);
     return;
   }
-  const int bid = blockIdx.x - n_cond;
-  const int rows = p.blend_rows;  // rows per chunk
-  const int line = (int)fastdiv((uint32_t)bid, p.by_blend_chunks);
-  const int w0 = (bid - line * p.blend_chunks) * rows;
+  // this wave's unit (rows [w0, w0 + rwv) of one line): the waves of a
+  // workgroup take consecutive units
+  const int unit = __builtin_amdgcn_readfirstlane(((int)blockIdx.x - n_cond) * kWaves + (int)(threadIdx.x >> 6));
+  if (unit >= p.gen_units) return;
+  const int rows = p.blend_rows;
+  const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
+  const int w0 = (unit - line * p.blend_chunks) * rows;
   const int b = (int)fastdiv((uint32_t)line, p.by_FH);
   const int fh = line - b * (p.F * p.H);
   const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
   if constexpr (R) {
     if (f < p.box_f0 || f >= p.box_f0 + p.box_nf || h < p.box_h0 || h >= p.box_h0 + p.box_nh ||
         w0 >= p.box_w0 + p.box_nw || w0 + rows <= p.box_w0) {
-      blend_zero_rows<IN, OUT>(p, out, (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W, w0, rows);
+      blend_zero_rows<IN, OUT>(p, out, (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W, w0);
       return;
     }
   }
   LineCombos lc;
   lc.init(p, f, h);
-  const int nw = p.ax[2].n;
-  // Each wave builds its own copy of the row table, so no wave waits for
-  // another before issuing its loads.
-  BlendShared& sm = smw[threadIdx.x >> 6];
-  for (int e = threadIdx.x & 63; e < lc.n * nw; e += 64) {
-    const int combo = (int)fastdiv((uint32_t)e, p.by_nw), iw = e - combo * nw;
-    int i, lf, sf, j, lh, sh;
-    lc.get(combo, f, h, i, lf, sf, j, lh, sh);
-    const bool own = held<R>(p, (i * p.ax[1].n + j) * nw + iw);
-    sm.rowoff[combo][iw] = own ? line_row0<R>(p, b, i, lf, j, lh, sh, iw) * V : kNotHeld;
-    if (iw == 0) sm.wfh[combo] = ramp_weight(p.ax[0], i, lf, sf) * ramp_weight(p.ax[1], j, lh, sh);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int64_t dst0 = (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W;
-  const int nc = lc.n;
-  if (nc == 1)
-    blend_chunk_rows<IN, OUT, 1, R>(p, sm, tile_out, out, dst0, w0);
-  else if (nc == 2)
-    blend_chunk_rows<IN, OUT, 2, R>(p, sm, tile_out, out, dst0, w0);
+  if (lc.n == 1)
+    blend_line<IN, OUT, 1, R>(p, lc, b, f, h, w0, tile_out, out);
+  else if (!F2 || lc.n == 2)
+    blend_line<IN, OUT, 2, R>(p, lc, b, f, h, w0, tile_out, out);
   else
-    blend_chunk_rows<IN, OUT, 4, R>(p, sm, tile_out, out, dst0, w0);
+    blend_line<IN, OUT, F2 ? 4 : 2, R>(p, lc, b, f, h, w0, tile_out, out);
 }
 
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
-  const int n_gen = p.B * p.F * p.H * p.blend_chunks;
+  const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0;
   // LDS for the cached conditioning path: rowtab, cap, k, then int64 bases
   const size_t lds = p.Nc > 0 && p.T <= kCondTiles
                          ? ((size_t)p.T * kCondTokens + p.T + kCondTokens + 1) * sizeof(int) + 8 + (size_t)p.T * 8
                          : 0;
-  if (p.world > 1)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, true>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
-                       reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
+  const dim3 grid(n_gen + n_cond), block(kBlock);
+  const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
+  const bool f2 = p.ax[0].n > 1;
+  if (p.world > 1 && f2)
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, true>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+  else if (p.world > 1)
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, false>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+  else if (f2)
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, true>), grid, block, lds, s, p, y, cond_row, out, n_gen);
   else
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, false>), dim3(n_gen + n_cond), dim3(kBlock), lds, s, p,
-                       reinterpret_cast<const u32x4*>(tile_out), cond_row, out, n_gen);
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, false>), grid, block, lds, s, p, y, cond_row, out, n_gen);
   return hipGetLastError();
 }
 
@@ -1057,7 +1080,7 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
-  const int n_lat = p.world > 1 ? p.B * p.box_nf * p.box_nh * p.box_nc : p.B * p.F * p.H * p.lat_chunks;
+  const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(a.n_sel + a.n_pos + n_lat);
   if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write

@@ -171,12 +171,15 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
                 (long long)(total_index * c.batch));
 
   dev.rpp = kThreads / dev.vin;
-  dev.rw = 64 / dev.vin;
-  dev.lat_rows = dev.rpp * kLatRows;
+  dev.lpr = (dev.vin + 1) / 2;  // vin <= 64, so lpr <= 32 and a wave holds at least two rows
+  dev.rwv = 64 / dev.lpr;
+  dev.lat_rows = dev.rwv;
   dev.lat_chunks = (dev.W + dev.lat_rows - 1) / dev.lat_rows;
-  dev.blend_rows = (kThreads / 64) * dev.rw * kBlendRows;
+  dev.blend_rows = dev.rwv;
   dev.blend_chunks = (dev.W + dev.blend_rows - 1) / dev.blend_rows;
+  dev.gen_units = dev.B * dev.F * dev.H * dev.blend_chunks;  // <= B * N < 2^31
   dev.by_vin = make_fastdiv((uint32_t)dev.vin);
+  dev.by_lpr = make_fastdiv((uint32_t)dev.lpr);
   dev.by_H = make_fastdiv((uint32_t)dev.H);
   dev.by_FH = make_fastdiv((uint32_t)(dev.F * dev.H));
   dev.by_nw = make_fastdiv((uint32_t)dev.ax[2].n);
@@ -222,6 +225,7 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
     if (parts > 64) parts = 64;
     dev.pos_parts = (int32_t)parts;
   }
+  dev.lat_units = world == 1 ? dev.B * dev.F * dev.H * dev.lat_chunks : dev.B * dev.box_nf * dev.box_nh * dev.box_nc;
   dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));
   dev.by_box_fh = make_fastdiv((uint32_t)(dev.box_nf * dev.box_nh > 0 ? dev.box_nf * dev.box_nh : 1));
   dev.by_box_c = make_fastdiv((uint32_t)(dev.box_nc > 0 ? dev.box_nc : 1));

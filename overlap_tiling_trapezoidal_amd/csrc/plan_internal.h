@@ -107,8 +107,6 @@ TDP_HD Covers split_covers(const AxisSplit& a, int x) {
 
 // Launch shape shared by the host planner and the kernels.
 constexpr int kThreads = 256;   // threads per workgroup
-constexpr int kLatRows = 1;     // latent rows per lane in one extract workgroup
-constexpr int kBlendRows = 2;   // generated rows per lane in one blend workgroup
 
 // Everything a kernel needs about a plan; passed by value (kernel argument).
 struct PlanDev {
@@ -124,11 +122,16 @@ struct PlanDev {
   int32_t normalize;  // subtract the per-tile offsets
   int32_t pos_parts;  // position workgroups per (tile, batch element, axis)
   // Launch geometry and invariant divisors (multiply-shift), from the host:
-  int32_t rpp;        // rows per workgroup pass: kThreads / vin
-  int32_t rw;         // rows per wave instruction: 64 / vin
-  int32_t lat_rows, lat_chunks;      // extract: rows per latent workgroup, chunks per line
-  int32_t blend_rows, blend_chunks;  // blend: rows per workgroup, chunks per line
-  FastDiv by_vin, by_H, by_FH, by_nw, by_lat_chunks, by_blend_chunks;
+  int32_t rpp;        // rows per workgroup pass, one vector per lane: kThreads / vin
+  // Generated rows of extract and blend: each lane moves two vectors of one
+  // row, q and lpr + q, so lpr = ceil(vin / 2) lanes share a row and a wave
+  // holds rwv = 64 / lpr rows.  The unit of work is one wave's rows of one
+  // (b, f, h) line; a workgroup takes kThreads / 64 consecutive units.
+  int32_t lpr, rwv;
+  int32_t lat_rows, lat_chunks;      // extract: rows per wave unit (rwv), units per line
+  int32_t blend_rows, blend_chunks;  // blend: rows per wave unit (rwv), units per line
+  int32_t lat_units, gen_units;      // wave units of extract (whole latent or rank box) and of blend
+  FastDiv by_vin, by_lpr, by_H, by_FH, by_nw, by_lat_chunks, by_blend_chunks;
   // Round-robin share (TDP docs, "What it is": tile t runs on rank t mod
   // world).  world == 1 is the whole plan.  A rank plan holds the tiles with
   // t mod world == rank, local index t / world, in uniform slots of
