@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "plan_internal.h"
 
@@ -888,14 +890,66 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     blend_line<IN, OUT, F2 ? 4 : 2, R>(p, lc, b, f, h, w0, tile_out, out);
 }
 
+// Occupancy caps.  Both kernels move more bytes per microsecond with fewer
+// workgroups sharing a compute unit than the registers allow (7 or 8 per
+// CU): fewer requests in flight per CU, and the long position and selection
+// workgroups of extract finish sooner.  Measured on the 4K-class latent:
+// extract 22.2 us at 7 per CU, 21.0 us at 3, 22.5 us at 2; blend 18.9 us at
+// 8, 18.4 us at 4, 19.7 us at 3.  Extracts with fewer latent workgroups are
+// set by their position and selection chains and do best at 2 per CU
+// (full-res latent 7.7 -> 6.6 us, conditioned 23.2 -> 20.4 us).  A launch
+// holds the cap by asking for dynamic LDS that only k workgroups fit in.
+struct DeviceShape {
+  int lds_per_cu;     // bytes of LDS per compute unit (0: unknown)
+  int lds_per_block;  // largest LDS request of one workgroup
+  int cus;            // compute units
+};
+DeviceShape device_shape() {
+  static std::atomic<int> cache[64][3];  // value + 1; 0 = not queried yet
+  DeviceShape d{0, 0, 0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return d;
+  const hipDeviceAttribute_t attr[3] = {hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                        hipDeviceAttributeMaxSharedMemoryPerBlock,
+                                        hipDeviceAttributeMultiprocessorCount};
+  int v[3];
+  for (int i = 0; i < 3; ++i) {
+    int c = cache[dev][i].load(std::memory_order_relaxed);
+    if (c == 0) {
+      int x = 0;
+      if (hipDeviceGetAttribute(&x, attr[i], dev) != hipSuccess || x < 0) x = 0;
+      c = x + 1;
+      cache[dev][i].store(c, std::memory_order_relaxed);
+    }
+    v[i] = c - 1;
+  }
+  d.lds_per_cu = v[0];
+  d.lds_per_block = v[1];
+  d.cus = v[2];
+  return d;
+}
+// Dynamic LDS for a launch that needs `need` bytes and should put at most
+// k workgroups on one compute unit (the static LDS of the kernel is small
+// and only lowers the count further).
+size_t capped_lds(const DeviceShape& d, size_t need, int k) {
+  if (d.lds_per_cu <= 0) return need;
+  size_t cap = (size_t)d.lds_per_cu / (size_t)(k + 1) + 1;  // k of these fit, k + 1 do not
+  if (d.lds_per_block > 0 && cap > (size_t)d.lds_per_block) cap = need;
+  return need > cap ? need : cap;
+}
+constexpr int kExtractWgsPerCu = 3;       // latent-dominated extracts
+constexpr int kExtractWgsPerCuChain = 2;  // extracts set by their position / selection chains
+constexpr int kBlendWgsPerCu = 4;
+
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
   const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0;
   // LDS for the cached conditioning path: rowtab, cap, k, then int64 bases
-  const size_t lds = p.Nc > 0 && p.T <= kCondTiles
-                         ? ((size_t)p.T * kCondTokens + p.T + kCondTokens + 1) * sizeof(int) + 8 + (size_t)p.T * 8
-                         : 0;
+  const size_t cond_lds = p.Nc > 0 && p.T <= kCondTiles
+                              ? ((size_t)p.T * kCondTokens + p.T + kCondTokens + 1) * sizeof(int) + 8 + (size_t)p.T * 8
+                              : 0;
+  const size_t lds = capped_lds(device_shape(), cond_lds, kBlendWgsPerCu);
   const dim3 grid(n_gen + n_cond), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   const bool f2 = p.ax[0].n > 1;
@@ -1048,6 +1102,7 @@ __global__ __launch_bounds__(kBlock) void blend_finish_kernel(const f32x4* __res
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
+
 }  // namespace
 }  // namespace tdp
 
@@ -1084,7 +1139,11 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(a.n_sel + a.n_pos + n_lat);
   if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
-  const size_t ext_lds = (size_t)p.B * 6 * sizeof(float);
+  // more than eight latent workgroups per compute unit: the latent copy sets
+  // the length, otherwise the position and selection chains do
+  const DeviceShape ds = device_shape();
+  const int k = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256) ? kExtractWgsPerCu : kExtractWgsPerCuChain;
+  const size_t ext_lds = capped_lds(ds, (size_t)p.B * 6 * sizeof(float), k);
   if (p.world > 1)
     hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), ext_lds, s, p, a);
   else
