@@ -51,6 +51,7 @@ constexpr int kBlock = kThreads;
 constexpr int kWaves = kBlock / 64;
 constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy pass)
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
+constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
 constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
 constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
@@ -219,6 +220,7 @@ struct ExtractArgs {
   int32_t* tile_count;
   int32_t* cond_row;     // (T, Nc)
   int n_sel, n_pos, pos_parts;
+  int pos_one_pass;      // position workgroups hold their part in registers (one pass)
 };
 
 // Source token (within one batch element) of generated row r of a tile:
@@ -440,6 +442,56 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
   f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
   int32_t* idx = a.tile_index + tb.s.index_base;
   const bool write_index = (b == 0 && d == 0);
+  const int own = r_end - r_begin;
+  if (a.pos_one_pass && own <= kBlock * kOwnRows) {
+    // One pass: the part's own [start, end) pairs are loaded into registers
+    // (their indices stored at once) together with the starts of the rest
+    // of the plane, so the shifted pairs need no second round of loads.
+    // Without normalization the shift is 0 and the rest is not read.
+    // Slots past the part (a workgroup-uniform test) load nothing; within
+    // the last slot, idle lanes re-read a valid row of the tile.
+    const int rs = own > 0 ? r_begin : 0;
+    f32x2 v[kOwnRows];
+#pragma unroll
+    for (int u = 0; u < kOwnRows; ++u) {
+      v[u] = f32x2{INFINITY, INFINITY};
+      if (u * kBlock < own) {
+        const int r = r_begin + u * kBlock + (int)threadIdx.x;
+        const int n = tile_row_source(p, tb, r < r_end ? r : rs);
+        v[u] = ld_plane(src, n);
+        if (write_index && r < r_end) st_nt(idx + r, (int32_t)n);
+      }
+    }
+    // rows outside [r_begin, r_end): starts only; past the end, row 0 again
+    // (a repeat does not change a minimum)
+    const int rest = p.normalize ? gen - own : 0;
+    const float* starts = reinterpret_cast<const float*>(src);
+    float lo = INFINITY;
+    for (int r0 = 0; r0 < rest; r0 += kBlock * kMinUnroll) {
+      float m[kMinUnroll];
+#pragma unroll
+      for (int u = 0; u < kMinUnroll; ++u) {
+        m[u] = INFINITY;
+        if (r0 + u * kBlock < rest) {
+          const int rr = r0 + u * kBlock + (int)threadIdx.x;
+          const int r = rr < rest ? (rr < r_begin ? rr : rr + own) : 0;
+          const int n = tile_row_source(p, tb, r);
+          m[u] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(starts) + ((uint32_t)n << 3));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMinUnroll; ++u) lo = fminf(lo, m[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kOwnRows; ++u) lo = fminf(lo, v[u].x);  // idle lanes hold a row of the tile or +inf
+    const float off = p.normalize ? block_minmax(lo, -INFINITY, sm.red).x : 0.0f;  // uniform branch
+#pragma unroll
+    for (int u = 0; u < kOwnRows; ++u) {
+      const int r = r_begin + u * kBlock + (int)threadIdx.x;
+      if (r < r_end) st_nt(dst + r, v[u] - off);
+    }
+    return;
+  }
   const float off = p.normalize ? tile_plane_min_start(p, tb, src, sm.red) : 0.0f;
   for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
     int n[kPosUnroll];
@@ -1133,17 +1185,20 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   a.tile_count = tile_count;
   a.cond_row = cond_row;
   a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
-  a.pos_parts = p.pos_parts;
-  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
+  // More than eight latent workgroups per compute unit: the latent copy
+  // sets the length (3 per CU, positions in one pass); otherwise the
+  // position and selection chains do (2 per CU, two-pass positions).
+  const DeviceShape ds = device_shape();
+  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
+  a.pos_one_pass = latent_bound ? 1 : 0;
+  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(a.n_sel + a.n_pos + n_lat);
   if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
-  // more than eight latent workgroups per compute unit: the latent copy sets
-  // the length, otherwise the position and selection chains do
-  const DeviceShape ds = device_shape();
-  const int k = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256) ? kExtractWgsPerCu : kExtractWgsPerCuChain;
-  const size_t ext_lds = capped_lds(ds, (size_t)p.B * 6 * sizeof(float), k);
+  const size_t ext_lds =
+      capped_lds(ds, (size_t)p.B * 6 * sizeof(float), latent_bound ? kExtractWgsPerCu : kExtractWgsPerCuChain);
   if (p.world > 1)
     hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), ext_lds, s, p, a);
   else

@@ -208,22 +208,31 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
     dev.box_c0 = lo[2] / dev.lat_rows;
     dev.box_nc = (hi[2] + dev.lat_rows - 1) / dev.lat_rows - dev.box_c0;
   }
-  // Position workgroups per (tile, batch element, axis) plane: each reduces
-  // the whole plane's minimum start, then shifts its part of the tokens.
-  // More parts shorten each workgroup's copy pass (at most 1024 rows each),
-  // but every part re-reads the plane; those re-reads are kept below 3/4 of
-  // the latent bytes the plan reads, so that on large latents they do not
-  // compete with the latent copy (measured: 4 parts beat 8 and 16 on the
-  // 4K-class latent, while small latents gain from the shorter chain).
+  // Position workgroups per (tile, batch element, axis) plane.  Every part
+  // re-reads the rest of the plane for its minimum start, and those
+  // re-reads are kept below 3/4 of the latent bytes the plan reads so that
+  // on large latents they do not compete with the latent copy.  Two paths
+  // (the launch picks one, with the occupancy cap):
+  //  - one pass: a part holds its tokens in registers (at most kThreads *
+  //    kPosOwnRows) while the minimum is reduced, so the plan uses the
+  //    fewest parts that fit (4K-class latent: extract 21.1 -> 20.0 us);
+  //  - two passes (minimum, then the part's copy from L2): parts of at
+  //    most 1024 rows shorten the copy chain, which the smaller latents
+  //    gain from (full-res 6.8 us against 7.1 us one-pass).
+  // Measured: 4 parts beat 2 and 8 on the 4K-class latent.
   {
     const int64_t cells = world == 1 ? N : (int64_t)dev.box_nf * dev.box_nh * dev.box_nw;
     const int64_t latent_bytes = (int64_t)c.batch * cells * row_bytes;
     const int64_t plane_bytes = (int64_t)dev.T_local * c.batch * 3 * max_gen * 8;
-    int64_t parts = (max_gen + 1023) / 1024;
-    if (plane_bytes > 0 && parts * plane_bytes * 4 > latent_bytes * 3) parts = latent_bytes * 3 / (plane_bytes * 4);
-    if (parts < 1) parts = 1;
-    if (parts > 64) parts = 64;
-    dev.pos_parts = (int32_t)parts;
+    auto parts_for = [&](int64_t hold) {
+      int64_t parts = (max_gen + hold - 1) / hold;
+      if (plane_bytes > 0 && parts * plane_bytes * 4 > latent_bytes * 3) parts = latent_bytes * 3 / (plane_bytes * 4);
+      if (parts < 1) parts = 1;
+      if (parts > 64) parts = 64;
+      return (int32_t)parts;
+    };
+    dev.pos_parts = parts_for(1024);
+    dev.pos_parts_one = dev.normalize ? parts_for((int64_t)kThreads * kPosOwnRows) : dev.pos_parts;
   }
   dev.lat_units = world == 1 ? dev.B * dev.F * dev.H * dev.lat_chunks : dev.B * dev.box_nf * dev.box_nh * dev.box_nc;
   dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));

@@ -107,6 +107,7 @@ TDP_HD Covers split_covers(const AxisSplit& a, int x) {
 
 // Launch shape shared by the host planner and the kernels.
 constexpr int kThreads = 256;   // threads per workgroup
+constexpr int kPosOwnRows = 16;  // position rows per thread one extract position workgroup holds
 
 // Everything a kernel needs about a plan; passed by value (kernel argument).
 struct PlanDev {
@@ -120,7 +121,8 @@ struct PlanDev {
   int32_t in_dtype;
   int32_t out_dtype;
   int32_t normalize;  // subtract the per-tile offsets
-  int32_t pos_parts;  // position workgroups per (tile, batch element, axis)
+  int32_t pos_parts;      // position workgroups per (tile, batch element, axis), two-pass path
+  int32_t pos_parts_one;  // the same for the one-pass path (parts held in registers)
   // Launch geometry and invariant divisors (multiply-shift), from the host:
   int32_t rpp;        // rows per workgroup pass, one vector per lane: kThreads / vin
   // Generated rows of extract and blend: each lane moves two vectors of one

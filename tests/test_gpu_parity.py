@@ -121,11 +121,12 @@ def test_deterministic_repeat(cuda):
     assert results[0][2] == results[1][2]
 
 
-def test_positions_not_normalized(cuda):
-    wl = WORKLOADS["conditioned"]
+@pytest.mark.parametrize("name", ["conditioned", "4k"])
+def test_positions_not_normalized(name, cuda):
+    wl = WORKLOADS[name]
     inp = make_inputs(wl)
     plan = plan_for(wl, normalize=False)
-    _, _, bufs = gpu_extract(plan, inp, cuda, "conditioned raw positions")
+    _, _, bufs = gpu_extract(plan, inp, cuda, f"{name} raw positions")
     check_extract(plan, bufs, oracle_extract(wl, inp, normalize=False), wl.num_cond)
 
 
@@ -164,6 +165,12 @@ EDGE = {
     # twelve selection chunks: kept tokens counted across chunks
     "many_cond": dict(shape=(2, 8, 12), tiling=((1, 0), (2, 2), (2, 3)), num_cond=3000, seed=7),
     "batch64": dict(shape=(2, 4, 6), tiling=((1, 0), (2, 1), (2, 2)), batch=64, channels=16, seed=8),
+    # more than eight latent workgroups per compute unit: one-pass position
+    # workgroups (parts held in registers), width not a multiple of the
+    # wave's rows, random positions; the second also tiles frames and batch
+    "latent_bound_random_pos": dict(shape=(8, 64, 130), tiling=((1, 0), (3, 6), (4, 10)), random_pos=True, seed=9),
+    "latent_bound_batch2_frames": dict(shape=(8, 40, 130), tiling=((2, 2), (2, 4), (3, 8)), batch=2,
+                                       random_pos=True, seed=10),
 }
 
 
