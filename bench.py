@@ -241,7 +241,7 @@ def cpu_baseline(wl, inp, extract_bytes, blend_bytes, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="4k")
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (cache-cold launches)")
