@@ -52,8 +52,6 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy pass)
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
-constexpr int kMaxCombos = 4;      // <= 2 covering tiles on frames x 2 on height
-constexpr int kMaxTiles = TDP_MAX_TILES_PER_AXIS;
 constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
 constexpr int kSelPlanes = 6;      // position planes reduced per pass by a selection workgroup
 constexpr int kSelRows = 4;        // rows per thread per pass of that reduction
@@ -78,11 +76,6 @@ __device__ inline TileSlot slot_of(const PlanDev& p, int i, int j, int k) {
   else
     return tile_slot_whole(p, i, j, k);
 }
-
-// Row-table entry of a tile a rank plan does not hold.  Real entries can be
-// negative (the row of width cell 0 lies before a tile that starts past it),
-// so the mark is a value no entry reaches.
-constexpr int64_t kNotHeld = INT64_MIN;
 
 template <bool R>
 __device__ inline bool held(const PlanDev& p, int t) {

@@ -182,7 +182,6 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
   dev.by_lpr = make_fastdiv((uint32_t)dev.lpr);
   dev.by_H = make_fastdiv((uint32_t)dev.H);
   dev.by_FH = make_fastdiv((uint32_t)(dev.F * dev.H));
-  dev.by_nw = make_fastdiv((uint32_t)dev.ax[2].n);
   dev.by_lat_chunks = make_fastdiv((uint32_t)dev.lat_chunks);
   dev.by_blend_chunks = make_fastdiv((uint32_t)dev.blend_chunks);
 

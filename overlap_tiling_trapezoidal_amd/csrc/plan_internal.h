@@ -133,7 +133,7 @@ struct PlanDev {
   int32_t lat_rows, lat_chunks;      // extract: rows per wave unit (rwv), units per line
   int32_t blend_rows, blend_chunks;  // blend: rows per wave unit (rwv), units per line
   int32_t lat_units, gen_units;      // wave units of extract (whole latent or rank box) and of blend
-  FastDiv by_vin, by_lpr, by_H, by_FH, by_nw, by_lat_chunks, by_blend_chunks;
+  FastDiv by_vin, by_lpr, by_H, by_FH, by_lat_chunks, by_blend_chunks;
   // Round-robin share (TDP docs, "What it is": tile t runs on rank t mod
   // world).  world == 1 is the whole plan.  A rank plan holds the tiles with
   // t mod world == rank, local index t / world, in uniform slots of
