@@ -511,8 +511,8 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
 // moves vectors q and lpr + q of row w0 + r, so each load and
 // store instruction covers 16 * lpr contiguous bytes of every row it
 // touches.  Tile rows come in closed form from the lane's width covers and
-// the line's frame x height combos (workgroup-uniform), with no tables and
-// no barrier; the loads are issued before any of that is computed.  A rank
+// the line's frame x height combos (wave-uniform), with no tables and no
+// barrier; the loads are issued before any of that is computed.  A rank
 // plan reads only the rows that one of its tiles covers.
 template <bool R>
 __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, int blk) {
