@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "plan_internal.h"
@@ -52,10 +53,10 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy pass)
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
-constexpr int kSelChunk = kBlock;  // conditioning tokens per selection workgroup
+constexpr int kSelChunk = 128;     // conditioning tokens per selection workgroup (<= kBlock)
 constexpr int kSelPlanes = 6;      // position planes reduced per pass by a selection workgroup
 constexpr int kSelRows = 4;        // rows per thread per pass of that reduction
-constexpr int kCopyBatch = 8;      // kept conditioning rows in flight per lane
+constexpr int kCopyBatch = 16;     // kept conditioning rows in flight per lane
 constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
 constexpr int kCondTokens = 16;        // conditioning tokens per blend workgroup
 constexpr int kCondTiles = 256;        // plans up to this many tiles cache cond_row and slots in LDS
@@ -227,6 +228,7 @@ __device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r
 }
 
 struct SelShared {
+  float2 ext_red[kWaves][kSelPlanes];  // per-wave (min start, max end) of the planes of one pass
   int wave_tot[kWaves];
   int kept_c[kSelChunk];     // kept tokens of this chunk, ascending
   int base;                  // kept tokens of this tile before this chunk
@@ -304,39 +306,78 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
           hi[q] = fmaxf(hi[q], v[u][q].y);
         }
     }
+    // all planes of the pass reduced together: one exchange, two barriers
+    // (the order is block_minmax's: within each wave, then waves in order)
 #pragma unroll
     for (int q = 0; q < kSelPlanes; ++q) {
-      const float2 x = block_minmax(lo[q], hi[q], sm.red);
-      if (threadIdx.x == 0 && e0 + q < p.B * 3) {
-        ext[2 * (e0 + q)] = x.x;
-        ext[2 * (e0 + q) + 1] = x.y;
-      }
+      lo[q] = wave_min(lo[q]);
+      hi[q] = wave_max(hi[q]);
     }
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+      for (int q = 0; q < kSelPlanes; ++q) sm.sel.ext_red[threadIdx.x >> 6][q] = make_float2(lo[q], hi[q]);
+    __syncthreads();
+    if (threadIdx.x < kSelPlanes && e0 + (int)threadIdx.x < p.B * 3) {
+      const int q = threadIdx.x;
+      float2 x = sm.sel.ext_red[0][q];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        x.x = fminf(x.x, sm.sel.ext_red[w][q].x);
+        x.y = fmaxf(x.y, sm.sel.ext_red[w][q].y);
+      }
+      ext[2 * (e0 + q)] = x.x;
+      ext[2 * (e0 + q) + 1] = x.y;
+    }
+    __syncthreads();  // ext_red is reused by the next pass
   }
   __syncthreads();
 
   // 2. keep test.  The kept tokens before this chunk are counted again here
-  //    (cheap compares) so that chunks compact independently.
-  // Every batch element is tested (no early exit), so the loads of all of
-  // them can be in flight together.
-  auto keeps = [&](int c) -> bool {
-    bool keep = false;
-#pragma unroll 4
-    for (int b = 0; b < p.B; ++b) {
-      const f32x2* pc = a.pos + (int64_t)b * 3 * p.rows + p.N + c;
-      const f32x2 x0 = pc[0], x1 = pc[p.rows], x2 = pc[2 * (int64_t)p.rows];
-      const float* e = ext + b * 6;
-      const bool inside =
-          x0.x < e[1] && x0.y > e[0] && x1.x < e[3] && x1.y > e[2] && x2.x < e[5] && x2.y > e[4];
-      keep = keep || inside || x0.x < 0.0f;
+  //    (cheap compares) so that chunks compact independently.  The test
+  //    takes NT tokens at a time and every batch element (two per pass, a
+  //    repeat for an odd count: OR does not mind), with all of their loads
+  //    issued before any compare.
+  auto keep_tokens = [&](const int* cs, bool* keep, auto nt) {
+    constexpr int NT = decltype(nt)::value;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) keep[u] = false;
+    for (int b0 = 0; b0 < p.B; b0 += 2) {
+      f32x2 x[NT][2][3];
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const f32x2* pc = a.pos + (int64_t)min(b0 + k, p.B - 1) * 3 * p.rows + p.N + cs[u];
+          x[u][k][0] = pc[0];
+          x[u][k][1] = pc[p.rows];
+          x[u][k][2] = pc[2 * (int64_t)p.rows];
+        }
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float* e = ext + min(b0 + k, p.B - 1) * 6;
+          const bool inside = x[u][k][0].x < e[1] && x[u][k][0].y > e[0] && x[u][k][1].x < e[3] &&
+                              x[u][k][1].y > e[2] && x[u][k][2].x < e[5] && x[u][k][2].y > e[4];
+          keep[u] = keep[u] || inside || x[u][k][0].x < 0.0f;
+        }
     }
-    return keep;
   };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = chunk * kSelChunk;
   int before = 0;
-#pragma unroll 4
-  for (int c = threadIdx.x; c < c0; c += kBlock) before += keeps(c) ? 1 : 0;
+  for (int g = 0; g < c0; g += 4 * kBlock) {
+    int cs[4];
+    bool k4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = g + u * kBlock + (int)threadIdx.x;
+      cs[u] = c < c0 ? c : 0;  // token 0 exists whenever selection runs; not counted
+    }
+    keep_tokens(cs, k4, std::integral_constant<int, 4>{});
+#pragma unroll
+    for (int u = 0; u < 4; ++u) before += (k4[u] && g + u * kBlock + (int)threadIdx.x < c0) ? 1 : 0;
+  }
   for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
   if (lane == 0) sm.sel.wave_tot[wave] = before;
   __syncthreads();
@@ -344,8 +385,16 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
     sm.sel.base = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
   __syncthreads();
   const int base = sm.sel.base;
+  // thread j < kSelChunk tests token c0 + j of this chunk
   const int c = c0 + threadIdx.x;
-  const bool keep = c < p.Nc && keeps(c);
+  const bool mine = (int)threadIdx.x < kSelChunk && c < p.Nc;
+  bool keep;
+  {
+    const int cs[1] = {mine ? c : 0};
+    bool k1[1];
+    keep_tokens(cs, k1, std::integral_constant<int, 1>{});
+    keep = mine && k1[0];
+  }
   const uint64_t mask = __ballot(keep);
   const int in_wave = __popcll(mask & ((1ull << lane) - 1ull));
   __syncthreads();  // wave_tot reuse
@@ -355,7 +404,7 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
   for (int w = 0; w < wave; ++w) offset += sm.sel.wave_tot[w];
   const int n_kept = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
   const int idx = offset + in_wave;  // rank of c among this chunk's kept tokens
-  if (c < p.Nc) {
+  if (mine) {
     const int row = tb.s.gen + base + idx;
     a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
     if (keep) {
@@ -375,26 +424,32 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
   const int rpp = p.rpp;
   const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
   if (r < rpp) {
-    for (int b = 0; b < p.B; ++b) {
-      const u32x4* src = a.latent + ((int64_t)b * p.rows + p.N) * V + vv;
-      u32x4* dst = a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base) * V + vv;
-      for (int j0 = r; j0 < n_kept; j0 += rpp * kCopyBatch) {
-        u32x4 v[kCopyBatch];
+    // Kept rows of every batch element in one flat loop, kCopyBatch loads
+    // before any store: the memory counter a load waits on also counts
+    // earlier stores, so a round of stores ahead of the next loads would
+    // put their write latency into the chain (B = 2 and 256 kept tokens:
+    // 32 rows per lane, one round).
+    const int total = p.B * n_kept;
+    for (int i0 = r; i0 < total; i0 += rpp * kCopyBatch) {
+      u32x4 v[kCopyBatch];
 #pragma unroll
-        for (int q = 0; q < kCopyBatch; ++q) {
-          const int j = j0 + q * rpp;
-          v[q] = ld_nt(src + (int64_t)sm.sel.kept_c[j < n_kept ? j : j0] * V);
-        }
+      for (int q = 0; q < kCopyBatch; ++q) {
+        const int i = min(i0 + q * rpp, total - 1);
+        const int b = i / n_kept, j = i - b * n_kept;
+        v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + sm.sel.kept_c[j]) * V + vv);
+      }
 #pragma unroll
-        for (int q = 0; q < kCopyBatch; ++q) {
-          const int j = j0 + q * rpp;
-          if (j < n_kept) st_nt(dst + (int64_t)j * V, v[q]);
+      for (int q = 0; q < kCopyBatch; ++q) {
+        const int i = i0 + q * rpp;
+        if (i < total) {
+          const int b = i / n_kept, j = i - b * n_kept;
+          st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + j) * V + vv, v[q]);
         }
       }
     }
   }
-  // n_kept <= kSelChunk == kBlock: thread j copies token j on every plane
-  static_assert(kSelChunk == kBlock, "one kept token per thread");
+  // n_kept <= kSelChunk <= kBlock: thread j copies token j on every plane
+  static_assert(kSelChunk <= kBlock, "one kept token per thread");
   const int j = threadIdx.x;
   const int cj = j < n_kept ? sm.sel.kept_c[j] : 0;  // token 0 exists whenever selection runs
   for (int bd0 = 0; bd0 < p.B * 3; bd0 += kSelPlanes) {  // bd = b * 3 + d
