@@ -430,19 +430,20 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
     // put their write latency into the chain (B = 2 and 256 kept tokens:
     // 32 rows per lane, one round).
     const int total = p.B * n_kept;
+    const FastDiv by_kept = make_fastdiv((uint32_t)(n_kept > 0 ? n_kept : 1));  // workgroup-uniform
     for (int i0 = r; i0 < total; i0 += rpp * kCopyBatch) {
       u32x4 v[kCopyBatch];
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) {
         const int i = min(i0 + q * rpp, total - 1);
-        const int b = i / n_kept, j = i - b * n_kept;
+        const int b = (int)fastdiv((uint32_t)i, by_kept), j = i - b * n_kept;
         v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + sm.sel.kept_c[j]) * V + vv);
       }
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) {
         const int i = i0 + q * rpp;
         if (i < total) {
-          const int b = i / n_kept, j = i - b * n_kept;
+          const int b = (int)fastdiv((uint32_t)i, by_kept), j = i - b * n_kept;
           st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + j) * V + vv, v[q]);
         }
       }

@@ -32,7 +32,7 @@ struct FastDiv {
   uint32_t m;
   uint32_t l;
 };
-inline FastDiv make_fastdiv(uint32_t d) {
+TDP_HD FastDiv make_fastdiv(uint32_t d) {
   uint32_t l = 0;
   while ((1ull << l) < d) ++l;
   FastDiv f;
