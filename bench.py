@@ -111,11 +111,11 @@ def rank_share_rate(torch, tdp, dev, sets, wl, world, rank, reps):
     def ex(i):
         s, b = sets[i % len(sets)], rs[i % len(sets)]["bufs"]
         tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
-                        b["tile_count"], b["cond_row"], gstream)
+                        b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"], gstream)
 
     def bl(i):
         r = rs[i % len(sets)]
-        tdp.tdp_blend(plan, r["bufs"]["tile_lat"], r["bufs"]["cond_row"], r["out"], gstream)
+        tdp.tdp_blend(plan, r["bufs"]["tile_lat"], r["bufs"]["cond_row"], r["bufs"]["cond_k"], r["out"], gstream)
 
     ex_ms = graph_time_ms(torch, gstream, ex, reps)
     bl_ms = graph_time_ms(torch, gstream, bl, reps)
@@ -294,11 +294,11 @@ def main():
     def extract(s, st=None):
         b = s["bufs"]
         tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
-                        b["tile_count"], b["cond_row"], st or stream)
+                        b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"], st or stream)
 
     def blend(s, st=None):
         b = s["bufs"]
-        tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], s["out"], st or stream)
+        tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], b["cond_k"], s["out"], st or stream)
 
     # prime every set, then warm up the pipeline
     for s in sets:
@@ -368,11 +368,11 @@ def main():
         b = sets[i % R]["bufs"]
         s = sets[i % R]
         tdp.tdp_extract(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
-                        b["tile_count"], b["cond_row"], gstream)
+                        b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"], gstream)
 
     def blend_g(i):
         s = sets[i % R]
-        tdp.tdp_blend(plan, s["bufs"]["tile_lat"], s["bufs"]["cond_row"], s["out"], gstream)
+        tdp.tdp_blend(plan, s["bufs"]["tile_lat"], s["bufs"]["cond_row"], s["bufs"]["cond_k"], s["out"], gstream)
 
     ex_ms = graph_time_ms(torch, gstream, extract_g, reps)
     bl_ms = graph_time_ms(torch, gstream, blend_g, reps)
@@ -388,7 +388,7 @@ def main():
         s = sets[i % R]
         acc = accs[i % 2]
         for t in range(T):
-            tdp.tdp_blend_tile(plan, t, views[i % R][t], s["bufs"]["cond_row"], acc, gstream)
+            tdp.tdp_blend_tile(plan, t, views[i % R][t], s["bufs"]["cond_row"], s["bufs"]["cond_k"], acc, gstream)
         tdp.tdp_blend_finish(plan, acc, s["out"], gstream)
 
     st_ms = graph_time_ms(torch, gstream, stream_g, max(8, reps // 4))

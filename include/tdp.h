@@ -137,7 +137,9 @@ typedef struct {
   int64_t tile_pos_floats;  /* floats of tile_pos                             */
   int64_t tile_index_ints;  /* int32 entries of tile_index                    */
   int64_t cond_row_ints;    /* int32 entries of cond_row: T * Nc              */
+  int64_t cond_k_ints;      /* int32 entries of cond_k: Nc                    */
   int64_t out_elems;        /* elements of out: B * (N + Nc) * C              */
+  int64_t workspace_bytes;  /* device workspace of tdp_extract (0 if Nc == 0) */
 } tdp_sizes;
 
 /* ---- plan (host only; no GPU needed) ------------------------------------ */
@@ -157,11 +159,15 @@ typedef struct {
 int tdp_plan_create(const tdp_config* cfg, tdp_plan** out);
 void tdp_plan_destroy(tdp_plan* plan);
 
-/* Number of tiles T (row-major over the three axes). */
+/* Number of tiles T = n_f * n_h * n_w: the product of the per-axis tile
+ * counts of the TileCountConfig (TDP docs, "API"); 16 for the 4 x 4 split
+ * that "What it is" runs on 4 GPUs.  TDP_EINVAL for a null argument. */
 int tdp_plan_num_tiles(const tdp_plan* plan, int32_t* num_tiles);
 
 /* The n intervals [starts[i], ends[i]) of one axis (0 frames, 1 height,
- * 2 width); both arrays hold at least n entries. */
+ * 2 width) as split_by_count lays them out (mold #673, "Scope"; the closed
+ * form is tdp_plan_create's); both arrays hold at least n entries.
+ * TDP_EINVAL for a null argument or an axis outside 0..2. */
 int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t* ends);
 
 /* The 1-D trapezoidal window of tile i on one axis, one fp32 per cell of
@@ -177,10 +183,18 @@ int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w);
  * the kernels run for every latent row.  Guarded plans only. */
 int tdp_plan_cell_tiles(const tdp_plan* plan, int axis, int32_t x, int32_t* tiles, int32_t* count);
 
-/* Geometry and slot offsets of tile t. */
+/* Geometry and slot offsets of tile t, t = (i_f * n_h + i_h) * n_w + i_w:
+ * the tile as one rank would run it (TDP docs, "What it is": each GPU
+ * denoises its own tiles; mold #673, "Scope": tile enumeration), and where
+ * tdp_extract puts its rows.  TDP_EINVAL for a null argument or t outside
+ * [0, T). */
 int tdp_plan_tile(const tdp_plan* plan, int32_t t, tdp_tile_info* info);
 
-/* Sizes of every buffer the caller allocates for tdp_extract / tdp_blend. */
+/* Sizes of every buffer the caller allocates for tdp_extract / tdp_blend:
+ * the tile-major buffers hold each tile's latent slice, positions and kept
+ * conditioning tokens (TDP docs, "Position normalization" and "Shared
+ * negative (reference) positions"), plus the selection tables and the
+ * workspace.  TDP_EINVAL for a null argument. */
 int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes);
 
 /* Round-robin owner of tile t among `world` ranks: t mod world (TDP docs,
@@ -249,16 +263,23 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
 
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
 
-/* Gather all tiles, every latent row read once, in one launch that needs
- * no scratch memory.
+/* Gather all tiles, every latent row read once.  Without conditioning
+ * tokens this is one launch; with them a selection launch runs first and
+ * leaves its tables in `workspace`.
  *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
  *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
  *        tile_count (one per slot: T, or a rank's share) int32:
  *          gen_t + kept_t.
  *        cond_row (T * Nc) int32: row of conditioning token c inside tile
- *          t's slot, or -1 when t does not keep it; the number of
- *          non-negative entries in column c is k, the count of tiles that
- *          keep c.  May be NULL when Nc == 0.
+ *          t's slot, or -1 when t does not keep it.
+ *        cond_k (Nc) int32: k, the number of tiles that keep token c (the
+ *          non-negative entries of column c of cond_row); the blend weighs
+ *          the token by 1/k (TDP docs, "Shared negative (reference)
+ *          positions").  cond_row and cond_k may be NULL when Nc == 0.
+ *   workspace  device scratch of tdp_sizes.workspace_bytes bytes, 16-byte
+ *        aligned (NULL allowed when that is 0).  Caller-owned; its contents
+ *        between calls mean nothing, and calls that share it must not
+ *        overlap.
  * Positions: the tile's offset on axis d for batch element b is the minimum
  * start over its generated tokens; with TDP_NORMALIZE_POSITIONS it is
  * subtracted from both ends of every row the tile holds (one fp32
@@ -277,20 +298,22 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
  * pointers, TDP_EHIP on launch failure. */
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 void* tile_lat, float* tile_pos, int32_t* tile_index,
-                int32_t* tile_count, int32_t* cond_row, void* stream);
+                int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
+                void* workspace, void* stream);
 
 /* Blend tile outputs (tile-major slots with tile_lat's layout and dtype,
  * rows as tdp_extract placed them) into out (B, N+Nc, C) out_dtype:
  *   generated token:    sum over covering tiles t, ascending, of
  *                       (wF*wH)*wW * y_t  (separable trapezoid),
- *   conditioning token: (1/k) * sum over the k tiles that keep it, ascending
- *                       (k read off cond_row); 0 when k == 0,
+ *   conditioning token: (1/k) * sum over the tiles that keep it, ascending
+ *                       (rows from cond_row, k = cond_k[c]); 0 when k == 0,
  * fp32 accumulation, no normalization pass (mold #673, "A bug found while
- * porting"), bf16 output rounded to nearest even.  cond_row is tdp_extract's
- * output for the same plan (may be NULL when Nc == 0).  Device pointers
- * except `plan`; tile_out/out 16-byte aligned. */
+ * porting"), bf16 output rounded to nearest even.  cond_row and cond_k are
+ * tdp_extract's outputs for the same plan (NULL allowed when Nc == 0).
+ * Device pointers except `plan`; tile_out/out 16-byte aligned, cond_row and
+ * cond_k 4-byte aligned. */
 int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row,
-              void* out, void* stream);
+              const int32_t* cond_k, void* out, void* stream);
 
 /* Streaming blend, for schedules that produce one tile output at a time
  * (TDP docs, "What it is": a rank runs its tiles in turn and their blended
@@ -304,10 +327,11 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * no tile keeps are set to 0 at t = 0.  Call for t = 0, 1, ..., T-1 in this
  * order on one stream: acc then holds tdp_blend's fp32 sums bit for bit.
  * Any other order gives wrong sums.  Calls that share acc must not overlap.
- * tile_out/acc 16-byte aligned device pointers; cond_row as for tdp_blend.
+ * tile_out/acc 16-byte aligned device pointers; cond_row and cond_k as for
+ * tdp_blend.
  * Returns TDP_EINVAL for a bad tile index or pointer, or a rank plan. */
 int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
-                   float* acc, void* stream);
+                   const int32_t* cond_k, float* acc, void* stream);
 
 /* Round the accumulator (B, N+Nc, C) fp32 to the plan's out_dtype into out
  * (round to nearest even for bf16; a copy for fp32, nothing when out == acc).
@@ -367,8 +391,14 @@ int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_
 int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream);
 
 /* ---- errors ------------------------------------------------------------ */
+/* Errors are reported, never produced silently, and a guard violation names
+ * the axis and the largest overlap it allows (mold #673, "A bug found while
+ * porting": the guard overlap <= dim / (n + 1)).  tdp_status_string names a
+ * status code (a static string; "unknown status" for other values). */
 const char* tdp_status_string(int status);
-const char* tdp_last_error(void); /* thread-local, never NULL */
+/* The message of the last failure on the calling thread (thread-local,
+ * never NULL; "" before the first failure). */
+const char* tdp_last_error(void);
 
 #ifdef __cplusplus
 }

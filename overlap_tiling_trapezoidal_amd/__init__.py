@@ -73,7 +73,9 @@ class tdp_sizes(ctypes.Structure):
         ("tile_pos_floats", ctypes.c_int64),
         ("tile_index_ints", ctypes.c_int64),
         ("cond_row_ints", ctypes.c_int64),
+        ("cond_k_ints", ctypes.c_int64),
         ("out_elems", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -149,9 +151,9 @@ def load_library(path: str = LIB_PATH):
         "tdp_tiling_quality": (ctypes.c_int, [i32, i32p, i32p, i32p, i32p, i32, ctypes.POINTER(tdp_quality),
                                               ctypes.POINTER(ctypes.c_int64)]),
         "tdp_plan_quality": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_quality), ctypes.POINTER(ctypes.c_int64)]),
-        "tdp_extract": (ctypes.c_int, [vp] * 9),
-        "tdp_blend": (ctypes.c_int, [vp] * 5),
-        "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp]),
+        "tdp_extract": (ctypes.c_int, [vp] * 11),
+        "tdp_blend": (ctypes.c_int, [vp] * 6),
+        "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
         "tdp_pixel_plan_create": (ctypes.c_int, [ctypes.POINTER(tdp_pixel_config), ctypes.POINTER(vp)]),
         "tdp_pixel_plan_destroy": (None, [vp]),
@@ -376,7 +378,8 @@ def tdp_plan_quality(plan: Plan, world: int) -> dict:
 
 
 def allocate_extract_outputs(plan: Plan, device="cuda"):
-    """Caller-owned buffers for tdp_extract / tdp_blend, sized by the plan."""
+    """Caller-owned buffers for tdp_extract / tdp_blend, sized by the plan
+    (the keys are tdp_extract's argument names)."""
     import torch
     s = tdp_plan_sizes(plan)
     dev = torch.device(device)
@@ -386,6 +389,8 @@ def allocate_extract_outputs(plan: Plan, device="cuda"):
         "tile_index": torch.empty(s.tile_index_ints, dtype=torch.int32, device=dev),
         "tile_count": torch.empty(max(s.num_slots, 1), dtype=torch.int32, device=dev),
         "cond_row": torch.empty(max(s.cond_row_ints, 1), dtype=torch.int32, device=dev),
+        "cond_k": torch.empty(max(s.cond_k_ints, 1), dtype=torch.int32, device=dev),
+        "workspace": torch.empty(max(s.workspace_bytes, 1), dtype=torch.uint8, device=dev),
     }
 
 
@@ -405,13 +410,14 @@ def _stream_handle(stream, device):
 
 
 def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
-                cond_row=None, stream=None):
+                cond_row=None, cond_k=None, workspace=None, stream=None):
     """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
     import torch
     c = plan.cfg
     s = tdp_plan_sizes(plan)
     rows = plan.tokens + c.num_cond
     dev = latent.device
+    none = ctypes.c_void_p(None)
     args = [
         plan.handle,
         _ptr(latent, "latent", _torch_dtype(c.in_dtype), c.batch * rows * c.channels, dev),
@@ -420,22 +426,27 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
         _ptr(tile_pos, "tile_pos", torch.float32, s.tile_pos_floats, dev),
         _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
         _ptr(tile_count, "tile_count", torch.int32, s.num_slots, dev),
-        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
+        _ptr(cond_k, "cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
+        _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes else none,
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_extract(*args))
 
 
-def tdp_blend(plan: Plan, tile_out, cond_row, out, stream=None):
-    """Enqueue the blend of tile outputs into ``out`` on ``stream``."""
+def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):
+    """Enqueue the blend of tile outputs into ``out`` on ``stream``
+    (``cond_row`` and ``cond_k`` from tdp_extract; ignored when Nc == 0)."""
     import torch
     c = plan.cfg
     s = tdp_plan_sizes(plan)
     dev = tile_out.device
+    none = ctypes.c_void_p(None)
     args = [
         plan.handle,
         _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
-        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
+        _ptr(cond_k, "cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
         _ptr(out, "out", _torch_dtype(c.out_dtype), s.out_elems, dev),
         _stream_handle(stream, dev),
     ]
@@ -450,18 +461,19 @@ def allocate_accumulator(plan: Plan, device="cuda"):
                        device=torch.device(device))
 
 
-def tdp_blend_tile(plan: Plan, t: int, tile_out, cond_row, acc, stream=None):
+def tdp_blend_tile(plan: Plan, t: int, tile_out, cond_row, cond_k, acc, stream=None):
     """Enqueue the streaming blend of tile t's slot ``tile_out`` into ``acc``."""
     import torch
     c = plan.cfg
     info = tdp_plan_tile(plan, t)
     dev = acc.device
     rows = plan.tokens + c.num_cond
+    none = ctypes.c_void_p(None)
     _check(load_library().tdp_blend_tile(
         plan.handle, t,
         _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), c.batch * info.capacity * c.channels, dev),
-        _ptr(cond_row, "cond_row", torch.int32, c.num_cond * tdp_plan_num_tiles(plan), dev) if c.num_cond
-        else ctypes.c_void_p(None),
+        _ptr(cond_row, "cond_row", torch.int32, c.num_cond * tdp_plan_num_tiles(plan), dev) if c.num_cond else none,
+        _ptr(cond_k, "cond_k", torch.int32, c.num_cond, dev) if c.num_cond else none,
         _ptr(acc, "acc", torch.float32, c.batch * rows * c.channels, dev),
         _stream_handle(stream, dev)))
 
@@ -475,13 +487,6 @@ def tdp_blend_finish(plan: Plan, acc, out, stream=None):
     _check(load_library().tdp_blend_finish(plan.handle, _ptr(acc, "acc", torch.float32, n, dev),
                                            _ptr(out, "out", _torch_dtype(c.out_dtype), n, dev),
                                            _stream_handle(stream, dev)))
-
-
-def cond_keep_counts(plan: Plan, cond_row):
-    """k per conditioning token: tiles whose cond_row entry is non-negative."""
-    c = plan.cfg
-    T = tdp_plan_num_tiles(plan)
-    return (cond_row[: T * c.num_cond].view(T, c.num_cond) >= 0).sum(dim=0)
 
 
 def tile_views(plan: Plan, buffers, counts=None):

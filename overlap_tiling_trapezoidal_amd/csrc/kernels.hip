@@ -53,10 +53,10 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy pass)
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
-constexpr int kSelChunk = 128;     // conditioning tokens per selection workgroup (<= kBlock)
-constexpr int kSelPlanes = 6;      // position planes reduced per pass by a selection workgroup
-constexpr int kSelRows = 4;        // rows per thread per pass of that reduction
+constexpr int kSelLoads = 24;      // position loads in flight per thread in the extent launch
 constexpr int kCopyBatch = 16;     // kept conditioning rows in flight per lane
+constexpr int kCopyTokens = 64;    // conditioning tokens per compaction workgroup: a quarter chunk
+constexpr int kCopyParts = kCondChunk / kCopyTokens;
 constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
 constexpr int kCondTokens = 16;        // conditioning tokens per blend workgroup
 constexpr int kCondTiles = 256;        // plans up to this many tiles cache cond_row and slots in LDS
@@ -213,9 +213,25 @@ struct ExtractArgs {
   int32_t* tile_index;
   int32_t* tile_count;
   int32_t* cond_row;     // (T, Nc)
+  int32_t* cond_k;       // (Nc)
+  const char* ws;        // workspace with the selection launch's tables (Nc > 0), else null
   int n_sel, n_pos, pos_parts;
   int pos_one_pass;      // position workgroups hold their part in registers (one pass)
 };
+
+// Tables of the selection launch in the workspace (layout in PlanDev).
+__device__ inline const float2* ws_ext(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<const float2*>(a.ws + ws_layout(p).ext);
+}
+__device__ inline const uint32_t* ws_keep(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<const uint32_t*>(a.ws + ws_layout(p).keep);
+}
+__device__ inline const int32_t* ws_cnt(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<const int32_t*>(a.ws + ws_layout(p).cnt);
+}
+__device__ inline const int32_t* ws_tot(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<const int32_t*>(a.ws + ws_layout(p).tot);
+}
 
 // Source token (within one batch element) of generated row r of a tile:
 // r = (lf * sh + lh) * sw + x.
@@ -227,14 +243,12 @@ __device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r
   return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + x;
 }
 
-struct SelShared {
-  float2 ext_red[kWaves][kSelPlanes];  // per-wave (min start, max end) of the planes of one pass
-  int wave_tot[kWaves];
-  int kept_c[kSelChunk];     // kept tokens of this chunk, ascending
-  int base;                  // kept tokens of this tile before this chunk
+struct CopyShared {
+  int wave_sum[kWaves];
+  int kept_c[kCopyTokens];   // kept tokens of this quarter chunk, ascending
 };
 union ExtractShared {
-  SelShared sel;
+  CopyShared sel;
   float2 red[kWaves];
 };
 
@@ -268,157 +282,77 @@ __device__ float tile_plane_min_start(const PlanDev& p, const TileBox& tb, const
   return block_minmax(lo, -INFINITY, red).x;
 }
 
-// Selection workgroup: tile t, conditioning tokens [c0, c0 + kSelChunk).
-// Every tile is tested, held or not, because k counts all of them; only a
-// held tile's rows are written.
+// Compaction and copy workgroup (extract launch, Nc > 0): tile t, quarter
+// `sub` of chunk k (kCopyTokens conditioning tokens), from the selection
+// launches' tables.  The tile's kept tokens before it are the totals of the
+// earlier superchunks, the counts of the earlier chunks of its superchunk
+// and the keep bits of the earlier quarters, so no workgroup re-tests
+// earlier tokens and the work per workgroup barely grows with Nc (one total
+// per kChunksPerSuper chunks).  Writes cond_row for every tile (k counts the
+// tiles of all ranks), the index entries and rows of a held tile, the
+// tile's count (from its last workgroup) and, from one workgroup per
+// quarter, cond_k of the quarter's tokens.  Quarters keep the copy of a
+// chunk's kept rows (up to 256 tokens times the batch) off a single compute
+// unit.
 template <bool R>
-__device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, float* ext,
-                                  int t, int chunk) {
+__device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int t, int k,
+                                   int sub) {
   const TileBox tb = tile_box<R>(p, t);
   const bool own = held<R>(p, t);
-
-  // 1. extent [min start, max end) of the tile on every (batch, axis): six
-  //    planes per pass, each row's source index shared by the planes.
-  for (int e0 = 0; e0 < p.B * 3; e0 += kSelPlanes) {
-    float lo[kSelPlanes], hi[kSelPlanes];
-#pragma unroll
-    for (int q = 0; q < kSelPlanes; ++q) {
-      lo[q] = INFINITY;
-      hi[q] = -INFINITY;
-    }
-    for (int r0 = 0; r0 < tb.s.gen; r0 += kBlock * kSelRows) {
-      f32x2 v[kSelRows][kSelPlanes];
-#pragma unroll
-      for (int u = 0; u < kSelRows; ++u) {
-        const int r = r0 + u * kBlock + (int)threadIdx.x;
-        const int n = tile_row_source(p, tb, r < tb.s.gen ? r : 0);  // a repeat keeps min and max
-#pragma unroll
-        for (int q = 0; q < kSelPlanes; ++q) {
-          const int e = min(e0 + q, p.B * 3 - 1);                     // so does a repeated plane
-          v[u][q] = ld_plane(a.pos + (int64_t)e * p.rows, n);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kSelRows; ++u)
-#pragma unroll
-        for (int q = 0; q < kSelPlanes; ++q) {
-          lo[q] = fminf(lo[q], v[u][q].x);
-          hi[q] = fmaxf(hi[q], v[u][q].y);
-        }
-    }
-    // all planes of the pass reduced together: one exchange, two barriers
-    // (the order is block_minmax's: within each wave, then waves in order)
-#pragma unroll
-    for (int q = 0; q < kSelPlanes; ++q) {
-      lo[q] = wave_min(lo[q]);
-      hi[q] = wave_max(hi[q]);
-    }
-    if ((threadIdx.x & 63) == 0)
-#pragma unroll
-      for (int q = 0; q < kSelPlanes; ++q) sm.sel.ext_red[threadIdx.x >> 6][q] = make_float2(lo[q], hi[q]);
-    __syncthreads();
-    if (threadIdx.x < kSelPlanes && e0 + (int)threadIdx.x < p.B * 3) {
-      const int q = threadIdx.x;
-      float2 x = sm.sel.ext_red[0][q];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        x.x = fminf(x.x, sm.sel.ext_red[w][q].x);
-        x.y = fmaxf(x.y, sm.sel.ext_red[w][q].y);
-      }
-      ext[2 * (e0 + q)] = x.x;
-      ext[2 * (e0 + q) + 1] = x.y;
-    }
-    __syncthreads();  // ext_red is reused by the next pass
-  }
-  __syncthreads();
-
-  // 2. keep test.  The kept tokens before this chunk are counted again here
-  //    (cheap compares) so that chunks compact independently.  The test
-  //    takes NT tokens at a time and every batch element (two per pass, a
-  //    repeat for an odd count: OR does not mind), with all of their loads
-  //    issued before any compare.
-  auto keep_tokens = [&](const int* cs, bool* keep, auto nt) {
-    constexpr int NT = decltype(nt)::value;
-#pragma unroll
-    for (int u = 0; u < NT; ++u) keep[u] = false;
-    for (int b0 = 0; b0 < p.B; b0 += 2) {
-      f32x2 x[NT][2][3];
-#pragma unroll
-      for (int u = 0; u < NT; ++u)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const f32x2* pc = a.pos + (int64_t)min(b0 + k, p.B - 1) * 3 * p.rows + p.N + cs[u];
-          x[u][k][0] = pc[0];
-          x[u][k][1] = pc[p.rows];
-          x[u][k][2] = pc[2 * (int64_t)p.rows];
-        }
-#pragma unroll
-      for (int u = 0; u < NT; ++u)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float* e = ext + min(b0 + k, p.B - 1) * 6;
-          const bool inside = x[u][k][0].x < e[1] && x[u][k][0].y > e[0] && x[u][k][1].x < e[3] &&
-                              x[u][k][1].y > e[2] && x[u][k][2].x < e[5] && x[u][k][2].y > e[4];
-          keep[u] = keep[u] || inside || x[u][k][0].x < 0.0f;
-        }
-    }
-  };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = chunk * kSelChunk;
+  // 1. kept tokens of this tile before the chunk: the totals of the earlier
+  //    superchunks and the counts of the earlier chunks of its own
+  const int sup = k / kChunksPerSuper, k0 = sup * kChunksPerSuper;
   int before = 0;
-  for (int g = 0; g < c0; g += 4 * kBlock) {
-    int cs[4];
-    bool k4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = g + u * kBlock + (int)threadIdx.x;
-      cs[u] = c < c0 ? c : 0;  // token 0 exists whenever selection runs; not counted
-    }
-    keep_tokens(cs, k4, std::integral_constant<int, 4>{});
-#pragma unroll
-    for (int u = 0; u < 4; ++u) before += (k4[u] && g + u * kBlock + (int)threadIdx.x < c0) ? 1 : 0;
-  }
+  const int32_t* tot = ws_tot(p, a);
+  for (int i = threadIdx.x; i < sup; i += kBlock) before += tot[(int64_t)t * p.n_super + i];
+  if ((int)threadIdx.x < k - k0) before += ws_cnt(p, a)[(int64_t)t * p.n_chunks + k0 + threadIdx.x];
   for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
-  if (lane == 0) sm.sel.wave_tot[wave] = before;
+  if (lane == 0) sm.sel.wave_sum[wave] = before;
+  // 2. the chunk's keep bits: earlier quarters, then the rank of each of
+  //    this quarter's tokens (thread j < kCopyTokens takes token j)
+  const uint32_t* words = ws_keep(p, a) + ((int64_t)t * p.n_chunks + k) * kKeepWords;
+  uint32_t wv[kKeepWords];
+#pragma unroll
+  for (int i = 0; i < kKeepWords; ++i) wv[i] = words[i];  // same address on every lane
   __syncthreads();
-  if (threadIdx.x == 0)
-    sm.sel.base = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
-  __syncthreads();
-  const int base = sm.sel.base;
-  // thread j < kSelChunk tests token c0 + j of this chunk
-  const int c = c0 + threadIdx.x;
-  const bool mine = (int)threadIdx.x < kSelChunk && c < p.Nc;
-  bool keep;
-  {
-    const int cs[1] = {mine ? c : 0};
-    bool k1[1];
-    keep_tokens(cs, k1, std::integral_constant<int, 1>{});
-    keep = mine && k1[0];
+  static_assert(kCopyTokens == 64 && kKeepWords == 2 * kCopyParts, "a quarter is two keep words");
+  const int chunk_base = sm.sel.wave_sum[0] + sm.sel.wave_sum[1] + sm.sel.wave_sum[2] + sm.sel.wave_sum[3];
+  int base = chunk_base;  // kept tokens of the tile before this quarter
+  int chunk_kept = 0;
+  uint64_t mask = 0;
+#pragma unroll
+  for (int i = 0; i < kKeepWords; ++i) {
+    const int pc = __popc(wv[i]);
+    base += i < 2 * sub ? pc : 0;
+    chunk_kept += pc;
+    if (i == 2 * sub) mask |= wv[i];
+    if (i == 2 * sub + 1) mask |= (uint64_t)wv[i] << 32;
   }
-  const uint64_t mask = __ballot(keep);
-  const int in_wave = __popcll(mask & ((1ull << lane) - 1ull));
-  __syncthreads();  // wave_tot reuse
-  if (lane == 0) sm.sel.wave_tot[wave] = __popcll(mask);
-  __syncthreads();
-  int offset = 0;
-  for (int w = 0; w < wave; ++w) offset += sm.sel.wave_tot[w];
-  const int n_kept = sm.sel.wave_tot[0] + sm.sel.wave_tot[1] + sm.sel.wave_tot[2] + sm.sel.wave_tot[3];
-  const int idx = offset + in_wave;  // rank of c among this chunk's kept tokens
-  if (mine) {
-    const int row = tb.s.gen + base + idx;
+  const int n_kept = __popcll(mask);
+  const int j = threadIdx.x;
+  const int c = k * kCondChunk + sub * kCopyTokens + j;
+  if (j < kCopyTokens && c < p.Nc) {
+    const bool keep = (mask >> j) & 1ull;
+    const int rank = __popcll(mask & ((1ull << j) - 1ull));
+    const int row = tb.s.gen + base + rank;
     a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
-    if (keep) {
-      if (own) a.tile_index[tb.s.index_base + row] = p.N + c;
-      sm.sel.kept_c[idx] = c;
-    }
+    if (keep) sm.sel.kept_c[rank] = c;
+    if (own && keep) a.tile_index[tb.s.index_base + row] = p.N + c;
   }
-  const bool last_chunk = c0 + kSelChunk >= p.Nc;
-  if (own && last_chunk && threadIdx.x == 0)
-    a.tile_count[R ? (int)fastdiv((uint32_t)t, p.by_world) : t] = tb.s.gen + base + n_kept;
+  if (own && k == p.n_chunks - 1 && sub == kCopyParts - 1 && threadIdx.x == 0)
+    a.tile_count[R ? (int)fastdiv((uint32_t)t, p.by_world) : t] = tb.s.gen + chunk_base + chunk_kept;
+  // 3. k of the quarter's tokens: keep bits of every tile (one workgroup per quarter)
+  if (t == (k * kCopyParts + sub) % p.T && j < kCopyTokens && c < p.Nc) {
+    const uint32_t* col = ws_keep(p, a) + (int64_t)k * kKeepWords + 2 * sub + (j >> 5);
+    int kc = 0;
+    for (int u = 0; u < p.T; ++u) kc += (col[(int64_t)u * p.n_chunks * kKeepWords] >> (j & 31)) & 1u;
+    a.cond_k[c] = kc;
+  }
   if (!own) return;  // workgroup-uniform
   __syncthreads();
 
-  // 3. copy the kept rows: latent vectors, then shifted positions.  Loads
+  // 4. copy the kept rows: latent vectors, then shifted positions.  Loads
   //    go out in batches (then their stores), not one round trip per row.
   const int V = p.vin;
   const int rpp = p.rpp;
@@ -427,8 +361,7 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
     // Kept rows of every batch element in one flat loop, kCopyBatch loads
     // before any store: the memory counter a load waits on also counts
     // earlier stores, so a round of stores ahead of the next loads would
-    // put their write latency into the chain (B = 2 and 256 kept tokens:
-    // 32 rows per lane, one round).
+    // put their write latency into the chain.
     const int total = p.B * n_kept;
     const FastDiv by_kept = make_fastdiv((uint32_t)(n_kept > 0 ? n_kept : 1));  // workgroup-uniform
     for (int i0 = r; i0 < total; i0 += rpp * kCopyBatch) {
@@ -436,37 +369,37 @@ __device__ void extract_selection(const PlanDev& p, const ExtractArgs& a, Extrac
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) {
         const int i = min(i0 + q * rpp, total - 1);
-        const int b = (int)fastdiv((uint32_t)i, by_kept), j = i - b * n_kept;
-        v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + sm.sel.kept_c[j]) * V + vv);
+        const int b = (int)fastdiv((uint32_t)i, by_kept), jj = i - b * n_kept;
+        v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + sm.sel.kept_c[jj]) * V + vv);
       }
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) {
         const int i = i0 + q * rpp;
         if (i < total) {
-          const int b = (int)fastdiv((uint32_t)i, by_kept), j = i - b * n_kept;
-          st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + j) * V + vv, v[q]);
+          const int b = (int)fastdiv((uint32_t)i, by_kept), jj = i - b * n_kept;
+          st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + jj) * V + vv, v[q]);
         }
       }
     }
   }
-  // n_kept <= kSelChunk <= kBlock: thread j copies token j on every plane
-  static_assert(kSelChunk <= kBlock, "one kept token per thread");
-  const int j = threadIdx.x;
-  const int cj = j < n_kept ? sm.sel.kept_c[j] : 0;  // token 0 exists whenever selection runs
-  for (int bd0 = 0; bd0 < p.B * 3; bd0 += kSelPlanes) {  // bd = b * 3 + d
-    f32x2 v[kSelPlanes];
+  // thread j copies kept token j on every (batch, axis) plane
+  constexpr int kPlanes = 6;
+  const int cj = j < n_kept ? sm.sel.kept_c[j] : 0;  // token 0 exists whenever this runs
+  for (int bd0 = 0; bd0 < p.B * 3; bd0 += kPlanes) {  // bd = b * 3 + d
+    f32x2 v[kPlanes];
+    float o[kPlanes];
 #pragma unroll
-    for (int q = 0; q < kSelPlanes; ++q) {
+    for (int q = 0; q < kPlanes; ++q) {
       const int bd = min(bd0 + q, p.B * 3 - 1);
       v[q] = a.pos[(int64_t)bd * p.rows + p.N + cj];
+      o[q] = p.normalize ? ws_ext(p, a)[(int64_t)t * p.B * 3 + bd].x : 0.0f;
     }
 #pragma unroll
-    for (int q = 0; q < kSelPlanes; ++q) {
+    for (int q = 0; q < kPlanes; ++q) {
       const int bd = bd0 + q;
       if (bd < p.B * 3 && j < n_kept) {
-        const float o = p.normalize ? ext[bd * 2] : 0.0f;
         const int b = bd / 3, d = bd - b * 3;
-        st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v[q] - o);
+        st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v[q] - o[q]);
       }
     }
   }
@@ -542,6 +475,40 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
     return;
   }
   const float off = p.normalize ? tile_plane_min_start(p, tb, src, sm.red) : 0.0f;
+  for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
+    int n[kPosUnroll];
+    f32x2 v[kPosUnroll];
+#pragma unroll
+    for (int u = 0; u < kPosUnroll; ++u) {
+      const int r = r0 + u * kBlock + (int)threadIdx.x;
+      n[u] = tile_row_source(p, tb, r < r_end ? r : r_begin);
+      v[u] = ld_plane(src, n[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kPosUnroll; ++u) {
+      const int r = r0 + u * kBlock + (int)threadIdx.x;
+      if (r < r_end) {
+        st_nt(dst + r, v[u] - off);
+        if (write_index) st_nt(idx + r, (int32_t)n[u]);
+      }
+    }
+  }
+}
+
+// Positions workgroup with the shift `off` already known (Nc > 0: the
+// extent the keep launch stored): it only copies its part of the plane
+// (shifted pairs and source indices).
+template <bool R>
+__device__ void extract_positions_copy(const PlanDev& p, const ExtractArgs& a, int t, int b, int d, int part,
+                                       float off) {
+  const TileBox tb = tile_box<R>(p, t);
+  const int gen = tb.s.gen;
+  const int per = (gen + a.pos_parts - 1) / a.pos_parts;
+  const int r_begin = min(gen, part * per), r_end = min(gen, r_begin + per);
+  const f32x2* src = a.pos + ((int64_t)b * 3 + d) * p.rows;
+  f32x2* dst = a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap;
+  int32_t* idx = a.tile_index + tb.s.index_base;
+  const bool write_index = (b == 0 && d == 0);
   for (int r0 = r_begin; r0 < r_end; r0 += kBlock * kPosUnroll) {
     int n[kPosUnroll];
     f32x2 v[kPosUnroll];
@@ -654,24 +621,172 @@ __device__ inline void xcd_group(int bid, int items, int parts, int& item, int& 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Conditioning selection launch (plans with Nc > 0)
+// ---------------------------------------------------------------------------
+
+struct SelectArgs {
+  const f32x2* pos;  // (B, 3, rows) [start, end)
+  float2* part;      // workspace tables (layout in WsLayout)
+  float2* ext;
+  uint32_t* keep;
+  int32_t* cnt;
+  int32_t* tot;
+};
+
+// Extent launch: workgroup (tile t, part q) reduces [min start, max end)
+// over rows [q * ext_rows, (q + 1) * ext_rows) of tile t's generated tokens
+// on every (batch, axis) plane, NP planes per pass with all of a pass's
+// loads in flight and one exchange for all of them.  Part 0 also zeroes the
+// tile's superchunk totals, which the keep launch adds to.  Every tile is
+// reduced, in rank plans too, since k counts the tiles of all ranks.
+template <int NP>
+__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const SelectArgs a) {
+  __shared__ float2 red[kWaves][NP];
+  int t, q;
+  xcd_group(blockIdx.x, p.T, p.ext_parts, t, q);  // the parts of a tile share an L2
+  const TileBox tb = tile_box<false>(p, t);
+  const int r_begin = min(tb.s.gen, q * p.ext_rows), r_end = min(tb.s.gen, r_begin + p.ext_rows);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int planes = p.B * 3;
+  constexpr int RP = kSelLoads / NP;  // rows per thread per pass
+  if (q == 0)
+    for (int i = tid; i < p.n_super; i += kBlock) a.tot[(int64_t)t * p.n_super + i] = 0;
+  float2* out = a.part + ((int64_t)t * p.ext_parts + q) * planes;
+  // (a repeated row or plane leaves a minimum and a maximum as they are;
+  // an empty part stores +inf and -inf, which the combine ignores)
+  for (int e0 = 0; e0 < planes; e0 += NP) {
+    float lo[NP], hi[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      lo[k] = INFINITY;
+      hi[k] = -INFINITY;
+    }
+    for (int r0 = r_begin; r0 < r_end; r0 += kBlock * RP) {
+      f32x2 v[RP][NP];
+#pragma unroll
+      for (int u = 0; u < RP; ++u) {
+        const int r = r0 + u * kBlock + tid;
+        const int n = tile_row_source(p, tb, r < r_end ? r : r_begin);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) v[u][k] = ld_plane(a.pos + (int64_t)min(e0 + k, planes - 1) * p.rows, n);
+      }
+#pragma unroll
+      for (int u = 0; u < RP; ++u)
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          lo[k] = fminf(lo[k], v[u][k].x);
+          hi[k] = fmaxf(hi[k], v[u][k].y);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      lo[k] = wave_min(lo[k]);
+      hi[k] = wave_max(hi[k]);
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int k = 0; k < NP; ++k) red[wave][k] = make_float2(lo[k], hi[k]);
+    __syncthreads();
+    if (tid < NP && e0 + tid < planes) {
+      float2 x = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        x.x = fminf(x.x, red[w][tid].x);
+        x.y = fmaxf(x.y, red[w][tid].y);
+      }
+      out[e0 + tid] = x;
+    }
+    __syncthreads();  // red is reused by the next pass
+  }
+}
+
+// Keep launch: workgroup (tile t, chunk k), one token per thread.  The
+// tile's extent is the combination of its parts (chunk 0 stores it for the
+// extract launch: normalization offsets and the kept rows' shift).  A token
+// is kept when, for some batch element, its interval overlaps the extent on
+// all three axes (half-open) or its time start is negative (TDP docs,
+// "Shared negative (reference) positions"), on the positions as given.
+// Writes the chunk's keep bits and count and adds the count to its
+// superchunk's total.
+__global__ __launch_bounds__(kBlock) void keep_kernel(const PlanDev p, const SelectArgs a) {
+  extern __shared__ float2 ext_s[];  // (B * 3) extent of tile t
+  __shared__ int wave_kept[kWaves];
+  const int t = blockIdx.x / p.n_chunks, k = blockIdx.x - t * p.n_chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int planes = p.B * 3;
+  const int c = k * kCondChunk + tid;
+  const int cs = c < p.Nc ? c : 0;  // token 0 exists whenever this runs; masked below
+  // positions of the token for two batch elements (an odd batch repeats the
+  // last one: OR does not mind), issued before the extent is combined
+  auto load_token = [&](int b0, f32x2 (&x)[2][3]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x2* pc = a.pos + (int64_t)min(b0 + kb, p.B - 1) * 3 * p.rows + p.N + cs;
+      x[kb][0] = pc[0];
+      x[kb][1] = pc[p.rows];
+      x[kb][2] = pc[2 * (int64_t)p.rows];
+    }
+  };
+  f32x2 x[2][3];
+  load_token(0, x);
+  const float2* parts = a.part + (int64_t)t * p.ext_parts * planes;
+  for (int e = tid; e < planes; e += kBlock) {
+    float2 m = parts[e];
+    for (int q = 1; q < p.ext_parts; ++q) {
+      const float2 y = parts[(int64_t)q * planes + e];
+      m.x = fminf(m.x, y.x);
+      m.y = fmaxf(m.y, y.y);
+    }
+    ext_s[e] = m;
+    if (k == 0) a.ext[(int64_t)t * planes + e] = m;
+  }
+  __syncthreads();
+  bool keep = false;
+  for (int b0 = 0; b0 < p.B; b0 += 2) {
+    if (b0 > 0) load_token(b0, x);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float2* e = ext_s + min(b0 + kb, p.B - 1) * 3;
+      const bool inside = x[kb][0].x < e[0].y && x[kb][0].y > e[0].x && x[kb][1].x < e[1].y &&
+                          x[kb][1].y > e[1].x && x[kb][2].x < e[2].y && x[kb][2].y > e[2].x;
+      keep = keep || inside || x[kb][0].x < 0.0f;
+    }
+  }
+  // keep bits: the 64 tokens of a wave are two words of the chunk
+  const uint64_t mask = __ballot(keep && c < p.Nc);
+  if (lane == 0) {
+    uint32_t* words = a.keep + ((int64_t)t * p.n_chunks + k) * kKeepWords + 2 * wave;
+    words[0] = (uint32_t)mask;
+    words[1] = (uint32_t)(mask >> 32);
+    wave_kept[wave] = __popcll(mask);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n += wave_kept[w];
+    a.cnt[(int64_t)t * p.n_chunks + k] = n;
+    atomicAdd(a.tot + (int64_t)t * p.n_super + k / kChunksPerSuper, n);
+  }
+}
+
 // One launch, three kinds of workgroups (independent, disjoint outputs):
-//   [0, n_sel)                 conditioning selection per (tile, chunk);
+//   [0, n_sel)                 conditioning tokens per (tile, quarter chunk) (Nc > 0);
 //   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
 //   [.., + latent blocks)      generated latent rows per (line, chunk).
-// Selection and position workgroups are few and long (each reduces a whole
-// tile plane), so they come first and run under the latent copy.
-// Rank plans: selection over every tile, positions over the held tiles.
+// Conditioning and position workgroups are few and run a longer chain of
+// dependent loads, so they come first and run under the latent copy.
+// Rank plans: conditioning tokens over every tile, positions over the held
+// tiles.
 template <bool R>
 __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
-  extern __shared__ float dyn[];  // selection: ext[B][3][2]
   __shared__ ExtractShared sm;
   int bid = blockIdx.x;
   if (bid < a.n_sel) {
-    // every chunk of a tile reduces the tile's position planes: keep them on one XCD
-    const int per_tile = (p.Nc + kSelChunk - 1) / kSelChunk;
-    int t, chunk;
-    xcd_group(bid, p.T, per_tile, t, chunk);
-    extract_selection<R>(p, a, sm, dyn, t, chunk);
+    const int per_tile = p.n_chunks * kCopyParts;
+    const int t = bid / per_tile, rem = bid - t * per_tile;
+    extract_cond_chunk<R>(p, a, sm, t, rem / kCopyParts, rem % kCopyParts);
     return;
   }
   bid -= a.n_sel;
@@ -682,7 +797,12 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
     const int d = plane % 3;
     const int b = (plane / 3) % p.B;
     const int slot = plane / (3 * p.B);
-    extract_positions<R>(p, a, sm, R ? p.rank + slot * p.world : slot, slot, b, d, part);
+    const int t = R ? p.rank + slot * p.world : slot;
+    if (a.ws)
+      extract_positions_copy<R>(p, a, t, b, d, part,
+                                p.normalize ? ws_ext(p, a)[((int64_t)t * p.B + b) * 3 + d].x : 0.0f);
+    else
+      extract_positions<R>(p, a, sm, t, slot, b, d, part);
     return;
   }
   extract_latent<R>(p, a, bid - a.n_pos);
@@ -826,7 +946,8 @@ __device__ void blend_line(const PlanDev& p, const LineCombos& lc, int b, int f,
 // tile but sums only the tiles it holds (capacity 0 for the others).
 template <int IN, int OUT, bool R>
 __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ tile_out,
-                                  const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
+                                  const int32_t* __restrict__ cond_row, const int32_t* __restrict__ cond_k,
+                                  void* __restrict__ out, int cid) {
   constexpr int E = InVec<IN>::E;
   // LDS: rowtab[T][kCondTokens], cap[T], k[kCondTokens], n[kCondTokens],
   // list[kCondTokens][T] (slot rows of the terms, ascending t), base[T] (int64)
@@ -854,17 +975,16 @@ __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ ti
     rowtab[e] = jj < ntok ? cond_row[(int64_t)t * p.Nc + c0 + jj] : -1;
   }
   __syncthreads();
-  // per token: k (tiles that keep it) and the vector offsets of the terms
-  // summed here (kept rows tdp_extract could have written), ascending t
+  // per token: k (tiles that keep it, from extract) and the terms summed
+  // here (kept rows tdp_extract could have written), ascending t
   if (threadIdx.x < kCondTokens) {
     const int jj = threadIdx.x;
-    int kc = 0, n = 0;
+    int n = 0;
     for (int t = 0; t < p.T; ++t) {
       const int row = rowtab[t * kCondTokens + jj];
-      kc += row >= 0;
       if (row >= 0 && row < cap[t]) list[jj * p.T + n++] = t;
     }
-    kcount[jj] = kc;
+    kcount[jj] = jj < ntok ? cond_k[c0 + jj] : 0;
     nterms[jj] = n;
   }
   __syncthreads();
@@ -910,7 +1030,8 @@ __device__ void blend_cond_cached(const PlanDev& p, const u32x4* __restrict__ ti
 // The same sum for plans with more than kCondTiles tiles, one tile at a time.
 template <int IN, int OUT, bool R>
 __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ tile_out,
-                                  const int32_t* __restrict__ cond_row, void* __restrict__ out, int cid) {
+                                  const int32_t* __restrict__ cond_row, const int32_t* __restrict__ cond_k,
+                                  void* __restrict__ out, int cid) {
   constexpr int E = InVec<IN>::E;
   const int V = p.vin;
   const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
@@ -921,8 +1042,7 @@ __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ ti
   const int ntok = min(kCondTokens, p.Nc - c0);
   for (int jj = r; jj < ntok; jj += p.rpp) {
     const int c = c0 + jj;
-    int kc = 0;
-    for (int t = 0; t < p.T; ++t) kc += cond_row[(int64_t)t * p.Nc + c] >= 0;
+    const int kc = cond_k[c];
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
@@ -967,15 +1087,16 @@ __device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_
 template <int IN, int OUT, bool R, bool F2>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
                                                        const int32_t* __restrict__ cond_row,
+                                                       const int32_t* __restrict__ cond_k,
                                                        void* __restrict__ out, int n_gen_blocks) {
   // conditioning workgroups first: each is a short dependent chain, so they
   // start early and run under the generated rows
   const int n_cond = (int)gridDim.x - n_gen_blocks;
   if ((int)blockIdx.x < n_cond) {
     if (p.T <= kCondTiles)
-      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, out, blockIdx.x);
+      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, blockIdx.x);
     else
-      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, out, blockIdx.x);
+      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, blockIdx.x);
     return;
   }
   // this wave's unit (rows [w0, w0 + rwv) of one line): the waves of a
@@ -1057,7 +1178,8 @@ constexpr int kExtractWgsPerCuChain = 2;  // extracts set by their position / se
 constexpr int kBlendWgsPerCu = 4;
 
 template <int IN, int OUT>
-hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, void* out, hipStream_t s) {
+hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
+                        void* out, hipStream_t s) {
   const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0;
   // LDS for the cached conditioning path: rowtab, cap, k, then int64 bases
@@ -1071,13 +1193,13 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   const bool f2 = p.ax[0].n > 1;
   if (p.world > 1 && f2)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, true>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, true>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else if (p.world > 1)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, false>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, true, false>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else if (f2)
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, true>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, true>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else
-    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, false>), grid, block, lds, s, p, y, cond_row, out, n_gen);
+    hipLaunchKernelGGL((blend_kernel<IN, OUT, false, false>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   return hipGetLastError();
 }
 
@@ -1141,7 +1263,8 @@ __device__ void stream_gen_rows(const PlanDev& p, const TileBox& tb, int i, int 
 // set to 0 when t == 0.
 template <int IN>
 __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u32x4* __restrict__ tile_out,
-                                 const int32_t* __restrict__ cond_row, float* __restrict__ acc, int cap_t) {
+                                 const int32_t* __restrict__ cond_row, const int32_t* __restrict__ cond_k,
+                                 float* __restrict__ acc, int cap_t) {
   constexpr int E = InVec<IN>::E;
   const int V = p.vin;
   const int rpp = p.rpp;
@@ -1151,11 +1274,10 @@ __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u
   for (int jj = lr; jj < nrows; jj += rpp) {
     const int c = c0 + jj;
     const int row = cond_row[(int64_t)t * p.Nc + c];
-    int kc = 0;
+    const int kc = cond_k[c];
     bool first = true, any = false;  // any: some tile holds a row blend_kernel sums
     for (int u = 0; u < p.T; ++u) {
       const int ru = cond_row[(int64_t)u * p.Nc + c];
-      kc += ru >= 0;
       if (ru >= 0) {
         int iu, ju, ku;
         tile_grid(p, u, iu, ju, ku);
@@ -1166,8 +1288,8 @@ __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u
       }
     }
     f32x4* a4 = reinterpret_cast<f32x4*>(acc + (((int64_t)b * p.rows + p.N + c) * V + vv) * E);
-    if (row < 0 || row >= cap_t) {
-      if (t == 0 && !any)
+    if (row < 0 || row >= cap_t || kc <= 0) {
+      if (t == 0 && (!any || kc <= 0))
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) a4[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       continue;
@@ -1190,6 +1312,7 @@ __device__ void stream_cond_rows(const PlanDev& p, int t, int b, int c0, const u
 template <int IN>
 __global__ __launch_bounds__(kBlock) void blend_tile_kernel(const PlanDev p, int t, const u32x4* __restrict__ tile_out,
                                                             const int32_t* __restrict__ cond_row,
+                                                            const int32_t* __restrict__ cond_k,
                                                             float* __restrict__ acc, int gen_per_b, int n_gen) {
   int i, j, k;
   tile_grid(p, t, i, j, k);
@@ -1203,7 +1326,7 @@ __global__ __launch_bounds__(kBlock) void blend_tile_kernel(const PlanDev p, int
   const int per_b = (p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock;
   const int cid = bid - n_gen;
   const int b = cid / per_b;
-  stream_cond_rows<IN>(p, t, b, (cid - b * per_b) * kCondRowsPerBlock, tile_out, cond_row, acc, tb.s.cap);
+  stream_cond_rows<IN>(p, t, b, (cid - b * per_b) * kCondRowsPerBlock, tile_out, cond_row, cond_k, acc, tb.s.cap);
 }
 
 // acc (fp32) -> out (OUT), four values per thread.
@@ -1219,6 +1342,67 @@ __global__ __launch_bounds__(kBlock) void blend_finish_kernel(const f32x4* __res
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
+// Enqueue extract: with conditioning tokens, the extent and keep launches
+// first (their tables go to `ws`), then the extract launch.  Arguments are
+// valid.
+int launch_extract(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
+                   int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws,
+                   hipStream_t s, const char* who) {
+  ExtractArgs a;
+  a.latent = reinterpret_cast<const u32x4*>(latent);
+  a.pos = reinterpret_cast<const f32x2*>(pos);
+  a.tile_lat = reinterpret_cast<u32x4*>(tile_lat);
+  a.tile_pos = reinterpret_cast<f32x2*>(tile_pos);
+  a.tile_index = tile_index;
+  a.tile_count = tile_count;
+  a.cond_row = cond_row;
+  a.cond_k = cond_k;
+  a.ws = nullptr;
+  const DeviceShape ds = device_shape();
+  if (p.Nc > 0) {
+    SelectArgs sa;
+    sa.pos = a.pos;
+    const WsLayout wl = ws_layout(p);
+    sa.part = reinterpret_cast<float2*>(ws + wl.part);
+    sa.ext = reinterpret_cast<float2*>(ws + wl.ext);
+    sa.keep = reinterpret_cast<uint32_t*>(ws + wl.keep);
+    sa.cnt = reinterpret_cast<int32_t*>(ws + wl.cnt);
+    sa.tot = reinterpret_cast<int32_t*>(ws + wl.tot);
+    a.ws = ws;
+    const dim3 egrid((unsigned)(p.T * p.ext_parts)), block(kBlock);
+    if (p.B == 1)
+      hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, sa);
+    else
+      hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, sa);
+    hipLaunchKernelGGL(keep_kernel, dim3((unsigned)(p.T * p.n_chunks)), block, (size_t)p.B * 3 * sizeof(float2), s, p,
+                       sa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
+  }
+  a.n_sel = p.Nc > 0 ? p.T * p.n_chunks * kCopyParts : 0;
+  const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
+  // More than eight latent workgroups per compute unit: the latent copy
+  // sets the length (3 per CU, positions in one pass); otherwise the
+  // position chains do (2 per CU, parts of at most 1024 rows).  With
+  // conditioning tokens the positions only copy (the shift is known) and
+  // the compaction workgroups share the launch with the latent copy (3 per
+  // CU).
+  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
+  a.pos_one_pass = latent_bound ? 1 : 0;
+  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  const dim3 grid(a.n_sel + a.n_pos + n_lat);
+  if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
+  const size_t lds = capped_lds(ds, 0, latent_bound || p.Nc > 0 ? kExtractWgsPerCu : kExtractWgsPerCuChain);
+  if (p.world > 1)
+    hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), lds, s, p, a);
+  else
+    hipLaunchKernelGGL(extract_kernel<false>, grid, dim3(kBlock), lds, s, p, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return TDP_OK;
+}
+
 
 }  // namespace
 }  // namespace tdp
@@ -1228,62 +1412,40 @@ using namespace tdp;
 extern "C" {
 
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
-                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, void* stream) {
+                int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, void* workspace,
+                void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_extract: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_extract: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (!latent || !pos) return fail(TDP_EINVAL, "tdp_extract: null device pointer");
   if (p.T_local > 0 && (!tile_lat || !tile_pos || !tile_index || !tile_count))
     return fail(TDP_EINVAL, "tdp_extract: null device pointer");
-  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_extract: cond_row is required when num_cond > 0");
-  if (!aligned(latent, 16) || !aligned(tile_lat, 16))
-    return fail(TDP_EINVAL, "tdp_extract: latent and tile_lat must be 16-byte aligned");
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "tdp_extract: cond_row and cond_k are required when num_cond > 0");
+  if (ws_layout(p).bytes > 0 && !workspace)
+    return fail(TDP_EINVAL, "tdp_extract: workspace of %lld bytes is required (tdp_plan_sizes)",
+                (long long)ws_layout(p).bytes);
+  if (!aligned(latent, 16) || !aligned(tile_lat, 16) || !aligned(workspace, 16))
+    return fail(TDP_EINVAL, "tdp_extract: latent, tile_lat and workspace must be 16-byte aligned");
   if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
-      !aligned(cond_row, 4))
+      !aligned(cond_row, 4) || !aligned(cond_k, 4))
     return fail(TDP_EINVAL, "tdp_extract: pos/tile_pos need 8-byte and int buffers 4-byte alignment");
-  ExtractArgs a;
-  a.latent = reinterpret_cast<const u32x4*>(latent);
-  a.pos = reinterpret_cast<const f32x2*>(pos);
-  a.tile_lat = reinterpret_cast<u32x4*>(tile_lat);
-  a.tile_pos = reinterpret_cast<f32x2*>(tile_pos);
-  a.tile_index = tile_index;
-  a.tile_count = tile_count;
-  a.cond_row = cond_row;
-  a.n_sel = p.Nc > 0 ? p.T * ((p.Nc + kSelChunk - 1) / kSelChunk) : 0;
-  const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
-  // More than eight latent workgroups per compute unit: the latent copy
-  // sets the length (3 per CU, positions in one pass); otherwise the
-  // position and selection chains do (2 per CU, two-pass positions).
-  const DeviceShape ds = device_shape();
-  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
-  a.pos_one_pass = latent_bound ? 1 : 0;
-  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
-  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid(a.n_sel + a.n_pos + n_lat);
-  if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
-  const size_t ext_lds =
-      capped_lds(ds, (size_t)p.B * 6 * sizeof(float), latent_bound ? kExtractWgsPerCu : kExtractWgsPerCuChain);
-  if (p.world > 1)
-    hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), ext_lds, s, p, a);
-  else
-    hipLaunchKernelGGL(extract_kernel<false>, grid, dim3(kBlock), ext_lds, s, p, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_extract: kernel launch failed: %s", hipGetErrorString(e));
-  return TDP_OK;
+  return launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
+                        static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream), "tdp_extract");
 }
 
-int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row, float* acc,
-                   void* stream) {
+int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
+                   const int32_t* cond_k, float* acc, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_blend_tile: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend_tile: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (p.world > 1) return fail(TDP_EINVAL, "tdp_blend_tile: rank plans take tdp_blend (streaming is for whole plans)");
   if (t < 0 || t >= p.T) return fail(TDP_EINVAL, "tdp_blend_tile: tile index %d out of range [0, %d)", t, p.T);
   if (!tile_out || !acc) return fail(TDP_EINVAL, "tdp_blend_tile: null device pointer");
-  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend_tile: cond_row is required when num_cond > 0");
-  if (!aligned(tile_out, 16) || !aligned(acc, 16) || !aligned(cond_row, 4))
-    return fail(TDP_EINVAL, "tdp_blend_tile: tile_out and acc must be 16-byte aligned");
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "tdp_blend_tile: cond_row and cond_k are required when num_cond > 0");
+  if (!aligned(tile_out, 16) || !aligned(acc, 16) || !aligned(cond_row, 4) || !aligned(cond_k, 4))
+    return fail(TDP_EINVAL, "tdp_blend_tile: tile_out and acc need 16-byte, cond_row and cond_k 4-byte alignment");
   int i, j, k;
   tile_grid(p, t, i, j, k);
   const TileSlot slot = tile_slot_whole(p, i, j, k);
@@ -1295,10 +1457,10 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   if (p.in_dtype == TDP_BF16)
     hipLaunchKernelGGL(blend_tile_kernel<TDP_BF16>, dim3(n_gen + n_cond), dim3(kBlock), 0, s, p, (int)t, y, cond_row,
-                       acc, gen_per_b, n_gen);
+                       cond_k, acc, gen_per_b, n_gen);
   else
     hipLaunchKernelGGL(blend_tile_kernel<TDP_F32>, dim3(n_gen + n_cond), dim3(kBlock), 0, s, p, (int)t, y, cond_row,
-                       acc, gen_per_b, n_gen);
+                       cond_k, acc, gen_per_b, n_gen);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend_tile: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
@@ -1324,25 +1486,27 @@ int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* st
   return TDP_OK;
 }
 
-int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, void* out, void* stream) {
+int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k, void* out,
+              void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_blend: null plan");
   if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend: plan was built with TDP_UNGUARDED");
   const PlanDev& p = plan->dev;
   if (!out || (!tile_out && p.T_local > 0)) return fail(TDP_EINVAL, "tdp_blend: null device pointer");
-  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "tdp_blend: cond_row is required when num_cond > 0");
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "tdp_blend: cond_row and cond_k are required when num_cond > 0");
   if (!aligned(tile_out, 16) || !aligned(out, 16))
     return fail(TDP_EINVAL, "tdp_blend: tile_out and out must be 16-byte aligned");
-  if (!aligned(cond_row, 4)) return fail(TDP_EINVAL, "tdp_blend: misaligned cond_row");
+  if (!aligned(cond_row, 4) || !aligned(cond_k, 4)) return fail(TDP_EINVAL, "tdp_blend: misaligned cond_row or cond_k");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
-    e = launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, out, s);
+    e = launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
   else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, out, s);
+    e = launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
   else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, out, s);
+    e = launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
   else
-    e = launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, out, s);
+    e = launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend: kernel launch failed: %s", hipGetErrorString(e));
   return TDP_OK;
 }

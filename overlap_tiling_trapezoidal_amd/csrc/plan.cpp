@@ -227,11 +227,26 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
       int64_t parts = (max_gen + hold - 1) / hold;
       if (plane_bytes > 0 && parts * plane_bytes * 4 > latent_bytes * 3) parts = latent_bytes * 3 / (plane_bytes * 4);
       if (parts < 1) parts = 1;
-      if (parts > 64) parts = 64;
+      if (parts > kMaxExtParts) parts = kMaxExtParts;
       return (int32_t)parts;
     };
     dev.pos_parts = parts_for(1024);
     dev.pos_parts_one = dev.normalize ? parts_for((int64_t)kThreads * kPosOwnRows) : dev.pos_parts;
+  }
+  // Workspace of the conditioning selection (every tile is tested, rank
+  // plans included, since k counts the tiles of all ranks).
+  if (c.num_cond > 0) {
+    dev.n_chunks = (c.num_cond + kCondChunk - 1) / kCondChunk;
+    dev.n_super = (dev.n_chunks + kChunksPerSuper - 1) / kChunksPerSuper;
+    // extent parts: about kExtPartBytes of positions (B * 3 planes of 8-byte
+    // pairs per row) each, at least one row per part
+    const int64_t row_bytes_pos = (int64_t)c.batch * 3 * 8;
+    int64_t rows = kExtPartBytes / row_bytes_pos;
+    if (rows < 1) rows = 1;
+    int64_t parts = (max_gen + rows - 1) / rows;
+    if (parts > kMaxExtParts) parts = kMaxExtParts;
+    dev.ext_parts = (int32_t)parts;
+    dev.ext_rows = (int32_t)((max_gen + parts - 1) / parts);
   }
   dev.lat_units = world == 1 ? dev.B * dev.F * dev.H * dev.lat_chunks : dev.B * dev.box_nf * dev.box_nh * dev.box_nc;
   dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));
@@ -355,7 +370,9 @@ int tdp_plan_sizes(const tdp_plan* plan, tdp_sizes* sizes) {
   sizes->tile_pos_floats = plan->total_index * p.B * 6;
   sizes->tile_index_ints = plan->total_index;
   sizes->cond_row_ints = (int64_t)p.T * p.Nc;
+  sizes->cond_k_ints = p.Nc;
   sizes->out_elems = (int64_t)p.B * p.rows * p.C;
+  sizes->workspace_bytes = ws_layout(p).bytes;
   return TDP_OK;
 }
 

@@ -51,8 +51,9 @@ def poisoned_buffers(plan, device):
     bufs = tdp.allocate_extract_outputs(plan, device)
     bufs["tile_lat"].view(torch.int16 if bufs["tile_lat"].dtype == torch.bfloat16 else torch.int32).fill_(POISON)
     bufs["tile_pos"].fill_(float("nan"))
-    for k in ("tile_index", "tile_count", "cond_row"):
+    for k in ("tile_index", "tile_count", "cond_row", "cond_k"):
         bufs[k].fill_(POISON)
+    bufs["workspace"].fill_(0xA5)  # every table the selection launch leaves is written before it is read
     return bufs
 
 
@@ -89,8 +90,8 @@ def check_extract(plan, bufs, ex, num_cond):
         for t, et in enumerate(ex["tiles"]):
             want[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
         assert np.array_equal(cond_row, want)
-        k = tdp.cond_keep_counts(plan, bufs["cond_row"]).cpu().numpy()
-        assert np.array_equal(k, ex["k"])
+        k = bufs["cond_k"][:num_cond].cpu().numpy()
+        assert np.array_equal(k, ex["k"].astype(np.int32))
 
 
 def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
@@ -121,7 +122,7 @@ def slot_buffer_from_tiles(plan, tile_arrays, dtype_code, rng=None):
     return buf
 
 
-def gpu_blend(plan, tile_out_np, cond_row, device, label=""):
+def gpu_blend(plan, tile_out_np, cond_row, cond_k, device, label=""):
     c = plan.cfg
     if tile_out_np.dtype == np.uint16:
         y = torch.from_numpy(tile_out_np.view(np.int16)).view(torch.bfloat16).to(device)
@@ -130,18 +131,20 @@ def gpu_blend(plan, tile_out_np, cond_row, device, label=""):
     out = tdp.allocate_output(plan, device)
     out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32).fill_(POISON)
     note(f"blend {label}")
-    tdp.tdp_blend(plan, y, cond_row, out)
+    tdp.tdp_blend(plan, y, cond_row, cond_k, out)
     torch.cuda.synchronize()
     return out
 
 
 def cond_tables(plan, ex, num_cond, device):
-    """The oracle's selection in the library's cond_row format."""
+    """The oracle's selection in the library's format: (cond_row, cond_k)."""
     T = len(ex["tiles"])
     cond_row = np.full((T, max(num_cond, 1)), -1, np.int32)
     for t, et in enumerate(ex["tiles"]):
         cond_row[t, et["kept"]] = et["n_gen"] + np.arange(len(et["kept"]))
-    return torch.from_numpy(cond_row.reshape(-1)).to(device)
+    cond_k = np.zeros(max(num_cond, 1), np.int32)
+    cond_k[:num_cond] = ex["k"]
+    return torch.from_numpy(cond_row.reshape(-1)).to(device), torch.from_numpy(cond_k).to(device)
 
 
 def check_blend(out: torch.Tensor, ref: np.ndarray, mag: np.ndarray, out_dtype: int):

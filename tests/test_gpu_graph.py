@@ -38,14 +38,15 @@ def test_graph_replays_match_eager(name, cuda):
 
     def step():
         tdp.tdp_extract(plan, lat, pos, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"],
-                        bufs["tile_count"], bufs["cond_row"], s)
-        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out, s)
+                        bufs["tile_count"], bufs["cond_row"], bufs["cond_k"], bufs["workspace"], s)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out, s)
         for t, inf in enumerate(infos):
             view = bufs["tile_lat"][inf.lat_offset: inf.lat_offset + c.batch * inf.capacity * c.channels]
-            tdp.tdp_blend_tile(plan, t, view, bufs["cond_row"], acc, s)
+            tdp.tdp_blend_tile(plan, t, view, bufs["cond_row"], bufs["cond_k"], acc, s)
         tdp.tdp_blend_finish(plan, acc, out_s, s)
 
-    outputs = (out, out_s, acc, bufs["tile_lat"], bufs["tile_pos"], bufs["cond_row"])
+    outputs = (out, out_s, acc, bufs["tile_lat"], bufs["tile_pos"], bufs["cond_row"], bufs["cond_k"],
+               bufs["workspace"])
 
     def scramble():
         # slot rows past tile_count are never written: give them the same
@@ -59,7 +60,8 @@ def test_graph_replays_match_eager(name, cuda):
         step()
     torch.cuda.synchronize()
     ref = {k: _bits(v) for k, v in (("out", out), ("out_s", out_s), ("tile_lat", bufs["tile_lat"]),
-                                    ("tile_pos", bufs["tile_pos"]), ("cond_row", bufs["cond_row"]))}
+                                    ("tile_pos", bufs["tile_pos"]), ("cond_row", bufs["cond_row"]),
+                                    ("cond_k", bufs["cond_k"]))}
     assert torch.equal(ref["out"], ref["out_s"])
 
     g = torch.cuda.CUDAGraph()
@@ -74,7 +76,7 @@ def test_graph_replays_match_eager(name, cuda):
             g.replay()
         torch.cuda.synchronize()
         for k, v in (("out", out), ("out_s", out_s), ("tile_lat", bufs["tile_lat"]),
-                     ("tile_pos", bufs["tile_pos"]), ("cond_row", bufs["cond_row"])):
+                     ("tile_pos", bufs["tile_pos"]), ("cond_row", bufs["cond_row"]), ("cond_k", bufs["cond_k"])):
             assert torch.equal(_bits(v), ref[k]), (rep, k)
 
 
@@ -95,10 +97,10 @@ def test_rank_plan_graph_replays_match_eager(world, rank, cuda):
 
     def step():
         tdp.tdp_extract(plan, lat, pos, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"],
-                        bufs["tile_count"], bufs["cond_row"], s)
-        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out, s)
+                        bufs["tile_count"], bufs["cond_row"], bufs["cond_k"], bufs["workspace"], s)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out, s)
 
-    outputs = (out, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"], bufs["cond_row"])
+    outputs = (out, bufs["tile_lat"], bufs["tile_pos"], bufs["tile_index"], bufs["cond_row"], bufs["cond_k"])
 
     def scramble():
         for t in outputs:

@@ -46,8 +46,8 @@ def test_blend_random_tiles(name, out_dtype, cuda):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    cond_row = cond_tables(plan, ex, wl.num_cond, cuda)
-    out = gpu_blend(plan, buf, cond_row, cuda, f"{name} {out_dtype}")
+    cond_row, cond_k = cond_tables(plan, ex, wl.num_cond, cuda)
+    out = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"{name} {out_dtype}")
     check_blend(out, ref, mag, plan.cfg.out_dtype)
 
 
@@ -70,7 +70,7 @@ def test_end_to_end_stand_in_denoiser(name, cuda):
         out_views[t]["lat"].copy_(torch.add(torch.mul(x, float(a[t])), float(b[t])).to(tile_out.dtype))
     out = tdp.allocate_output(plan, cuda)
     note(f"blend e2e {name}")
-    tdp.tdp_blend(plan, tile_out, bufs["cond_row"], out)
+    tdp.tdp_blend(plan, tile_out, bufs["cond_row"], bufs["cond_k"], out)
     torch.cuda.synchronize()
 
     ex = oracle_extract(wl, inp)
@@ -92,7 +92,7 @@ def test_identity_round_trip(name, cuda):
     lat, _, bufs = gpu_extract(plan, inp, cuda, name)
     out = tdp.allocate_output(plan, cuda)
     note(f"blend identity {name}")
-    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
+    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
     torch.cuda.synchronize()
     if wl.dtype == "bf16":
         assert torch.equal(out.float(), lat.float())   # -0.0 may come back as +0.0
@@ -109,7 +109,7 @@ def test_deterministic_repeat(cuda):
         _, _, bufs = gpu_extract(plan, inp, cuda, f"conditioned rep {rep}")
         out = tdp.allocate_output(plan, cuda)
         note(f"blend conditioned rep {rep}")
-        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
         torch.cuda.synchronize()
         counts = bufs["tile_count"].cpu().numpy()
         views = tdp.tile_views(plan, bufs, counts)
@@ -164,6 +164,12 @@ EDGE = {
     "tiles272_cond": dict(shape=(1, 16, 17), tiling=((1, 0), (16, 0), (17, 0)), channels=16, num_cond=20, seed=6),
     # twelve selection chunks: kept tokens counted across chunks
     "many_cond": dict(shape=(2, 8, 12), tiling=((1, 0), (2, 2), (2, 3)), num_cond=3000, seed=7),
+    # five selection workgroups per tile (4096 tokens each) and a ragged last
+    # chunk: the kept tokens before a chunk come from earlier superchunks' totals
+    "cond_16k": dict(shape=(2, 12, 20), tiling=((1, 0), (2, 2), (3, 3)), batch=2, num_cond=16484, seed=11),
+    # a superchunk boundary with a one-token last chunk, odd batch
+    "cond_4097_batch3": dict(shape=(3, 10, 14), tiling=((2, 1), (2, 2), (2, 3)), batch=3, num_cond=4097,
+                             seed=12, random_pos=True),
     "batch64": dict(shape=(2, 4, 6), tiling=((1, 0), (2, 1), (2, 2)), batch=64, channels=16, seed=8),
     # more than eight latent workgroups per compute unit: one-pass position
     # workgroups (parts held in registers), width not a multiple of the
@@ -187,7 +193,7 @@ def test_edge_cases(case, cuda):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    out = gpu_blend(plan, buf, bufs["cond_row"], cuda, case)
+    out = gpu_blend(plan, buf, bufs["cond_row"], bufs["cond_k"], cuda, case)
     check_blend(out, ref, mag, tdp.TDP_F32)
 
 
@@ -207,7 +213,7 @@ def test_cond_tokens_kept_by_no_tile(cuda):
     check_extract(plan, bufs, ex, wl.num_cond)
     out = tdp.allocate_output(plan, cuda)
     note("blend k0")
-    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
+    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
     torch.cuda.synchronize()
     assert torch.all(out[:, N:] == 0)
 
@@ -222,8 +228,8 @@ def test_mixed_dtypes(cuda):
         buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
         ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
         ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, 0)
-        cond_row = cond_tables(plan, ex, 0, cuda)
-        out = gpu_blend(plan, buf, cond_row, cuda, f"{in_dtype}->{out_dtype}")
+        cond_row, cond_k = cond_tables(plan, ex, 0, cuda)
+        out = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"{in_dtype}->{out_dtype}")
         check_blend(out, ref, mag, plan.cfg.out_dtype)
 
 
@@ -234,7 +240,7 @@ def test_window_weights_bit_exact(cuda):
     plan = plan_for(wl, out_dtype="f32")
     ex = oracle_extract(wl, inp)
     tiles = [np.ones((1, len(et["rows"]), 16), np.float32) for et in ex["tiles"]]
-    out = gpu_blend(plan, slot_buffer_from_tiles(plan, tiles, tdp.TDP_F32), cond_tables(plan, ex, 0, cuda),
+    out = gpu_blend(plan, slot_buffer_from_tiles(plan, tiles, tdp.TDP_F32), *cond_tables(plan, ex, 0, cuda),
                     cuda, "onehot")
     got = out.cpu().numpy()[0, :, 0]
     # expected: fp32 sum over covering tiles of fl(fl(wF*wH)*wW) with plan windows
@@ -263,7 +269,7 @@ def test_bf16_output_rounding_bit_exact(cuda):
     wl = Workload("round", 1, C, (1, 1, W), ((1, 0), (1, 0), (1, 0)), dtype="f32", seed=0)
     plan = plan_for(wl, out_dtype="bf16")
     ex = O.extract(y, grid_positions(1, (1, 1, W), (1, 1, 1)), wl.shape, wl.tiling, 0)
-    out = gpu_blend(plan, slot_buffer_from_tiles(plan, [y], tdp.TDP_F32), cond_tables(plan, ex, 0, cuda),
+    out = gpu_blend(plan, slot_buffer_from_tiles(plan, [y], tdp.TDP_F32), *cond_tables(plan, ex, 0, cuda),
                     cuda, "rounding")
     ref, _ = O.blend([y], ex, wl.shape, wl.tiling, 0)   # one term: exact in fp32 (-0.0 sums to +0.0)
     want = O.f32_to_bf16_bits(ref.astype(np.float32))
@@ -307,5 +313,5 @@ def test_random_configs(seed, cuda):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    out = gpu_blend(plan, buf, bufs["cond_row"], cuda, label)
+    out = gpu_blend(plan, buf, bufs["cond_row"], bufs["cond_k"], cuda, label)
     check_blend(out, ref, mag, plan.cfg.out_dtype)

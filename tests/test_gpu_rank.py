@@ -27,7 +27,7 @@ def rank_plan(wl, world, rank, out_dtype="f32", normalize=True):
     return tdp.tdp_plan_create_rank(cfg, world, rank)
 
 
-def gpu_partial(plan, buf_np, cond_row, device, label):
+def gpu_partial(plan, buf_np, cond_row, cond_k, device, label):
     if buf_np.dtype == np.uint16:
         y = torch.from_numpy(buf_np.view(np.int16)).view(torch.bfloat16).to(device)
     else:
@@ -35,7 +35,7 @@ def gpu_partial(plan, buf_np, cond_row, device, label):
     out = tdp.allocate_output(plan, device)
     out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32).fill_(POISON)
     note(f"rank blend {label}")
-    tdp.tdp_blend(plan, y, cond_row, out)
+    tdp.tdp_blend(plan, y, cond_row, cond_k, out)
     torch.cuda.synchronize()
     return out
 
@@ -54,7 +54,7 @@ def run_all_ranks(wl, inp, world, device, seed, out_dtype="f32", normalize=True)
         _, _, bufs = gpu_extract(plan, inp, device, label)
         check_extract(plan, bufs, ex, wl.num_cond)
         buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
-        out = gpu_partial(plan, buf, bufs["cond_row"], device, label)
+        out = gpu_partial(plan, buf, bufs["cond_row"], bufs["cond_k"], device, label)
         ref, mag = O.rank_partial(ys, ex, wl.shape, wl.tiling, wl.num_cond, world, rank)
         check_blend(out, ref, mag, plan.cfg.out_dtype)
         if out.dtype == torch.float32:
@@ -110,7 +110,7 @@ def test_rank_identity_all_reduce_returns_latent(cuda):
         lat, _, bufs = gpu_extract(plan, inp, cuda, f"4k identity rank {rank}")
         out = tdp.allocate_output(plan, cuda)
         note(f"rank blend identity 4k rank {rank}")
-        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], out)
+        tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], out)
         torch.cuda.synchronize()
         total = out.clone() if total is None else total.add_(out)
     x = lat.float()

@@ -32,7 +32,7 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu()
 
 
-def stream_blend(plan, y, cond_row, device, separate=False, label=""):
+def stream_blend(plan, y, cond_row, cond_k, device, separate=False, label=""):
     """Blend tile by tile; `separate` hands each tile over in its own buffer."""
     c = plan.cfg
     acc = tdp.allocate_accumulator(plan, device)
@@ -41,7 +41,7 @@ def stream_blend(plan, y, cond_row, device, separate=False, label=""):
     for t in range(tdp.tdp_plan_num_tiles(plan)):
         info = tdp.tdp_plan_tile(plan, t)
         view = y[info.lat_offset: info.lat_offset + c.batch * info.capacity * c.channels]
-        tdp.tdp_blend_tile(plan, t, view.clone() if separate else view, cond_row, acc)
+        tdp.tdp_blend_tile(plan, t, view.clone() if separate else view, cond_row, cond_k, acc)
     out = tdp.allocate_output(plan, device)
     out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32).fill_(-7)
     tdp.tdp_blend_finish(plan, acc, out)
@@ -58,21 +58,21 @@ def _setup(wl, out_dtype, device):
     buf = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
     ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
-    cond_row = cond_tables(plan, ex, wl.num_cond, device)
+    cond_row, cond_k = cond_tables(plan, ex, wl.num_cond, device)
     if buf.dtype == np.uint16:
         y = torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16).to(device)
     else:
         y = torch.from_numpy(buf).to(device)
-    return plan, buf, y, cond_row, ref, mag
+    return plan, buf, y, cond_row, cond_k, ref, mag
 
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_stream_equals_blend_bit_exact(name, out_dtype, cuda):
     wl = CASES[name]
-    plan, buf, y, cond_row, ref, mag = _setup(wl, out_dtype, cuda)
-    whole = gpu_blend(plan, buf, cond_row, cuda, f"{name} {out_dtype}")
-    acc, out = stream_blend(plan, y, cond_row, cuda, label=f"{name} {out_dtype}")
+    plan, buf, y, cond_row, cond_k, ref, mag = _setup(wl, out_dtype, cuda)
+    whole = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"{name} {out_dtype}")
+    acc, out = stream_blend(plan, y, cond_row, cond_k, cuda, label=f"{name} {out_dtype}")
     assert torch.equal(_bits(out), _bits(whole))
     check_blend(out, ref, mag, plan.cfg.out_dtype)
     if out_dtype == "f32":
@@ -82,9 +82,9 @@ def test_stream_equals_blend_bit_exact(name, out_dtype, cuda):
 @pytest.mark.parametrize("name", ["conditioned", "cond_frames", "tiny"])
 def test_stream_separate_tile_buffers(name, cuda):
     wl = CASES[name]
-    plan, buf, y, cond_row, ref, mag = _setup(wl, "f32", cuda)
-    _, joined = stream_blend(plan, y, cond_row, cuda, label=f"{name} joined")
-    _, apart = stream_blend(plan, y, cond_row, cuda, separate=True, label=f"{name} separate")
+    plan, buf, y, cond_row, cond_k, ref, mag = _setup(wl, "f32", cuda)
+    _, joined = stream_blend(plan, y, cond_row, cond_k, cuda, label=f"{name} joined")
+    _, apart = stream_blend(plan, y, cond_row, cond_k, cuda, separate=True, label=f"{name} separate")
     assert torch.equal(_bits(apart), _bits(joined))
     check_blend(apart, ref, mag, plan.cfg.out_dtype)
 
@@ -100,8 +100,8 @@ def test_stream_tokens_kept_by_no_tile(cuda):
     plan = plan_for(wl, out_dtype="f32")
     _, _, bufs = gpu_extract(plan, inp, cuda, "k0s")
     whole = tdp.allocate_output(plan, cuda)
-    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], whole)
-    acc, out = stream_blend(plan, bufs["tile_lat"], bufs["cond_row"], cuda, label="k0s")
+    tdp.tdp_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], whole)
+    acc, out = stream_blend(plan, bufs["tile_lat"], bufs["cond_row"], bufs["cond_k"], cuda, label="k0s")
     assert torch.all(out[:, N:N + 10] == 0)
     assert torch.equal(_bits(out), _bits(whole))
 
@@ -117,8 +117,8 @@ def test_stream_random_configs(seed, cuda):
                   tuple(d for d, _ in axes), tuple(t for _, t in axes), num_cond=int(rng.choice([0, 7, 64])),
                   num_ref=2, dtype=dtype, seed=3000 + seed)
     out_dtype = "bf16" if rng.random() < 0.5 else "f32"
-    plan, buf, y, cond_row, ref, mag = _setup(wl, out_dtype, cuda)
-    whole = gpu_blend(plan, buf, cond_row, cuda, f"rand {seed}")
-    _, out = stream_blend(plan, y, cond_row, cuda, label=f"rand {seed}")
+    plan, buf, y, cond_row, cond_k, ref, mag = _setup(wl, out_dtype, cuda)
+    whole = gpu_blend(plan, buf, cond_row, cond_k, cuda, f"rand {seed}")
+    _, out = stream_blend(plan, y, cond_row, cond_k, cuda, label=f"rand {seed}")
     assert torch.equal(_bits(out), _bits(whole))
     check_blend(out, ref, mag, plan.cfg.out_dtype)

@@ -79,6 +79,8 @@ def test_plan_matches_oracle(name):
     s = tdp.tdp_plan_sizes(plan)
     assert (s.tile_lat_elems, s.tile_pos_floats, s.tile_index_ints) == (lat_off, pos_off, idx_off)
     assert s.cond_row_ints == len(tiles) * wl.num_cond
+    assert s.cond_k_ints == wl.num_cond
+    assert (s.workspace_bytes > 0) == (wl.num_cond > 0)
     assert s.out_elems == wl.batch * (wl.tokens + wl.num_cond) * wl.channels
 
 
@@ -173,18 +175,59 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
     cfg = tdp.make_config(1, 8, (1, 1, 21), ((1, 0), (1, 0), (3, 8)), unguarded=True)
     plan = tdp.tdp_plan_create(cfg)
     null = ctypes.c_void_p(None)
-    assert lib.tdp_extract(plan.handle, *([null] * 8)) == tdp.TDP_EGUARD
-    assert lib.tdp_blend(plan.handle, *([null] * 4)) == tdp.TDP_EGUARD
+    assert lib.tdp_extract(plan.handle, *([null] * 10)) == tdp.TDP_EGUARD
+    assert lib.tdp_blend(plan.handle, *([null] * 5)) == tdp.TDP_EGUARD
     good = tdp.tdp_plan_create(tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2))))
-    assert lib.tdp_extract(good.handle, *([null] * 8)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, *([null] * 10)) == tdp.TDP_EINVAL
     assert "null" in tdp.tdp_last_error()
-    assert lib.tdp_blend(good.handle, *([null] * 4)) == tdp.TDP_EINVAL
-    assert lib.tdp_extract(None, *([null] * 8)) == tdp.TDP_EINVAL
+    assert lib.tdp_blend(good.handle, *([null] * 5)) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(None, *([null] * 10)) == tdp.TDP_EINVAL
     # misaligned pointers are refused too
     odd = ctypes.c_void_p(0x1002)
     al = ctypes.c_void_p(0x1000)
-    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, null) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(good.handle, odd, al, al, al, al, al, null, null, null, null) == tdp.TDP_EINVAL
     assert "aligned" in tdp.tdp_last_error()
+
+
+def test_cond_k_and_workspace_arguments(lib):
+    """With conditioning tokens, tdp_extract needs cond_row, cond_k and the
+    workspace, and tdp_blend / tdp_blend_tile need cond_row and cond_k; null
+    and misaligned ones are refused on the host, before any launch."""
+    wl = WORKLOADS["conditioned"]
+    plan = plan_for(wl)
+    s = tdp.tdp_plan_sizes(plan)
+    T = len(O.enumerate_tiles(wl.shape, wl.tiling))
+    assert s.cond_k_ints == wl.num_cond
+    assert s.workspace_bytes >= T * wl.batch * 3 * 8 + T * wl.num_cond // 8 and s.workspace_bytes % 256 == 0
+    assert tdp.tdp_plan_sizes(plan_for(WORKLOADS["4k"])).workspace_bytes == 0
+    null = ctypes.c_void_p(None)
+    al = ctypes.c_void_p(0x1000)
+    odd4 = ctypes.c_void_p(0x1002)   # not 4-byte aligned
+    odd16 = ctypes.c_void_p(0x1008)  # 8- but not 16-byte aligned
+    #                      latent pos tile_lat tile_pos index count cond_row cond_k workspace stream
+    assert lib.tdp_extract(plan.handle, al, al, al, al, al, al, al, null, al, null) == tdp.TDP_EINVAL
+    assert "cond_k" in tdp.tdp_last_error()
+    assert lib.tdp_extract(plan.handle, al, al, al, al, al, al, null, al, al, null) == tdp.TDP_EINVAL
+    assert "cond_row" in tdp.tdp_last_error()
+    assert lib.tdp_extract(plan.handle, al, al, al, al, al, al, al, al, null, null) == tdp.TDP_EINVAL
+    assert "workspace" in tdp.tdp_last_error()
+    assert lib.tdp_extract(plan.handle, al, al, al, al, al, al, al, odd4, al, null) == tdp.TDP_EINVAL
+    assert "align" in tdp.tdp_last_error()
+    assert lib.tdp_extract(plan.handle, al, al, al, al, al, al, al, al, odd16, null) == tdp.TDP_EINVAL
+    assert "workspace" in tdp.tdp_last_error()
+    #                    tile_out cond_row cond_k out stream
+    assert lib.tdp_blend(plan.handle, al, al, null, al, null) == tdp.TDP_EINVAL
+    assert "cond_k" in tdp.tdp_last_error()
+    assert lib.tdp_blend(plan.handle, al, al, odd4, al, null) == tdp.TDP_EINVAL
+    assert lib.tdp_blend_tile(plan.handle, 0, al, al, null, al, null) == tdp.TDP_EINVAL
+    assert "cond_k" in tdp.tdp_last_error()
+    assert lib.tdp_blend_tile(plan.handle, 0, al, al, odd4, al, null) == tdp.TDP_EINVAL
+    # without conditioning tokens none of the three is needed: the null
+    # pointers pass validation (the launch itself needs a GPU, so it is not
+    # reached here: a null latent is refused first)
+    plain = plan_for(WORKLOADS["fullres"])
+    assert lib.tdp_extract(plain.handle, null, al, al, al, al, al, null, null, null, null) == tdp.TDP_EINVAL
+    assert "null device pointer" in tdp.tdp_last_error()
 
 
 def test_4k_sizes():
@@ -258,12 +301,12 @@ def test_rank_plan_errors(lib):
     plan = tdp.tdp_plan_create_rank(cfg, 2, 1)
     al = ctypes.c_void_p(0x1000)
     null = ctypes.c_void_p(None)
-    assert lib.tdp_blend_tile(plan.handle, 1, al, null, al, null) == tdp.TDP_EINVAL
+    assert lib.tdp_blend_tile(plan.handle, 1, al, null, null, al, null) == tdp.TDP_EINVAL
     assert "rank plans" in tdp.tdp_last_error()
     assert lib.tdp_blend_finish(plan.handle, al, al, null) == tdp.TDP_EINVAL
     # a rank that holds tiles still needs its tile buffers
-    assert lib.tdp_extract(plan.handle, al, al, null, null, null, null, null, null) == tdp.TDP_EINVAL
-    assert lib.tdp_blend(plan.handle, null, null, al, null) == tdp.TDP_EINVAL
+    assert lib.tdp_extract(plan.handle, al, al, null, null, null, null, null, null, null, null) == tdp.TDP_EINVAL
+    assert lib.tdp_blend(plan.handle, null, null, null, al, null) == tdp.TDP_EINVAL
 
 
 def _brute_cover(ivs, x):
