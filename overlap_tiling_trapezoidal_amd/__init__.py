@@ -172,11 +172,15 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def header_functions(path: str = HEADER_PATH) -> list[str]:
-    """Names of the functions include/tdp.h declares."""
+def _header_functions_in(path: str) -> list[str]:
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(tdp_[a-z_]+)\s*\(", text)))
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/tdp.h declares."""
+    return _header_functions_in(path)
 
 
 def _check(status: int):

@@ -9,6 +9,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtdp.so")
 SOURCES = [os.path.join(HERE, "csrc", n) for n in ("plan.cpp", "quality.cpp", "kernels.hip", "pixel.hip")]
+# memory-system ceilings for the measurement script (not the hot path)
+CEILING_LIB = os.path.join(HERE, "libtdp_ceiling.so")
+CEILING_SOURCES = [os.path.join(HERE, "csrc", "ceiling.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -32,16 +35,23 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libtdp.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Build libtdp.so and libtdp_ceiling.so in place; returns libtdp.so's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(CEILING_SOURCES, CEILING_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,80 @@
+// HBM ceilings of the memory system for the measurement script: how fast a
+// plain streaming copy, a read and a write move bytes on this GPU, so that
+// the hot path's GB/s can be read against what the hardware gives a
+// hand-written kernel rather than only against the vendor peak.
+//
+// Workgroups of 256 threads; thread i of workgroup g moves the 16-byte
+// vectors g * 512 + i and g * 512 + 256 + i (two loads in flight, then two
+// stores), so one wave instruction covers 1 KB contiguous.  Loads carry the
+// non-temporal hint.  Stores either carry it too (the policy of the hot
+// path's kernels) or write with device scope (cache-policy bit sc1: each
+// line goes through the L2 to memory at once instead of waiting as a dirty
+// line for the write-back that ends the kernel), through raw buffer stores.
+// Buffers must be 16-byte aligned and hold `bytes`, a multiple of 8192.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tdp_ceiling.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBlock = 256;
+constexpr int kVecPerBlock = 2 * kBlock;  // 8 KB per workgroup
+constexpr int kRawBufferDword3 = 0x00020000;  // gfx9: raw (unformatted) buffer
+constexpr int kStoreDeviceScope = 16;         // cache policy sc1
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kRawBufferDword3);
+}
+
+template <int MODE>  // 0 copy, nt stores; 1 copy, device-scope stores; 2 read; 3 write
+__global__ __launch_bounds__(kBlock) void ceiling_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         u32x4* __restrict__ sink) {
+  const size_t base = (size_t)blockIdx.x * kVecPerBlock + threadIdx.x;
+  if (MODE == 3) {
+    const u32x4 z = {blockIdx.x, threadIdx.x, 0u, 0u};
+    __builtin_nontemporal_store(z, dst + base);
+    __builtin_nontemporal_store(z, dst + base + kBlock);
+    return;
+  }
+  const u32x4 a = __builtin_nontemporal_load(src + base);
+  const u32x4 b = __builtin_nontemporal_load(src + base + kBlock);
+  if (MODE == 0) {
+    __builtin_nontemporal_store(a, dst + base);
+    __builtin_nontemporal_store(b, dst + base + kBlock);
+  } else if (MODE == 1) {
+    // a descriptor over this workgroup's 8 KB of dst (wave-uniform base)
+    const __amdgpu_buffer_rsrc_t r = rsrc(dst + (size_t)blockIdx.x * kVecPerBlock, kVecPerBlock * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, (int)(threadIdx.x * 16), 0, kStoreDeviceScope);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, (int)((threadIdx.x + kBlock) * 16), 0, kStoreDeviceScope);
+  } else {
+    const u32x4 x = a ^ b;
+    if (x.x == 0x9e3779b9u && x.y == 0x7f4a7c15u && x.z == 0x85ebca6bu && x.w == 0xc2b2ae35u)
+      sink[threadIdx.x] = x;  // practically never: keeps the loads
+  }
+}
+
+}  // namespace
+
+extern "C" int tdp_ceiling_run(int mode, const void* src, void* dst, void* sink, size_t bytes, void* stream) {
+  if (mode < 0 || mode > 3) return -1;
+  if (bytes == 0 || bytes % (kVecPerBlock * 16) != 0) return -1;
+  if ((mode != 3 && !src) || (mode != 2 && !dst) || (mode == 2 && !sink)) return -1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(sink)) & 15)
+    return -1;
+  const size_t blocks = bytes / (kVecPerBlock * 16);
+  if (blocks > 0x7fffffffu) return -1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const u32x4* in = reinterpret_cast<const u32x4*>(src);
+  u32x4* out = reinterpret_cast<u32x4*>(dst);
+  u32x4* snk = reinterpret_cast<u32x4*>(sink);
+  const dim3 grid((unsigned)blocks), block(kBlock);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(ceiling_kernel<0>, grid, block, 0, s, in, out, snk); break;
+    case 1: hipLaunchKernelGGL(ceiling_kernel<1>, grid, block, 0, s, in, out, snk); break;
+    case 2: hipLaunchKernelGGL(ceiling_kernel<2>, grid, block, 0, s, in, out, snk); break;
+    default: hipLaunchKernelGGL(ceiling_kernel<3>, grid, block, 0, s, in, out, snk); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}

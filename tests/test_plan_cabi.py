@@ -36,6 +36,23 @@ def test_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def test_ceiling_library_exports_and_rejects_bad_arguments():
+    """The measurement library loads, exports what include/tdp_ceiling.h
+    declares and refuses bad arguments on the host (nothing enqueued)."""
+    from overlap_tiling_trapezoidal_amd import ceiling
+    clib = ceiling.load_library()
+    names = ceiling.header_functions()
+    assert names == ["tdp_ceiling_run"]
+    for name in names:
+        assert ctypes.cast(getattr(clib, name), ctypes.c_void_p).value
+    al, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(None)
+    assert clib.tdp_ceiling_run(5, al, al, al, 8192, null) == -1        # mode
+    assert clib.tdp_ceiling_run(0, al, al, null, 8000, null) == -1      # size
+    assert clib.tdp_ceiling_run(0, null, al, null, 8192, null) == -1    # src
+    assert clib.tdp_ceiling_run(2, al, null, null, 8192, null) == -1    # sink
+    assert clib.tdp_ceiling_run(0, ctypes.c_void_p(0x1008), al, null, 8192, null) == -1  # alignment
+
+
 def fp32_rne(q: Fraction) -> np.float32:
     """Correctly rounded float32 of an exact rational (ties to even)."""
     f = np.float32(float(q))
