@@ -301,6 +301,31 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
                 void* workspace, void* stream);
 
+/* Largest workspace tdp_extract_noalloc serves (1 MiB: Nc up to about a
+ * million conditioning tokens on a handful of tiles; tdp_sizes gives a
+ * plan's figure). */
+#define TDP_STATIC_SCRATCH_BYTES (1 << 20)
+
+/* tdp_extract without the workspace argument, for callers that cannot
+ * allocate device memory: work recorded under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The selection tables go to a
+ * static device array of TDP_STATIC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends; its address is
+ * looked up once per device, on the first call with that device current.
+ * No allocation, and no clearing by the host: the selection launch zeroes
+ * the totals it accumulates before accumulating them.  Arguments, layouts,
+ * ownership, results and errors as tdp_extract; in addition TDP_EINVAL
+ * (nothing enqueued) when the plan's tdp_sizes.workspace_bytes exceed
+ * TDP_STATIC_SCRATCH_BYTES, and TDP_EHIP when the array's address cannot be
+ * found.  All calls on one GPU share the array, which keeps the last call's
+ * contents: calls that may run at the same time on one GPU (two streams, or
+ * threads without ordering) race and give wrong tables; calls in order on
+ * one stream are safe. */
+int tdp_extract_noalloc(const tdp_plan* plan, const void* latent, const float* pos,
+                        void* tile_lat, float* tile_pos, int32_t* tile_index,
+                        int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
+                        void* stream);
+
 /* Blend tile outputs (tile-major slots with tile_lat's layout and dtype,
  * rows as tdp_extract placed them) into out (B, N+Nc, C) out_dtype:
  *   generated token:    sum over covering tiles t, ascending, of

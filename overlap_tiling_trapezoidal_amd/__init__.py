@@ -29,6 +29,7 @@ TDP_BF16 = 1
 TDP_NORMALIZE_POSITIONS = 0x1
 TDP_UNGUARDED = 0x2
 TDP_MAX_TILES_PER_AXIS = 32
+TDP_STATIC_SCRATCH_BYTES = 1 << 20
 
 _DTYPES = {"f32": TDP_F32, "float32": TDP_F32, "bf16": TDP_BF16, "bfloat16": TDP_BF16}
 
@@ -152,6 +153,7 @@ def load_library(path: str = LIB_PATH):
                                               ctypes.POINTER(ctypes.c_int64)]),
         "tdp_plan_quality": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_quality), ctypes.POINTER(ctypes.c_int64)]),
         "tdp_extract": (ctypes.c_int, [vp] * 11),
+        "tdp_extract_noalloc": (ctypes.c_int, [vp] * 10),
         "tdp_blend": (ctypes.c_int, [vp] * 6),
         "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
@@ -413,16 +415,14 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
-                cond_row=None, cond_k=None, workspace=None, stream=None):
-    """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
+def _extract_args(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k):
     import torch
     c = plan.cfg
     s = tdp_plan_sizes(plan)
     rows = plan.tokens + c.num_cond
     dev = latent.device
     none = ctypes.c_void_p(None)
-    args = [
+    return [
         plan.handle,
         _ptr(latent, "latent", _torch_dtype(c.in_dtype), c.batch * rows * c.channels, dev),
         _ptr(pos, "pos", torch.float32, c.batch * 3 * rows * 2, dev),
@@ -432,10 +432,30 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
         _ptr(tile_count, "tile_count", torch.int32, s.num_slots, dev),
         _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
         _ptr(cond_k, "cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
-        _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes else none,
-        _stream_handle(stream, dev),
     ]
+
+
+def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
+                cond_row=None, cond_k=None, workspace=None, stream=None):
+    """Enqueue the tile gather on ``stream`` (default: torch's current stream)."""
+    import torch
+    s = tdp_plan_sizes(plan)
+    dev = latent.device
+    args = _extract_args(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k)
+    args.append(_ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes
+                else ctypes.c_void_p(None))
+    args.append(_stream_handle(stream, dev))
     _check(load_library().tdp_extract(*args))
+
+
+def tdp_extract_noalloc(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,
+                        cond_row=None, cond_k=None, stream=None):
+    """tdp_extract with the library's static per-GPU workspace in place of a
+    caller's (for callers that cannot allocate device memory; calls that
+    overlap on one GPU race)."""
+    args = _extract_args(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k)
+    args.append(_stream_handle(stream, latent.device))
+    _check(load_library().tdp_extract_noalloc(*args))
 
 
 def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):

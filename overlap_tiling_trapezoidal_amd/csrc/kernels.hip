@@ -1404,34 +1404,104 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
 }
 
 
+// Checks tdp_extract and tdp_extract_noalloc share (the workspace aside).
+int check_extract(const tdp_plan* plan, const void* latent, const float* pos, const void* tile_lat,
+                  const float* tile_pos, const int32_t* tile_index, const int32_t* tile_count, const int32_t* cond_row,
+                  const int32_t* cond_k, const char* who) {
+  if (!plan) return fail(TDP_EINVAL, "%s: null plan", who);
+  if (!plan->guarded) return fail(TDP_EGUARD, "%s: plan was built with TDP_UNGUARDED", who);
+  const PlanDev& p = plan->dev;
+  if (!latent || !pos) return fail(TDP_EINVAL, "%s: null device pointer", who);
+  if (p.T_local > 0 && (!tile_lat || !tile_pos || !tile_index || !tile_count))
+    return fail(TDP_EINVAL, "%s: null device pointer", who);
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "%s: cond_row and cond_k are required when num_cond > 0", who);
+  if (!aligned(latent, 16) || !aligned(tile_lat, 16))
+    return fail(TDP_EINVAL, "%s: latent and tile_lat must be 16-byte aligned", who);
+  if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
+      !aligned(cond_row, 4) || !aligned(cond_k, 4))
+    return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
+  return TDP_OK;
+}
+
+
 }  // namespace
 }  // namespace tdp
 
 using namespace tdp;
+
+// Workspace of tdp_extract_noalloc: one copy on every GPU the library runs
+// on, kept until the process ends.  Host code never passes this name to a
+// kernel (on the host it only stands for the symbol); it passes the device
+// address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) char scratch[TDP_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::atomic<char*> g_scratch[kScratchDevices];  // device address per device; null until looked up
+
+// Address of `scratch` on the current device, looked up on the first call
+// with that device current; null (with the error recorded) on failure.
+char* scratch_on_current_device(const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(TDP_EHIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kScratchDevices) {
+    fail(TDP_EHIP, "%s: device %d is beyond the %d the static workspace serves", who, dev, kScratchDevices);
+    return nullptr;
+  }
+  char* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    fail(TDP_EHIP, "%s: no device address for the static workspace: %s", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch[dev].store(ptr, std::memory_order_release);  // racing first calls store the same address
+  return ptr;
+}
+
+}  // namespace
 
 extern "C" {
 
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
                 int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, void* workspace,
                 void* stream) {
-  if (!plan) return fail(TDP_EINVAL, "tdp_extract: null plan");
-  if (!plan->guarded) return fail(TDP_EGUARD, "tdp_extract: plan was built with TDP_UNGUARDED");
+  const int st = check_extract(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
+                               "tdp_extract");
+  if (st != TDP_OK) return st;
   const PlanDev& p = plan->dev;
-  if (!latent || !pos) return fail(TDP_EINVAL, "tdp_extract: null device pointer");
-  if (p.T_local > 0 && (!tile_lat || !tile_pos || !tile_index || !tile_count))
-    return fail(TDP_EINVAL, "tdp_extract: null device pointer");
-  if (p.Nc > 0 && (!cond_row || !cond_k))
-    return fail(TDP_EINVAL, "tdp_extract: cond_row and cond_k are required when num_cond > 0");
   if (ws_layout(p).bytes > 0 && !workspace)
     return fail(TDP_EINVAL, "tdp_extract: workspace of %lld bytes is required (tdp_plan_sizes)",
                 (long long)ws_layout(p).bytes);
-  if (!aligned(latent, 16) || !aligned(tile_lat, 16) || !aligned(workspace, 16))
-    return fail(TDP_EINVAL, "tdp_extract: latent, tile_lat and workspace must be 16-byte aligned");
-  if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
-      !aligned(cond_row, 4) || !aligned(cond_k, 4))
-    return fail(TDP_EINVAL, "tdp_extract: pos/tile_pos need 8-byte and int buffers 4-byte alignment");
+  if (!aligned(workspace, 16)) return fail(TDP_EINVAL, "tdp_extract: workspace must be 16-byte aligned");
   return launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                         static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream), "tdp_extract");
+}
+
+int tdp_extract_noalloc(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat,
+                        float* tile_pos, int32_t* tile_index, int32_t* tile_count, int32_t* cond_row,
+                        int32_t* cond_k, void* stream) {
+  const int st = check_extract(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
+                               "tdp_extract_noalloc");
+  if (st != TDP_OK) return st;
+  const PlanDev& p = plan->dev;
+  const int64_t need = ws_layout(p).bytes;
+  if (need > (int64_t)TDP_STATIC_SCRATCH_BYTES)
+    return fail(TDP_EINVAL, "tdp_extract_noalloc: the plan needs %lld bytes of workspace, beyond the static %d",
+                (long long)need, (int)TDP_STATIC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_current_device("tdp_extract_noalloc");
+    if (!ws) return TDP_EHIP;
+  }
+  return launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k, ws,
+                        reinterpret_cast<hipStream_t>(stream), "tdp_extract_noalloc");
 }
 
 int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
