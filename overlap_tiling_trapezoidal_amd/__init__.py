@@ -15,7 +15,13 @@ import os
 import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtdp.so")
+DEFAULT_LIB_PATH = os.path.join(_HERE, "libtdp.so")
+# TDP_LIBRARY names another build to load instead, e.g. the host-only planner
+# built with address and undefined-behaviour sanitizers for the CPU tests
+# (build.py --host-sanitized); such a build may lack the device entry points.
+LIB_PATH = os.environ.get("TDP_LIBRARY") or DEFAULT_LIB_PATH
+DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_blend", "tdp_blend_tile", "tdp_blend_finish",
+                    "tdp_pixel_blend")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp.h")
 
 # ---- constants (mirror include/tdp.h) --------------------------------------
@@ -125,11 +131,12 @@ class TdpError(RuntimeError):
 
 
 _lib = None
+HOST_ONLY = False  # the loaded build has the host planner only (no device entry points)
 
 
 def load_library(path: str = LIB_PATH):
     """Load libtdp.so; raises ImportError when it has not been built."""
-    global _lib
+    global _lib, HOST_ONLY
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
@@ -166,10 +173,16 @@ def load_library(path: str = LIB_PATH):
         "tdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tdp_last_error": (ctypes.c_char_p, []),
     }
+    missing = [name for name in sig if not hasattr(lib, name)]
+    if missing and (path == DEFAULT_LIB_PATH or any(m not in DEVICE_FUNCTIONS for m in missing)):
+        raise ImportError(f"{path} does not export {', '.join(missing)}")
     for name, (res, args) in sig.items():
+        if name in missing:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    HOST_ONLY = bool(missing)
     _lib = lib
     return lib
 

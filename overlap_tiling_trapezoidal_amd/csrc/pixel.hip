@@ -19,42 +19,9 @@
 // for every row, each wave takes consecutive rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <string.h>
-
-#include <new>
 
 #include "device_common.h"
-#include "plan_internal.h"
-
-namespace tdp {
-
-struct PixelDev {
-  AxisSplit ax[2];   // latent split of height and width
-  int32_t s[2];      // pixels per cell
-  int32_t o[2];      // pixel overlaps s * overlap
-  int32_t B, C, Fo;
-  int32_t Hp, Wp;    // output pixel rows and columns
-  int32_t rows;      // B * C * Fo * Hp output rows
-  int32_t in_dtype, out_dtype;
-  FastDiv by_s[2];   // pixel -> cell
-  FastDiv by_hp;     // output row -> (b, c, f)
-};
-
-// Element offset of tile (i, j): B*C*Fo*s_h*s_w times the latent cells of
-// the tiles before it in row-major order.
-TDP_HD int64_t pixel_tile_offset(const PixelDev& p, int i, int j) {
-  const int64_t cells = (int64_t)split_prefix(p.ax[0], i) * split_total(p.ax[1]) +
-                        (int64_t)split_size(p.ax[0], i) * split_prefix(p.ax[1], j);
-  return (int64_t)p.B * p.C * p.Fo * p.s[0] * p.s[1] * cells;
-}
-
-}  // namespace tdp
-
-struct tdp_pixel_plan {
-  tdp_pixel_config cfg;
-  tdp::PixelDev dev;
-  int64_t tile_elems, out_elems;
-};
+#include "pixel_internal.h"
 
 namespace tdp {
 namespace {
@@ -142,91 +109,6 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 using namespace tdp;
 
 extern "C" {
-
-int tdp_pixel_plan_create(const tdp_pixel_config* cfg, tdp_pixel_plan** out) {
-  if (!cfg || !out) return fail(TDP_EINVAL, "tdp_pixel_plan_create: null argument");
-  *out = nullptr;
-  const tdp_pixel_config c = *cfg;
-  if (c.batch < 1 || c.channels < 1 || c.frames < 1)
-    return fail(TDP_EINVAL, "batch, channels and frames must be >= 1 (got %d, %d, %d)", c.batch, c.channels,
-                c.frames);
-  if (c.height < 1 || c.width < 1) return fail(TDP_EINVAL, "latent height and width must be >= 1");
-  if (c.scale[0] < 1 || c.scale[1] < 1)
-    return fail(TDP_EINVAL, "scale must be >= 1 pixel per cell (got %d, %d)", c.scale[0], c.scale[1]);
-  const int ein = dtype_bytes(c.in_dtype), eout = dtype_bytes(c.out_dtype);
-  if (!ein || !eout) return fail(TDP_EINVAL, "dtypes must be TDP_F32 or TDP_BF16");
-  PixelDev d;
-  memset(&d, 0, sizeof d);
-  const int32_t dims[2] = {c.height, c.width};
-  for (int a = 0; a < 2; ++a) {
-    const int st = build_axis(1 + a, dims[a], c.axis[a], true, &d.ax[a]);
-    if (st != TDP_OK) return st;
-  }
-  const int vec = 16 / ein;
-  if (c.scale[1] % vec != 0)
-    return fail(TDP_ESHAPE,
-                "width scale %d: pixel tiles must start and end on 16-byte vectors, so it must be a multiple of "
-                "%d for this input dtype",
-                c.scale[1], vec);
-  const int64_t hp = (int64_t)c.height * c.scale[0], wp = (int64_t)c.width * c.scale[1];
-  const int64_t rows = (int64_t)c.batch * c.channels * c.frames * hp;
-  if (hp > INT32_MAX || wp > INT32_MAX || rows > INT32_MAX)
-    return fail(TDP_ESHAPE, "%lld output rows of %lld pixels exceed the int32 range", (long long)rows,
-                (long long)wp);
-  for (int a = 0; a < 2; ++a) {
-    d.s[a] = c.scale[a];
-    d.o[a] = c.axis[a].overlap * c.scale[a];
-    d.by_s[a] = make_fastdiv((uint32_t)c.scale[a]);
-  }
-  d.B = c.batch;
-  d.C = c.channels;
-  d.Fo = c.frames;
-  d.Hp = (int32_t)hp;
-  d.Wp = (int32_t)wp;
-  d.rows = (int32_t)rows;
-  d.in_dtype = c.in_dtype;
-  d.out_dtype = c.out_dtype;
-  d.by_hp = make_fastdiv((uint32_t)hp);
-  tdp_pixel_plan* p = new (std::nothrow) tdp_pixel_plan;
-  if (!p) return fail(TDP_EINVAL, "out of host memory");
-  p->cfg = c;
-  p->dev = d;
-  p->tile_elems = (int64_t)c.batch * c.channels * c.frames * c.scale[0] * c.scale[1] *
-                  ((int64_t)split_total(d.ax[0]) * split_total(d.ax[1]));
-  p->out_elems = rows * wp;
-  *out = p;
-  return TDP_OK;
-}
-
-void tdp_pixel_plan_destroy(tdp_pixel_plan* plan) { delete plan; }
-
-int tdp_pixel_plan_tile(const tdp_pixel_plan* plan, int32_t t, tdp_pixel_tile* out) {
-  if (!plan || !out) return fail(TDP_EINVAL, "tdp_pixel_plan_tile: null argument");
-  const PixelDev& d = plan->dev;
-  const int T = d.ax[0].n * d.ax[1].n;
-  if (t < 0 || t >= T) return fail(TDP_EINVAL, "tile index %d out of range [0, %d)", t, T);
-  const int i = t / d.ax[1].n, j = t % d.ax[1].n;
-  tdp_pixel_tile r;
-  r.index = t;
-  r.grid[0] = i;
-  r.grid[1] = j;
-  r.origin[0] = d.s[0] * split_start(d.ax[0], i);
-  r.origin[1] = d.s[1] * split_start(d.ax[1], j);
-  r.shape[0] = d.s[0] * split_size(d.ax[0], i);
-  r.shape[1] = d.s[1] * split_size(d.ax[1], j);
-  r.offset = pixel_tile_offset(d, i, j);
-  r.elems = (int64_t)d.B * d.C * d.Fo * r.shape[0] * r.shape[1];
-  *out = r;
-  return TDP_OK;
-}
-
-int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_t* out_elems, int32_t* num_tiles) {
-  if (!plan || !tile_elems || !out_elems || !num_tiles) return fail(TDP_EINVAL, "tdp_pixel_plan_sizes: null argument");
-  *tile_elems = plan->tile_elems;
-  *out_elems = plan->out_elems;
-  *num_tiles = plan->dev.ax[0].n * plan->dev.ax[1].n;
-  return TDP_OK;
-}
 
 int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream) {
   if (!plan) return fail(TDP_EINVAL, "tdp_pixel_blend: null plan");

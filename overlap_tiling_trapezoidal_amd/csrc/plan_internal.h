@@ -24,7 +24,7 @@
 
 namespace tdp {
 
-// Unsigned division by an invariant d >= 1 for numerators below 2^31, by
+// Unsigned division by an invariant d >= 1 for numerators up to 2^31, by
 // multiplication (Granlund & Montgomery, "Division by invariant integers
 // using multiplication", PLDI 1994): with l = ceil(log2 d) and
 // m = floor(2^32 * (2^l - d) / d) + 1, q = (mulhi(m, x) + x) >> l.
@@ -46,7 +46,7 @@ TDP_HD uint32_t fastdiv(uint32_t x, const FastDiv& f) {
 }
 
 struct AxisSplit {
-  int32_t dim;         // cells on the axis (<= TDP_MAX_AXIS, so products stay below 2^31)
+  int32_t dim;         // cells on the axis (<= TDP_MAX_AXIS, so products stay at most 2^31)
   int32_t n;           // tiles on the axis
   int32_t o;           // overlap in cells
   int32_t size_min;    // floor(s / n) + o: every tile size is size_min or size_min + 1
@@ -55,8 +55,9 @@ struct AxisSplit {
   FastDiv by_size[2];  // division by size_min and size_min + 1
 };
 
+// i * s <= n * dim <= 32 * 2^26 = 2^31: unsigned, and within fastdiv's range.
 TDP_HD int split_start(const AxisSplit& a, int i) {
-  return (int)fastdiv((uint32_t)(i * (a.dim - a.o)), a.by_n);
+  return (int)fastdiv((uint32_t)i * (uint32_t)(a.dim - a.o), a.by_n);
 }
 TDP_HD int split_size(const AxisSplit& a, int i) { return split_start(a, i + 1) + a.o - split_start(a, i); }
 TDP_HD int split_prefix(const AxisSplit& a, int i) { return split_start(a, i) + i * a.o; }
@@ -70,7 +71,7 @@ TDP_HD uint32_t div_by_size(const AxisSplit& a, uint32_t x, int size) {
 // The last tile that contains cell x: the largest i with a_i <= x.
 // a_i <= x  <=>  i * s < (x + 1) * n  <=>  i <= ((x + 1) * n - 1) / s.
 TDP_HD int split_last_cover(const AxisSplit& a, int x) {
-  const int i = (int)fastdiv((uint32_t)((x + 1) * a.n - 1), a.by_s);
+  const int i = (int)fastdiv((uint32_t)(x + 1) * (uint32_t)a.n - 1u, a.by_s);  // <= 2^31 - 1
   return i < a.n - 1 ? i : a.n - 1;
 }
 

@@ -56,6 +56,7 @@ def test_pixel_plan_errors(kw, status):
     assert ei.value.status == status
 
 
+@pytest.mark.device_abi
 def test_pixel_blend_rejects_bad_pointers():
     import ctypes
     plan = make(CONFIGS[0])

@@ -28,6 +28,15 @@ def plan_for(wl, **kw):
     return tdp.tdp_plan_create(cfg)
 
 
+def test_exports_the_host_planner(lib):
+    """Every declared function but the device entry points, in any build."""
+    names = [n for n in tdp.header_functions() if n not in tdp.DEVICE_FUNCTIONS]
+    assert len(names) >= 19
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.device_abi
 def test_exports_every_declared_symbol(lib):
     names = tdp.header_functions()
     assert len(names) >= 12
@@ -36,6 +45,7 @@ def test_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+@pytest.mark.device_abi
 def test_ceiling_library_exports_and_rejects_bad_arguments():
     """The measurement library loads, exports what include/tdp_ceiling.h
     declares and refuses bad arguments on the host (nothing enqueued)."""
@@ -186,6 +196,7 @@ def test_unknown_flags_and_nulls(lib):
     assert lib.tdp_status_string(tdp.TDP_EGUARD).startswith(b"TDP_EGUARD")
 
 
+@pytest.mark.device_abi
 def test_device_calls_reject_bad_plans_before_launch(lib):
     # Validation happens on the host before anything is enqueued, so these
     # run without a GPU.
@@ -206,6 +217,7 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
     assert "aligned" in tdp.tdp_last_error()
 
 
+@pytest.mark.device_abi
 def test_cond_k_and_workspace_arguments(lib):
     """With conditioning tokens, tdp_extract needs cond_row, cond_k and the
     workspace, and tdp_blend / tdp_blend_tile need cond_row and cond_k; null
@@ -314,7 +326,12 @@ def test_rank_plan_errors(lib):
     with pytest.raises(tdp.TdpError) as ei:
         tdp.tdp_plan_create_rank(bad, 2, 0)
     assert ei.value.status == tdp.TDP_EGUARD
+
+
+@pytest.mark.device_abi
+def test_rank_plan_device_call_errors(lib):
     # the streaming blend is for whole plans; refused before any launch
+    cfg = tdp.make_config(1, 128, (4, 8, 8), ((1, 0), (2, 2), (2, 2)))
     plan = tdp.tdp_plan_create_rank(cfg, 2, 1)
     al = ctypes.c_void_p(0x1000)
     null = ctypes.c_void_p(None)
@@ -348,11 +365,14 @@ def test_cell_tiles_match_brute_force():
 
 
 def test_large_axes_near_limit():
-    # Products i*(dim-o) and (x+1)*n stay below 2^31 up to TDP_MAX_AXIS cells.
+    # Products i*(dim-o) and (x+1)*n reach 2^31 at TDP_MAX_AXIS cells and 32
+    # tiles with no overlap (the first case); they are formed in uint32.
     limit = 1 << 26
     rng = np.random.default_rng(9)
-    for dim, n in [(limit, 32), (limit - 7, 31), (limit // 3 + 1, 17), (123457, 32)]:
-        o = int(rng.integers(0, dim // (n + 1) + 1))
+    for dim, n, o in [(limit, 32, 0), (limit, 32, None), (limit - 7, 31, None), (limit // 3 + 1, 17, None),
+                      (123457, 32, None)]:
+        if o is None:
+            o = int(rng.integers(0, dim // (n + 1) + 1))
         plan = tdp.tdp_plan_create(tdp.make_config(1, 8, (dim, 1, 1), ((n, o), (1, 0), (1, 0))))
         ivs = O.split_by_count(dim, n, o)
         assert tdp.tdp_plan_intervals(plan, 0) == ivs

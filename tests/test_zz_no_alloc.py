@@ -61,6 +61,7 @@ def test_noalloc_matches_extract_on_successive_calls(cuda):
             check_extract(plan, got, ex, wl.num_cond)
 
 
+@pytest.mark.device_abi
 def test_noalloc_refuses_plans_beyond_the_static_workspace():
     lib = tdp.load_library()
     wl = Workload("huge_cond", 1, 16, (1, 16, 16), ((1, 0), (4, 0), (4, 0)), num_cond=4_000_000, dtype="bf16")
