@@ -264,8 +264,10 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
 
 /* Gather all tiles, every latent row read once.  Without conditioning
- * tokens this is one launch; with them a selection launch runs first and
- * leaves its tables in `workspace`.
+ * tokens this is one launch; with them an extent launch first leaves each
+ * tile's partial extents and cleared look-back flags in `workspace`, and a
+ * second launch selects and copies the conditioning tokens along with the
+ * generated rows (tdp_set_lookback_polls).
  *   in   latent (B, N+Nc, C) in_dtype; pos (B, 3, N+Nc, 2) float32.
  *   out  tile_lat, tile_pos, tile_index: tile-major slots (layout above).
  *        tile_count (one per slot: T, or a rank's share) int32:
@@ -301,6 +303,19 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
                 void* workspace, void* stream);
 
+/* Conditioning selection (Nc > 0), the second launch of tdp_extract: one
+ * workgroup per (tile, chunk of 64 tokens) tests its chunk and finds the
+ * tile's kept tokens before it: those of the 16 chunks before it from
+ * their tokens, those of earlier chunks from the flags their workgroups
+ * publish (look-back).  A flag still unpublished after `polls` reads is not
+ * waited for: the workgroup counts that chunk from its tokens itself, so
+ * the result never depends on the order in which workgroups start and no
+ * wait is unbounded.  The default is 256 reads; 0 counts every unpublished
+ * chunk at once.  Results are the same for every value.  Process-wide;
+ * applies to tdp_extract and tdp_extract_noalloc calls enqueued afterwards.
+ * TDP_EINVAL for polls < 0. */
+int tdp_set_lookback_polls(int32_t polls);
+
 /* Largest workspace tdp_extract_noalloc serves (1 MiB: Nc up to about a
  * million conditioning tokens on a handful of tiles; tdp_sizes gives a
  * plan's figure). */
@@ -312,8 +327,8 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
  * static device array of TDP_STATIC_SCRATCH_BYTES bytes that the library
  * holds on every GPU it runs on until the process ends; its address is
  * looked up once per device, on the first call with that device current.
- * No allocation, and no clearing by the host: the selection launch zeroes
- * the totals it accumulates before accumulating them.  Arguments, layouts,
+ * No allocation, and no clearing by the host: the extent launch clears
+ * the look-back flags before the selection reads them.  Arguments, layouts,
  * ownership, results and errors as tdp_extract; in addition TDP_EINVAL
  * (nothing enqueued) when the plan's tdp_sizes.workspace_bytes exceed
  * TDP_STATIC_SCRATCH_BYTES, and TDP_EHIP when the array's address cannot be

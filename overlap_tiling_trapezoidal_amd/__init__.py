@@ -20,8 +20,8 @@ DEFAULT_LIB_PATH = os.path.join(_HERE, "libtdp.so")
 # built with address and undefined-behaviour sanitizers for the CPU tests
 # (build.py --host-sanitized); such a build may lack the device entry points.
 LIB_PATH = os.environ.get("TDP_LIBRARY") or DEFAULT_LIB_PATH
-DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_blend", "tdp_blend_tile", "tdp_blend_finish",
-                    "tdp_pixel_blend")
+DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_set_lookback_polls", "tdp_blend", "tdp_blend_tile",
+                    "tdp_blend_finish", "tdp_pixel_blend")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp.h")
 
 # ---- constants (mirror include/tdp.h) --------------------------------------
@@ -161,6 +161,7 @@ def load_library(path: str = LIB_PATH):
         "tdp_plan_quality": (ctypes.c_int, [vp, i32, ctypes.POINTER(tdp_quality), ctypes.POINTER(ctypes.c_int64)]),
         "tdp_extract": (ctypes.c_int, [vp] * 11),
         "tdp_extract_noalloc": (ctypes.c_int, [vp] * 10),
+        "tdp_set_lookback_polls": (ctypes.c_int, [i32]),
         "tdp_blend": (ctypes.c_int, [vp] * 6),
         "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
@@ -459,6 +460,12 @@ def tdp_extract(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_co
                 else ctypes.c_void_p(None))
     args.append(_stream_handle(stream, dev))
     _check(load_library().tdp_extract(*args))
+
+
+def tdp_set_lookback_polls(polls: int):
+    """Reads of an unpublished look-back flag before a conditioning selection
+    wave counts that chunk itself (process-wide; results do not depend on it)."""
+    _check(load_library().tdp_set_lookback_polls(int(polls)))
 
 
 def tdp_extract_noalloc(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count,

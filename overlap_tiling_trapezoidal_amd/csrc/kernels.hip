@@ -54,9 +54,9 @@ constexpr int kPosUnroll = 8;      // position rows in flight per thread (copy p
 constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start pass)
 constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
 constexpr int kSelLoads = 24;      // position loads in flight per thread in the extent launch
-constexpr int kCopyBatch = 16;     // kept conditioning rows in flight per lane
-constexpr int kCopyTokens = 64;    // conditioning tokens per compaction workgroup: a quarter chunk
-constexpr int kCopyParts = kCondChunk / kCopyTokens;
+constexpr int kCopyBatch = 8;      // kept conditioning vectors in flight per thread
+constexpr int kLookbackPolls = 256;  // reads of an unpublished flag before a wave counts that chunk itself
+constexpr int kDirectChunks = 16;    // earlier chunks a selection workgroup counts from their tokens
 constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
 constexpr int kCondTokens = 16;        // conditioning tokens per blend workgroup
 constexpr int kCondTiles = 256;        // plans up to this many tiles cache cond_row and slots in LDS
@@ -214,23 +214,21 @@ struct ExtractArgs {
   int32_t* tile_count;
   int32_t* cond_row;     // (T, Nc)
   int32_t* cond_k;       // (Nc)
-  const char* ws;        // workspace with the selection launch's tables (Nc > 0), else null
-  int n_sel, n_pos, pos_parts;
+  char* ws;              // workspace: extent partials and look-back flags (Nc > 0), else null
+  int n_ext, n_sel, n_pos, pos_parts;
   int pos_one_pass;      // position workgroups hold their part in registers (one pass)
+  int lookback_polls;    // reads of an unpublished flag before a wave counts that chunk itself
 };
 
-// Tables of the selection launch in the workspace (layout in PlanDev).
-__device__ inline const float2* ws_ext(const PlanDev& p, const ExtractArgs& a) {
-  return reinterpret_cast<const float2*>(a.ws + ws_layout(p).ext);
+// Tables of the conditioning selection in the workspace (layout in WsLayout).
+__device__ inline const float2* ws_part(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<const float2*>(a.ws + ws_layout(p).part);
 }
-__device__ inline const uint32_t* ws_keep(const PlanDev& p, const ExtractArgs& a) {
-  return reinterpret_cast<const uint32_t*>(a.ws + ws_layout(p).keep);
+__device__ inline float2* ws_part_w(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<float2*>(a.ws + ws_layout(p).part);
 }
-__device__ inline const int32_t* ws_cnt(const PlanDev& p, const ExtractArgs& a) {
-  return reinterpret_cast<const int32_t*>(a.ws + ws_layout(p).cnt);
-}
-__device__ inline const int32_t* ws_tot(const PlanDev& p, const ExtractArgs& a) {
-  return reinterpret_cast<const int32_t*>(a.ws + ws_layout(p).tot);
+__device__ inline uint32_t* ws_flags(const PlanDev& p, const ExtractArgs& a) {
+  return reinterpret_cast<uint32_t*>(a.ws + ws_layout(p).flags);
 }
 
 // Source token (within one batch element) of generated row r of a tile:
@@ -243,12 +241,7 @@ __device__ inline int tile_row_source(const PlanDev& p, const TileBox& tb, int r
   return ((tb.f0 + lf) * p.H + (tb.h0 + lh)) * p.W + tb.w0 + x;
 }
 
-struct CopyShared {
-  int wave_sum[kWaves];
-  int kept_c[kCopyTokens];   // kept tokens of this quarter chunk, ascending
-};
-union ExtractShared {
-  CopyShared sel;
+struct ExtractShared {
   float2 red[kWaves];
 };
 
@@ -282,124 +275,340 @@ __device__ float tile_plane_min_start(const PlanDev& p, const TileBox& tb, const
   return block_minmax(lo, -INFINITY, red).x;
 }
 
-// Compaction and copy workgroup (extract launch, Nc > 0): tile t, quarter
-// `sub` of chunk k (kCopyTokens conditioning tokens), from the selection
-// launches' tables.  The tile's kept tokens before it are the totals of the
-// earlier superchunks, the counts of the earlier chunks of its superchunk
-// and the keep bits of the earlier quarters, so no workgroup re-tests
-// earlier tokens and the work per workgroup barely grows with Nc (one total
-// per kChunksPerSuper chunks).  Writes cond_row for every tile (k counts the
-// tiles of all ranks), the index entries and rows of a held tile, the
-// tile's count (from its last workgroup) and, from one workgroup per
-// quarter, cond_k of the quarter's tokens.  Quarters keep the copy of a
-// chunk's kept rows (up to 256 tokens times the batch) off a single compute
-// unit.
-template <bool R>
-__device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, ExtractShared& sm, int t, int k,
-                                   int sub) {
-  const TileBox tb = tile_box<R>(p, t);
-  const bool own = held<R>(p, t);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // 1. kept tokens of this tile before the chunk: the totals of the earlier
-  //    superchunks and the counts of the earlier chunks of its own
-  const int sup = k / kChunksPerSuper, k0 = sup * kChunksPerSuper;
-  int before = 0;
-  const int32_t* tot = ws_tot(p, a);
-  for (int i = threadIdx.x; i < sup; i += kBlock) before += tot[(int64_t)t * p.n_super + i];
-  if ((int)threadIdx.x < k - k0) before += ws_cnt(p, a)[(int64_t)t * p.n_chunks + k0 + threadIdx.x];
-  for (int m = 32; m >= 1; m >>= 1) before += __shfl_xor(before, m, 64);
-  if (lane == 0) sm.sel.wave_sum[wave] = before;
-  // 2. the chunk's keep bits: earlier quarters, then the rank of each of
-  //    this quarter's tokens (thread j < kCopyTokens takes token j)
-  const uint32_t* words = ws_keep(p, a) + ((int64_t)t * p.n_chunks + k) * kKeepWords;
-  uint32_t wv[kKeepWords];
-#pragma unroll
-  for (int i = 0; i < kKeepWords; ++i) wv[i] = words[i];  // same address on every lane
-  __syncthreads();
-  static_assert(kCopyTokens == 64 && kKeepWords == 2 * kCopyParts, "a quarter is two keep words");
-  const int chunk_base = sm.sel.wave_sum[0] + sm.sel.wave_sum[1] + sm.sel.wave_sum[2] + sm.sel.wave_sum[3];
-  int base = chunk_base;  // kept tokens of the tile before this quarter
-  int chunk_kept = 0;
-  uint64_t mask = 0;
-#pragma unroll
-  for (int i = 0; i < kKeepWords; ++i) {
-    const int pc = __popc(wv[i]);
-    base += i < 2 * sub ? pc : 0;
-    chunk_kept += pc;
-    if (i == 2 * sub) mask |= wv[i];
-    if (i == 2 * sub + 1) mask |= (uint64_t)wv[i] << 32;
-  }
-  const int n_kept = __popcll(mask);
-  const int j = threadIdx.x;
-  const int c = k * kCondChunk + sub * kCopyTokens + j;
-  if (j < kCopyTokens && c < p.Nc) {
-    const bool keep = (mask >> j) & 1ull;
-    const int rank = __popcll(mask & ((1ull << j) - 1ull));
-    const int row = tb.s.gen + base + rank;
-    a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
-    if (keep) sm.sel.kept_c[rank] = c;
-    if (own && keep) a.tile_index[tb.s.index_base + row] = p.N + c;
-  }
-  if (own && k == p.n_chunks - 1 && sub == kCopyParts - 1 && threadIdx.x == 0)
-    a.tile_count[R ? (int)fastdiv((uint32_t)t, p.by_world) : t] = tb.s.gen + chunk_base + chunk_kept;
-  // 3. k of the quarter's tokens: keep bits of every tile (one workgroup per quarter)
-  if (t == (k * kCopyParts + sub) % p.T && j < kCopyTokens && c < p.Nc) {
-    const uint32_t* col = ws_keep(p, a) + (int64_t)k * kKeepWords + 2 * sub + (j >> 5);
-    int kc = 0;
-    for (int u = 0; u < p.T; ++u) kc += (col[(int64_t)u * p.n_chunks * kKeepWords] >> (j & 31)) & 1u;
-    a.cond_k[c] = kc;
-  }
-  if (!own) return;  // workgroup-uniform
-  __syncthreads();
+// ---- conditioning selection in the extract launch (Nc > 0) ----
+//
+// Look-back words (flags table, zeroed by the extent launch): 0 until
+// published, then kFlagAgg with the chunk's own kept count, or kFlagPrefix
+// with the tile's kept count over chunks 0..k.  Counts stay below 2^29.
+// Words are read and written with device-scope atomics, so a wave on
+// another accelerator die sees them.
+constexpr uint32_t kFlagAgg = 1u << 30;
+constexpr uint32_t kFlagPrefix = 1u << 31;
+constexpr uint32_t kFlagCount = kFlagAgg - 1u;
 
-  // 4. copy the kept rows: latent vectors, then shifted positions.  Loads
-  //    go out in batches (then their stores), not one round trip per row.
-  const int V = p.vin;
-  const int rpp = p.rpp;
-  const int r = (int)fastdiv(threadIdx.x, p.by_vin), vv = threadIdx.x - r * V;
-  if (r < rpp) {
-    // Kept rows of every batch element in one flat loop, kCopyBatch loads
-    // before any store: the memory counter a load waits on also counts
-    // earlier stores, so a round of stores ahead of the next loads would
-    // put their write latency into the chain.
-    const int total = p.B * n_kept;
-    const FastDiv by_kept = make_fastdiv((uint32_t)(n_kept > 0 ? n_kept : 1));  // workgroup-uniform
-    for (int i0 = r; i0 < total; i0 += rpp * kCopyBatch) {
-      u32x4 v[kCopyBatch];
+__device__ inline void flag_publish(uint32_t* f, uint32_t v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t flag_read(uint32_t* f) {
+  return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline int wave_sum_int(int v) {
 #pragma unroll
-      for (int q = 0; q < kCopyBatch; ++q) {
-        const int i = min(i0 + q * rpp, total - 1);
-        const int b = (int)fastdiv((uint32_t)i, by_kept), jj = i - b * n_kept;
-        v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + sm.sel.kept_c[jj]) * V + vv);
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Position (from 0) of the set bit of m with j set bits below it (j < popcount(m)).
+__device__ inline int nth_set_bit(uint64_t m, int j) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const uint64_t lo = m & ((1ull << w) - 1ull);
+    const int cnt = __popcll(lo);
+    const bool up = j >= cnt;
+    j = up ? j - cnt : j;
+    m = up ? m >> w : lo;
+    pos += up ? w : 0;
+  }
+  return pos;
+}
+
+// The tile's extent, its parts combined, into ext[0 .. B*3) (whole
+// workgroup; eight parts' loads in flight per thread).
+__device__ void combine_extent(const PlanDev& p, const ExtractArgs& a, int t, float2* ext) {
+  const int planes = p.B * 3;
+  const float2* parts = ws_part(p, a) + (int64_t)t * p.ext_parts * planes;
+  for (int e = threadIdx.x; e < planes; e += kBlock) {
+    float2 m = make_float2(INFINITY, -INFINITY);
+    for (int q0 = 0; q0 < p.ext_parts; q0 += 8) {
+      float2 y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = parts[(int64_t)min(q0 + u, p.ext_parts - 1) * planes + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        m.x = fminf(m.x, y[u].x);
+        m.y = fmaxf(m.y, y[u].y);
       }
+    }
+    ext[e] = m;
+  }
+}
+
+// Minimum start of tile t on plane bd = b * 3 + d, its parts combined
+// (eight parts' loads in flight).
+__device__ inline float tile_min_start(const PlanDev& p, const ExtractArgs& a, int t, int bd) {
+  const int planes = p.B * 3;
+  const float2* parts = ws_part(p, a) + (int64_t)t * p.ext_parts * planes + bd;
+  float m = INFINITY;
+  for (int q0 = 0; q0 < p.ext_parts; q0 += 8) {
+    float y[8];
 #pragma unroll
-      for (int q = 0; q < kCopyBatch; ++q) {
-        const int i = i0 + q * rpp;
-        if (i < total) {
-          const int b = (int)fastdiv((uint32_t)i, by_kept), jj = i - b * n_kept;
-          st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + tb.s.gen + base + jj) * V + vv, v[q]);
-        }
+    for (int u = 0; u < 8; ++u) y[u] = parts[(int64_t)min(q0 + u, p.ext_parts - 1) * planes].x;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fminf(m, y[u]);
+  }
+  return m;
+}
+
+// Positions of the token of lane l of chunk ch for batch elements b0 and
+// b0 + 1 (an odd batch repeats the last: the keep test ORs over them).
+struct TokenPos {
+  f32x2 x[2][3];
+};
+__device__ inline TokenPos load_token_pos(const PlanDev& p, const f32x2* __restrict__ pos, int ch, int b0) {
+  const int c = ch * kCondChunk + (int)(threadIdx.x & 63);
+  const int cs = c < p.Nc ? c : 0;  // token 0 exists whenever this runs; masked by the test
+  TokenPos tp;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const f32x2* pc = pos + (int64_t)min(b0 + kb, p.B - 1) * 3 * p.rows + p.N + cs;
+    tp.x[kb][0] = pc[0];
+    tp.x[kb][1] = pc[p.rows];
+    tp.x[kb][2] = pc[2 * (int64_t)p.rows];
+  }
+  return tp;
+}
+
+// Keep bits of chunk ch (one wave) for the tile whose extent (B * 3 planes
+// of [min start, max end)) is ext; lane l tests token ch * kCondChunk + l,
+// its positions for batch elements 0 and 1 already in tp.  A token is kept
+// when, for some batch element, its interval overlaps the extent on all
+// three axes (half-open) or its time start is negative (TDP docs, "Shared
+// negative (reference) positions"), on the positions as given.
+__device__ uint64_t chunk_keep_mask(const PlanDev& p, const f32x2* __restrict__ pos, const float2* ext, int ch,
+                                    TokenPos tp) {
+  const int c = ch * kCondChunk + (int)(threadIdx.x & 63);
+  bool keep = false;
+  for (int b0 = 0; b0 < p.B; b0 += 2) {
+    if (b0 > 0) tp = load_token_pos(p, pos, ch, b0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float2* e = ext + min(b0 + kb, p.B - 1) * 3;
+      const f32x2* x = tp.x[kb];
+      const bool inside = x[0].x < e[0].y && x[0].y > e[0].x && x[1].x < e[1].y && x[1].y > e[1].x &&
+                          x[2].x < e[2].y && x[2].y > e[2].x;
+      keep = keep || inside || x[0].x < 0.0f;
+    }
+  }
+  return __ballot(keep && c < p.Nc);
+}
+
+// Kept tokens of the tile in chunks 0..ch-1 (ch >= 1; one wave), from those
+// chunks' flags, the nearest 64 per read: aggregates add up to the first
+// inclusive prefix.  A chunk whose word is still 0 after a.lookback_polls
+// reads is counted here from its tokens, so no wave depends on the order in
+// which workgroups start.
+__device__ int lookback(const PlanDev& p, const ExtractArgs& a, uint32_t* flags, const float2* ext, int ch) {
+  const int lane = threadIdx.x & 63;
+  int before = 0, j = ch - 1, polls = 0;
+  while (true) {
+    const int jj = j - lane;
+    const uint32_t f = jj >= 0 ? flag_read(flags + jj) : kFlagPrefix;  // before chunk 0: a prefix of 0
+    const uint64_t pre = __ballot((f & kFlagPrefix) != 0);
+    const uint64_t wait = __ballot(f == 0);
+    const int first_pre = pre ? (int)__builtin_ctzll(pre) : 64;
+    const int first_wait = wait ? (int)__builtin_ctzll(wait) : 64;
+    const int n = min(first_pre + 1, first_wait);  // lanes [0, n) are counted now
+    before += wave_sum_int(lane < n ? (int)(f & kFlagCount) : 0);
+    if (first_pre < first_wait) return before;
+    j -= n;  // chunk j is the first one not counted yet
+    if (n > 0) polls = 0;
+    if (n == 64) continue;
+    if (++polls > a.lookback_polls) {  // chunk j has not published: count it here
+      before += __popcll(chunk_keep_mask(p, a.pos, ext, j, load_token_pos(p, a.pos, j, 0)));
+      --j;
+      polls = 0;
+    } else {
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+}
+
+// Kept row jj (< n) of batch element b and vector vv for flat index e of
+// the (b, kept j, vector) copy order.
+struct KeptVec {
+  int b, jj, vv;
+};
+__device__ inline KeptVec kept_vec(const PlanDev& p, const FastDiv& by_n, int n, int e) {
+  KeptVec k;
+  const int row = (int)fastdiv((uint32_t)e, p.by_vin);
+  k.vv = e - row * p.vin;
+  k.b = (int)fastdiv((uint32_t)row, by_n);
+  k.jj = row - k.b * n;
+  return k;
+}
+
+struct CondShared {
+  uint64_t mask;        // keep bits of the chunk
+  int direct[kWaves];   // kept tokens of the chunks each wave counted
+  int before;           // kept tokens of the tile before the chunk
+};
+
+// Selection workgroup (Nc > 0): chunk ch of the conditioning tokens
+// against tile t.  The tile's kept tokens before the chunk: those of the
+// kDirectChunks chunks before it are counted here from their tokens (tested
+// in the same pass as the chunk's own), those of earlier chunks come from
+// their flags by look-back (wave 0), so with up to kDirectChunks + 1 chunks
+// per tile no workgroup waits on another.  When the chunk's rows of every
+// batch element fit one round of loads (B * kCondChunk * V <= kBlock *
+// kCopyBatch), every token's latent vectors and positions are loaded with
+// the extent, before the test, and only the kept ones stored: one round
+// trip for the whole workgroup (every tile re-reads the chunk, mostly from
+// cache).  Then cond_row (every tile: k counts the tiles of all ranks),
+// cond_k, and for a held tile the index entries, the rows, the shifted
+// positions and, from the last chunk, the tile's count.
+template <bool R>
+__device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondShared& sm, float2* ext, int t,
+                                   int ch) {
+  constexpr int kPer = (kDirectChunks + 1 + kWaves - 1) / kWaves;  // chunks per wave
+  constexpr int kPosPer = (kCondChunk * 6 + kBlock - 1) / kBlock;   // position pairs per thread, B <= 2
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* flags = ws_flags(p, a) + (int64_t)t * p.n_chunks;
+  const bool publish = p.n_chunks > kDirectChunks + 1;  // some workgroup reads flags
+  const int j0 = max(0, ch - kDirectChunks);            // first chunk tested here
+  const bool held_t = held<R>(p, t);
+  const int V = p.vin;
+  const int c0 = p.N + ch * kCondChunk;
+  const int ntok = min(kCondChunk, p.Nc - ch * kCondChunk);
+  // (b, token j, vector) of the whole chunk, token-minor over vectors
+  const int all_vec = p.B * kCondChunk * V;
+  const bool early = held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
+  u32x4 v[kCopyBatch];
+  f32x2 w[kPosPer];
+  if (early) {
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = min(q * kBlock + tid, all_vec - 1);
+      const int row = (int)fastdiv((uint32_t)e, p.by_vin), vv = e - row * V;
+      const int b = row / kCondChunk, j = min(row - b * kCondChunk, ntok - 1);
+      v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + c0 + j) * V + vv);
+    }
+#pragma unroll
+    for (int q = 0; q < kPosPer; ++q) {
+      const int e = min(q * kBlock + tid, p.B * 3 * kCondChunk - 1);
+      const int bd = e / kCondChunk, j = min(e - bd * kCondChunk, ntok - 1);
+      w[q] = a.pos[(int64_t)bd * p.rows + c0 + j];
+    }
+  }
+  // chunks j0..ch: wave w takes j0 + w, j0 + w + 4, ...; their positions
+  // are in flight while the extent is combined
+  TokenPos tp[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) tp[i] = load_token_pos(p, a.pos, min(j0 + wave + i * kWaves, ch), 0);
+  combine_extent(p, a, t, ext);
+  __syncthreads();
+  int direct = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = j0 + wave + i * kWaves;
+    if (j <= ch) {  // wave-uniform
+      const uint64_t m = chunk_keep_mask(p, a.pos, ext, j, tp[i]);
+      if (j < ch) {
+        direct += __popcll(m);
+      } else if (lane == 0) {
+        sm.mask = m;
+        if (publish && j0 > 0) flag_publish(flags + ch, kFlagAgg | (uint32_t)__popcll(m));
       }
     }
   }
-  // thread j copies kept token j on every (batch, axis) plane
-  constexpr int kPlanes = 6;
-  const int cj = j < n_kept ? sm.sel.kept_c[j] : 0;  // token 0 exists whenever this runs
-  for (int bd0 = 0; bd0 < p.B * 3; bd0 += kPlanes) {  // bd = b * 3 + d
-    f32x2 v[kPlanes];
-    float o[kPlanes];
+  if (lane == 0) sm.direct[wave] = direct;
+  __syncthreads();
+  const uint64_t mask = sm.mask;
+  const int n = __popcll(mask);
+  const TileBox tb = tile_box<R>(p, t);
+  const bool copy = held_t && n > 0 && !early;  // the copy after the test
+  const FastDiv by_n = make_fastdiv((uint32_t)(n > 0 ? n : 1));
+  const int total = p.B * n * V;
+  if (copy) {
 #pragma unroll
-    for (int q = 0; q < kPlanes; ++q) {
-      const int bd = min(bd0 + q, p.B * 3 - 1);
-      v[q] = a.pos[(int64_t)bd * p.rows + p.N + cj];
-      o[q] = p.normalize ? ws_ext(p, a)[(int64_t)t * p.B * 3 + bd].x : 0.0f;
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const KeptVec k = kept_vec(p, by_n, n, min(q * kBlock + tid, total - 1));
+      v[q] = ld_nt(a.latent + ((int64_t)k.b * p.rows + c0 + nth_set_bit(mask, k.jj)) * V + k.vv);
+    }
+  }
+  int before = sm.direct[0] + sm.direct[1] + sm.direct[2] + sm.direct[3];
+  if (j0 > 0) {  // workgroup-uniform
+    if (wave == 0) {
+      before += lookback(p, a, flags, ext, j0);
+      if (lane == 0) {
+        flag_publish(flags + ch, kFlagPrefix | (uint32_t)(before + n));
+        sm.before = before;
+      }
+    }
+    __syncthreads();
+    before = sm.before;
+  } else if (publish && tid == 0) {
+    flag_publish(flags + ch, kFlagPrefix | (uint32_t)(before + n));
+  }
+  const int first = tb.s.gen + before;  // slot row of the chunk's first kept token
+  if (tid < kCondChunk) {
+    const int c = ch * kCondChunk + tid;
+    const bool keep = (mask >> tid) & 1ull;
+    const int row = first + __popcll(mask & ((1ull << tid) - 1ull));
+    if (c < p.Nc) a.cond_row[(int64_t)t * p.Nc + c] = keep ? row : -1;
+    if (keep) atomicAdd(a.cond_k + c, 1);
+    if (keep && held_t) a.tile_index[tb.s.index_base + row] = p.N + c;
+  }
+  if (held_t && ch == p.n_chunks - 1 && tid == 0)
+    a.tile_count[R ? (int)fastdiv((uint32_t)t, p.by_world) : t] = first + n;
+  if (early) {  // the kept ones of the vectors and positions already loaded
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = q * kBlock + tid;
+      const int row = (int)fastdiv((uint32_t)e, p.by_vin), vv = e - row * V;
+      const int b = row / kCondChunk, j = row - b * kCondChunk;
+      if (e < all_vec && ((mask >> j) & 1ull)) {
+        const int r = __popcll(mask & ((1ull << j) - 1ull));
+        st_nt(a.tile_lat + (tb.s.row_base + (int64_t)b * tb.s.cap + first + r) * V + vv, v[q]);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < kPlanes; ++q) {
-      const int bd = bd0 + q;
-      if (bd < p.B * 3 && j < n_kept) {
-        const int b = bd / 3, d = bd - b * 3;
-        st_nt(a.tile_pos + 3 * tb.s.row_base + ((int64_t)b * 3 + d) * tb.s.cap + tb.s.gen + base + j, v[q] - o[q]);
+    for (int q = 0; q < kPosPer; ++q) {
+      const int e = q * kBlock + tid;
+      const int bd = e / kCondChunk, j = e - bd * kCondChunk;
+      if (e < p.B * 3 * kCondChunk && ((mask >> j) & 1ull)) {
+        const int r = __popcll(mask & ((1ull << j) - 1ull));
+        const float o = p.normalize ? ext[bd].x : 0.0f;
+        st_nt(a.tile_pos + 3 * tb.s.row_base + (int64_t)bd * tb.s.cap + first + r, w[q] - o);
+      }
+    }
+    return;
+  }
+  if (!copy) return;
+  for (int e0 = 0; e0 < total; e0 += kBlock * kCopyBatch) {
+    if (e0 > 0) {
+#pragma unroll
+      for (int q = 0; q < kCopyBatch; ++q) {
+        const KeptVec k = kept_vec(p, by_n, n, min(e0 + q * kBlock + tid, total - 1));
+        v[q] = ld_nt(a.latent + ((int64_t)k.b * p.rows + c0 + nth_set_bit(mask, k.jj)) * V + k.vv);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = e0 + q * kBlock + tid;
+      if (e < total) {
+        const KeptVec k = kept_vec(p, by_n, n, e);
+        st_nt(a.tile_lat + (tb.s.row_base + (int64_t)k.b * tb.s.cap + first + k.jj) * V + k.vv, v[q]);
+      }
+    }
+  }
+  const int ptotal = p.B * 3 * n;  // (plane b * 3 + d, kept j)
+  for (int e0 = 0; e0 < ptotal; e0 += kBlock * kCopyBatch) {
+    f32x2 y[kCopyBatch];
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = min(e0 + q * kBlock + tid, ptotal - 1);
+      const int bd = (int)fastdiv((uint32_t)e, by_n), jj = e - bd * n;
+      y[q] = a.pos[(int64_t)bd * p.rows + c0 + nth_set_bit(mask, jj)];
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = e0 + q * kBlock + tid;
+      if (e < ptotal) {
+        const int bd = (int)fastdiv((uint32_t)e, by_n), jj = e - bd * n;
+        const float o = p.normalize ? ext[bd].x : 0.0f;
+        st_nt(a.tile_pos + 3 * tb.s.row_base + (int64_t)bd * tb.s.cap + first + jj, y[q] - o);
       }
     }
   }
@@ -495,9 +704,9 @@ __device__ void extract_positions(const PlanDev& p, const ExtractArgs& a, Extrac
   }
 }
 
-// Positions workgroup with the shift `off` already known (Nc > 0: the
-// extent the keep launch stored): it only copies its part of the plane
-// (shifted pairs and source indices).
+// Positions workgroup with the shift `off` already known (Nc > 0: from the
+// tile's extent parts): it only copies its part of the plane (shifted pairs
+// and source indices).
 template <bool R>
 __device__ void extract_positions_copy(const PlanDev& p, const ExtractArgs& a, int t, int b, int d, int part,
                                        float off) {
@@ -622,37 +831,34 @@ __device__ inline void xcd_group(int bid, int items, int parts, int& item, int& 
 }
 
 // ---------------------------------------------------------------------------
-// Conditioning selection launch (plans with Nc > 0)
+// Conditioning tokens: the extent launch (plans with Nc > 0)
 // ---------------------------------------------------------------------------
 
-struct SelectArgs {
-  const f32x2* pos;  // (B, 3, rows) [start, end)
-  float2* part;      // workspace tables (layout in WsLayout)
-  float2* ext;
-  uint32_t* keep;
-  int32_t* cnt;
-  int32_t* tot;
-};
-
-// Extent launch: workgroup (tile t, part q) reduces [min start, max end)
-// over rows [q * ext_rows, (q + 1) * ext_rows) of tile t's generated tokens
-// on every (batch, axis) plane, NP planes per pass with all of a pass's
-// loads in flight and one exchange for all of them.  Part 0 also zeroes the
-// tile's superchunk totals, which the keep launch adds to.  Every tile is
-// reduced, in rank plans too, since k counts the tiles of all ranks.
+// Extent launch (Nc > 0), ahead of the selection launch: workgroup (tile
+// t, part q) reduces [min start, max end) over rows [q * ext_rows, (q + 1)
+// * ext_rows) of tile t's generated tokens on every (batch, axis) plane, NP
+// planes per pass with all of a pass's loads in flight and one exchange for
+// all of them.  It also clears what the selection launch counts into: part
+// 0 the tile's look-back flags, and the workgroups together cond_k.  Every
+// tile is reduced, in rank plans too, since k counts the tiles of all
+// ranks.
 template <int NP>
-__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const SelectArgs a) {
+__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const ExtractArgs a) {
   __shared__ float2 red[kWaves][NP];
+  const int bid = blockIdx.x;
   int t, q;
-  xcd_group(blockIdx.x, p.T, p.ext_parts, t, q);  // the parts of a tile share an L2
+  xcd_group(bid, p.T, p.ext_parts, t, q);  // the parts of a tile share an L2
   const TileBox tb = tile_box<false>(p, t);
   const int r_begin = min(tb.s.gen, q * p.ext_rows), r_end = min(tb.s.gen, r_begin + p.ext_rows);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int planes = p.B * 3;
   constexpr int RP = kSelLoads / NP;  // rows per thread per pass
-  if (q == 0)
-    for (int i = tid; i < p.n_super; i += kBlock) a.tot[(int64_t)t * p.n_super + i] = 0;
-  float2* out = a.part + ((int64_t)t * p.ext_parts + q) * planes;
+  if (q == 0) {
+    uint32_t* flags = ws_flags(p, a) + (int64_t)t * p.n_chunks;
+    for (int i = tid; i < p.n_chunks; i += kBlock) flags[i] = 0u;
+  }
+  for (int c = bid * kBlock + tid; c < p.Nc; c += (int)gridDim.x * kBlock) a.cond_k[c] = 0;
+  float2* out = ws_part_w(p, a) + ((int64_t)t * p.ext_parts + q) * planes;
   // (a repeated row or plane leaves a minimum and a maximum as they are;
   // an empty part stores +inf and -inf, which the combine ignores)
   for (int e0 = 0; e0 < planes; e0 += NP) {
@@ -701,111 +907,70 @@ __global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const S
   }
 }
 
-// Keep launch: workgroup (tile t, chunk k), one token per thread.  The
-// tile's extent is the combination of its parts (chunk 0 stores it for the
-// extract launch: normalization offsets and the kept rows' shift).  A token
-// is kept when, for some batch element, its interval overlaps the extent on
-// all three axes (half-open) or its time start is negative (TDP docs,
-// "Shared negative (reference) positions"), on the positions as given.
-// Writes the chunk's keep bits and count and adds the count to its
-// superchunk's total.
-__global__ __launch_bounds__(kBlock) void keep_kernel(const PlanDev p, const SelectArgs a) {
-  extern __shared__ float2 ext_s[];  // (B * 3) extent of tile t
-  __shared__ int wave_kept[kWaves];
-  const int t = blockIdx.x / p.n_chunks, k = blockIdx.x - t * p.n_chunks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int planes = p.B * 3;
-  const int c = k * kCondChunk + tid;
-  const int cs = c < p.Nc ? c : 0;  // token 0 exists whenever this runs; masked below
-  // positions of the token for two batch elements (an odd batch repeats the
-  // last one: OR does not mind), issued before the extent is combined
-  auto load_token = [&](int b0, f32x2 (&x)[2][3]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f32x2* pc = a.pos + (int64_t)min(b0 + kb, p.B - 1) * 3 * p.rows + p.N + cs;
-      x[kb][0] = pc[0];
-      x[kb][1] = pc[p.rows];
-      x[kb][2] = pc[2 * (int64_t)p.rows];
-    }
-  };
-  f32x2 x[2][3];
-  load_token(0, x);
-  const float2* parts = a.part + (int64_t)t * p.ext_parts * planes;
-  for (int e = tid; e < planes; e += kBlock) {
-    float2 m = parts[e];
-    for (int q = 1; q < p.ext_parts; ++q) {
-      const float2 y = parts[(int64_t)q * planes + e];
-      m.x = fminf(m.x, y.x);
-      m.y = fmaxf(m.y, y.y);
-    }
-    ext_s[e] = m;
-    if (k == 0) a.ext[(int64_t)t * planes + e] = m;
-  }
-  __syncthreads();
-  bool keep = false;
-  for (int b0 = 0; b0 < p.B; b0 += 2) {
-    if (b0 > 0) load_token(b0, x);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float2* e = ext_s + min(b0 + kb, p.B - 1) * 3;
-      const bool inside = x[kb][0].x < e[0].y && x[kb][0].y > e[0].x && x[kb][1].x < e[1].y &&
-                          x[kb][1].y > e[1].x && x[kb][2].x < e[2].y && x[kb][2].y > e[2].x;
-      keep = keep || inside || x[kb][0].x < 0.0f;
-    }
-  }
-  // keep bits: the 64 tokens of a wave are two words of the chunk
-  const uint64_t mask = __ballot(keep && c < p.Nc);
-  if (lane == 0) {
-    uint32_t* words = a.keep + ((int64_t)t * p.n_chunks + k) * kKeepWords + 2 * wave;
-    words[0] = (uint32_t)mask;
-    words[1] = (uint32_t)(mask >> 32);
-    wave_kept[wave] = __popcll(mask);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) n += wave_kept[w];
-    a.cnt[(int64_t)t * p.n_chunks + k] = n;
-    atomicAdd(a.tot + (int64_t)t * p.n_super + k / kChunksPerSuper, n);
-  }
+// Every position workgroup of a launch: (tile, batch, axis, part) of `bid`.
+struct PosWork {
+  int t, slot, b, d, part;
+};
+template <bool R>
+__device__ inline PosWork pos_work(const PlanDev& p, const ExtractArgs& a, int bid) {
+  // every part of a plane reads the whole plane: keep them on one XCD
+  PosWork w;
+  int plane;
+  xcd_group(bid, a.n_pos / a.pos_parts, a.pos_parts, plane, w.part);
+  w.d = plane % 3;
+  w.b = (plane / 3) % p.B;
+  w.slot = plane / (3 * p.B);
+  w.t = R ? p.rank + w.slot * p.world : w.slot;
+  return w;
 }
 
-// One launch, three kinds of workgroups (independent, disjoint outputs):
-//   [0, n_sel)                 conditioning tokens per (tile, quarter chunk) (Nc > 0);
-//   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part);
-//   [.., + latent blocks)      generated latent rows per (line, chunk).
-// Conditioning and position workgroups are few and run a longer chain of
-// dependent loads, so they come first and run under the latent copy.
-// Rank plans: conditioning tokens over every tile, positions over the held
-// tiles.
+// Extract without conditioning tokens: one launch, two kinds of
+// workgroups that share nothing:
+//   [0, n_pos)                 positions per (tile, batch, axis, part);
+//   [n_pos, + latent blocks)   generated latent rows per (line, chunk).
+// Position workgroups are few and run a longer chain of dependent loads,
+// so they come first and run under the latent copy.  Rank plans: the held
+// tiles only.
 template <bool R>
 __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const ExtractArgs a) {
   __shared__ ExtractShared sm;
-  int bid = blockIdx.x;
-  if (bid < a.n_sel) {
-    const int per_tile = p.n_chunks * kCopyParts;
-    const int t = bid / per_tile, rem = bid - t * per_tile;
-    extract_cond_chunk<R>(p, a, sm, t, rem / kCopyParts, rem % kCopyParts);
-    return;
-  }
-  bid -= a.n_sel;
+  const int bid = blockIdx.x;
   if (bid < a.n_pos) {
-    // every part of a plane reads the whole plane: keep them on one XCD
-    int plane, part;
-    xcd_group(bid, a.n_pos / a.pos_parts, a.pos_parts, plane, part);
-    const int d = plane % 3;
-    const int b = (plane / 3) % p.B;
-    const int slot = plane / (3 * p.B);
-    const int t = R ? p.rank + slot * p.world : slot;
-    if (a.ws)
-      extract_positions_copy<R>(p, a, t, b, d, part,
-                                p.normalize ? ws_ext(p, a)[((int64_t)t * p.B + b) * 3 + d].x : 0.0f);
-    else
-      extract_positions<R>(p, a, sm, t, slot, b, d, part);
+    const PosWork w = pos_work<R>(p, a, bid);
+    extract_positions<R>(p, a, sm, w.t, w.slot, w.b, w.d, w.part);
     return;
   }
   extract_latent<R>(p, a, bid - a.n_pos);
+}
+
+// Extract with conditioning tokens, after the extent launch: one launch,
+// three kinds of workgroups:
+//   [0, n_sel)                 one per (tile, chunk of kCondChunk tokens),
+//                              tile-major: selection and kept rows;
+//   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part),
+//                              shifted by the tile's extent parts;
+//   [.., + latent blocks)      generated latent rows per (line, chunk).
+// Only wave 0 of a selection workgroup waits on others (the flags of the
+// tile's earlier chunks), never without bound.  Rank plans: selection over
+// every tile (k counts the tiles of all ranks), the rest for the held
+// tiles.
+template <bool R>
+__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
+  const int bid = blockIdx.x;
+  if (bid < a.n_sel) {
+    extern __shared__ float2 ext_s[];  // dynamic: at least B * 3 (the launch asks for it)
+    __shared__ CondShared cs;
+    const int t = bid / p.n_chunks;
+    extract_cond_chunk<R>(p, a, cs, ext_s, t, bid - t * p.n_chunks);
+    return;
+  }
+  if (bid - a.n_sel < a.n_pos) {
+    const PosWork w = pos_work<R>(p, a, bid - a.n_sel);
+    extract_positions_copy<R>(p, a, w.t, w.b, w.d, w.part,
+                              p.normalize ? tile_min_start(p, a, w.t, w.b * 3 + w.d) : 0.0f);
+    return;
+  }
+  extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -1342,9 +1507,13 @@ __global__ __launch_bounds__(kBlock) void blend_finish_kernel(const f32x4* __res
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
-// Enqueue extract: with conditioning tokens, the extent and keep launches
-// first (their tables go to `ws`), then the extract launch.  Arguments are
-// valid.
+// Reads of an unpublished look-back flag before a selection wave counts the
+// chunk itself (process-wide; tdp_set_lookback_polls).
+std::atomic<int> g_lookback_polls{kLookbackPolls};
+
+// Enqueue extract: the gather (with conditioning tokens, the extent parts
+// too, into `ws`), then with conditioning tokens the selection launch.
+// Arguments are valid.
 int launch_extract(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
                    int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws,
                    hipStream_t s, const char* who) {
@@ -1357,52 +1526,55 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
   a.tile_count = tile_count;
   a.cond_row = cond_row;
   a.cond_k = cond_k;
-  a.ws = nullptr;
+  a.ws = p.Nc > 0 ? ws : nullptr;
+  a.n_ext = p.Nc > 0 ? p.T * p.ext_parts : 0;
+  a.n_sel = p.Nc > 0 ? p.T * p.n_chunks : 0;
+  a.lookback_polls = g_lookback_polls.load(std::memory_order_relaxed);
   const DeviceShape ds = device_shape();
-  if (p.Nc > 0) {
-    SelectArgs sa;
-    sa.pos = a.pos;
-    const WsLayout wl = ws_layout(p);
-    sa.part = reinterpret_cast<float2*>(ws + wl.part);
-    sa.ext = reinterpret_cast<float2*>(ws + wl.ext);
-    sa.keep = reinterpret_cast<uint32_t*>(ws + wl.keep);
-    sa.cnt = reinterpret_cast<int32_t*>(ws + wl.cnt);
-    sa.tot = reinterpret_cast<int32_t*>(ws + wl.tot);
-    a.ws = ws;
-    const dim3 egrid((unsigned)(p.T * p.ext_parts)), block(kBlock);
-    if (p.B == 1)
-      hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, sa);
-    else
-      hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, sa);
-    hipLaunchKernelGGL(keep_kernel, dim3((unsigned)(p.T * p.n_chunks)), block, (size_t)p.B * 3 * sizeof(float2), s, p,
-                       sa);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
-  }
-  a.n_sel = p.Nc > 0 ? p.T * p.n_chunks * kCopyParts : 0;
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
+  const dim3 block(kBlock);
+  if (p.Nc > 0) {
+    // extent launch, then selection with the positions (copies: the shift
+    // is known) and the latent rows, 3 workgroups per CU
+    const dim3 egrid((unsigned)a.n_ext);
+    if (p.B == 1)
+      hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, a);
+    else
+      hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: extent launch failed: %s", who, hipGetErrorString(e));
+    a.pos_one_pass = 0;
+    a.pos_parts = p.pos_parts;
+    a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+    const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat));
+    // the tile's extent, and at most kExtractWgsPerCu workgroups per CU
+    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2), kExtractWgsPerCu);
+    if (p.world > 1)
+      hipLaunchKernelGGL(select_kernel<true>, sgrid, block, lds, s, p, a);
+    else
+      hipLaunchKernelGGL(select_kernel<false>, sgrid, block, lds, s, p, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
+    return TDP_OK;
+  }
   // More than eight latent workgroups per compute unit: the latent copy
   // sets the length (3 per CU, positions in one pass); otherwise the
-  // position chains do (2 per CU, parts of at most 1024 rows).  With
-  // conditioning tokens the positions only copy (the shift is known) and
-  // the compaction workgroups share the launch with the latent copy (3 per
-  // CU).
+  // position chains do (2 per CU, parts of at most 1024 rows).
   const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
   a.pos_one_pass = latent_bound ? 1 : 0;
   a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
   a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
-  const dim3 grid(a.n_sel + a.n_pos + n_lat);
-  if (grid.x == 0) return TDP_OK;  // a rank without tiles and no conditioning: nothing to write
-  const size_t lds = capped_lds(ds, 0, latent_bound || p.Nc > 0 ? kExtractWgsPerCu : kExtractWgsPerCuChain);
+  const dim3 grid(a.n_pos + n_lat);
+  if (grid.x == 0) return TDP_OK;  // a rank without tiles: nothing to write
+  const size_t lds = capped_lds(ds, 0, latent_bound ? kExtractWgsPerCu : kExtractWgsPerCuChain);
   if (p.world > 1)
-    hipLaunchKernelGGL(extract_kernel<true>, grid, dim3(kBlock), lds, s, p, a);
+    hipLaunchKernelGGL(extract_kernel<true>, grid, block, lds, s, p, a);
   else
-    hipLaunchKernelGGL(extract_kernel<false>, grid, dim3(kBlock), lds, s, p, a);
+    hipLaunchKernelGGL(extract_kernel<false>, grid, block, lds, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
   return TDP_OK;
 }
-
 
 // Checks tdp_extract and tdp_extract_noalloc share (the workspace aside).
 int check_extract(const tdp_plan* plan, const void* latent, const float* pos, const void* tile_lat,
@@ -1423,7 +1595,6 @@ int check_extract(const tdp_plan* plan, const void* latent, const float* pos, co
     return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
   return TDP_OK;
 }
-
 
 }  // namespace
 }  // namespace tdp
@@ -1482,6 +1653,12 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos, void
   if (!aligned(workspace, 16)) return fail(TDP_EINVAL, "tdp_extract: workspace must be 16-byte aligned");
   return launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                         static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream), "tdp_extract");
+}
+
+int tdp_set_lookback_polls(int32_t polls) {
+  if (polls < 0) return fail(TDP_EINVAL, "tdp_set_lookback_polls: polls must be >= 0 (got %d)", polls);
+  g_lookback_polls.store(polls, std::memory_order_relaxed);
+  return TDP_OK;
 }
 
 int tdp_extract_noalloc(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat,

@@ -237,7 +237,6 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
   // plans included, since k counts the tiles of all ranks).
   if (c.num_cond > 0) {
     dev.n_chunks = (c.num_cond + kCondChunk - 1) / kCondChunk;
-    dev.n_super = (dev.n_chunks + kChunksPerSuper - 1) / kChunksPerSuper;
     // extent parts: about kExtPartBytes of positions (B * 3 planes of 8-byte
     // pairs per row) each, at least one row per part
     const int64_t row_bytes_pos = (int64_t)c.batch * 3 * 8;

@@ -109,14 +109,13 @@ TDP_HD Covers split_covers(const AxisSplit& a, int x) {
 // Launch shape shared by the host planner and the kernels.
 constexpr int kThreads = 256;   // threads per workgroup
 constexpr int kPosOwnRows = 16;  // position rows per thread one extract position workgroup holds
-// Conditioning-token selection (plans with Nc > 0) runs in two launches
-// ahead of the extract launch, every workgroup small, since one compute unit
-// reads only a few tens of GB/s: partial extents of each tile (parts of
-// about kExtPartBytes of positions), then the keep test of each (tile, chunk
-// of kCondChunk tokens).  The extract launch compacts and copies per chunk.
-constexpr int kCondChunk = kThreads;           // 256: one token per thread
-constexpr int kKeepWords = kCondChunk / 32;     // keep-bit words per chunk
-constexpr int kChunksPerSuper = 16;            // chunks whose counts one total sums
+// Conditioning-token selection (plans with Nc > 0): an extent launch ahead
+// of the extract launch reduces partial extents of each tile (parts of about
+// kExtPartBytes of positions, every workgroup small, since one compute unit
+// reads only a few tens of GB/s); in the extract launch each wave then tests
+// one chunk of kCondChunk tokens against one tile and finds the tile's kept
+// tokens before its chunk by look-back over the earlier chunks' flags.
+constexpr int kCondChunk = 64;                 // one token per lane of a wave
 constexpr int kExtPartBytes = 24 * 1024;       // position bytes one extent workgroup reads
 constexpr int kMaxExtParts = 64;              // extent parts per tile at most
 
@@ -159,32 +158,27 @@ struct PlanDev {
   int32_t box_f0, box_nf, box_h0, box_nh, box_c0, box_nc;
   int32_t box_w0, box_nw;  // the same box on width, in cells
   FastDiv by_box_h, by_box_fh, by_box_c;
-  // Conditioning selection (Nc > 0): chunks of kCondChunk tokens, groups of
-  // kChunksPerSuper chunks ("superchunks"), extent parts of ext_rows rows
-  // per tile (WsLayout places their tables).
-  int32_t n_chunks, n_super, ext_parts, ext_rows;
+  // Conditioning selection (Nc > 0): chunks of kCondChunk tokens, extent
+  // parts of ext_rows rows per tile (WsLayout places their tables).
+  int32_t n_chunks, ext_parts, ext_rows;
 };
 
 // Workspace of the conditioning selection: byte offsets of its tables, each
 // 256-byte aligned (every size is 0 when Nc == 0):
-//   part (T, ext_parts, B, 3) float2  [min start, max end) over one part of a tile's rows
-//   ext  (T, B, 3) float2  the same over the whole tile (its extent)
-//   keep (T, n_chunks, kKeepWords) uint32  keep bit of token c: word c / 32, bit c % 32
-//   cnt  (T, n_chunks) int32  kept tokens of each chunk
-//   tot  (T, n_super) int32   kept tokens of each superchunk
+//   part  (T, ext_parts, B, 3) float2  [min start, max end) over one part of a tile's rows
+//   flags (T, n_chunks) uint32  look-back word of each (tile, chunk): 0 until
+//         published, then a status bit and the chunk's kept count or the
+//         tile's kept count up to and including the chunk
 // Derived from the plan in closed form, so kernels need no extra arguments.
 struct WsLayout {
-  int64_t part, ext, keep, cnt, tot, bytes;
+  int64_t part, flags, bytes;
 };
 TDP_HD int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 TDP_HD WsLayout ws_layout(const PlanDev& p) {
   WsLayout w;
   w.part = 0;
-  w.ext = align256((int64_t)p.T * p.ext_parts * p.B * 3 * 8);
-  w.keep = w.ext + align256((int64_t)p.T * p.B * 3 * 8);
-  w.cnt = w.keep + align256((int64_t)p.T * p.n_chunks * kKeepWords * 4);
-  w.tot = w.cnt + align256((int64_t)p.T * p.n_chunks * 4);
-  w.bytes = p.Nc > 0 ? w.tot + align256((int64_t)p.T * p.n_super * 4) : 0;
+  w.flags = align256((int64_t)p.T * p.ext_parts * p.B * 3 * 8);
+  w.bytes = p.Nc > 0 ? w.flags + align256((int64_t)p.T * p.n_chunks * 4) : 0;
   return w;
 }
 

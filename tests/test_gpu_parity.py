@@ -170,6 +170,11 @@ EDGE = {
     # a superchunk boundary with a one-token last chunk, odd batch
     "cond_4097_batch3": dict(shape=(3, 10, 14), tiling=((2, 1), (2, 2), (2, 3)), batch=3, num_cond=4097,
                              seed=12, random_pos=True),
+    # rows too wide to load a whole chunk at once (512 channels): kept rows
+    # are copied after the test; and with fp32 rows, batch 2
+    "cond_wide_rows": dict(shape=(2, 6, 20), tiling=((1, 0), (2, 2), (2, 3)), channels=512, num_cond=300, seed=13),
+    "cond_f32_batch2": dict(shape=(2, 8, 12), tiling=((1, 0), (2, 2), (2, 3)), batch=2, channels=36, dtype="f32",
+                            num_cond=150, seed=14, random_pos=True),
     "batch64": dict(shape=(2, 4, 6), tiling=((1, 0), (2, 1), (2, 2)), batch=64, channels=16, seed=8),
     # more than eight latent workgroups per compute unit: one-pass position
     # workgroups (parts held in registers), width not a multiple of the
@@ -195,6 +200,23 @@ def test_edge_cases(case, cuda):
     ref, mag = O.blend(ys, ex, wl.shape, wl.tiling, wl.num_cond)
     out = gpu_blend(plan, buf, bufs["cond_row"], bufs["cond_k"], cuda, case)
     check_blend(out, ref, mag, tdp.TDP_F32)
+
+
+@pytest.mark.parametrize("polls", [0, 1])
+@pytest.mark.parametrize("case", ["cond_16k", "many_cond", "cond_4097_batch3", "cond_random_pos"])
+def test_lookback_counts_unpublished_chunks_itself(case, polls, cuda):
+    """With a tiny poll limit a selection wave counts an earlier chunk from
+    its tokens whenever that chunk's flag is not yet published: the same
+    rows, counts and k as the oracle, bit for bit."""
+    kw = dict(EDGE[case])
+    wl, inp = _custom_case(**kw)
+    plan = plan_for(wl)
+    tdp.tdp_set_lookback_polls(polls)
+    try:
+        _, _, bufs = gpu_extract(plan, inp, cuda, f"{case} lookback polls={polls}")
+    finally:
+        tdp.tdp_set_lookback_polls(256)
+    check_extract(plan, bufs, oracle_extract(wl, inp), wl.num_cond)
 
 
 def test_cond_tokens_kept_by_no_tile(cuda):

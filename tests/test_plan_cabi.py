@@ -218,6 +218,14 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
 
 
 @pytest.mark.device_abi
+def test_lookback_polls_setting(lib):
+    assert lib.tdp_set_lookback_polls(-1) == tdp.TDP_EINVAL
+    assert "polls" in tdp.tdp_last_error()
+    for polls in (0, 1, 256):
+        tdp.tdp_set_lookback_polls(polls)
+
+
+@pytest.mark.device_abi
 def test_cond_k_and_workspace_arguments(lib):
     """With conditioning tokens, tdp_extract needs cond_row, cond_k and the
     workspace, and tdp_blend / tdp_blend_tile need cond_row and cond_k; null
@@ -227,7 +235,8 @@ def test_cond_k_and_workspace_arguments(lib):
     s = tdp.tdp_plan_sizes(plan)
     T = len(O.enumerate_tiles(wl.shape, wl.tiling))
     assert s.cond_k_ints == wl.num_cond
-    assert s.workspace_bytes >= T * wl.batch * 3 * 8 + T * wl.num_cond // 8 and s.workspace_bytes % 256 == 0
+    # at least one extent part per tile and one look-back word per (tile, 64 tokens)
+    assert s.workspace_bytes >= T * wl.batch * 3 * 8 + T * (-(-wl.num_cond // 64)) * 4 and s.workspace_bytes % 256 == 0
     assert tdp.tdp_plan_sizes(plan_for(WORKLOADS["4k"])).workspace_bytes == 0
     null = ctypes.c_void_p(None)
     al = ctypes.c_void_p(0x1000)

@@ -20,8 +20,8 @@ import overlap_tiling_trapezoidal_amd as tdp
 from harness import check_extract, note, plan_for, poisoned_buffers, to_device_latent
 from synth import WORKLOADS, Workload, make_inputs
 
-# (shape, tiling, batch, num_cond, seed): workspace of 15616 bytes, then 9472
-# (the conditioned workload), then none
+# workspace of 6912 bytes (16484 tokens), then 6656 (the conditioned
+# workload), then none
 CALLS = [
     ("cond_16k", Workload("cond_16k", 2, 128, (2, 12, 20), ((1, 0), (2, 2), (3, 3)), num_cond=16484,
                           num_ref=4121, dtype="bf16", seed=11)),
