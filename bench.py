@@ -22,7 +22,10 @@ once, each output written once; overlap re-reads not credited), the
 fraction of the 8 TB/s HBM peak, a roofline entry for the dominant kernel,
 the CPU oracle's rate on the same workload, the same step measured on each
 of the five workloads (``workloads``) and what plain hand-written streaming
-kernels move on this GPU (``ceilings``, from libtdp_ceiling.so).
+kernels move on this GPU (``ceilings``, from libtdp_ceiling.so), also with
+the extract's and the blend's own read:write mix at their own sizes
+(``same_mix_ceilings``: a scatter writing each byte it reads twice, a
+gather reading two bytes per byte written; ``frac_of_same_mix``).
 
 Roofline: each operation is one kernel launch.  Its average duration comes
 from a CUDA-graph replay of K back-to-back launches (rotating buffer sets)
@@ -277,23 +280,48 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
 
 def ceiling_rates(torch, dev, nbytes=256 << 20, passes=12):
     """GB/s of plain hand-written streaming kernels (libtdp_ceiling.so):
-    copies with non-temporal or device-scope stores, a read, a write.  Each
-    pass uses a buffer pair the previous pass did not touch (1 GB of traffic
-    between two uses of a buffer)."""
+    copies with non-temporal or device-scope stores, a read, a write, a
+    gather (two reads per write) and a scatter (two writes per read).  Each
+    pass uses a buffer pair the previous pass did not touch (at least 1 GB
+    of traffic between two uses of a buffer)."""
     from overlap_tiling_trapezoidal_amd import ceiling
-    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(4)]
+    bufs = [torch.empty(2 * nbytes, dtype=torch.uint8, device=dev) for _ in range(4)]
     for b in bufs:
         b.fill_(1)
     sink = torch.empty(4096, dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream(dev)
-    out = {"bytes_per_buffer": nbytes}
+    out = {"bytes_per_pass": nbytes}
     for mode in ceiling.MODES:
         def run(i, mode=mode):
             ceiling.run(mode, bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4], sink, nbytes, stream)
         ms = graph_time_ms(torch, stream, run, passes)
-        moved = 2 * nbytes if mode.startswith("copy") else nbytes
-        out[mode + "_gbs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+        out[mode + "_gbs"] = round(ceiling.MOVED[mode] * nbytes / (ms * 1e-3) / 1e9, 1)
     del bufs
+    return out
+
+
+def same_mix_ceilings(torch, dev, extract_read, blend_write, sets=8, passes=32):
+    """The hand-written scatter and gather at the sizes of this workload's
+    extract (reads `extract_read` bytes, writes twice that) and blend
+    (writes `blend_write`, reads twice that), over `sets` rotating buffer
+    sets as the bench rotates its own: GB/s and microseconds per pass."""
+    from overlap_tiling_trapezoidal_amd import ceiling
+    sink = torch.empty(4096, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(dev)
+    out = {}
+    for op, mode, nb in (("extract", "scatter", extract_read), ("blend", "gather", blend_write)):
+        nb = max(8192, nb // 8192 * 8192)
+        small = [torch.ones(nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
+        large = [torch.ones(2 * nb, dtype=torch.uint8, device=dev) for _ in range(sets)]
+        src, dst = (small, large) if mode == "scatter" else (large, small)
+
+        def run(i, mode=mode, nb=nb, src=src, dst=dst):
+            ceiling.run(mode, src[i % sets], dst[i % sets], sink, nb, stream)
+        ms = graph_time_ms(torch, stream, run, passes)
+        moved = ceiling.MOVED[mode] * nb
+        out[op] = {"mode": mode, "bytes": moved, "us": round(ms * 1e3, 3),
+                   "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
+        del small, large, src, dst
     return out
 
 
@@ -501,6 +529,10 @@ def main():
     del src, dst
     ceilings = ceiling_rates(torch, dev)
     best_copy = max(ceilings["copy_nt_gbs"], ceilings["copy_device_scope_gbs"])
+    e_in_b = 2 if wl.dtype == "bf16" else 4
+    rows = wl.tokens + wl.num_cond
+    mix = same_mix_ceilings(torch, dev, wl.batch * rows * (wl.channels * e_in_b + 3 * 8),
+                            wl.batch * rows * wl.channels * e_in_b)
 
     # the same step on every workload (this run's own figures for its workload)
     table = {}
@@ -552,6 +584,11 @@ def main():
         "torch_copy_gbs": round(copy_gbs, 1),
         "ceilings": ceilings,
         "frac_of_best_copy": round(gbs / best_copy, 4),
+        "same_mix_ceilings": mix,
+        "frac_of_same_mix": {
+            "extract": round((ex_bytes / (ex_ms * 1e-3) / 1e9) / mix["extract"]["gbs"], 4),
+            "blend": round((bl_bytes / (bl_ms * 1e-3) / 1e9) / mix["blend"]["gbs"], 4),
+        },
         "target": "70% of the 8 TB/s peak on the 4K-class latent (5600 GB/s, 36.3 us per step)",
         "meets_target": bool(wl.name == "4k" and gbs >= 0.7 * HBM_PEAK_GBS),
         "workloads": table,

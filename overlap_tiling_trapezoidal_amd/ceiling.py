@@ -12,7 +12,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtdp_ceiling.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp_ceiling.h")
 
-MODES = {"copy_nt": 0, "copy_device_scope": 1, "read": 2, "write": 3}
+MODES = {"copy_nt": 0, "copy_device_scope": 1, "read": 2, "write": 3, "gather": 4, "scatter": 5}
+# bytes one pass moves, as a multiple of its `nbytes` argument
+MOVED = {"copy_nt": 2, "copy_device_scope": 2, "read": 1, "write": 1, "gather": 3, "scatter": 3}
 _lib = None
 
 

@@ -5,7 +5,10 @@
 //
 // Workgroups of 256 threads; thread i of workgroup g moves the 16-byte
 // vectors g * 512 + i and g * 512 + 256 + i (two loads in flight, then two
-// stores), so one wave instruction covers 1 KB contiguous.  Loads carry the
+// stores), so one wave instruction covers 1 KB contiguous.  Two mixed
+// modes match the read:write mixes of the tiled path: a gather (two reads
+// per write, the blend's mix) and a scatter (two writes per read, the
+// extract's), each over a second half of the larger buffer.  Loads carry the
 // non-temporal hint.  Stores either carry it too (the policy of the hot
 // path's kernels) or write with device scope (cache-policy bit sc1: each
 // line goes through the L2 to memory at once instead of waiting as a dirty
@@ -28,10 +31,31 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, kRawBufferDword3);
 }
 
-template <int MODE>  // 0 copy, nt stores; 1 copy, device-scope stores; 2 read; 3 write
+// 0 copy, nt stores; 1 copy, device-scope stores; 2 read; 3 write;
+// 4 gather: dst = src + src[n ..]; 5 scatter: dst = dst[n ..] = src
+// (n = vectors of one pass)
+template <int MODE>
 __global__ __launch_bounds__(kBlock) void ceiling_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                         u32x4* __restrict__ sink) {
+                                                         u32x4* __restrict__ sink, size_t n) {
   const size_t base = (size_t)blockIdx.x * kVecPerBlock + threadIdx.x;
+  if (MODE == 4) {
+    const u32x4 a = __builtin_nontemporal_load(src + base);
+    const u32x4 b = __builtin_nontemporal_load(src + base + kBlock);
+    const u32x4 c = __builtin_nontemporal_load(src + n + base);
+    const u32x4 d = __builtin_nontemporal_load(src + n + base + kBlock);
+    __builtin_nontemporal_store(a + c, dst + base);
+    __builtin_nontemporal_store(b + d, dst + base + kBlock);
+    return;
+  }
+  if (MODE == 5) {
+    const u32x4 a = __builtin_nontemporal_load(src + base);
+    const u32x4 b = __builtin_nontemporal_load(src + base + kBlock);
+    __builtin_nontemporal_store(a, dst + base);
+    __builtin_nontemporal_store(b, dst + base + kBlock);
+    __builtin_nontemporal_store(a, dst + n + base);
+    __builtin_nontemporal_store(b, dst + n + base + kBlock);
+    return;
+  }
   if (MODE == 3) {
     const u32x4 z = {blockIdx.x, threadIdx.x, 0u, 0u};
     __builtin_nontemporal_store(z, dst + base);
@@ -58,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void ceiling_kernel(const u32x4* __restrict
 }  // namespace
 
 extern "C" int tdp_ceiling_run(int mode, const void* src, void* dst, void* sink, size_t bytes, void* stream) {
-  if (mode < 0 || mode > 3) return -1;
+  if (mode < 0 || mode > 5) return -1;
   if (bytes == 0 || bytes % (kVecPerBlock * 16) != 0) return -1;
   if ((mode != 3 && !src) || (mode != 2 && !dst) || (mode == 2 && !sink)) return -1;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(sink)) & 15)
@@ -69,12 +93,15 @@ extern "C" int tdp_ceiling_run(int mode, const void* src, void* dst, void* sink,
   const u32x4* in = reinterpret_cast<const u32x4*>(src);
   u32x4* out = reinterpret_cast<u32x4*>(dst);
   u32x4* snk = reinterpret_cast<u32x4*>(sink);
+  const size_t n = bytes / 16;
   const dim3 grid((unsigned)blocks), block(kBlock);
   switch (mode) {
-    case 0: hipLaunchKernelGGL(ceiling_kernel<0>, grid, block, 0, s, in, out, snk); break;
-    case 1: hipLaunchKernelGGL(ceiling_kernel<1>, grid, block, 0, s, in, out, snk); break;
-    case 2: hipLaunchKernelGGL(ceiling_kernel<2>, grid, block, 0, s, in, out, snk); break;
-    default: hipLaunchKernelGGL(ceiling_kernel<3>, grid, block, 0, s, in, out, snk); break;
+    case 0: hipLaunchKernelGGL(ceiling_kernel<0>, grid, block, 0, s, in, out, snk, n); break;
+    case 1: hipLaunchKernelGGL(ceiling_kernel<1>, grid, block, 0, s, in, out, snk, n); break;
+    case 2: hipLaunchKernelGGL(ceiling_kernel<2>, grid, block, 0, s, in, out, snk, n); break;
+    case 3: hipLaunchKernelGGL(ceiling_kernel<3>, grid, block, 0, s, in, out, snk, n); break;
+    case 4: hipLaunchKernelGGL(ceiling_kernel<4>, grid, block, 0, s, in, out, snk, n); break;
+    default: hipLaunchKernelGGL(ceiling_kernel<5>, grid, block, 0, s, in, out, snk, n); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -56,7 +56,7 @@ def test_ceiling_library_exports_and_rejects_bad_arguments():
     for name in names:
         assert ctypes.cast(getattr(clib, name), ctypes.c_void_p).value
     al, null = ctypes.c_void_p(0x1000), ctypes.c_void_p(None)
-    assert clib.tdp_ceiling_run(5, al, al, al, 8192, null) == -1        # mode
+    assert clib.tdp_ceiling_run(6, al, al, al, 8192, null) == -1        # mode
     assert clib.tdp_ceiling_run(0, al, al, null, 8000, null) == -1      # size
     assert clib.tdp_ceiling_run(0, null, al, null, 8192, null) == -1    # src
     assert clib.tdp_ceiling_run(2, al, null, null, 8192, null) == -1    # sink
