@@ -316,9 +316,9 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
  * TDP_EINVAL for polls < 0. */
 int tdp_set_lookback_polls(int32_t polls);
 
-/* Largest workspace tdp_extract_noalloc serves (1 MiB: Nc up to about a
- * million conditioning tokens on a handful of tiles; tdp_sizes gives a
- * plan's figure). */
+/* Largest workspace tdp_extract_noalloc serves (1 MiB: the look-back flags
+ * take 4 bytes per tile and 64 conditioning tokens, so T * Nc up to about
+ * 16 million; tdp_sizes gives a plan's figure). */
 #define TDP_STATIC_SCRATCH_BYTES (1 << 20)
 
 /* tdp_extract without the workspace argument, for callers that cannot
