@@ -17,9 +17,11 @@ Floating point is fp64 unless a value must match a fixed-precision result bit
 for bit (fp32 position shifts, bf16 rounding).  The pages leave several steps
 open; each function names the reading it takes.  Every function is pinned
 by ``tests/test_oracle_pins.py`` against values the pages print, closed forms
-or invariants.  One reading stays parity unpinned: which strides of
+or invariants.  Two readings stay parity unpinned: which strides of
 ``split_by_count`` take the remainder when ``dim - overlap`` is not a multiple
-of the tile count (the pages' table is met by more than one choice).
+of the tile count (the pages' table is met by more than one choice), and the
+order of the tiles (the pages say round-robin but give no order; the blend
+is pinned not to depend on it beyond summation rounding).
 """
 from __future__ import annotations
 

@@ -6,6 +6,7 @@ hand-built cases with answers worked out by hand.  ``test_mutants_fail_pins``
 plants plausible mistakes in copies of oracle functions and checks that a pin
 catches each one.
 """
+import collections
 import itertools
 from fractions import Fraction
 from pathlib import Path
@@ -16,7 +17,7 @@ import torch
 
 import oracle as O
 from oracle import tdp_oracle as OT
-from synth import WORKLOADS, denoiser_params, grid_positions, make_inputs
+from synth import WORKLOADS, Workload, denoiser_params, grid_positions, make_inputs
 
 GOLDEN = Path(__file__).parent / "golden"
 
@@ -161,11 +162,32 @@ def test_decoded_area_closed_form(name):
         assert O.guard_holds(dim, n, o)
 
 
-def test_tile_order_is_row_major():
-    tiles = O.enumerate_tiles((16, 32, 48), ((2, 2), (3, 6), (3, 8)))
-    grids = [t["grid"] for t in tiles]
-    assert grids == list(itertools.product(range(2), range(3), range(3)))
-    assert [O.round_robin_rank(t["index"], 4) for t in tiles[:6]] == [0, 1, 2, 3, 0, 1]
+def test_tile_order_is_a_free_reading():
+    """The pages fix round-robin (TDP docs, "What it is": 16 tiles on 4
+    GPUs) but no tile order, so the row-major order (reading g6) is a free
+    choice, parity unpinned.  What holds for any order is pinned here:
+    the enumeration lists every cell of the tile grid once, 16 tiles on 4
+    ranks give each rank 4, and the blend does not depend on the order
+    beyond summation rounding (the same tiles in a shuffled order agree to
+    fp64 rounding)."""
+    shape, tiling = (4, 10, 12), ((2, 1), (2, 2), (3, 3))
+    tiles = O.enumerate_tiles(shape, tiling)
+    grids = [tuple(t["grid"]) for t in tiles]
+    assert len(set(grids)) == len(grids) == 2 * 2 * 3
+    assert set(grids) == set(itertools.product(range(2), range(2), range(3)))
+    sixteen = O.enumerate_tiles((1, 16, 16), ((1, 0), (4, 2), (4, 2)))
+    per_rank = collections.Counter(O.round_robin_rank(t["index"], 4) for t in sixteen)
+    assert sorted(per_rank.values()) == [4, 4, 4, 4]
+    wl = Workload("order", 2, 8, shape, tiling, num_cond=40, num_ref=10, dtype="f32", seed=3)
+    inp = make_inputs(wl)
+    ex = O.extract(inp["latent"], inp["pos"], shape, tiling, wl.num_cond)
+    rng = np.random.default_rng(17)
+    ys = [rng.standard_normal((2, len(et["rows"]), 8)) for et in ex["tiles"]]
+    ref, _ = O.blend(ys, ex, shape, tiling, wl.num_cond)
+    perm = rng.permutation(len(ys))
+    shuffled = dict(ex, tiles=[ex["tiles"][i] for i in perm])
+    out, _ = O.blend([ys[i] for i in perm], shuffled, shape, tiling, wl.num_cond)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
 # --- p4: extract moves the right rows -------------------------------------
