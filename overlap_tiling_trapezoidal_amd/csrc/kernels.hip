@@ -446,18 +446,22 @@ struct CondShared {
 };
 
 // Selection workgroup (Nc > 0): chunk ch of the conditioning tokens
-// against tile t.  The tile's kept tokens before the chunk: those of the
-// kDirectChunks chunks before it are counted here from their tokens (tested
-// in the same pass as the chunk's own), those of earlier chunks come from
-// their flags by look-back (wave 0), so with up to kDirectChunks + 1 chunks
-// per tile no workgroup waits on another.  When the chunk's rows of every
-// batch element fit one round of loads (B * kCondChunk * V <= kBlock *
-// kCopyBatch), every token's latent vectors and positions are loaded with
-// the extent, before the test, and only the kept ones stored: one round
-// trip for the whole workgroup (every tile re-reads the chunk, mostly from
-// cache).  Then cond_row (every tile: k counts the tiles of all ranks),
-// cond_k, and for a held tile the index entries, the rows, the shifted
-// positions and, from the last chunk, the tile's count.
+// against tile t.  Two regimes, by the number of chunks per tile:
+//   small (at most kDirectChunks + 1 chunks): every earlier chunk of the
+//     tile is counted here from its tokens, tested in the same pass as the
+//     chunk's own, so no workgroup waits on another; and when the chunk's
+//     rows of every batch element fit one round of loads (B * kCondChunk * V
+//     <= kBlock * kCopyBatch), every token's latent vectors and positions
+//     are loaded with the extent, before the test, and only the kept ones
+//     stored: one round trip for the whole workgroup;
+//   large: the earlier chunks' kept tokens come from their flags by
+//     look-back (wave 0) and only the kept rows are loaded, after the test,
+//     so each token's rows and positions are read about once per keeping
+//     tile (re-testing or re-reading whole chunks would multiply the reads
+//     by the window or by T).
+// Then cond_row (every tile: k counts the tiles of all ranks), cond_k, and
+// for a held tile the index entries, the rows, the shifted positions and,
+// from the last chunk, the tile's count.
 template <bool R>
 __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondShared& sm, float2* ext, int t,
                                    int ch) {
@@ -465,15 +469,16 @@ __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondS
   constexpr int kPosPer = (kCondChunk * 6 + kBlock - 1) / kBlock;   // position pairs per thread, B <= 2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* flags = ws_flags(p, a) + (int64_t)t * p.n_chunks;
-  const bool publish = p.n_chunks > kDirectChunks + 1;  // some workgroup reads flags
-  const int j0 = max(0, ch - kDirectChunks);            // first chunk tested here
+  const bool small = p.n_chunks <= kDirectChunks + 1;   // workgroup-uniform
+  const bool publish = !small;                           // some workgroup reads flags
+  const int j0 = small ? 0 : ch;                         // first chunk tested here
   const bool held_t = held<R>(p, t);
   const int V = p.vin;
   const int c0 = p.N + ch * kCondChunk;
   const int ntok = min(kCondChunk, p.Nc - ch * kCondChunk);
   // (b, token j, vector) of the whole chunk, token-minor over vectors
   const int all_vec = p.B * kCondChunk * V;
-  const bool early = held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
+  const bool early = small && held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
   u32x4 v[kCopyBatch];
   f32x2 w[kPosPer];
   if (early) {
@@ -495,7 +500,8 @@ __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondS
   // are in flight while the extent is combined
   TokenPos tp[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) tp[i] = load_token_pos(p, a.pos, min(j0 + wave + i * kWaves, ch), 0);
+  for (int i = 0; i < kPer; ++i)
+    if (j0 + wave + i * kWaves <= ch) tp[i] = load_token_pos(p, a.pos, j0 + wave + i * kWaves, 0);
   combine_extent(p, a, t, ext);
   __syncthreads();
   int direct = 0;
