@@ -446,7 +446,9 @@ struct CondShared {
 };
 
 // Selection workgroup (Nc > 0): chunk ch of the conditioning tokens
-// against tile t.  Two regimes, by the number of chunks per tile:
+// against tile t.  Two regimes, by the number of chunks per tile (SMALL:
+// each its own instantiation, so the large one carries none of the small
+// one's registers):
 //   small (at most kDirectChunks + 1 chunks): every earlier chunk of the
 //     tile is counted here from its tokens, tested in the same pass as the
 //     chunk's own, so no workgroup waits on another; and when the chunk's
@@ -462,23 +464,22 @@ struct CondShared {
 // Then cond_row (every tile: k counts the tiles of all ranks), cond_k, and
 // for a held tile the index entries, the rows, the shifted positions and,
 // from the last chunk, the tile's count.
-template <bool R>
+template <bool R, bool SMALL>
 __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondShared& sm, float2* ext, int t,
                                    int ch) {
-  constexpr int kPer = (kDirectChunks + 1 + kWaves - 1) / kWaves;  // chunks per wave
+  constexpr int kPer = SMALL ? (kDirectChunks + 1 + kWaves - 1) / kWaves : 1;  // chunks per wave
   constexpr int kPosPer = (kCondChunk * 6 + kBlock - 1) / kBlock;   // position pairs per thread, B <= 2
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* flags = ws_flags(p, a) + (int64_t)t * p.n_chunks;
-  const bool small = p.n_chunks <= kDirectChunks + 1;   // workgroup-uniform
-  const bool publish = !small;                           // some workgroup reads flags
-  const int j0 = small ? 0 : ch;                         // first chunk tested here
+  constexpr bool publish = !SMALL;  // some workgroup reads flags
+  const int j0 = SMALL ? 0 : ch;    // first chunk tested here
   const bool held_t = held<R>(p, t);
   const int V = p.vin;
   const int c0 = p.N + ch * kCondChunk;
   const int ntok = min(kCondChunk, p.Nc - ch * kCondChunk);
   // (b, token j, vector) of the whole chunk, token-minor over vectors
   const int all_vec = p.B * kCondChunk * V;
-  const bool early = small && held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
+  const bool early = SMALL && held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
   u32x4 v[kCopyBatch];
   f32x2 w[kPosPer];
   if (early) {
@@ -960,14 +961,14 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
 // tile's earlier chunks), never without bound.  Rank plans: selection over
 // every tile (k counts the tiles of all ranks), the rest for the held
 // tiles.
-template <bool R>
+template <bool R, bool SMALL>
 __global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
   const int bid = blockIdx.x;
   if (bid < a.n_sel) {
     extern __shared__ float2 ext_s[];  // dynamic: at least B * 3 (the launch asks for it)
     __shared__ CondShared cs;
     const int t = bid / p.n_chunks;
-    extract_cond_chunk<R>(p, a, cs, ext_s, t, bid - t * p.n_chunks);
+    extract_cond_chunk<R, SMALL>(p, a, cs, ext_s, t, bid - t * p.n_chunks);
     return;
   }
   if (bid - a.n_sel < a.n_pos) {
@@ -1347,6 +1348,7 @@ size_t capped_lds(const DeviceShape& d, size_t need, int k) {
 constexpr int kExtractWgsPerCu = 3;       // latent-dominated extracts
 constexpr int kExtractWgsPerCuChain = 2;  // extracts set by their position / selection chains
 constexpr int kBlendWgsPerCu = 4;
+constexpr int kSelectWgsPerCuLarge = 6;   // selection launches of plans with many chunks per tile
 
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
@@ -1553,12 +1555,21 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
     a.pos_parts = p.pos_parts;
     a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
     const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat));
-    // the tile's extent, and at most kExtractWgsPerCu workgroups per CU
-    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2), kExtractWgsPerCu);
-    if (p.world > 1)
-      hipLaunchKernelGGL(select_kernel<true>, sgrid, block, lds, s, p, a);
+    // the tile's extent, and a cap on workgroups per CU: plans with few
+    // chunks per tile (no waits, every chunk tested in one pass) at
+    // kExtractWgsPerCu, plans with more (look-back chains, little work per
+    // workgroup) at kSelectWgsPerCuLarge
+    const bool small = p.n_chunks <= kDirectChunks + 1;
+    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2),
+                                  small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
+    if (p.world > 1 && small)
+      hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, lds, s, p, a);
+    else if (p.world > 1)
+      hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, lds, s, p, a);
+    else if (small)
+      hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
     else
-      hipLaunchKernelGGL(select_kernel<false>, sgrid, block, lds, s, p, a);
+      hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
