@@ -21,7 +21,8 @@ Prints one JSON line (stdout): GB/s of compulsory bytes (each input read
 once, each output written once; overlap re-reads not credited), the
 fraction of the 8 TB/s HBM peak, a roofline entry for the dominant kernel,
 the CPU oracle's rate on the same workload, the same step measured on each
-of the five workloads (``workloads``) and what plain hand-written streaming
+of the five workloads (``workloads``), the conditioned shape's extract with
+1024 to 16384 conditioning tokens (``selection_scaling``) and what plain hand-written streaming
 kernels move on this GPU (``ceilings``, from libtdp_ceiling.so), also with
 the extract's and the blend's own read:write mix at their own sizes
 (``same_mix_ceilings``: a scatter writing each byte it reads twice, a
@@ -276,6 +277,39 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
         "step_us": round(st_ms * 1e3, 3), "bytes_per_step": ex_b + bl_b,
         "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
     }
+
+
+def selection_scaling(torch, tdp, dev, counts=(1024, 4096, 16384), sets_n=8, steps=32):
+    """Extract of the conditioned shape (B=2, 18 tiles) with more and more
+    conditioning tokens (a quarter of them at negative time, as in the
+    conditioned workload): microseconds and GB/s of its compulsory bytes,
+    graph-timed over rotating buffer sets as the workloads are."""
+    import numpy as np
+    from synth import WORKLOADS, Workload, make_inputs
+    base = WORKLOADS["conditioned"]
+    out = []
+    for nc in counts:
+        wl = Workload(f"conditioned_{nc}", base.batch, base.channels, base.shape, base.tiling, num_cond=nc,
+                      num_ref=nc // 4, dtype=base.dtype, seed=base.seed)
+        inp = make_inputs(wl)
+        plan = tdp.tdp_plan_create(tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, nc,
+                                                   in_dtype=wl.dtype, out_dtype=wl.dtype))
+        T = tdp.tdp_plan_num_tiles(plan)
+        lat = torch.from_numpy(inp["latent"].view(np.int16)).view(torch.bfloat16).to(dev)
+        pos = torch.from_numpy(inp["pos"]).to(dev)
+        sets = [(lat.clone(), pos.clone(), tdp.allocate_extract_outputs(plan, dev)) for _ in range(sets_n)]
+        stream = torch.cuda.Stream(dev)
+
+        def ex(i):
+            la, po, b = sets[i % sets_n]
+            tdp.tdp_extract(plan, la, po, stream=stream, **b)
+        ms = graph_time_ms(torch, stream, ex, steps)
+        counts_t = sets[0][2]["tile_count"].cpu().numpy()
+        ex_b, _, S = compulsory_bytes(wl, counts_t, T, 2, 2)
+        out.append({"num_cond": nc, "tile_rows": S, "extract_us": round(ms * 1e3, 3), "extract_bytes": ex_b,
+                    "extract_gbs": round(ex_b / (ms * 1e-3) / 1e9, 1)})
+        del sets
+    return out
 
 
 def ceiling_rates(torch, dev, nbytes=256 << 20, passes=12):
@@ -536,10 +570,13 @@ def main():
 
     # the same step on every workload (this run's own figures for its workload)
     table = {}
+    scaling = None
     if not args.no_workloads:
         for name, w in WORKLOADS.items():
             log(f"[bench] workload {name}")
             table[name] = workload_rates(torch, tdp, dev, w)
+        log("[bench] selection scaling")
+        scaling = selection_scaling(torch, tdp, dev)
 
     dom = ("extract", ex_bytes, ex_ms, "extract_kernel") if ex_ms >= bl_ms else \
           ("blend", bl_bytes, bl_ms, "blend_kernel")
@@ -592,6 +629,7 @@ def main():
         "target": "70% of the 8 TB/s peak on the 4K-class latent (5600 GB/s, 36.3 us per step)",
         "meets_target": bool(wl.name == "4k" and gbs >= 0.7 * HBM_PEAK_GBS),
         "workloads": table,
+        "selection_scaling": scaling,
         "roofline": {
             "bound": "hbm",
             "kernel": f"{dom[0]} ({dom[3]})",

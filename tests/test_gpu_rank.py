@@ -77,6 +77,7 @@ def test_rank_shares_match_oracle(name, world, cuda):
                                         ("w_one", 5), ("frame_tiles", 3), ("f32_channels", 2),
                                         ("batch3_random_pos", 3), ("cond_random_pos", 5),
                                         ("cond_random_pos", 16), ("tiles272_cond", 5), ("many_cond", 3),
+                                        ("cond_4097_batch3", 4), ("cond_wide_rows", 3),
                                         ("wide_4096", 2), ("odd_vectors", 3)])
 def test_rank_edge_cases(case, world, cuda):
     """Includes ranks that hold no tile (world above the tile count), plans
