@@ -1,8 +1,12 @@
 """Throughput of the tiled extract + blend hot path on one MI355X.
 
-One step = tdp_extract + tdp_blend over one synthetic latent (all tiles, run
-locally; the per-tile denoiser is not part of the path and is the identity
-here).  Inputs are resident in HBM before the timed region starts.
+One step = one extract and one blend of the same synthetic latent's size
+(all tiles, run locally; the per-tile denoiser is not part of the path and
+is the identity here), enqueued as one tdp_pipeline_step: the extract of
+one buffer set and the blend of another, one launch for whole plans without
+conditioning tokens.  The same steps as two calls each (tdp_extract, then
+tdp_blend) are reported beside it (``two_calls``).  Inputs are resident in
+HBM before the timed region starts.
 
 Caches: the 4K working set (~204 MB) fits the 256 MB Infinity Cache, so a
 loop over one buffer set would time cache hits.  The bench rotates over
@@ -28,14 +32,15 @@ the extract's and the blend's own read:write mix at their own sizes
 (``same_mix_ceilings``: a scatter writing each byte it reads twice, a
 gather reading two bytes per byte written; ``frac_of_same_mix``).
 
-Roofline: each operation is one kernel launch.  Its average duration comes
-from a CUDA-graph replay of K back-to-back launches (rotating buffer sets)
-between two HIP events on the launch stream, so host launch overhead does
-not enter it.  `traffic` is the HBM bytes per launch that rocprofv3's
-FETCH_SIZE and WRITE_SIZE counters read for that kernel, each scaled by
-what the counter reads for a device copy of known size; the figures live
-in profiles/extract_kernel_4k_pmc.md with a hash of the kernel sources, and
-are reported only while the sources still match that hash.
+Roofline: the dominant kernel is the one launch of a step (pipeline_kernel)
+when the step is fused, else the longer of extract_kernel and blend_kernel.
+Its average duration comes from a CUDA-graph replay of back-to-back launches
+(rotating buffer sets) between two HIP events on the launch stream, so host
+launch overhead does not enter it.  `traffic` is the HBM bytes per launch
+that rocprofv3's FETCH_SIZE and WRITE_SIZE counters read for that kernel,
+each scaled by what the counter reads for a device copy of known size; the
+figures live in profiles/pipeline_kernel_4k_pmc.md with a hash of the kernel
+sources, and are reported only while the sources still match that hash.
 """
 from __future__ import annotations
 
@@ -54,7 +59,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 KERNEL_SOURCES = ("overlap_tiling_trapezoidal_amd/csrc/kernels.hip", "overlap_tiling_trapezoidal_amd/csrc/plan.cpp",
                   "overlap_tiling_trapezoidal_amd/csrc/plan_internal.h",
                   "overlap_tiling_trapezoidal_amd/csrc/device_common.h", "include/tdp.h")
-PMC_SUMMARY = "profiles/extract_kernel_4k_pmc.md"
+PMC_SUMMARY = "profiles/pipeline_kernel_4k_pmc.md"
 
 
 def log(msg):
@@ -219,10 +224,10 @@ def graph_time_ms(torch, stream, fn, reps):
 
 
 def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
-    """Extract, blend and pipelined step of one workload, each timed as a
-    graph replay of `steps` launches over `sets_n` rotating buffer sets (the
-    blend `sets_n // 2` steps behind the extract), with the GB/s of its
-    compulsory bytes."""
+    """Extract, blend and pipelined step (tdp_pipeline_step) of one workload,
+    each timed as a graph replay of `steps` launches over `sets_n` rotating
+    buffer sets (the blend `sets_n // 2` steps behind the extract), with the
+    GB/s of its compulsory bytes."""
     import numpy as np
     from synth import make_inputs
     inp = make_inputs(wl)
@@ -251,8 +256,9 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
         tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], b["cond_k"], s["out"], stream)
 
     def step(i):
-        ex(i)
-        bl(i - lag)
+        s, q = sets[i % sets_n], sets[(i - lag) % sets_n]
+        tdp.tdp_pipeline_step(plan, s["latent"], s["pos"], stream=stream, **s["bufs"], tile_out=q["bufs"]["tile_lat"],
+                              blend_cond_row=q["bufs"]["cond_row"], blend_cond_k=q["bufs"]["cond_k"], out=q["out"])
 
     with torch.cuda.stream(stream):
         for i in range(sets_n):
@@ -449,12 +455,25 @@ def main():
         b = s["bufs"]
         tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], b["cond_k"], s["out"], st or stream)
 
+    def step(i, st=None):
+        """Pipelined step i: extract set i mod R and blend set (i - D) mod R,
+        one tdp_pipeline_step (one launch where the plan allows)."""
+        s, q = sets[i % R], sets[(i - D) % R]
+        b = s["bufs"]
+        tdp.tdp_pipeline_step(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
+                              b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"],
+                              tile_out=q["bufs"]["tile_lat"], blend_cond_row=q["bufs"]["cond_row"],
+                              blend_cond_k=q["bufs"]["cond_k"], out=q["out"], stream=st or stream)
+
+    def step_two_calls(i, st=None):
+        extract(sets[i % R], st)
+        blend(sets[(i - D) % R], st)
+
     # prime every set, then warm up the pipeline
     for s in sets:
         extract(s)
     for i in range(args.warmup):
-        extract(sets[i % R])
-        blend(sets[(i - D) % R])
+        step(i)
     torch.cuda.synchronize()
     counts = sets[0]["bufs"]["tile_count"].cpu().numpy()
     e_in = 2 if wl.dtype == "bf16" else 4
@@ -469,8 +488,7 @@ def main():
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        extract(sets[i % R])
-        blend(sets[(i - D) % R])
+        step(i)
     stop.record(stream)
     enqueue = time.perf_counter() - wall0
     torch.cuda.synchronize()
@@ -480,8 +498,7 @@ def main():
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     evs[0].record(stream)
     for i in range(K):
-        extract(sets[i % R])
-        blend(sets[(i - D) % R])
+        step(i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
@@ -494,8 +511,7 @@ def main():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=pstream):
         for i in range(K):
-            extract(sets[i % R], pstream)
-            blend(sets[(i - D) % R], pstream)
+            step(i, pstream)
     with torch.cuda.stream(pstream):
         graph.replay()
     torch.cuda.synchronize()
@@ -508,6 +524,10 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(stop) / K
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    del graph
+    # the same K steps as two calls each (tdp_extract, then tdp_blend)
+    two_ms = graph_time_ms(torch, pstream, lambda i: step_two_calls(i, pstream), K)
+    fused = wl.num_cond == 0  # whole plan without conditioning tokens: one launch per step
 
     # per-operation launch durations (graph replay, launch stream)
     gstream = torch.cuda.Stream(dev)
@@ -578,8 +598,11 @@ def main():
         log("[bench] selection scaling")
         scaling = selection_scaling(torch, tdp, dev)
 
-    dom = ("extract", ex_bytes, ex_ms, "extract_kernel") if ex_ms >= bl_ms else \
-          ("blend", bl_bytes, bl_ms, "blend_kernel")
+    if fused:  # the step is one launch: that kernel is the dominant one
+        dom = ("extract + blend, one launch", step_bytes, ms_per_step, "pipeline_kernel")
+    else:
+        dom = ("extract", ex_bytes, ex_ms, "extract_kernel") if ex_ms >= bl_ms else \
+              ("blend", bl_bytes, bl_ms, "blend_kernel")
     achieved = dom[1] / (dom[2] * 1e-3) / 1e9
     traffic = measured_traffic(wl.name, dom[3]) if not args.no_normalize else None
     result = {
@@ -607,6 +630,9 @@ def main():
             "normalize_positions": not args.no_normalize,
         },
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "step_call": "tdp_pipeline_step (one launch)" if fused else "tdp_pipeline_step (extract, then blend)",
+        "two_calls": {"ms_per_step": round(two_ms, 5), "value": round(step_bytes / (two_ms * 1e-3) / 1e9, 2),
+                      "note": "the same K steps as tdp_extract + tdp_blend, two launches each"},
         "ops": {
             "extract_ms": round(ex_ms, 5), "extract_bytes": ex_bytes,
             "extract_gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),

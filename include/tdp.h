@@ -355,6 +355,28 @@ int tdp_extract_noalloc(const tdp_plan* plan, const void* latent, const float* p
 int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row,
               const int32_t* cond_k, void* out, void* stream);
 
+/* One step of a pipelined loop, for callers that have the extract of one
+ * latent and the blend of an earlier latent's tile outputs ready together
+ * (latents in flight one after another, each tiled, its tiles denoised and
+ * their outputs blended back: TDP docs, "What it is").  Enqueues what
+ * tdp_extract(plan, latent, ..., workspace) followed by tdp_blend(plan,
+ * tile_out, blend_cond_row, blend_cond_k, out) would, with bit-identical
+ * results.  For whole plans without conditioning tokens both run as one
+ * launch, the extract's workgroups first, so the blend's fill the GPU while
+ * the extract's drain; other plans enqueue the two one after the other.
+ * The two halves may run at the same time, so the blend's buffers must be
+ * none of the extract's: TDP_EINVAL, nothing enqueued, when tile_out,
+ * blend_cond_row or blend_cond_k overlaps a buffer the extract writes, or
+ * out overlaps a buffer the extract reads or writes (extents from
+ * tdp_plan_sizes).  Other arguments, alignments and errors as the two
+ * calls; one plan serves both halves. */
+int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos,
+                      void* tile_lat, float* tile_pos, int32_t* tile_index,
+                      int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
+                      void* workspace, const void* tile_out,
+                      const int32_t* blend_cond_row, const int32_t* blend_cond_k,
+                      void* out, void* stream);
+
 /* Streaming blend, for schedules that produce one tile output at a time
  * (TDP docs, "What it is": a rank runs its tiles in turn and their blended
  * outputs are accumulated in place).  Adds tile t's outputs into the fp32

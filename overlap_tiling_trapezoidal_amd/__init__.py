@@ -20,8 +20,8 @@ DEFAULT_LIB_PATH = os.path.join(_HERE, "libtdp.so")
 # built with address and undefined-behaviour sanitizers for the CPU tests
 # (build.py --host-sanitized); such a build may lack the device entry points.
 LIB_PATH = os.environ.get("TDP_LIBRARY") or DEFAULT_LIB_PATH
-DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_set_lookback_polls", "tdp_blend", "tdp_blend_tile",
-                    "tdp_blend_finish", "tdp_pixel_blend")
+DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_set_lookback_polls", "tdp_pipeline_step", "tdp_blend",
+                    "tdp_blend_tile", "tdp_blend_finish", "tdp_pixel_blend")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp.h")
 
 # ---- constants (mirror include/tdp.h) --------------------------------------
@@ -162,6 +162,7 @@ def load_library(path: str = LIB_PATH):
         "tdp_extract": (ctypes.c_int, [vp] * 11),
         "tdp_extract_noalloc": (ctypes.c_int, [vp] * 10),
         "tdp_set_lookback_polls": (ctypes.c_int, [i32]),
+        "tdp_pipeline_step": (ctypes.c_int, [vp] * 15),
         "tdp_blend": (ctypes.c_int, [vp] * 6),
         "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
@@ -495,6 +496,29 @@ def tdp_blend(plan: Plan, tile_out, cond_row, cond_k, out, stream=None):
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_blend(*args))
+
+
+def tdp_pipeline_step(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row=None,
+                      cond_k=None, workspace=None, *, tile_out, blend_cond_row=None, blend_cond_k=None, out,
+                      stream=None):
+    """Enqueue tdp_extract of ``latent`` and tdp_blend of ``tile_out`` (an
+    earlier latent's tile outputs, none of this extract's buffers) as one
+    step, one launch where the plan allows."""
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    dev = latent.device
+    none = ctypes.c_void_p(None)
+    args = _extract_args(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k)
+    args.append(_ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes else none)
+    args += [
+        _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
+        _ptr(blend_cond_row, "blend_cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
+        _ptr(blend_cond_k, "blend_cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
+        _ptr(out, "out", _torch_dtype(c.out_dtype), s.out_elems, dev),
+        _stream_handle(stream, dev),
+    ]
+    _check(load_library().tdp_pipeline_step(*args))
 
 
 def allocate_accumulator(plan: Plan, device="cuda"):

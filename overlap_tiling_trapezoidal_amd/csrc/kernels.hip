@@ -1298,6 +1298,45 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     blend_line<IN, OUT, F2 ? 4 : 2, R>(p, lc, b, f, h, w0, tile_out, out);
 }
 
+// One step of a pipelined loop (whole plans without conditioning tokens):
+// the extract of one latent and the blend of other tile outputs that share
+// no buffer with it, as one launch.  Grid: the extract's workgroups
+// (positions, then latent rows) and then the blend's, so the blend's fill
+// the compute units as the extract's drain instead of waiting for a kernel
+// boundary.  Each workgroup runs exactly the code of its own kernel.
+template <int IN, int OUT, bool F2>
+__global__ __launch_bounds__(kBlock) void pipeline_kernel(const PlanDev p, const ExtractArgs a,
+                                                          const u32x4* __restrict__ tile_out,
+                                                          void* __restrict__ out, int n_ext) {
+  __shared__ ExtractShared sm;
+  const int bid = blockIdx.x;
+  if (bid < n_ext) {
+    if (bid < a.n_pos) {
+      const PosWork w = pos_work<false>(p, a, bid);
+      extract_positions<false>(p, a, sm, w.t, w.slot, w.b, w.d, w.part);
+      return;
+    }
+    extract_latent<false>(p, a, bid - a.n_pos);
+    return;
+  }
+  const int unit = __builtin_amdgcn_readfirstlane((bid - n_ext) * kWaves + (int)(threadIdx.x >> 6));
+  if (unit >= p.gen_units) return;
+  const int rows = p.blend_rows;
+  const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
+  const int w0 = (unit - line * p.blend_chunks) * rows;
+  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
+  const int fh = line - b * (p.F * p.H);
+  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+  LineCombos lc;
+  lc.init(p, f, h);
+  if (lc.n == 1)
+    blend_line<IN, OUT, 1, false>(p, lc, b, f, h, w0, tile_out, out);
+  else if (!F2 || lc.n == 2)
+    blend_line<IN, OUT, 2, false>(p, lc, b, f, h, w0, tile_out, out);
+  else
+    blend_line<IN, OUT, F2 ? 4 : 2, false>(p, lc, b, f, h, w0, tile_out, out);
+}
+
 // Occupancy caps.  Both kernels move more bytes per microsecond with fewer
 // workgroups sharing a compute unit than the registers allow (7 or 8 per
 // CU): fewer requests in flight per CU, and the long position and selection
@@ -1349,6 +1388,7 @@ constexpr int kExtractWgsPerCu = 3;       // latent-dominated extracts
 constexpr int kExtractWgsPerCuChain = 2;  // extracts set by their position / selection chains
 constexpr int kBlendWgsPerCu = 4;
 constexpr int kSelectWgsPerCuLarge = 6;   // selection launches of plans with many chunks per tile
+constexpr int kPipelineWgsPerCu = 4;      // pipeline step (extract and blend in one launch)
 
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
@@ -1373,6 +1413,47 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
     hipLaunchKernelGGL((blend_kernel<IN, OUT, false, true>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else
     hipLaunchKernelGGL((blend_kernel<IN, OUT, false, false>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
+  return hipGetLastError();
+}
+
+// The extract half's arguments of a pipeline step (whole plan, Nc == 0),
+// as launch_extract sets them up.
+ExtractArgs pipeline_extract_args(const PlanDev& p, const void* latent, const float* pos, void* tile_lat,
+                                  float* tile_pos, int32_t* tile_index, int32_t* tile_count, const DeviceShape& ds,
+                                  int& n_lat) {
+  ExtractArgs a;
+  a.latent = reinterpret_cast<const u32x4*>(latent);
+  a.pos = reinterpret_cast<const f32x2*>(pos);
+  a.tile_lat = reinterpret_cast<u32x4*>(tile_lat);
+  a.tile_pos = reinterpret_cast<f32x2*>(tile_pos);
+  a.tile_index = tile_index;
+  a.tile_count = tile_count;
+  a.cond_row = nullptr;
+  a.cond_k = nullptr;
+  a.ws = nullptr;
+  a.n_ext = 0;
+  a.n_sel = 0;
+  a.lookback_polls = 0;
+  n_lat = (p.lat_units + kWaves - 1) / kWaves;
+  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
+  a.pos_one_pass = latent_bound ? 1 : 0;
+  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  return a;
+}
+
+template <int IN, int OUT>
+hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, const void* tile_out, void* out,
+                           const DeviceShape& ds, hipStream_t s) {
+  const int n_ext = a.n_pos + n_lat;
+  const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
+  const size_t lds = capped_lds(ds, 0, kPipelineWgsPerCu);
+  const dim3 grid((unsigned)(n_ext + n_gen)), block(kBlock);
+  const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
+  if (p.ax[0].n > 1)
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, true>), grid, block, lds, s, p, a, y, out, n_ext);
+  else
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, false>), grid, block, lds, s, p, a, y, out, n_ext);
   return hipGetLastError();
 }
 
@@ -1613,6 +1694,40 @@ int check_extract(const tdp_plan* plan, const void* latent, const float* pos, co
   return TDP_OK;
 }
 
+// Checks of tdp_blend's arguments (shared with tdp_pipeline_step).
+int check_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
+                const void* out, const char* who) {
+  if (!plan) return fail(TDP_EINVAL, "%s: null plan", who);
+  if (!plan->guarded) return fail(TDP_EGUARD, "%s: plan was built with TDP_UNGUARDED", who);
+  const PlanDev& p = plan->dev;
+  if (!out || (!tile_out && p.T_local > 0)) return fail(TDP_EINVAL, "%s: null device pointer", who);
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "%s: cond_row and cond_k are required when num_cond > 0", who);
+  if (!aligned(tile_out, 16) || !aligned(out, 16))
+    return fail(TDP_EINVAL, "%s: tile_out and out must be 16-byte aligned", who);
+  if (!aligned(cond_row, 4) || !aligned(cond_k, 4)) return fail(TDP_EINVAL, "%s: misaligned cond_row or cond_k", who);
+  return TDP_OK;
+}
+
+// The blend of a checked plan, by dtypes.
+hipError_t blend_dispatch(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
+                          void* out, hipStream_t s) {
+  if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
+    return launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
+  if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
+    return launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+  if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
+    return launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+  return launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
+}
+
+// Byte ranges [a, a + na) and [b, b + nb) share a byte (null or empty: no).
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
 }  // namespace
 }  // namespace tdp
 
@@ -1752,26 +1867,72 @@ int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* st
 
 int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k, void* out,
               void* stream) {
-  if (!plan) return fail(TDP_EINVAL, "tdp_blend: null plan");
-  if (!plan->guarded) return fail(TDP_EGUARD, "tdp_blend: plan was built with TDP_UNGUARDED");
+  const int st = check_blend(plan, tile_out, cond_row, cond_k, out, "tdp_blend");
+  if (st != TDP_OK) return st;
+  const hipError_t e = blend_dispatch(plan->dev, tile_out, cond_row, cond_k, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend: kernel launch failed: %s", hipGetErrorString(e));
+  return TDP_OK;
+}
+
+int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
+                      int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, void* workspace,
+                      const void* tile_out, const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
+                      void* stream) {
+  const char* who = "tdp_pipeline_step";
+  int st = check_extract(plan, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k, who);
+  if (st != TDP_OK) return st;
+  st = check_blend(plan, tile_out, blend_cond_row, blend_cond_k, out, who);
+  if (st != TDP_OK) return st;
   const PlanDev& p = plan->dev;
-  if (!out || (!tile_out && p.T_local > 0)) return fail(TDP_EINVAL, "tdp_blend: null device pointer");
-  if (p.Nc > 0 && (!cond_row || !cond_k))
-    return fail(TDP_EINVAL, "tdp_blend: cond_row and cond_k are required when num_cond > 0");
-  if (!aligned(tile_out, 16) || !aligned(out, 16))
-    return fail(TDP_EINVAL, "tdp_blend: tile_out and out must be 16-byte aligned");
-  if (!aligned(cond_row, 4) || !aligned(cond_k, 4)) return fail(TDP_EINVAL, "tdp_blend: misaligned cond_row or cond_k");
+  const int64_t ws_bytes = ws_layout(p).bytes;
+  if (ws_bytes > 0 && !workspace)
+    return fail(TDP_EINVAL, "%s: workspace of %lld bytes is required (tdp_plan_sizes)", who, (long long)ws_bytes);
+  if (!aligned(workspace, 16)) return fail(TDP_EINVAL, "%s: workspace must be 16-byte aligned", who);
+  // the blend's buffers must be none of the extract's: the two halves may
+  // run at the same time
+  tdp_sizes z;
+  tdp_plan_sizes(plan, &z);
+  const int64_t ein = dtype_bytes(p.in_dtype), eout = dtype_bytes(p.out_dtype);
+  const int64_t rows = (int64_t)p.B * p.rows;
+  const struct { const void* ptr; int64_t bytes; } ext_w[] = {
+      {tile_lat, z.tile_lat_elems * ein}, {tile_pos, z.tile_pos_floats * 4}, {tile_index, z.tile_index_ints * 4},
+      {tile_count, z.num_slots * 4},      {cond_row, z.cond_row_ints * 4},   {cond_k, z.cond_k_ints * 4},
+      {workspace, ws_bytes}},
+    ext_r[] = {{latent, rows * p.C * ein}, {pos, rows * 3 * 8}},
+    bl_r[] = {{tile_out, z.tile_lat_elems * ein}, {blend_cond_row, z.cond_row_ints * 4}, {blend_cond_k, z.cond_k_ints * 4}};
+  const int64_t out_bytes = z.out_elems * eout;
+  for (const auto& w : ext_w) {
+    for (const auto& r : bl_r)
+      if (overlap(w.ptr, w.bytes, r.ptr, r.bytes))
+        return fail(TDP_EINVAL, "%s: the blend reads a buffer the extract writes", who);
+    if (overlap(w.ptr, w.bytes, out, out_bytes))
+      return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract writes", who);
+  }
+  for (const auto& r : ext_r)
+    if (overlap(r.ptr, r.bytes, out, out_bytes))
+      return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.Nc > 0 || p.world > 1) {  // one after the other
+    st = launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
+                        static_cast<char*>(workspace), s, who);
+    if (st != TDP_OK) return st;
+    const hipError_t e = blend_dispatch(p, tile_out, blend_cond_row, blend_cond_k, out, s);
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: blend launch failed: %s", who, hipGetErrorString(e));
+    return TDP_OK;
+  }
+  const DeviceShape ds = device_shape();
+  int n_lat = 0;
+  const ExtractArgs a = pipeline_extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, ds, n_lat);
   hipError_t e;
   if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
-    e = launch_blend<TDP_BF16, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_pipeline<TDP_BF16, TDP_BF16>(p, a, n_lat, tile_out, out, ds, s);
   else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_BF16, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_pipeline<TDP_BF16, TDP_F32>(p, a, n_lat, tile_out, out, ds, s);
   else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
-    e = launch_blend<TDP_F32, TDP_F32>(p, tile_out, cond_row, cond_k, out, s);
+    e = launch_pipeline<TDP_F32, TDP_F32>(p, a, n_lat, tile_out, out, ds, s);
   else
-    e = launch_blend<TDP_F32, TDP_BF16>(p, tile_out, cond_row, cond_k, out, s);
-  if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend: kernel launch failed: %s", hipGetErrorString(e));
+    e = launch_pipeline<TDP_F32, TDP_BF16>(p, a, n_lat, tile_out, out, ds, s);
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
   return TDP_OK;
 }
 

@@ -70,11 +70,12 @@ def test_traffic_record_is_ignored_when_sources_change(monkeypatch):
             rec = json.loads(line)
     assert rec is not None and rec["workload"] == "4k"
     monkeypatch.setattr(bench, "sources_hash", lambda: rec["sources_sha256_16"])
-    t = bench.measured_traffic("4k", "extract_kernel")
-    assert t == rec["traffic"]["extract_kernel"]["fetch_bytes"] + rec["traffic"]["extract_kernel"]["write_bytes"]
-    assert bench.measured_traffic("fullres", "extract_kernel") is None
+    for kernel in ("pipeline_kernel", "extract_kernel", "blend_kernel"):
+        t = bench.measured_traffic("4k", kernel)
+        assert t == rec["traffic"][kernel]["fetch_bytes"] + rec["traffic"][kernel]["write_bytes"]
+    assert bench.measured_traffic("fullres", "pipeline_kernel") is None
     monkeypatch.setattr(bench, "sources_hash", lambda: "0" * 16)
-    assert bench.measured_traffic("4k", "extract_kernel") is None
+    assert bench.measured_traffic("4k", "pipeline_kernel") is None
 
 
 def test_more_than_one_gpu_is_refused():

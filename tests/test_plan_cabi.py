@@ -218,6 +218,32 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
 
 
 @pytest.mark.device_abi
+def test_pipeline_step_refuses_before_launch(lib):
+    """Bad and overlapping arguments are refused on the host (no GPU call)."""
+    plan = plan_for(WORKLOADS["4k"])
+    s = tdp.tdp_plan_sizes(plan)
+    null = ctypes.c_void_p(None)
+    base = {k: ctypes.c_void_p((i + 1) << 36) for i, k in enumerate(
+        ("latent", "pos", "tile_lat", "tile_pos", "index", "count", "tile_out", "out"))}
+
+    def call(**over):
+        a = dict(base, **over)
+        return lib.tdp_pipeline_step(plan.handle, a["latent"], a["pos"], a["tile_lat"], a["tile_pos"], a["index"],
+                                     a["count"], null, null, null, a["tile_out"], null, null, a["out"], null)
+    assert call(tile_out=base["tile_lat"]) == tdp.TDP_EINVAL
+    assert "reads a buffer the extract writes" in tdp.tdp_last_error()
+    inside = ctypes.c_void_p(base["tile_lat"].value + (s.tile_lat_elems * 2 // 32) * 16)
+    assert call(tile_out=inside) == tdp.TDP_EINVAL           # starts inside tile_lat
+    assert call(out=base["tile_pos"]) == tdp.TDP_EINVAL
+    assert "writes a buffer the extract writes" in tdp.tdp_last_error()
+    assert call(out=ctypes.c_void_p(base["latent"].value + 4096)) == tdp.TDP_EINVAL
+    assert "writes a buffer the extract reads" in tdp.tdp_last_error()
+    assert call(out=null) == tdp.TDP_EINVAL
+    assert call(tile_out=ctypes.c_void_p(base["tile_out"].value + 8)) == tdp.TDP_EINVAL   # misaligned
+    assert lib.tdp_pipeline_step(None, *([null] * 14)) == tdp.TDP_EINVAL
+
+
+@pytest.mark.device_abi
 def test_lookback_polls_setting(lib):
     assert lib.tdp_set_lookback_polls(-1) == tdp.TDP_EINVAL
     assert "polls" in tdp.tdp_last_error()
