@@ -962,8 +962,7 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
 // every tile (k counts the tiles of all ranks), the rest for the held
 // tiles.
 template <bool R, bool SMALL>
-__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
-  const int bid = blockIdx.x;
+__device__ void select_body(const PlanDev& p, const ExtractArgs& a, int bid) {
   if (bid < a.n_sel) {
     extern __shared__ float2 ext_s[];  // dynamic: at least B * 3 (the launch asks for it)
     __shared__ CondShared cs;
@@ -978,6 +977,10 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const E
     return;
   }
   extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
+}
+template <bool R, bool SMALL>
+__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
+  select_body<R, SMALL>(p, a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1256,24 +1259,23 @@ __device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_
 // F2: the frame axis is tiled, so a line can have four frame x height
 // combos; only plans with a tiled frame axis carry that path (and its
 // registers).
+// Workgroup `bid` of a blend whose first n_cond workgroups take the
+// conditioning rows.
 template <int IN, int OUT, bool R, bool F2>
-__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
-                                                       const int32_t* __restrict__ cond_row,
-                                                       const int32_t* __restrict__ cond_k,
-                                                       void* __restrict__ out, int n_gen_blocks) {
+__device__ void blend_body(const PlanDev& p, const u32x4* __restrict__ tile_out, const int32_t* __restrict__ cond_row,
+                           const int32_t* __restrict__ cond_k, void* __restrict__ out, int bid, int n_cond) {
   // conditioning workgroups first: each is a short dependent chain, so they
   // start early and run under the generated rows
-  const int n_cond = (int)gridDim.x - n_gen_blocks;
-  if ((int)blockIdx.x < n_cond) {
+  if (bid < n_cond) {
     if (p.T <= kCondTiles)
-      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, blockIdx.x);
+      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
     else
-      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, blockIdx.x);
+      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
     return;
   }
   // this wave's unit (rows [w0, w0 + rwv) of one line): the waves of a
   // workgroup take consecutive units
-  const int unit = __builtin_amdgcn_readfirstlane(((int)blockIdx.x - n_cond) * kWaves + (int)(threadIdx.x >> 6));
+  const int unit = __builtin_amdgcn_readfirstlane((bid - n_cond) * kWaves + (int)(threadIdx.x >> 6));
   if (unit >= p.gen_units) return;
   const int rows = p.blend_rows;
   const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
@@ -1296,6 +1298,32 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
     blend_line<IN, OUT, 2, R>(p, lc, b, f, h, w0, tile_out, out);
   else
     blend_line<IN, OUT, F2 ? 4 : 2, R>(p, lc, b, f, h, w0, tile_out, out);
+}
+template <int IN, int OUT, bool R, bool F2>
+__global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
+                                                       const int32_t* __restrict__ cond_row,
+                                                       const int32_t* __restrict__ cond_k,
+                                                       void* __restrict__ out, int n_gen_blocks) {
+  blend_body<IN, OUT, R, F2>(p, tile_out, cond_row, cond_k, out, blockIdx.x, (int)gridDim.x - n_gen_blocks);
+}
+
+// One step of a pipelined loop for whole plans with conditioning tokens,
+// after the extent launch: the selection launch's workgroups (selection,
+// positions, latent rows), then the blend's (its conditioning rows, then its
+// generated rows), as one launch, so the blend's bulk copy runs under the
+// selection's dependent chains and fills the units as the extract drains.
+template <int IN, int OUT, bool F2, bool SMALL>
+__global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, const ExtractArgs a,
+                                                               const u32x4* __restrict__ tile_out,
+                                                               const int32_t* __restrict__ blend_cond_row,
+                                                               const int32_t* __restrict__ blend_cond_k,
+                                                               void* __restrict__ out, int n_ext, int n_bcond) {
+  const int bid = blockIdx.x;
+  if (bid < n_ext) {
+    select_body<false, SMALL>(p, a, bid);
+    return;
+  }
+  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
 }
 
 // One step of a pipelined loop (whole plans without conditioning tokens):
@@ -1390,18 +1418,21 @@ constexpr int kBlendWgsPerCu = 4;
 constexpr int kSelectWgsPerCuLarge = 6;   // selection launches of plans with many chunks per tile
 constexpr int kPipelineWgsPerCu = 4;      // pipeline step (extract and blend in one launch)
 
+// The blend's conditioning workgroups, and the LDS of its cached path:
+// rowtab, cap, k, n, list (ints), then 8-aligned int64 bases.
+int blend_cond_blocks(const PlanDev& p) { return p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0; }
+size_t blend_cond_lds(const PlanDev& p) {
+  return p.Nc > 0 && p.T <= kCondTiles
+             ? ((size_t)2 * p.T * kCondTokens + p.T + 2 * kCondTokens) * sizeof(int) + 8 + (size_t)p.T * 8
+             : 0;
+}
+
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
                         void* out, hipStream_t s) {
   const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
-  const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0;
-  // LDS for the cached conditioning path: rowtab, cap, k, then int64 bases
-  // rowtab, cap, k, n, list (ints), then 8-aligned int64 bases
-  const size_t cond_lds = p.Nc > 0 && p.T <= kCondTiles
-                              ? ((size_t)2 * p.T * kCondTokens + p.T + 2 * kCondTokens) * sizeof(int) + 8 +
-                                    (size_t)p.T * 8
-                              : 0;
-  const size_t lds = capped_lds(device_shape(), cond_lds, kBlendWgsPerCu);
+  const int n_cond = blend_cond_blocks(p);
+  const size_t lds = capped_lds(device_shape(), blend_cond_lds(p), kBlendWgsPerCu);
   const dim3 grid(n_gen + n_cond), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   const bool f2 = p.ax[0].n > 1;
@@ -1454,6 +1485,38 @@ hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, co
     hipLaunchKernelGGL((pipeline_kernel<IN, OUT, true>), grid, block, lds, s, p, a, y, out, n_ext);
   else
     hipLaunchKernelGGL((pipeline_kernel<IN, OUT, false>), grid, block, lds, s, p, a, y, out, n_ext);
+  return hipGetLastError();
+}
+
+// Plans whose tiles have few chunks: no waits, every chunk tested in one pass.
+bool select_small(const PlanDev& p) { return p.n_chunks <= kDirectChunks + 1; }
+
+// The pipeline step of a whole plan with conditioning tokens, after
+// launch_extent: its selection launch and the blend as one launch.
+template <int IN, int OUT>
+hipError_t launch_pipeline_cond(const PlanDev& p, const ExtractArgs& a, int n_lat, const void* tile_out,
+                                const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
+                                const DeviceShape& ds, hipStream_t s) {
+  const int n_ext = a.n_sel + a.n_pos + n_lat;
+  const int n_bcond = blend_cond_blocks(p);
+  const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
+  const size_t sel_lds = (size_t)p.B * 3 * sizeof(float2), bl_lds = blend_cond_lds(p);
+  const size_t lds = capped_lds(ds, sel_lds > bl_lds ? sel_lds : bl_lds, kPipelineWgsPerCu);
+  const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
+  const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
+  const bool f2 = p.ax[0].n > 1, small = select_small(p);
+  if (f2 && small)
+    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, true, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_ext, n_bcond);
+  else if (f2)
+    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, true, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_ext, n_bcond);
+  else if (small)
+    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, false, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_ext, n_bcond);
+  else
+    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, false, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_ext, n_bcond);
   return hipGetLastError();
 }
 
@@ -1603,9 +1666,8 @@ std::atomic<int> g_lookback_polls{kLookbackPolls};
 // Enqueue extract: the gather (with conditioning tokens, the extent parts
 // too, into `ws`), then with conditioning tokens the selection launch.
 // Arguments are valid.
-int launch_extract(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
-                   int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws,
-                   hipStream_t s, const char* who) {
+ExtractArgs extract_args(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
+                         int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws) {
   ExtractArgs a;
   a.latent = reinterpret_cast<const u32x4*>(latent);
   a.pos = reinterpret_cast<const f32x2*>(pos);
@@ -1619,28 +1681,44 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
   a.n_ext = p.Nc > 0 ? p.T * p.ext_parts : 0;
   a.n_sel = p.Nc > 0 ? p.T * p.n_chunks : 0;
   a.lookback_polls = g_lookback_polls.load(std::memory_order_relaxed);
+  a.pos_one_pass = 0;
+  a.pos_parts = p.pos_parts;
+  a.n_pos = 0;
+  return a;
+}
+
+// The extent launch (Nc > 0); then the selection launch's workgroups are
+// a.n_sel selection, a.n_pos positions (copies: the shift is known) and the
+// latent rows.
+int launch_extent(const PlanDev& p, ExtractArgs& a, hipStream_t s, const char* who) {
+  const dim3 egrid((unsigned)a.n_ext), block(kBlock);
+  if (p.B == 1)
+    hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, a);
+  else
+    hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: extent launch failed: %s", who, hipGetErrorString(e));
+  a.pos_one_pass = 0;
+  a.pos_parts = p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  return TDP_OK;
+}
+
+int launch_extract(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
+                   int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws,
+                   hipStream_t s, const char* who) {
+  ExtractArgs a = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k, ws);
   const DeviceShape ds = device_shape();
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
   const dim3 block(kBlock);
   if (p.Nc > 0) {
-    // extent launch, then selection with the positions (copies: the shift
-    // is known) and the latent rows, 3 workgroups per CU
-    const dim3 egrid((unsigned)a.n_ext);
-    if (p.B == 1)
-      hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, a);
-    else
-      hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: extent launch failed: %s", who, hipGetErrorString(e));
-    a.pos_one_pass = 0;
-    a.pos_parts = p.pos_parts;
-    a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+    const int st = launch_extent(p, a, s, who);
+    if (st != TDP_OK) return st;
     const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat));
     // the tile's extent, and a cap on workgroups per CU: plans with few
-    // chunks per tile (no waits, every chunk tested in one pass) at
-    // kExtractWgsPerCu, plans with more (look-back chains, little work per
-    // workgroup) at kSelectWgsPerCuLarge
-    const bool small = p.n_chunks <= kDirectChunks + 1;
+    // chunks per tile at kExtractWgsPerCu, plans with more (look-back
+    // chains, little work per workgroup) at kSelectWgsPerCuLarge
+    const bool small = select_small(p);
     const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2),
                                   small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
     if (p.world > 1 && small)
@@ -1651,7 +1729,7 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
       hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
     else
       hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
   }
@@ -1912,7 +1990,7 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     if (overlap(r.ptr, r.bytes, out, out_bytes))
       return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.Nc > 0 || p.world > 1) {  // one after the other
+  if (p.world > 1 || (p.Nc > 0 && p.in_dtype != p.out_dtype)) {  // one after the other
     st = launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                         static_cast<char*>(workspace), s, who);
     if (st != TDP_OK) return st;
@@ -1921,6 +1999,19 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     return TDP_OK;
   }
   const DeviceShape ds = device_shape();
+  if (p.Nc > 0) {  // the extent launch, then the selection launch and the blend as one
+    ExtractArgs ca = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
+                                  static_cast<char*>(workspace));
+    st = launch_extent(p, ca, s, who);
+    if (st != TDP_OK) return st;
+    const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
+    const hipError_t e =
+        p.in_dtype == TDP_BF16
+            ? launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, n_lat, tile_out, blend_cond_row, blend_cond_k, out, ds, s)
+            : launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, n_lat, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+    return TDP_OK;
+  }
   int n_lat = 0;
   const ExtractArgs a = pipeline_extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, ds, n_lat);
   hipError_t e;

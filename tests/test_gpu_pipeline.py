@@ -38,6 +38,16 @@ def _case(name):
         "odd_vectors": Workload("odd_vectors", 1, 48, (2, 6, 20), ((1, 0), (2, 2), (2, 3)), seed=23),
         "narrow_rows": Workload("narrow_rows", 1, 8, (2, 6, 20), ((1, 0), (2, 2), (2, 3)), seed=24),
         "wide_4096": Workload("wide_4096", 1, 16, (1, 2, 4096), ((1, 0), (2, 0), (3, 512)), seed=25),
+        # conditioning tokens: few chunks per tile, many (look-back), fp32
+        # rows, more than 256 tiles, rows too wide for one round of loads
+        "many_cond": Workload("many_cond", 1, 128, (2, 8, 12), ((1, 0), (2, 2), (2, 3)), num_cond=3000, num_ref=750,
+                              seed=26),
+        "cond_f32": Workload("cond_f32", 2, 36, (2, 8, 12), ((1, 0), (2, 2), (2, 3)), num_cond=150, num_ref=37,
+                             dtype="f32", seed=27),
+        "tiles272_cond": Workload("tiles272_cond", 1, 16, (1, 16, 17), ((1, 0), (16, 0), (17, 0)), num_cond=20,
+                                  num_ref=5, seed=28),
+        "cond_wide_rows": Workload("cond_wide_rows", 1, 512, (2, 6, 20), ((1, 0), (2, 2), (2, 3)), num_cond=300,
+                                   num_ref=75, seed=29),
     }
     return custom[name]
 
@@ -75,7 +85,8 @@ def _step_vs_two_calls(wl, cuda, out_dtype=None, world=1, rank=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ltx", "fullres", "4k", "conditioned", "frame_tiles", "f32_rows",
-                                  "odd_vectors", "narrow_rows", "wide_4096"])
+                                  "odd_vectors", "narrow_rows", "wide_4096", "many_cond", "cond_f32",
+                                  "tiles272_cond", "cond_wide_rows"])
 def test_step_equals_extract_then_blend(name, cuda):
     wl = _case(name)
     plan, inp_a, _, got_a, _, _ = _step_vs_two_calls(wl, cuda)
@@ -96,6 +107,13 @@ def test_step_fp32_output_and_oracle_blend(cuda):
 @pytest.mark.parametrize("world,rank", [(4, 1), (3, 0)])
 def test_step_rank_plans(world, rank, cuda):
     _step_vs_two_calls(WORKLOADS["fullres"], cuda, out_dtype="f32", world=world, rank=rank)
+    _step_vs_two_calls(WORKLOADS["conditioned"], cuda, out_dtype="f32", world=world, rank=rank)
+
+
+def test_step_conditioned_mixed_dtypes(cuda):
+    """bf16 tiles into an fp32 output with conditioning tokens: the two
+    launches one after the other."""
+    _step_vs_two_calls(WORKLOADS["conditioned"], cuda, out_dtype="f32")
 
 
 def test_step_refuses_shared_buffers(cuda):
