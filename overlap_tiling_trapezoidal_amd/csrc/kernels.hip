@@ -1447,32 +1447,6 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
   return hipGetLastError();
 }
 
-// The extract half's arguments of a pipeline step (whole plan, Nc == 0),
-// as launch_extract sets them up.
-ExtractArgs pipeline_extract_args(const PlanDev& p, const void* latent, const float* pos, void* tile_lat,
-                                  float* tile_pos, int32_t* tile_index, int32_t* tile_count, const DeviceShape& ds,
-                                  int& n_lat) {
-  ExtractArgs a;
-  a.latent = reinterpret_cast<const u32x4*>(latent);
-  a.pos = reinterpret_cast<const f32x2*>(pos);
-  a.tile_lat = reinterpret_cast<u32x4*>(tile_lat);
-  a.tile_pos = reinterpret_cast<f32x2*>(tile_pos);
-  a.tile_index = tile_index;
-  a.tile_count = tile_count;
-  a.cond_row = nullptr;
-  a.cond_k = nullptr;
-  a.ws = nullptr;
-  a.n_ext = 0;
-  a.n_sel = 0;
-  a.lookback_polls = 0;
-  n_lat = (p.lat_units + kWaves - 1) / kWaves;
-  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
-  a.pos_one_pass = latent_bound ? 1 : 0;
-  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
-  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
-  return a;
-}
-
 template <int IN, int OUT>
 hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, const void* tile_out, void* out,
                            const DeviceShape& ds, hipStream_t s) {
@@ -1704,6 +1678,19 @@ int launch_extent(const PlanDev& p, ExtractArgs& a, hipStream_t s, const char* w
   return TDP_OK;
 }
 
+// Extract without conditioning tokens: more than eight latent workgroups
+// per compute unit and the latent copy sets the length (3 per CU, positions
+// in one pass); otherwise the position chains do (2 per CU, parts of at most
+// 1024 rows).  Sets the position fields of `a`; returns whether the plan is
+// latent-bound.
+bool plain_setup(const PlanDev& p, ExtractArgs& a, const DeviceShape& ds, int n_lat) {
+  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
+  a.pos_one_pass = latent_bound ? 1 : 0;
+  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  return latent_bound;
+}
+
 int launch_extract(const PlanDev& p, const void* latent, const float* pos, void* tile_lat, float* tile_pos,
                    int32_t* tile_index, int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, char* ws,
                    hipStream_t s, const char* who) {
@@ -1733,13 +1720,7 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
   }
-  // More than eight latent workgroups per compute unit: the latent copy
-  // sets the length (3 per CU, positions in one pass); otherwise the
-  // position chains do (2 per CU, parts of at most 1024 rows).
-  const bool latent_bound = n_lat > 8 * (ds.cus > 0 ? ds.cus : 256);
-  a.pos_one_pass = latent_bound ? 1 : 0;
-  a.pos_parts = latent_bound ? p.pos_parts_one : p.pos_parts;
-  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  const bool latent_bound = plain_setup(p, a, ds, n_lat);
   const dim3 grid(a.n_pos + n_lat);
   if (grid.x == 0) return TDP_OK;  // a rank without tiles: nothing to write
   const size_t lds = capped_lds(ds, 0, latent_bound ? kExtractWgsPerCu : kExtractWgsPerCuChain);
@@ -2012,8 +1993,9 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
   }
-  int n_lat = 0;
-  const ExtractArgs a = pipeline_extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, ds, n_lat);
+  ExtractArgs a = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k, nullptr);
+  const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
+  plain_setup(p, a, ds, n_lat);
   hipError_t e;
   if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
     e = launch_pipeline<TDP_BF16, TDP_BF16>(p, a, n_lat, tile_out, out, ds, s);
