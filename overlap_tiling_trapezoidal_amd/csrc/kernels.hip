@@ -848,11 +848,14 @@ __device__ inline void xcd_group(int bid, int items, int parts, int& item, int& 
 // all of them.  It also clears what the selection launch counts into: part
 // 0 the tile's look-back flags, and the workgroups together cond_k.  Every
 // tile is reduced, in rank plans too, since k counts the tiles of all
-// ranks.
+// ranks.  In the pipeline step the workgroups past the first a.n_ext copy
+// the generated latent rows, which depend on neither the extents nor the
+// selection, so that the bulk of the extract's bytes shares no launch with
+// the blend; a plain extract keeps them in the selection launch, where
+// they stream while the selection's chains wait.
 template <int NP>
-__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const ExtractArgs a) {
+__device__ void extent_body(const PlanDev& p, const ExtractArgs& a, int bid) {
   __shared__ float2 red[kWaves][NP];
-  const int bid = blockIdx.x;
   int t, q;
   xcd_group(bid, p.T, p.ext_parts, t, q);  // the parts of a tile share an L2
   const TileBox tb = tile_box<false>(p, t);
@@ -864,7 +867,7 @@ __global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const E
     uint32_t* flags = ws_flags(p, a) + (int64_t)t * p.n_chunks;
     for (int i = tid; i < p.n_chunks; i += kBlock) flags[i] = 0u;
   }
-  for (int c = bid * kBlock + tid; c < p.Nc; c += (int)gridDim.x * kBlock) a.cond_k[c] = 0;
+  for (int c = bid * kBlock + tid; c < p.Nc; c += a.n_ext * kBlock) a.cond_k[c] = 0;
   float2* out = ws_part_w(p, a) + ((int64_t)t * p.ext_parts + q) * planes;
   // (a repeated row or plane leaves a minimum and a maximum as they are;
   // an empty part stores +inf and -inf, which the combine ignores)
@@ -913,6 +916,13 @@ __global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const E
     __syncthreads();  // red is reused by the next pass
   }
 }
+template <int NP, bool LAT>
+__global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const ExtractArgs a) {
+  if (!LAT || (int)blockIdx.x < a.n_ext)
+    extent_body<NP>(p, a, blockIdx.x);
+  else if constexpr (LAT)
+    extract_latent<false>(p, a, (int)blockIdx.x - a.n_ext);  // whole plans only
+}
 
 // Every position workgroup of a launch: (tile, batch, axis, part) of `bid`.
 struct PosWork {
@@ -956,12 +966,13 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
 //                              tile-major: selection and kept rows;
 //   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part),
 //                              shifted by the tile's extent parts;
-//   [.., + latent blocks)      generated latent rows per (line, chunk).
+//   [.., + latent blocks)      generated latent rows per (line, chunk),
+//                              when LAT (else the extent launch copies them).
 // Only wave 0 of a selection workgroup waits on others (the flags of the
 // tile's earlier chunks), never without bound.  Rank plans: selection over
 // every tile (k counts the tiles of all ranks), the rest for the held
 // tiles.
-template <bool R, bool SMALL>
+template <bool R, bool SMALL, bool LAT>
 __device__ void select_body(const PlanDev& p, const ExtractArgs& a, int bid) {
   if (bid < a.n_sel) {
     extern __shared__ float2 ext_s[];  // dynamic: at least B * 3 (the launch asks for it)
@@ -970,17 +981,17 @@ __device__ void select_body(const PlanDev& p, const ExtractArgs& a, int bid) {
     extract_cond_chunk<R, SMALL>(p, a, cs, ext_s, t, bid - t * p.n_chunks);
     return;
   }
-  if (bid - a.n_sel < a.n_pos) {
+  if (!LAT || bid - a.n_sel < a.n_pos) {
     const PosWork w = pos_work<R>(p, a, bid - a.n_sel);
     extract_positions_copy<R>(p, a, w.t, w.b, w.d, w.part,
                               p.normalize ? tile_min_start(p, a, w.t, w.b * 3 + w.d) : 0.0f);
     return;
   }
-  extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
+  if constexpr (LAT) extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
 }
 template <bool R, bool SMALL>
 __global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
-  select_body<R, SMALL>(p, a, blockIdx.x);
+  select_body<R, SMALL, true>(p, a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1308,10 +1319,10 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
 }
 
 // One step of a pipelined loop for whole plans with conditioning tokens,
-// after the extent launch: the selection launch's workgroups (selection,
-// positions, latent rows), then the blend's (its conditioning rows, then its
-// generated rows), as one launch, so the blend's bulk copy runs under the
-// selection's dependent chains and fills the units as the extract drains.
+// after the extent launch (which copies the generated latent rows): the
+// selection launch's workgroups (selection, positions), then the blend's
+// (its conditioning rows, then its generated rows), as one launch, so the
+// blend's bulk copy runs under the selection's dependent chains.
 template <int IN, int OUT, bool F2, bool SMALL>
 __global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, const ExtractArgs a,
                                                                const u32x4* __restrict__ tile_out,
@@ -1320,7 +1331,7 @@ __global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, 
                                                                void* __restrict__ out, int n_ext, int n_bcond) {
   const int bid = blockIdx.x;
   if (bid < n_ext) {
-    select_body<false, SMALL>(p, a, bid);
+    select_body<false, SMALL, false>(p, a, bid);
     return;
   }
   blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
@@ -1468,10 +1479,10 @@ bool select_small(const PlanDev& p) { return p.n_chunks <= kDirectChunks + 1; }
 // The pipeline step of a whole plan with conditioning tokens, after
 // launch_extent: its selection launch and the blend as one launch.
 template <int IN, int OUT>
-hipError_t launch_pipeline_cond(const PlanDev& p, const ExtractArgs& a, int n_lat, const void* tile_out,
+hipError_t launch_pipeline_cond(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
                                 const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
                                 const DeviceShape& ds, hipStream_t s) {
-  const int n_ext = a.n_sel + a.n_pos + n_lat;
+  const int n_ext = a.n_sel + a.n_pos;
   const int n_bcond = blend_cond_blocks(p);
   const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
   const size_t sel_lds = (size_t)p.B * 3 * sizeof(float2), bl_lds = blend_cond_lds(p);
@@ -1661,15 +1672,24 @@ ExtractArgs extract_args(const PlanDev& p, const void* latent, const float* pos,
   return a;
 }
 
-// The extent launch (Nc > 0); then the selection launch's workgroups are
-// a.n_sel selection, a.n_pos positions (copies: the shift is known) and the
-// latent rows.
-int launch_extent(const PlanDev& p, ExtractArgs& a, hipStream_t s, const char* who) {
-  const dim3 egrid((unsigned)a.n_ext), block(kBlock);
-  if (p.B == 1)
-    hipLaunchKernelGGL(extent_kernel<3>, egrid, block, 0, s, p, a);
+// The extent launch (Nc > 0), with the generated latent rows when
+// `with_latent` (whole plans); then the selection launch's workgroups are
+// a.n_sel selection, a.n_pos positions (copies: the shift is known) and,
+// unless the extent launch took them, the latent rows.
+int launch_extent(const PlanDev& p, ExtractArgs& a, const DeviceShape& ds, bool with_latent, hipStream_t s,
+                  const char* who) {
+  if (with_latent && p.world > 1) return fail(TDP_EINVAL, "%s: latent rows in the extent launch of a rank plan", who);
+  const int n_lat = with_latent ? (p.lat_units + kWaves - 1) / kWaves : 0;
+  const dim3 egrid((unsigned)(a.n_ext + n_lat)), block(kBlock);
+  const size_t lds = with_latent ? capped_lds(ds, 0, kExtractWgsPerCu) : 0;
+  if (p.B == 1 && with_latent)
+    hipLaunchKernelGGL((extent_kernel<3, true>), egrid, block, lds, s, p, a);
+  else if (p.B == 1)
+    hipLaunchKernelGGL((extent_kernel<3, false>), egrid, block, lds, s, p, a);
+  else if (with_latent)
+    hipLaunchKernelGGL((extent_kernel<6, true>), egrid, block, lds, s, p, a);
   else
-    hipLaunchKernelGGL(extent_kernel<6>, egrid, block, 0, s, p, a);
+    hipLaunchKernelGGL((extent_kernel<6, false>), egrid, block, lds, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "%s: extent launch failed: %s", who, hipGetErrorString(e));
   a.pos_one_pass = 0;
@@ -1699,7 +1719,7 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
   const dim3 block(kBlock);
   if (p.Nc > 0) {
-    const int st = launch_extent(p, a, s, who);
+    const int st = launch_extent(p, a, ds, false, s, who);
     if (st != TDP_OK) return st;
     const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat));
     // the tile's extent, and a cap on workgroups per CU: plans with few
@@ -1983,13 +2003,12 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
   if (p.Nc > 0) {  // the extent launch, then the selection launch and the blend as one
     ExtractArgs ca = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                                   static_cast<char*>(workspace));
-    st = launch_extent(p, ca, s, who);
+    st = launch_extent(p, ca, ds, true, s, who);
     if (st != TDP_OK) return st;
-    const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
     const hipError_t e =
         p.in_dtype == TDP_BF16
-            ? launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, n_lat, tile_out, blend_cond_row, blend_cond_k, out, ds, s)
-            : launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, n_lat, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+            ? launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s)
+            : launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
   }
