@@ -363,7 +363,10 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * tile_out, blend_cond_row, blend_cond_k, out) would, with bit-identical
  * results.  For whole plans without conditioning tokens both run as one
  * launch, the extract's workgroups first, so the blend's fill the GPU while
- * the extract's drain; other plans enqueue the two one after the other.
+ * the extract's drain; whole plans with conditioning tokens whose tiles and
+ * output share a dtype take two launches (the extents with the latent rows,
+ * then the selection with the blend); rank plans and other dtypes enqueue
+ * the two calls one after the other.
  * The two halves may run at the same time, so the blend's buffers must be
  * none of the extract's: TDP_EINVAL, nothing enqueued, when tile_out,
  * blend_cond_row or blend_cond_k overlaps a buffer the extract writes, or
@@ -376,6 +379,51 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
                       void* workspace, const void* tile_out,
                       const int32_t* blend_cond_row, const int32_t* blend_cond_k,
                       void* out, void* stream);
+
+/* The extract in two halves, for callers whose positions stay the same
+ * over many latents (the positions grid of a denoising stage).  Each tile's
+ * shift is its generated tokens' minimum start (TDP docs, "Position
+ * normalization") and a conditioning token's keep test reads only its
+ * interval and the tile's (TDP docs, "Shared negative (reference)
+ * positions"), so everything but the latent rows is a function of the
+ * positions alone.
+ *
+ * tdp_extract_positions writes what tdp_extract writes except tile_lat:
+ * tile_pos, tile_index, tile_count and, when Nc > 0, cond_row and cond_k,
+ * bit-identical to tdp_extract on the same plan and positions.  Arguments,
+ * layouts, workspace and errors as tdp_extract without latent and
+ * tile_lat. */
+int tdp_extract_positions(const tdp_plan* plan, const float* pos, float* tile_pos,
+                          int32_t* tile_index, int32_t* tile_count, int32_t* cond_row,
+                          int32_t* cond_k, void* workspace, void* stream);
+
+/* tdp_extract_latent writes tile_lat from latent (B, N+Nc, C) in_dtype:
+ * every held tile's generated rows (its slice of the grid, TDP docs, "What
+ * it is") and its kept conditioning rows at the slot rows cond_row gives.
+ * cond_row (T, Nc) int32 must come from tdp_extract_positions or
+ * tdp_extract on the same plan and positions (NULL allowed when Nc == 0);
+ * with it, tile_lat is bit-identical to tdp_extract's.  One launch, no
+ * workspace, no waiting between workgroups.  Device pointers except plan;
+ * latent and tile_lat 16-byte aligned, cond_row 4-byte aligned; TDP_EINVAL
+ * for a null or misaligned pointer (nothing enqueued), TDP_EHIP when the
+ * launch fails. */
+int tdp_extract_latent(const tdp_plan* plan, const void* latent, const int32_t* cond_row,
+                       void* tile_lat, void* stream);
+
+/* One step of a pipelined loop over latents that share one positions set:
+ * tdp_extract_latent(plan, latent, cond_row, tile_lat) and tdp_blend(plan,
+ * tile_out, blend_cond_row, blend_cond_k, out), bit-identical to the two
+ * calls.  Whole plans run both as one launch, the gather's workgroups
+ * first; rank plans enqueue the two calls in order.  cond_row and
+ * blend_cond_row may be the same buffer (both halves only read them).
+ * TDP_EINVAL, nothing enqueued, when tile_lat overlaps tile_out,
+ * blend_cond_row, blend_cond_k or out, or out overlaps latent or cond_row
+ * (extents from tdp_plan_sizes).  Other arguments, alignments and errors as
+ * the two calls. */
+int tdp_pipeline_latent_step(const tdp_plan* plan, const void* latent, const int32_t* cond_row,
+                             void* tile_lat, const void* tile_out,
+                             const int32_t* blend_cond_row, const int32_t* blend_cond_k,
+                             void* out, void* stream);
 
 /* Streaming blend, for schedules that produce one tile output at a time
  * (TDP docs, "What it is": a rank runs its tiles in turn and their blended

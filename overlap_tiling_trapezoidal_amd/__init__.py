@@ -20,7 +20,8 @@ DEFAULT_LIB_PATH = os.path.join(_HERE, "libtdp.so")
 # built with address and undefined-behaviour sanitizers for the CPU tests
 # (build.py --host-sanitized); such a build may lack the device entry points.
 LIB_PATH = os.environ.get("TDP_LIBRARY") or DEFAULT_LIB_PATH
-DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_set_lookback_polls", "tdp_pipeline_step", "tdp_blend",
+DEVICE_FUNCTIONS = ("tdp_extract", "tdp_extract_noalloc", "tdp_set_lookback_polls", "tdp_pipeline_step",
+                    "tdp_extract_positions", "tdp_extract_latent", "tdp_pipeline_latent_step", "tdp_blend",
                     "tdp_blend_tile", "tdp_blend_finish", "tdp_pixel_blend")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdp.h")
 
@@ -163,6 +164,9 @@ def load_library(path: str = LIB_PATH):
         "tdp_extract_noalloc": (ctypes.c_int, [vp] * 10),
         "tdp_set_lookback_polls": (ctypes.c_int, [i32]),
         "tdp_pipeline_step": (ctypes.c_int, [vp] * 15),
+        "tdp_extract_positions": (ctypes.c_int, [vp] * 9),
+        "tdp_extract_latent": (ctypes.c_int, [vp] * 5),
+        "tdp_pipeline_latent_step": (ctypes.c_int, [vp] * 9),
         "tdp_blend": (ctypes.c_int, [vp] * 6),
         "tdp_blend_tile": (ctypes.c_int, [vp, i32, vp, vp, vp, vp, vp]),
         "tdp_blend_finish": (ctypes.c_int, [vp] * 4),
@@ -519,6 +523,72 @@ def tdp_pipeline_step(plan: Plan, latent, pos, tile_lat, tile_pos, tile_index, t
         _stream_handle(stream, dev),
     ]
     _check(load_library().tdp_pipeline_step(*args))
+
+
+def tdp_extract_positions(plan: Plan, pos, tile_pos, tile_index, tile_count, cond_row=None, cond_k=None,
+                          workspace=None, stream=None):
+    """Enqueue what tdp_extract writes except the latent rows (tile positions,
+    index map, counts, cond_row, cond_k): once per positions set."""
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    rows = plan.tokens + c.num_cond
+    dev = pos.device
+    none = ctypes.c_void_p(None)
+    args = [
+        plan.handle,
+        _ptr(pos, "pos", torch.float32, c.batch * 3 * rows * 2, dev),
+        _ptr(tile_pos, "tile_pos", torch.float32, s.tile_pos_floats, dev),
+        _ptr(tile_index, "tile_index", torch.int32, s.tile_index_ints, dev),
+        _ptr(tile_count, "tile_count", torch.int32, s.num_slots, dev),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
+        _ptr(cond_k, "cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
+        _ptr(workspace, "workspace", torch.uint8, s.workspace_bytes, dev) if s.workspace_bytes else none,
+        _stream_handle(stream, dev),
+    ]
+    _check(load_library().tdp_extract_positions(*args))
+
+
+def _gather_args(plan: Plan, latent, cond_row, tile_lat):
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    rows = plan.tokens + c.num_cond
+    dev = latent.device
+    return [
+        plan.handle,
+        _ptr(latent, "latent", _torch_dtype(c.in_dtype), c.batch * rows * c.channels, dev),
+        _ptr(cond_row, "cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else ctypes.c_void_p(None),
+        _ptr(tile_lat, "tile_lat", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
+    ]
+
+
+def tdp_extract_latent(plan: Plan, latent, cond_row, tile_lat, stream=None):
+    """Enqueue the latent rows of every held tile into ``tile_lat``, at the
+    slot rows ``cond_row`` (from tdp_extract_positions) gives."""
+    args = _gather_args(plan, latent, cond_row, tile_lat)
+    args.append(_stream_handle(stream, latent.device))
+    _check(load_library().tdp_extract_latent(*args))
+
+
+def tdp_pipeline_latent_step(plan: Plan, latent, cond_row, tile_lat, *, tile_out, blend_cond_row=None,
+                             blend_cond_k=None, out, stream=None):
+    """Enqueue tdp_extract_latent of ``latent`` and tdp_blend of ``tile_out``
+    as one step (one launch for whole plans)."""
+    import torch
+    c = plan.cfg
+    s = tdp_plan_sizes(plan)
+    dev = latent.device
+    none = ctypes.c_void_p(None)
+    args = _gather_args(plan, latent, cond_row, tile_lat)
+    args += [
+        _ptr(tile_out, "tile_out", _torch_dtype(c.in_dtype), s.tile_lat_elems, dev),
+        _ptr(blend_cond_row, "blend_cond_row", torch.int32, s.cond_row_ints, dev) if c.num_cond else none,
+        _ptr(blend_cond_k, "blend_cond_k", torch.int32, s.cond_k_ints, dev) if c.num_cond else none,
+        _ptr(out, "out", _torch_dtype(c.out_dtype), s.out_elems, dev),
+        _stream_handle(stream, dev),
+    ]
+    _check(load_library().tdp_pipeline_latent_step(*args))
 
 
 def allocate_accumulator(plan: Plan, device="cuda"):

@@ -216,6 +216,7 @@ struct ExtractArgs {
   int32_t* cond_k;       // (Nc)
   char* ws;              // workspace: extent partials and look-back flags (Nc > 0), else null
   int n_ext, n_sel, n_pos, pos_parts;
+  int copy_latent;       // 0: positions, index, counts and selection only (no latent rows)
   int pos_one_pass;      // position workgroups hold their part in registers (one pass)
   int lookback_polls;    // reads of an unpublished flag before a wave counts that chunk itself
 };
@@ -479,7 +480,8 @@ __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondS
   const int ntok = min(kCondChunk, p.Nc - ch * kCondChunk);
   // (b, token j, vector) of the whole chunk, token-minor over vectors
   const int all_vec = p.B * kCondChunk * V;
-  const bool early = SMALL && held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
+  const bool lat = a.copy_latent != 0;
+  const bool early = lat && SMALL && held_t && all_vec <= kBlock * kCopyBatch && p.B <= 2;  // workgroup-uniform
   u32x4 v[kCopyBatch];
   f32x2 w[kPosPer];
   if (early) {
@@ -527,7 +529,7 @@ __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondS
   const bool copy = held_t && n > 0 && !early;  // the copy after the test
   const FastDiv by_n = make_fastdiv((uint32_t)(n > 0 ? n : 1));
   const int total = p.B * n * V;
-  if (copy) {
+  if (copy && lat) {
 #pragma unroll
     for (int q = 0; q < kCopyBatch; ++q) {
       const KeptVec k = kept_vec(p, by_n, n, min(q * kBlock + tid, total - 1));
@@ -583,7 +585,7 @@ __device__ void extract_cond_chunk(const PlanDev& p, const ExtractArgs& a, CondS
     return;
   }
   if (!copy) return;
-  for (int e0 = 0; e0 < total; e0 += kBlock * kCopyBatch) {
+  for (int e0 = 0; lat && e0 < total; e0 += kBlock * kCopyBatch) {
     if (e0 > 0) {
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) {
@@ -995,6 +997,70 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const E
 }
 
 // ---------------------------------------------------------------------------
+// latent gather from a selection already made (tdp_extract_latent)
+// ---------------------------------------------------------------------------
+
+// Workgroup (held tile slot, chunk of kCondChunk conditioning tokens): the
+// chunk's cond_row entries give each kept token's slot row, and the kept
+// tokens' rows are copied there, every batch element.  cond_row comes from
+// the selection of the same positions, so the rows land where tdp_extract
+// puts them.
+template <bool R>
+__device__ void gather_cond_chunk(const PlanDev& p, const ExtractArgs& a, int bid) {
+  __shared__ uint64_t mask_s;
+  __shared__ int row_s[kCondChunk];
+  const int slot = bid / p.n_chunks, ch = bid - slot * p.n_chunks;
+  const int t = R ? p.rank + slot * p.world : slot;
+  const int tid = threadIdx.x;
+  const int c0 = ch * kCondChunk;
+  if (tid < kCondChunk) {  // wave 0: one token per lane
+    const int c = c0 + tid;
+    const int row = c < p.Nc ? a.cond_row[(int64_t)t * p.Nc + c] : -1;
+    row_s[tid] = row;
+    const uint64_t m = __ballot(row >= 0);
+    if (tid == 0) mask_s = m;
+  }
+  __syncthreads();
+  const uint64_t mask = mask_s;
+  const int n = __popcll(mask);
+  if (n == 0) return;
+  const TileBox tb = tile_box<R>(p, t);
+  const int V = p.vin;
+  const FastDiv by_n = make_fastdiv((uint32_t)n);
+  const int total = p.B * n * V;  // (b, kept jj, vector)
+  for (int e0 = 0; e0 < total; e0 += kBlock * kCopyBatch) {
+    u32x4 v[kCopyBatch];
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const KeptVec k = kept_vec(p, by_n, n, min(e0 + q * kBlock + tid, total - 1));
+      v[q] = ld_nt(a.latent + ((int64_t)k.b * p.rows + p.N + c0 + nth_set_bit(mask, k.jj)) * V + k.vv);
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyBatch; ++q) {
+      const int e = e0 + q * kBlock + tid;
+      if (e < total) {
+        const KeptVec k = kept_vec(p, by_n, n, e);
+        const int row = row_s[nth_set_bit(mask, k.jj)];
+        st_nt(a.tile_lat + (tb.s.row_base + (int64_t)k.b * tb.s.cap + row) * V + k.vv, v[q]);
+      }
+    }
+  }
+}
+
+// tdp_extract_latent: [0, n_cg) conditioning chunks of the held tiles
+// (short chains, so first), then the generated latent rows per (line,
+// chunk), as in the extract.
+template <bool R>
+__global__ __launch_bounds__(kBlock) void gather_kernel(const PlanDev p, const ExtractArgs a, int n_cg) {
+  const int bid = blockIdx.x;
+  if (bid < n_cg) {
+    gather_cond_chunk<R>(p, a, bid);
+    return;
+  }
+  extract_latent<R>(p, a, bid - n_cg);
+}
+
+// ---------------------------------------------------------------------------
 // blend
 // ---------------------------------------------------------------------------
 
@@ -1337,6 +1403,29 @@ __global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, 
   blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
 }
 
+// One step of a pipelined loop whose positions do not change (whole plans):
+// the latent gather of one latent (tdp_extract_latent: conditioning chunks,
+// then generated rows) and the blend of other tile outputs, as one launch.
+// Every workgroup is a copy or a short chain; none waits on another.
+template <int IN, int OUT, bool F2>
+__global__ __launch_bounds__(kBlock) void pipeline_latent_kernel(const PlanDev p, const ExtractArgs a,
+                                                                 const u32x4* __restrict__ tile_out,
+                                                                 const int32_t* __restrict__ blend_cond_row,
+                                                                 const int32_t* __restrict__ blend_cond_k,
+                                                                 void* __restrict__ out, int n_cg, int n_ext,
+                                                                 int n_bcond) {
+  const int bid = blockIdx.x;
+  if (bid < n_cg) {
+    gather_cond_chunk<false>(p, a, bid);
+    return;
+  }
+  if (bid < n_ext) {
+    extract_latent<false>(p, a, bid - n_cg);
+    return;
+  }
+  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
+}
+
 // One step of a pipelined loop (whole plans without conditioning tokens):
 // the extract of one latent and the blend of other tile outputs that share
 // no buffer with it, as one launch.  Grid: the extract's workgroups
@@ -1455,6 +1544,29 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
     hipLaunchKernelGGL((blend_kernel<IN, OUT, false, true>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else
     hipLaunchKernelGGL((blend_kernel<IN, OUT, false, false>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
+  return hipGetLastError();
+}
+
+// The latent gather of one latent and the blend of other tile outputs
+// (whole plans), one launch: conditioning chunks, generated latent rows,
+// then the blend's conditioning and generated workgroups.
+template <int IN, int OUT>
+hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
+                                  const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
+                                  const DeviceShape& ds, hipStream_t s) {
+  const int n_cg = p.Nc > 0 ? p.T * p.n_chunks : 0;
+  const int n_ext = n_cg + (p.lat_units + kWaves - 1) / kWaves;
+  const int n_bcond = blend_cond_blocks(p);
+  const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
+  const size_t lds = capped_lds(ds, blend_cond_lds(p), kPipelineWgsPerCu);
+  const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
+  const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
+  if (p.ax[0].n > 1)
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_cg, n_ext, n_bcond);
+  else
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_cg, n_ext, n_bcond);
   return hipGetLastError();
 }
 
@@ -1666,6 +1778,7 @@ ExtractArgs extract_args(const PlanDev& p, const void* latent, const float* pos,
   a.n_ext = p.Nc > 0 ? p.T * p.ext_parts : 0;
   a.n_sel = p.Nc > 0 ? p.T * p.n_chunks : 0;
   a.lookback_polls = g_lookback_polls.load(std::memory_order_relaxed);
+  a.copy_latent = 1;
   a.pos_one_pass = 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = 0;
@@ -1753,6 +1866,70 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
   return TDP_OK;
 }
 
+// tdp_extract_positions: what tdp_extract writes except the latent rows.
+// Nc > 0: the extent launch, then the selection launch without its latent
+// blocks (selection workgroups copy only positions); Nc = 0: the position
+// workgroups of the plain extract, in parts of at most 1024 rows.
+int launch_positions(const PlanDev& p, const float* pos, float* tile_pos, int32_t* tile_index, int32_t* tile_count,
+                     int32_t* cond_row, int32_t* cond_k, char* ws, hipStream_t s, const char* who) {
+  ExtractArgs a = extract_args(p, nullptr, pos, nullptr, tile_pos, tile_index, tile_count, cond_row, cond_k, ws);
+  a.copy_latent = 0;
+  const DeviceShape ds = device_shape();
+  const dim3 block(kBlock);
+  if (p.Nc > 0) {
+    const int st = launch_extent(p, a, ds, false, s, who);
+    if (st != TDP_OK) return st;
+    const dim3 sgrid((unsigned)(a.n_sel + a.n_pos));
+    const bool small = select_small(p);
+    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2),
+                                  small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
+    if (p.world > 1 && small)
+      hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, lds, s, p, a);
+    else if (p.world > 1)
+      hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, lds, s, p, a);
+    else if (small)
+      hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
+    else
+      hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
+    return TDP_OK;
+  }
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  const dim3 grid((unsigned)a.n_pos);
+  if (grid.x == 0) return TDP_OK;  // a rank without tiles: nothing to write
+  const size_t lds = capped_lds(ds, 0, kExtractWgsPerCuChain);
+  if (p.world > 1)
+    hipLaunchKernelGGL(extract_kernel<true>, grid, block, lds, s, p, a);
+  else
+    hipLaunchKernelGGL(extract_kernel<false>, grid, block, lds, s, p, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return TDP_OK;
+}
+
+// Workgroups of the latent gather: conditioning chunks of the held tiles,
+// then generated latent blocks.
+int gather_cond_blocks(const PlanDev& p) { return p.Nc > 0 ? p.T_local * p.n_chunks : 0; }
+
+// tdp_extract_latent: the latent rows of every held tile.
+int launch_gather(const PlanDev& p, const void* latent, const int32_t* cond_row, void* tile_lat, hipStream_t s,
+                  const char* who) {
+  ExtractArgs a = extract_args(p, latent, nullptr, tile_lat, nullptr, nullptr, nullptr, const_cast<int32_t*>(cond_row),
+                               nullptr, nullptr);
+  const int n_cg = gather_cond_blocks(p);
+  const dim3 grid((unsigned)(n_cg + (p.lat_units + kWaves - 1) / kWaves)), block(kBlock);
+  if (grid.x == 0) return TDP_OK;  // a rank without tiles: nothing to write
+  const size_t lds = capped_lds(device_shape(), 0, kExtractWgsPerCu);
+  if (p.world > 1)
+    hipLaunchKernelGGL(gather_kernel<true>, grid, block, lds, s, p, a, n_cg);
+  else
+    hipLaunchKernelGGL(gather_kernel<false>, grid, block, lds, s, p, a, n_cg);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return TDP_OK;
+}
+
 // Checks tdp_extract and tdp_extract_noalloc share (the workspace aside).
 int check_extract(const tdp_plan* plan, const void* latent, const float* pos, const void* tile_lat,
                   const float* tile_pos, const int32_t* tile_index, const int32_t* tile_count, const int32_t* cond_row,
@@ -1770,6 +1947,37 @@ int check_extract(const tdp_plan* plan, const void* latent, const float* pos, co
   if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
       !aligned(cond_row, 4) || !aligned(cond_k, 4))
     return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
+  return TDP_OK;
+}
+
+// Checks of tdp_extract_positions' arguments (the workspace aside).
+int check_positions(const tdp_plan* plan, const float* pos, const float* tile_pos, const int32_t* tile_index,
+                    const int32_t* tile_count, const int32_t* cond_row, const int32_t* cond_k, const char* who) {
+  if (!plan) return fail(TDP_EINVAL, "%s: null plan", who);
+  if (!plan->guarded) return fail(TDP_EGUARD, "%s: plan was built with TDP_UNGUARDED", who);
+  const PlanDev& p = plan->dev;
+  if (!pos || (p.T_local > 0 && (!tile_pos || !tile_index || !tile_count)))
+    return fail(TDP_EINVAL, "%s: null device pointer", who);
+  if (p.Nc > 0 && (!cond_row || !cond_k))
+    return fail(TDP_EINVAL, "%s: cond_row and cond_k are required when num_cond > 0", who);
+  if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
+      !aligned(cond_row, 4) || !aligned(cond_k, 4))
+    return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
+  return TDP_OK;
+}
+
+// Checks of tdp_extract_latent's arguments (shared with
+// tdp_pipeline_latent_step).
+int check_gather(const tdp_plan* plan, const void* latent, const int32_t* cond_row, const void* tile_lat,
+                 const char* who) {
+  if (!plan) return fail(TDP_EINVAL, "%s: null plan", who);
+  if (!plan->guarded) return fail(TDP_EGUARD, "%s: plan was built with TDP_UNGUARDED", who);
+  const PlanDev& p = plan->dev;
+  if (!latent || (p.T_local > 0 && !tile_lat)) return fail(TDP_EINVAL, "%s: null device pointer", who);
+  if (p.Nc > 0 && !cond_row) return fail(TDP_EINVAL, "%s: cond_row is required when num_cond > 0", who);
+  if (!aligned(latent, 16) || !aligned(tile_lat, 16))
+    return fail(TDP_EINVAL, "%s: latent and tile_lat must be 16-byte aligned", who);
+  if (!aligned(cond_row, 4)) return fail(TDP_EINVAL, "%s: misaligned cond_row", who);
   return TDP_OK;
 }
 
@@ -1950,6 +2158,76 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
   if (st != TDP_OK) return st;
   const hipError_t e = blend_dispatch(plan->dev, tile_out, cond_row, cond_k, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TDP_EHIP, "tdp_blend: kernel launch failed: %s", hipGetErrorString(e));
+  return TDP_OK;
+}
+
+int tdp_extract_positions(const tdp_plan* plan, const float* pos, float* tile_pos, int32_t* tile_index,
+                          int32_t* tile_count, int32_t* cond_row, int32_t* cond_k, void* workspace, void* stream) {
+  const char* who = "tdp_extract_positions";
+  const int st = check_positions(plan, pos, tile_pos, tile_index, tile_count, cond_row, cond_k, who);
+  if (st != TDP_OK) return st;
+  const PlanDev& p = plan->dev;
+  if (ws_layout(p).bytes > 0 && !workspace)
+    return fail(TDP_EINVAL, "%s: workspace of %lld bytes is required (tdp_plan_sizes)", who,
+                (long long)ws_layout(p).bytes);
+  if (!aligned(workspace, 16)) return fail(TDP_EINVAL, "%s: workspace must be 16-byte aligned", who);
+  return launch_positions(p, pos, tile_pos, tile_index, tile_count, cond_row, cond_k, static_cast<char*>(workspace),
+                          reinterpret_cast<hipStream_t>(stream), who);
+}
+
+int tdp_extract_latent(const tdp_plan* plan, const void* latent, const int32_t* cond_row, void* tile_lat,
+                       void* stream) {
+  const char* who = "tdp_extract_latent";
+  const int st = check_gather(plan, latent, cond_row, tile_lat, who);
+  if (st != TDP_OK) return st;
+  return launch_gather(plan->dev, latent, cond_row, tile_lat, reinterpret_cast<hipStream_t>(stream), who);
+}
+
+int tdp_pipeline_latent_step(const tdp_plan* plan, const void* latent, const int32_t* cond_row, void* tile_lat,
+                             const void* tile_out, const int32_t* blend_cond_row, const int32_t* blend_cond_k,
+                             void* out, void* stream) {
+  const char* who = "tdp_pipeline_latent_step";
+  int st = check_gather(plan, latent, cond_row, tile_lat, who);
+  if (st != TDP_OK) return st;
+  st = check_blend(plan, tile_out, blend_cond_row, blend_cond_k, out, who);
+  if (st != TDP_OK) return st;
+  const PlanDev& p = plan->dev;
+  // the halves may run at the same time: tile_lat is written by the gather
+  // and must be none of the blend's buffers, and out none of the gather's
+  tdp_sizes z;
+  tdp_plan_sizes(plan, &z);
+  const int64_t ein = dtype_bytes(p.in_dtype), eout = dtype_bytes(p.out_dtype);
+  const int64_t lat_bytes = z.tile_lat_elems * ein, out_bytes = z.out_elems * eout;
+  const struct { const void* ptr; int64_t bytes; } bl[] = {
+      {tile_out, lat_bytes}, {blend_cond_row, z.cond_row_ints * 4}, {blend_cond_k, z.cond_k_ints * 4}, {out, out_bytes}},
+    gr[] = {{latent, (int64_t)p.B * p.rows * p.C * ein}, {cond_row, z.cond_row_ints * 4}};
+  for (const auto& b : bl)
+    if (overlap(tile_lat, lat_bytes, b.ptr, b.bytes))
+      return fail(TDP_EINVAL, "%s: the blend reads or writes tile_lat, which the gather writes", who);
+  for (const auto& g : gr)
+    if (overlap(g.ptr, g.bytes, out, out_bytes))
+      return fail(TDP_EINVAL, "%s: the blend writes a buffer the gather reads", who);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.world > 1) {  // one after the other
+    st = launch_gather(p, latent, cond_row, tile_lat, s, who);
+    if (st != TDP_OK) return st;
+    const hipError_t e = blend_dispatch(p, tile_out, blend_cond_row, blend_cond_k, out, s);
+    if (e != hipSuccess) return fail(TDP_EHIP, "%s: blend launch failed: %s", who, hipGetErrorString(e));
+    return TDP_OK;
+  }
+  const ExtractArgs a = extract_args(p, latent, nullptr, tile_lat, nullptr, nullptr, nullptr,
+                                     const_cast<int32_t*>(cond_row), nullptr, nullptr);
+  const DeviceShape ds = device_shape();
+  hipError_t e;
+  if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
+    e = launch_pipeline_latent<TDP_BF16, TDP_BF16>(p, a, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+  else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
+    e = launch_pipeline_latent<TDP_BF16, TDP_F32>(p, a, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+  else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
+    e = launch_pipeline_latent<TDP_F32, TDP_F32>(p, a, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+  else
+    e = launch_pipeline_latent<TDP_F32, TDP_BF16>(p, a, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
   return TDP_OK;
 }
 

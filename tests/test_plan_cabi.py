@@ -244,6 +244,55 @@ def test_pipeline_step_refuses_before_launch(lib):
 
 
 @pytest.mark.device_abi
+def test_split_extract_refuses_before_launch(lib):
+    """tdp_extract_positions, tdp_extract_latent and tdp_pipeline_latent_step
+    refuse null, misaligned and overlapping arguments on the host (no GPU
+    call); with conditioning tokens cond_row (and for the positions call
+    cond_k and the workspace) are required."""
+    wl = WORKLOADS["conditioned"]
+    plan = plan_for(wl)
+    s = tdp.tdp_plan_sizes(plan)
+    null = ctypes.c_void_p(None)
+    b = {k: ctypes.c_void_p((i + 1) << 36) for i, k in enumerate(
+        ("latent", "pos", "tile_lat", "tile_pos", "index", "count", "cond_row", "cond_k", "ws", "tile_out", "out",
+         "bcond_row", "bcond_k"))}
+
+    def positions(**over):
+        a = dict(b, **over)
+        return lib.tdp_extract_positions(plan.handle, a["pos"], a["tile_pos"], a["index"], a["count"], a["cond_row"],
+                                         a["cond_k"], a["ws"], null)
+
+    def gather(**over):
+        a = dict(b, **over)
+        return lib.tdp_extract_latent(plan.handle, a["latent"], a["cond_row"], a["tile_lat"], null)
+
+    def step(**over):
+        a = dict(b, **over)
+        return lib.tdp_pipeline_latent_step(plan.handle, a["latent"], a["cond_row"], a["tile_lat"], a["tile_out"],
+                                            a["bcond_row"], a["bcond_k"], a["out"], null)
+    for key in ("pos", "tile_pos", "index", "count", "cond_row", "cond_k", "ws"):
+        assert positions(**{key: null}) == tdp.TDP_EINVAL, key
+    assert "workspace" in (positions(ws=null), tdp.tdp_last_error())[1]
+    assert positions(pos=ctypes.c_void_p(b["pos"].value + 4)) == tdp.TDP_EINVAL      # pairs need 8 bytes
+    assert positions(ws=ctypes.c_void_p(b["ws"].value + 8)) == tdp.TDP_EINVAL        # workspace needs 16
+    for key in ("latent", "cond_row", "tile_lat"):
+        assert gather(**{key: null}) == tdp.TDP_EINVAL, key
+    assert "cond_row is required" in (gather(cond_row=null), tdp.tdp_last_error())[1]
+    assert gather(latent=ctypes.c_void_p(b["latent"].value + 8)) == tdp.TDP_EINVAL
+    assert gather(cond_row=ctypes.c_void_p(b["cond_row"].value + 2)) == tdp.TDP_EINVAL
+    assert step(tile_out=b["tile_lat"]) == tdp.TDP_EINVAL
+    assert "which the gather writes" in tdp.tdp_last_error()
+    assert step(bcond_row=ctypes.c_void_p(b["tile_lat"].value + (s.tile_lat_elems * 2 // 32) * 16)) == tdp.TDP_EINVAL
+    assert step(out=ctypes.c_void_p(b["latent"].value + 4096)) == tdp.TDP_EINVAL
+    assert "writes a buffer the gather reads" in tdp.tdp_last_error()
+    assert step(out=b["cond_row"]) == tdp.TDP_EINVAL
+    assert step(bcond_k=null) == tdp.TDP_EINVAL
+    assert step(out=ctypes.c_void_p(b["out"].value + 8)) == tdp.TDP_EINVAL
+    for f, n in ((lib.tdp_extract_positions, 8), (lib.tdp_extract_latent, 4), (lib.tdp_pipeline_latent_step, 8)):
+        assert f(None, *([null] * n)) == tdp.TDP_EINVAL
+
+
+@pytest.mark.device_abi
 def test_lookback_polls_setting(lib):
     assert lib.tdp_set_lookback_polls(-1) == tdp.TDP_EINVAL
     assert "polls" in tdp.tdp_last_error()
