@@ -25,7 +25,9 @@ Prints one JSON line (stdout): GB/s of compulsory bytes (each input read
 once, each output written once; overlap re-reads not credited), the
 fraction of the 8 TB/s HBM peak, a roofline entry for the dominant kernel,
 the CPU oracle's rate on the same workload, the same step measured on each
-of the five workloads (``workloads``), the conditioned shape's extract with
+of the five workloads (``workloads``, with the extract in two halves for
+latents that share one positions set: the per-latent gather and its
+pipelined step), the conditioned shape's extract and per-latent gather with
 1024 to 16384 conditioning tokens (``selection_scaling``) and what plain hand-written streaming
 kernels move on this GPU (``ceilings``, from libtdp_ceiling.so), also with
 the extract's and the blend's own read:write mix at their own sizes
@@ -83,6 +85,14 @@ def compulsory_bytes(wl, counts, num_tiles, e_in, e_out):
     extract = B * rows * C * e_in + B * rows * 24 + S * B * C * e_in + S * B * 24 + 4 * S + 4 * num_tiles + sel
     blend = S * B * C * e_in + B * rows * C * e_out + sel
     return extract, blend, S
+
+
+def latent_bytes(wl, S, num_tiles, e_in):
+    """Algorithmic bytes of one latent gather (tdp_extract_latent) from
+    selection tables made once per positions set: latent read
+    B*(N+Nc)*C*e + tile rows written S*B*C*e + cond_row read 4*T*Nc."""
+    B, C, Nc = wl.batch, wl.channels, wl.num_cond
+    return B * (wl.tokens + Nc) * C * e_in + S * B * C * e_in + 4 * num_tiles * Nc
 
 
 def naive_bytes(wl, S, e_in):
@@ -227,7 +237,11 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
     """Extract, blend and pipelined step (tdp_pipeline_step) of one workload,
     each timed as a graph replay of `steps` launches over `sets_n` rotating
     buffer sets (the blend `sets_n // 2` steps behind the extract), with the
-    GB/s of its compulsory bytes."""
+    GB/s of its compulsory bytes.  Also the extract in two halves for
+    latents that share one positions set: tdp_extract_positions (once per
+    set), the per-latent gather tdp_extract_latent, and the pipelined step
+    tdp_pipeline_latent_step (gather + blend), with the gather's own
+    compulsory bytes."""
     import numpy as np
     from synth import make_inputs
     inp = make_inputs(wl)
@@ -260,6 +274,25 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
         tdp.tdp_pipeline_step(plan, s["latent"], s["pos"], stream=stream, **s["bufs"], tile_out=q["bufs"]["tile_lat"],
                               blend_cond_row=q["bufs"]["cond_row"], blend_cond_k=q["bufs"]["cond_k"], out=q["out"])
 
+    # the two halves: every set has the same positions, so set 0's tables
+    # (written by its extract) serve every latent
+    tab = sets[0]["bufs"]
+
+    def positions(i):
+        b = sets[i % sets_n]["bufs"]
+        tdp.tdp_extract_positions(plan, sets[i % sets_n]["pos"], b["tile_pos"], b["tile_index"], b["tile_count"],
+                                  b["cond_row"], b["cond_k"], b["workspace"], stream=stream)
+
+    def gather(i):
+        s = sets[i % sets_n]
+        tdp.tdp_extract_latent(plan, s["latent"], tab["cond_row"], s["bufs"]["tile_lat"], stream=stream)
+
+    def latent_step(i):
+        s, q = sets[i % sets_n], sets[(i - lag) % sets_n]
+        tdp.tdp_pipeline_latent_step(plan, s["latent"], tab["cond_row"], s["bufs"]["tile_lat"],
+                                     tile_out=q["bufs"]["tile_lat"], blend_cond_row=tab["cond_row"],
+                                     blend_cond_k=tab["cond_k"], out=q["out"], stream=stream)
+
     with torch.cuda.stream(stream):
         for i in range(sets_n):
             ex(i)
@@ -271,6 +304,10 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
     bl_ms = graph_time_ms(torch, stream, bl, steps)
     st_ms = graph_time_ms(torch, stream, step, steps)
     gbs = (ex_b + bl_b) / (st_ms * 1e-3) / 1e9
+    pos_ms = graph_time_ms(torch, stream, positions, steps)
+    ga_ms = graph_time_ms(torch, stream, gather, steps)
+    ls_ms = graph_time_ms(torch, stream, latent_step, steps)
+    ga_b = latent_bytes(wl, S, T, e)
     return {
         "config": f"B={wl.batch} C={wl.channels} (F,H,W)={wl.shape} {wl.dtype}, tiles "
                   f"{tuple(n for n, _ in wl.tiling)} overlap {tuple(o for _, o in wl.tiling)}, {T} tiles, "
@@ -282,6 +319,11 @@ def workload_rates(torch, tdp, dev, wl, sets_n=8, steps=64):
         "blend_gbs": round(bl_b / (bl_ms * 1e-3) / 1e9, 1),
         "step_us": round(st_ms * 1e3, 3), "bytes_per_step": ex_b + bl_b,
         "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "positions_us": round(pos_ms * 1e3, 3),
+        "latent_us": round(ga_ms * 1e3, 3), "latent_bytes": ga_b,
+        "latent_gbs": round(ga_b / (ga_ms * 1e-3) / 1e9, 1),
+        "latent_step_us": round(ls_ms * 1e3, 3), "latent_step_bytes": ga_b + bl_b,
+        "latent_step_gbs": round((ga_b + bl_b) / (ls_ms * 1e-3) / 1e9, 1),
     }
 
 
@@ -309,11 +351,18 @@ def selection_scaling(torch, tdp, dev, counts=(1024, 4096, 16384), sets_n=8, ste
         def ex(i):
             la, po, b = sets[i % sets_n]
             tdp.tdp_extract(plan, la, po, stream=stream, **b)
+
+        def gather(i):
+            la, _, b = sets[i % sets_n]
+            tdp.tdp_extract_latent(plan, la, sets[0][2]["cond_row"], b["tile_lat"], stream=stream)
         ms = graph_time_ms(torch, stream, ex, steps)
+        ga_ms = graph_time_ms(torch, stream, gather, steps)
         counts_t = sets[0][2]["tile_count"].cpu().numpy()
         ex_b, _, S = compulsory_bytes(wl, counts_t, T, 2, 2)
+        ga_b = latent_bytes(wl, S, T, 2)
         out.append({"num_cond": nc, "tile_rows": S, "extract_us": round(ms * 1e3, 3), "extract_bytes": ex_b,
-                    "extract_gbs": round(ex_b / (ms * 1e-3) / 1e9, 1)})
+                    "extract_gbs": round(ex_b / (ms * 1e-3) / 1e9, 1), "latent_us": round(ga_ms * 1e3, 3),
+                    "latent_bytes": ga_b, "latent_gbs": round(ga_b / (ga_ms * 1e-3) / 1e9, 1)})
         del sets
     return out
 

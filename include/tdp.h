@@ -402,7 +402,9 @@ int tdp_extract_positions(const tdp_plan* plan, const float* pos, float* tile_po
  * it is") and its kept conditioning rows at the slot rows cond_row gives.
  * cond_row (T, Nc) int32 must come from tdp_extract_positions or
  * tdp_extract on the same plan and positions (NULL allowed when Nc == 0);
- * with it, tile_lat is bit-identical to tdp_extract's.  One launch, no
+ * with it, tile_lat is bit-identical to tdp_extract's (an entry outside
+ * [0, capacity) of its tile is skipped, so no row lands outside the tile's
+ * slot).  One launch, no
  * workspace, no waiting between workgroups.  Device pointers except plan;
  * latent and tile_lat 16-byte aligned, cond_row 4-byte aligned; TDP_EINVAL
  * for a null or misaligned pointer (nothing enqueued), TDP_EHIP when the

@@ -55,6 +55,7 @@ constexpr int kMinUnroll = 12;     // starts in flight per thread (minimum-start
 constexpr int kOwnRows = kPosOwnRows;  // own position rows a thread holds through the minimum pass
 constexpr int kSelLoads = 24;      // position loads in flight per thread in the extent launch
 constexpr int kCopyBatch = 8;      // kept conditioning vectors in flight per thread
+constexpr int kGatherTiles = 4;    // most held tiles per conditioning workgroup of the latent gather
 constexpr int kLookbackPolls = 256;  // reads of an unpublished flag before a wave counts that chunk itself
 constexpr int kDirectChunks = 16;    // earlier chunks a selection workgroup counts from their tokens
 constexpr int kCondRowsPerBlock = 64;  // conditioning tokens per workgroup (streaming, large plans)
@@ -1000,61 +1001,90 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const E
 // latent gather from a selection already made (tdp_extract_latent)
 // ---------------------------------------------------------------------------
 
-// Workgroup (held tile slot, chunk of kCondChunk conditioning tokens): the
-// chunk's cond_row entries give each kept token's slot row, and the kept
-// tokens' rows are copied there, every batch element.  cond_row comes from
-// the selection of the same positions, so the rows land where tdp_extract
-// puts them.
+// Held tiles per conditioning workgroup of the latent gather: kGatherTiles
+// when that still leaves a workgroup per compute unit, else half as many
+// (fewer tokens: more, shorter workgroups).
+__host__ __device__ inline int gather_tiles(const PlanDev& p) {
+  return p.n_chunks * ((p.T_local + kGatherTiles - 1) / kGatherTiles) >= 256 ? kGatherTiles : kGatherTiles / 2;
+}
+
+// Workgroup (chunk of kCondChunk conditioning tokens, group of gather_tiles
+// held tiles): it loads the chunk's rows (every batch element) and the
+// group's cond_row entries for those tokens in one round trip, then stores
+// each row at the slot row of every tile in the group that keeps it.  A
+// token kept by many tiles (a reference token is kept by all) is read once
+// per group, not once per tile; the groups of a chunk run on one XCD, so
+// its rows come from HBM about once.  cond_row comes from the selection of
+// the same positions, so the rows land where tdp_extract puts them.
 template <bool R>
-__device__ void gather_cond_chunk(const PlanDev& p, const ExtractArgs& a, int bid) {
-  __shared__ uint64_t mask_s;
-  __shared__ int row_s[kCondChunk];
-  const int slot = bid / p.n_chunks, ch = bid - slot * p.n_chunks;
-  const int t = R ? p.rank + slot * p.world : slot;
-  const int tid = threadIdx.x;
+__device__ void gather_cond_tokens(const PlanDev& p, const ExtractArgs& a, int bid) {
+  __shared__ int row_s[kGatherTiles][kCondChunk];  // slot row per (tile of the group, token); -1: not kept
+  __shared__ int64_t base_s[kGatherTiles];         // tile_lat row of slot row 0, batch 0
+  __shared__ int cap_s[kGatherTiles];
+  const int G = gather_tiles(p);
+  const int n_groups = (p.T_local + G - 1) / G;
+  int ch, grp;
+  xcd_group(bid, p.n_chunks, n_groups, ch, grp);  // the groups of a chunk share an L2
+  const int tid = threadIdx.x, V = p.vin;
   const int c0 = ch * kCondChunk;
-  if (tid < kCondChunk) {  // wave 0: one token per lane
-    const int c = c0 + tid;
-    const int row = c < p.Nc ? a.cond_row[(int64_t)t * p.Nc + c] : -1;
-    row_s[tid] = row;
-    const uint64_t m = __ballot(row >= 0);
-    if (tid == 0) mask_s = m;
-  }
-  __syncthreads();
-  const uint64_t mask = mask_s;
-  const int n = __popcll(mask);
-  if (n == 0) return;
-  const TileBox tb = tile_box<R>(p, t);
-  const int V = p.vin;
-  const FastDiv by_n = make_fastdiv((uint32_t)n);
-  const int total = p.B * n * V;  // (b, kept jj, vector)
-  for (int e0 = 0; e0 < total; e0 += kBlock * kCopyBatch) {
+  const int ntok = min(kCondChunk, p.Nc - c0);
+  const int s0 = grp * G, ng = min(G, p.T_local - s0);
+  const int all_vec = p.B * ntok * V;  // (b, token j, vector), vector fastest
+  const FastDiv by_ntok = make_fastdiv((uint32_t)ntok);
+  for (int e0 = 0; e0 < all_vec; e0 += kBlock * kCopyBatch) {
     u32x4 v[kCopyBatch];
 #pragma unroll
     for (int q = 0; q < kCopyBatch; ++q) {
-      const KeptVec k = kept_vec(p, by_n, n, min(e0 + q * kBlock + tid, total - 1));
-      v[q] = ld_nt(a.latent + ((int64_t)k.b * p.rows + p.N + c0 + nth_set_bit(mask, k.jj)) * V + k.vv);
+      const int e = min(e0 + q * kBlock + tid, all_vec - 1);
+      const int row = (int)fastdiv((uint32_t)e, p.by_vin), vv = e - row * V;
+      const int b = (int)fastdiv((uint32_t)row, by_ntok), j = row - b * ntok;
+      v[q] = ld_nt(a.latent + ((int64_t)b * p.rows + p.N + c0 + j) * V + vv);
+    }
+    if (e0 == 0) {  // the group's entries, in flight with the first rows
+      static_assert(kGatherTiles * kCondChunk <= kBlock, "one entry per thread");
+      const int gs = tid / kCondChunk, j = tid - gs * kCondChunk;
+      if (gs < ng) {
+        const int slot = s0 + gs;
+        const int t = R ? p.rank + slot * p.world : slot;
+        row_s[gs][j] = j < ntok ? a.cond_row[(int64_t)t * p.Nc + c0 + j] : -1;
+        if (j == 0) {
+          const TileBox tb = tile_box<R>(p, t);
+          base_s[gs] = tb.s.row_base;
+          cap_s[gs] = tb.s.cap;
+        }
+      }
+      __syncthreads();
     }
 #pragma unroll
     for (int q = 0; q < kCopyBatch; ++q) {
       const int e = e0 + q * kBlock + tid;
-      if (e < total) {
-        const KeptVec k = kept_vec(p, by_n, n, e);
-        const int row = row_s[nth_set_bit(mask, k.jj)];
-        st_nt(a.tile_lat + (tb.s.row_base + (int64_t)k.b * tb.s.cap + row) * V + k.vv, v[q]);
+      if (e < all_vec) {
+        const int row = (int)fastdiv((uint32_t)e, p.by_vin), vv = e - row * V;
+        const int b = (int)fastdiv((uint32_t)row, by_ntok), j = row - b * ntok;
+        for (int gs = 0; gs < ng; ++gs) {
+          const int r = row_s[gs][j];
+          if ((uint32_t)r < (uint32_t)cap_s[gs])  // -1: not kept; nothing lands outside the slot
+            st_nt(a.tile_lat + (base_s[gs] + (int64_t)b * cap_s[gs] + r) * V + vv, v[q]);
+        }
       }
     }
   }
 }
 
-// tdp_extract_latent: [0, n_cg) conditioning chunks of the held tiles
-// (short chains, so first), then the generated latent rows per (line,
-// chunk), as in the extract.
+// Conditioning workgroups of the latent gather: (chunk, group of held tiles).
+__host__ __device__ inline int gather_cond_blocks(const PlanDev& p) {
+  const int G = gather_tiles(p);
+  return p.Nc > 0 && p.T_local > 0 ? p.n_chunks * ((p.T_local + G - 1) / G) : 0;
+}
+
+// tdp_extract_latent: [0, n_cg) conditioning workgroups (chunk, group of
+// held tiles; one round trip each, so first), then the generated latent rows
+// per (line, chunk), as in the extract.
 template <bool R>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const PlanDev p, const ExtractArgs a, int n_cg) {
   const int bid = blockIdx.x;
   if (bid < n_cg) {
-    gather_cond_chunk<R>(p, a, bid);
+    gather_cond_tokens<R>(p, a, bid);
     return;
   }
   extract_latent<R>(p, a, bid - n_cg);
@@ -1416,7 +1446,7 @@ __global__ __launch_bounds__(kBlock) void pipeline_latent_kernel(const PlanDev p
                                                                  int n_bcond) {
   const int bid = blockIdx.x;
   if (bid < n_cg) {
-    gather_cond_chunk<false>(p, a, bid);
+    gather_cond_tokens<false>(p, a, bid);
     return;
   }
   if (bid < n_ext) {
@@ -1554,7 +1584,7 @@ template <int IN, int OUT>
 hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
                                   const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
                                   const DeviceShape& ds, hipStream_t s) {
-  const int n_cg = p.Nc > 0 ? p.T * p.n_chunks : 0;
+  const int n_cg = gather_cond_blocks(p);
   const int n_ext = n_cg + (p.lat_units + kWaves - 1) / kWaves;
   const int n_bcond = blend_cond_blocks(p);
   const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
@@ -1907,10 +1937,6 @@ int launch_positions(const PlanDev& p, const float* pos, float* tile_pos, int32_
   if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
   return TDP_OK;
 }
-
-// Workgroups of the latent gather: conditioning chunks of the held tiles,
-// then generated latent blocks.
-int gather_cond_blocks(const PlanDev& p) { return p.Nc > 0 ? p.T_local * p.n_chunks : 0; }
 
 // tdp_extract_latent: the latent rows of every held tile.
 int launch_gather(const PlanDev& p, const void* latent, const int32_t* cond_row, void* tile_lat, hipStream_t s,

@@ -55,6 +55,21 @@ def test_conditioned_counts_kept_rows():
     assert bl == S * row + rows * row + sel
 
 
+def test_latent_gather_bytes():
+    # the per-latent gather reads the latent once and writes the tile rows:
+    # at 4K the same bytes as the blend, which reads those rows and writes
+    # the output
+    wl = WORKLOADS["4k"]
+    counts, T = _oracle_counts(wl)
+    _, bl, S = bench.compulsory_bytes(wl, counts, T, 2, 2)
+    assert bench.latent_bytes(wl, S, T, 2) == 130560 * 256 + 247296 * 256 == bl
+    wl = WORKLOADS["conditioned"]
+    counts, T = _oracle_counts(wl)
+    S = int(sum(counts))
+    rows, row = wl.tokens + wl.num_cond, wl.batch * wl.channels * 2
+    assert bench.latent_bytes(wl, S, T, 2) == rows * row + S * row + 4 * T * wl.num_cond
+
+
 def test_stream_bytes_formula():
     wl = WORKLOADS["4k"]
     S, B, C, rows = 247296, 1, 128, 130560
