@@ -108,6 +108,18 @@ def test_rank_plans(name, world, rank, cuda):
     _halves_vs_extract(_case(name), cuda, world=world, rank=rank)
 
 
+@pytest.mark.parametrize("name,world,rank", [("many_cond", 6, 5), ("fullres", 5, 4)])
+def test_rank_without_tiles(name, world, rank, cuda):
+    """A rank past the last tile holds none: the positions call still writes
+    the selection tables (k counts every rank's tiles), and the gather and the
+    latent step have nothing to copy."""
+    wl = _case(name)
+    plan = _plan(wl, world=world, rank=rank)
+    assert tdp.held_tiles(plan) == []
+    _halves_vs_extract(wl, cuda, world=world, rank=rank)
+    _step_vs_two_calls(wl, cuda, out_dtype="f32", world=world, rank=rank)
+
+
 def _step_vs_two_calls(wl, cuda, out_dtype=None, world=1, rank=0):
     plan = _plan(wl, out_dtype, world, rank)
     inp_a, inp_b = make_inputs(wl), make_inputs(wl, seed=wl.seed + 1)
