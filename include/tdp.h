@@ -179,8 +179,9 @@ int tdp_plan_intervals(const tdp_plan* plan, int axis, int32_t* starts, int32_t*
 int tdp_plan_window(const tdp_plan* plan, int axis, int32_t i, float* w);
 
 /* Tiles of one axis that contain cell x, ascending: tiles[0..*count), with
- * *count 1 or 2 (at most two overlap under the guard).  This is the lookup
- * the kernels run for every latent row.  Guarded plans only. */
+ * *count 1 or 2 (at most two overlap under the guard, which keeps every tile
+ * at least twice the overlap: mold #673, "A bug found while porting").  This
+ * is the lookup the kernels run for every latent row.  Guarded plans only. */
 int tdp_plan_cell_tiles(const tdp_plan* plan, int axis, int32_t x, int32_t* tiles, int32_t* count);
 
 /* Geometry and slot offsets of tile t, t = (i_f * n_h + i_h) * n_w + i_w:
@@ -226,7 +227,8 @@ int tdp_plan_tile_rank(const tdp_plan* plan, int32_t t, int32_t world, int32_t* 
 int tdp_plan_create_rank(const tdp_config* cfg, int32_t world, int32_t rank, tdp_plan** out);
 
 /* The plan's round-robin world and rank (1 and 0 for a whole plan) and the
- * number of tiles it holds. */
+ * number of tiles it holds (tiles dealt round-robin to ranks: TDP docs,
+ * "What it is"). */
 int tdp_plan_local_tiles(const tdp_plan* plan, int32_t* world, int32_t* rank, int32_t* count);
 
 /* ---- plan quality (host only) -------------------------------------------- */
@@ -248,7 +250,11 @@ typedef struct {
                            /* idle ranks (world > tiles) count in the split   */
 } tdp_quality;
 
-/* Figures of any tiling given as per-axis intervals: ndim axes (1..8) of
+/* Cost figures of a tiling (DistVAE docs, "Choosing a tile window": "The
+ * two axes cost differently" for decoded area and seams, "Clipping
+ * unbalances a grid, not the tile count" for the load imbalance of an even
+ * tile count per rank, "The tile count caps the GPU count" for idle ranks).
+ * Figures of any tiling given as per-axis intervals: ndim axes (1..8) of
  * lengths dims[d], counts[d] >= 1 intervals each, listed axis after axis in
  * starts/ends (sum of counts entries, 0 <= start < end <= dims[d]); tiles
  * are their Cartesian product in row-major order (at most 2^20 tiles).
@@ -258,7 +264,8 @@ int tdp_tiling_quality(int32_t ndim, const int32_t* dims, const int32_t* counts,
                        const int32_t* ends, int32_t world, tdp_quality* out, int64_t* rank_cells);
 
 /* The same figures for a plan's generated-token tiles (frames, height,
- * width), e.g. to choose tile counts and overlaps before running. */
+ * width), e.g. to choose tile counts and overlaps before running (same
+ * passages as tdp_tiling_quality). */
 int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int64_t* rank_cells);
 
 /* ---- device operations (enqueue on `stream`) ----------------------------- */
@@ -303,7 +310,8 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
                 void* workspace, void* stream);
 
-/* Conditioning selection (Nc > 0), the second launch of tdp_extract: one
+/* Conditioning selection (Nc > 0; the keep rule of TDP docs, "Shared
+ * negative (reference) positions"), the second launch of tdp_extract: one
  * workgroup per (tile, chunk of 64 tokens) tests its chunk and finds the
  * tile's kept tokens before it: those of the 16 chunks before it from
  * their tokens, those of earlier chunks from the flags their workgroups
@@ -412,7 +420,9 @@ int tdp_extract_positions(const tdp_plan* plan, const float* pos, float* tile_po
 int tdp_extract_latent(const tdp_plan* plan, const void* latent, const int32_t* cond_row,
                        void* tile_lat, void* stream);
 
-/* One step of a pipelined loop over latents that share one positions set:
+/* One step of a pipelined loop over latents that share one positions set
+ * (latents in flight one after another, each tiled and blended back: TDP
+ * docs, "What it is"):
  * tdp_extract_latent(plan, latent, cond_row, tile_lat) and tdp_blend(plan,
  * tile_out, blend_cond_row, blend_cond_k, out), bit-identical to the two
  * calls.  Whole plans run both as one launch, the gather's workgroups
@@ -445,7 +455,9 @@ int tdp_pipeline_latent_step(const tdp_plan* plan, const void* latent, const int
 int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
                    const int32_t* cond_k, float* acc, void* stream);
 
-/* Round the accumulator (B, N+Nc, C) fp32 to the plan's out_dtype into out
+/* The last step of the streaming blend (the in-place sum of TDP docs, "What
+ * it is", rounded once): round the accumulator (B, N+Nc, C) fp32 to the
+ * plan's out_dtype into out
  * (round to nearest even for bf16; a copy for fp32, nothing when out == acc).
  * After tdp_blend_tile for every tile in order, out equals tdp_blend's
  * output bit for bit.  16-byte aligned device pointers. */
@@ -489,16 +501,20 @@ typedef struct {
  * (B*C*frames*H*scale_h rows). */
 int tdp_pixel_plan_create(const tdp_pixel_config* cfg, tdp_pixel_plan** out);
 void tdp_pixel_plan_destroy(tdp_pixel_plan* plan);
-/* Tile t's place: tiles are packed back to back in index order, each a
+/* Tile t's place: tiles are packed back to back in index order (row-major
+ * over height and width, as the latent tiles: mold #673, "Scope"), each a
  * (B, C, frames, rows, columns) array of in_dtype. */
 int tdp_pixel_plan_tile(const tdp_pixel_plan* plan, int32_t t, tdp_pixel_tile* out);
 /* Elements of the tile buffer and of the output (B, C, frames, H*scale_h,
- * W*scale_w); tile count. */
+ * W*scale_w), the decoded image the tiles come from (mold #673, "Scope");
+ * tile count. */
 int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_t* out_elems,
                          int32_t* num_tiles);
 
 /* out = sum over the tiles covering each pixel, ascending t, of
- * (wH * wW) * tile, fp32 accumulation from zero, rounded once to out_dtype.
+ * (wH * wW) * tile, fp32 accumulation from zero, rounded once to out_dtype
+ * (the trapezoids of the latent blend in pixel units, so the weights still
+ * sum to one: DistVAE docs, "Choosing a tile window"; mold #673, "Scope").
  * Device pointers, 16-byte aligned; tiles holds every tile as packed above. */
 int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream);
 
@@ -509,7 +525,8 @@ int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, vo
  * status code (a static string; "unknown status" for other values). */
 const char* tdp_status_string(int status);
 /* The message of the last failure on the calling thread (thread-local,
- * never NULL; "" before the first failure). */
+ * never NULL; "" before the first failure), naming the axis and limit of a
+ * guard violation as above (mold #673, "A bug found while porting"). */
 const char* tdp_last_error(void);
 
 #ifdef __cplusplus
