@@ -371,10 +371,9 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * tile_out, blend_cond_row, blend_cond_k, out) would, with bit-identical
  * results.  For whole plans without conditioning tokens both run as one
  * launch, the extract's workgroups first, so the blend's fill the GPU while
- * the extract's drain; whole plans with conditioning tokens whose tiles and
- * output share a dtype take two launches (the extents with the latent rows,
- * then the selection with the blend); rank plans and other dtypes enqueue
- * the two calls one after the other.
+ * the extract's drain; whole plans with conditioning tokens take two
+ * launches (the extents with the latent rows, then the selection with the
+ * blend); rank plans enqueue the two calls one after the other.
  * The two halves may run at the same time, so the blend's buffers must be
  * none of the extract's: TDP_EINVAL, nothing enqueued, when tile_out,
  * blend_cond_row or blend_cond_k overlaps a buffer the extract writes, or

@@ -2295,7 +2295,7 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     if (overlap(r.ptr, r.bytes, out, out_bytes))
       return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.world > 1 || (p.Nc > 0 && p.in_dtype != p.out_dtype)) {  // one after the other
+  if (p.world > 1) {  // one after the other
     st = launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                         static_cast<char*>(workspace), s, who);
     if (st != TDP_OK) return st;
@@ -2309,10 +2309,15 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
                                   static_cast<char*>(workspace));
     st = launch_extent(p, ca, ds, true, s, who);
     if (st != TDP_OK) return st;
-    const hipError_t e =
-        p.in_dtype == TDP_BF16
-            ? launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s)
-            : launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+    hipError_t e;
+    if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
+      e = launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+    else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
+      e = launch_pipeline_cond<TDP_BF16, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+    else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
+      e = launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+    else
+      e = launch_pipeline_cond<TDP_F32, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
     return TDP_OK;
   }

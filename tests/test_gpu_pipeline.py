@@ -6,8 +6,9 @@ Every output must equal, bit for bit, what tdp_extract and tdp_blend give
 as two calls on the same inputs; the extract half is also held to the
 oracle, and the blend half to the oracle's tolerance.  Covers fused plans
 (bf16 and fp32 rows, bf16 and fp32 output, a tiled frame axis, ragged and
-narrow rows) and plans that take the two launches one after the other
-(conditioning tokens, a rank's share), and a replayed graph of steps.
+narrow rows), plans with conditioning tokens (two launches, every dtype
+pairing), rank plans (the two calls one after the other), and a replayed
+graph of steps.
 """
 import numpy as np
 import pytest
@@ -110,10 +111,11 @@ def test_step_rank_plans(world, rank, cuda):
     _step_vs_two_calls(WORKLOADS["conditioned"], cuda, out_dtype="f32", world=world, rank=rank)
 
 
-def test_step_conditioned_mixed_dtypes(cuda):
-    """bf16 tiles into an fp32 output with conditioning tokens: the two
-    launches one after the other."""
-    _step_vs_two_calls(WORKLOADS["conditioned"], cuda, out_dtype="f32")
+@pytest.mark.parametrize("name,out_dtype", [("conditioned", "f32"), ("cond_f32", "bf16"), ("many_cond", "f32")])
+def test_step_conditioned_mixed_dtypes(name, out_dtype, cuda):
+    """Tiles and output of different dtypes with conditioning tokens (the
+    fused conditioned step for each pairing)."""
+    _step_vs_two_calls(_case(name), cuda, out_dtype=out_dtype)
 
 
 def test_step_refuses_shared_buffers(cuda):
