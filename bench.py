@@ -6,7 +6,11 @@ is the identity here), enqueued as one tdp_pipeline_step: the extract of
 one buffer set and the blend of another, one launch for whole plans without
 conditioning tokens.  The same steps as two calls each (tdp_extract, then
 tdp_blend) are reported beside it (``two_calls``).  Inputs are resident in
-HBM before the timed region starts.
+HBM before the timed region starts.  With ``--step latent`` a step is
+instead one tdp_pipeline_latent_step: the latent gather of one set and the
+blend of another, with the selection tables of one positions set made
+before the timed region (latents that share their positions), rated on the
+gather's and the blend's compulsory bytes.
 
 Caches: the 4K working set (~204 MB) fits the 256 MB Infinity Cache, so a
 loop over one buffer set would time cache hits.  The bench rotates over
@@ -453,6 +457,10 @@ def main():
     ap.add_argument("--no-normalize", action="store_true",
                     help="plan without TDP_NORMALIZE_POSITIONS (positions copied unshifted)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--step", choices=("full", "latent"), default="full",
+                    help="full: tdp_pipeline_step (the whole extract and a blend); latent: "
+                         "tdp_pipeline_latent_step over latents that share one positions set (the "
+                         "latent gather and a blend; tables from one tdp_extract_positions call)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -504,18 +512,32 @@ def main():
         b = s["bufs"]
         tdp.tdp_blend(plan, b["tile_lat"], b["cond_row"], b["cond_k"], s["out"], st or stream)
 
+    latent_steps = args.step == "latent"
+    tables = sets[0]["bufs"]  # every set has the same positions: one set's selection serves all
+
     def step(i, st=None):
         """Pipelined step i: extract set i mod R and blend set (i - D) mod R,
-        one tdp_pipeline_step (one launch where the plan allows)."""
+        one tdp_pipeline_step (one launch where the plan allows); with
+        --step latent, the latent gather of set i and the blend of set i - D,
+        one tdp_pipeline_latent_step."""
         s, q = sets[i % R], sets[(i - D) % R]
         b = s["bufs"]
+        if latent_steps:
+            tdp.tdp_pipeline_latent_step(plan, s["latent"], tables["cond_row"], b["tile_lat"],
+                                         tile_out=q["bufs"]["tile_lat"], blend_cond_row=tables["cond_row"],
+                                         blend_cond_k=tables["cond_k"], out=q["out"], stream=st or stream)
+            return
         tdp.tdp_pipeline_step(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
                               b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"],
                               tile_out=q["bufs"]["tile_lat"], blend_cond_row=q["bufs"]["cond_row"],
                               blend_cond_k=q["bufs"]["cond_k"], out=q["out"], stream=st or stream)
 
     def step_two_calls(i, st=None):
-        extract(sets[i % R], st)
+        if latent_steps:
+            s = sets[i % R]
+            tdp.tdp_extract_latent(plan, s["latent"], tables["cond_row"], s["bufs"]["tile_lat"], st or stream)
+        else:
+            extract(sets[i % R], st)
         blend(sets[(i - D) % R], st)
 
     # prime every set, then warm up the pipeline
@@ -527,7 +549,8 @@ def main():
     counts = sets[0]["bufs"]["tile_count"].cpu().numpy()
     e_in = 2 if wl.dtype == "bf16" else 4
     ex_bytes, bl_bytes, S = compulsory_bytes(wl, counts, T, e_in, e_in)
-    step_bytes = ex_bytes + bl_bytes
+    ga_bytes = latent_bytes(wl, S, T, e_in)
+    step_bytes = (ga_bytes if latent_steps else ex_bytes) + bl_bytes
 
     K = args.steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -576,7 +599,7 @@ def main():
     del graph
     # the same K steps as two calls each (tdp_extract, then tdp_blend)
     two_ms = graph_time_ms(torch, pstream, lambda i: step_two_calls(i, pstream), K)
-    fused = wl.num_cond == 0  # whole plan without conditioning tokens: one launch per step
+    fused = latent_steps or wl.num_cond == 0  # one launch per step
 
     # per-operation launch durations (graph replay, launch stream)
     gstream = torch.cuda.Stream(dev)
@@ -647,7 +670,9 @@ def main():
         log("[bench] selection scaling")
         scaling = selection_scaling(torch, tdp, dev)
 
-    if fused:  # the step is one launch: that kernel is the dominant one
+    if latent_steps:  # the step is one launch: that kernel is the dominant one
+        dom = ("latent gather + blend, one launch", step_bytes, ms_per_step, "pipeline_latent_kernel")
+    elif fused:
         dom = ("extract + blend, one launch", step_bytes, ms_per_step, "pipeline_kernel")
     else:
         dom = ("extract", ex_bytes, ex_ms, "extract_kernel") if ex_ms >= bl_ms else \
@@ -677,11 +702,15 @@ def main():
             "naive_bytes_per_step": step_bytes + naive_bytes(wl, S, e_in),
             "buffer_sets": R,
             "normalize_positions": not args.no_normalize,
+            "step": args.step,
         },
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "step_call": "tdp_pipeline_step (one launch)" if fused else "tdp_pipeline_step (extract, then blend)",
+        "step_call": ("tdp_pipeline_latent_step (one launch; tables from one tdp_extract_positions)"
+                      if latent_steps else "tdp_pipeline_step (one launch)" if fused
+                      else "tdp_pipeline_step (extents, then selection with the blend)"),
         "two_calls": {"ms_per_step": round(two_ms, 5), "value": round(step_bytes / (two_ms * 1e-3) / 1e9, 2),
-                      "note": "the same K steps as tdp_extract + tdp_blend, two launches each"},
+                      "note": ("the same K steps as tdp_extract_latent + tdp_blend" if latent_steps else
+                               "the same K steps as tdp_extract + tdp_blend") + ", two calls each"},
         "ops": {
             "extract_ms": round(ex_ms, 5), "extract_bytes": ex_bytes,
             "extract_gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
