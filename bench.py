@@ -143,16 +143,28 @@ def rank_share_rate(torch, tdp, dev, sets, wl, world, rank, reps):
         r = rs[i % len(sets)]
         tdp.tdp_blend(plan, r["bufs"]["tile_lat"], r["bufs"]["cond_row"], r["bufs"]["cond_k"], r["out"], gstream)
 
+    n = len(sets)
+
+    def step_fn(i):  # the rank's pipelined step: extract set i, partial blend of set i - n/2
+        s, b, q = sets[i % n], rs[i % n]["bufs"], rs[(i - n // 2) % n]
+        tdp.tdp_pipeline_step(plan, s["latent"], s["pos"], b["tile_lat"], b["tile_pos"], b["tile_index"],
+                              b["tile_count"], b["cond_row"], b["cond_k"], b["workspace"],
+                              tile_out=q["bufs"]["tile_lat"], out=q["out"], stream=gstream)
+
     ex_ms = graph_time_ms(torch, gstream, ex, reps)
     bl_ms = graph_time_ms(torch, gstream, bl, reps)
+    st_ms = graph_time_ms(torch, gstream, step_fn, reps)
     step = ex_ms + bl_ms
     return {"world": world, "rank": rank, "tiles": held, "tile_rows": S_r, "covered_rows": U,
+            "step_ms": round(st_ms, 5), "step_gbs": round((ex_bytes + bl_bytes) / (st_ms * 1e-3) / 1e9, 1),
             "extract_ms": round(ex_ms, 5), "extract_bytes": ex_bytes,
             "extract_gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
             "partial_blend_ms": round(bl_ms, 5), "partial_blend_bytes": bl_bytes,
             "partial_blend_gbs": round(bl_bytes / (bl_ms * 1e-3) / 1e9, 1),
             "gbs": round((ex_bytes + bl_bytes) / (step * 1e-3) / 1e9, 1),
-            "note": "partial buffer in fp32 over the whole latent; the all_reduce itself is not run"}
+            "note": "partial buffer in fp32 over the whole latent; the all_reduce itself is not run; "
+                    "gbs: extract and partial blend as separate launches, step_gbs: the rank's "
+                    "tdp_pipeline_step (one launch)"}
 
 
 def stream_bytes(wl, S, e_in, e_out):

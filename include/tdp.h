@@ -371,9 +371,11 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * tile_out, blend_cond_row, blend_cond_k, out) would, with bit-identical
  * results.  For whole plans without conditioning tokens both run as one
  * launch, the extract's workgroups first, so the blend's fill the GPU while
- * the extract's drain; whole plans with conditioning tokens take two
- * launches (the extents with the latent rows, then the selection with the
- * blend); rank plans enqueue the two calls one after the other.
+ * the extract's drain (a rank's share too: its tiles' extract and its
+ * partial buffer); whole plans with conditioning tokens take two launches
+ * (the extents with the latent rows, then the selection with the blend);
+ * rank plans with conditioning tokens enqueue the two calls one after the
+ * other.
  * The two halves may run at the same time, so the blend's buffers must be
  * none of the extract's: TDP_EINVAL, nothing enqueued, when tile_out,
  * blend_cond_row or blend_cond_k overlaps a buffer the extract writes, or
@@ -424,8 +426,8 @@ int tdp_extract_latent(const tdp_plan* plan, const void* latent, const int32_t* 
  * docs, "What it is"):
  * tdp_extract_latent(plan, latent, cond_row, tile_lat) and tdp_blend(plan,
  * tile_out, blend_cond_row, blend_cond_k, out), bit-identical to the two
- * calls.  Whole plans run both as one launch, the gather's workgroups
- * first; rank plans enqueue the two calls in order.  cond_row and
+ * calls.  One launch, the gather's workgroups first (rank plans too: the
+ * held tiles' rows, then the partial buffer).  cond_row and
  * blend_cond_row may be the same buffer (both halves only read them).
  * TDP_EINVAL, nothing enqueued, when tile_lat overlaps tile_out,
  * blend_cond_row, blend_cond_k or out, or out overlaps latent or cond_row

@@ -1366,23 +1366,12 @@ __device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_
 // F2: the frame axis is tiled, so a line can have four frame x height
 // combos; only plans with a tiled frame axis carry that path (and its
 // registers).
-// Workgroup `bid` of a blend whose first n_cond workgroups take the
-// conditioning rows.
+// Generated-row workgroup `gid` of a blend: each wave takes one unit (rows
+// [w0, w0 + rwv) of one line), the waves of a workgroup consecutive units.
+// A rank plan writes zeros on units outside its tiles' bounding box.
 template <int IN, int OUT, bool R, bool F2>
-__device__ void blend_body(const PlanDev& p, const u32x4* __restrict__ tile_out, const int32_t* __restrict__ cond_row,
-                           const int32_t* __restrict__ cond_k, void* __restrict__ out, int bid, int n_cond) {
-  // conditioning workgroups first: each is a short dependent chain, so they
-  // start early and run under the generated rows
-  if (bid < n_cond) {
-    if (p.T <= kCondTiles)
-      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
-    else
-      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
-    return;
-  }
-  // this wave's unit (rows [w0, w0 + rwv) of one line): the waves of a
-  // workgroup take consecutive units
-  const int unit = __builtin_amdgcn_readfirstlane((bid - n_cond) * kWaves + (int)(threadIdx.x >> 6));
+__device__ void blend_gen(const PlanDev& p, const u32x4* __restrict__ tile_out, void* __restrict__ out, int gid) {
+  const int unit = __builtin_amdgcn_readfirstlane(gid * kWaves + (int)(threadIdx.x >> 6));
   if (unit >= p.gen_units) return;
   const int rows = p.blend_rows;
   const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
@@ -1405,6 +1394,23 @@ __device__ void blend_body(const PlanDev& p, const u32x4* __restrict__ tile_out,
     blend_line<IN, OUT, 2, R>(p, lc, b, f, h, w0, tile_out, out);
   else
     blend_line<IN, OUT, F2 ? 4 : 2, R>(p, lc, b, f, h, w0, tile_out, out);
+}
+
+// Workgroup `bid` of a blend whose first n_cond workgroups take the
+// conditioning rows.
+template <int IN, int OUT, bool R, bool F2>
+__device__ void blend_body(const PlanDev& p, const u32x4* __restrict__ tile_out, const int32_t* __restrict__ cond_row,
+                           const int32_t* __restrict__ cond_k, void* __restrict__ out, int bid, int n_cond) {
+  // conditioning workgroups first: each is a short dependent chain, so they
+  // start early and run under the generated rows
+  if (bid < n_cond) {
+    if (p.T <= kCondTiles)
+      blend_cond_cached<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
+    else
+      blend_cond_direct<IN, OUT, R>(p, tile_out, cond_row, cond_k, out, bid);
+    return;
+  }
+  blend_gen<IN, OUT, R, F2>(p, tile_out, out, bid - n_cond);
 }
 template <int IN, int OUT, bool R, bool F2>
 __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
@@ -1433,11 +1439,11 @@ __global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, 
   blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
 }
 
-// One step of a pipelined loop whose positions do not change (whole plans):
+// One step of a pipelined loop whose positions do not change (R: a rank's share):
 // the latent gather of one latent (tdp_extract_latent: conditioning chunks,
 // then generated rows) and the blend of other tile outputs, as one launch.
 // Every workgroup is a copy or a short chain; none waits on another.
-template <int IN, int OUT, bool F2>
+template <int IN, int OUT, bool F2, bool R>
 __global__ __launch_bounds__(kBlock) void pipeline_latent_kernel(const PlanDev p, const ExtractArgs a,
                                                                  const u32x4* __restrict__ tile_out,
                                                                  const int32_t* __restrict__ blend_cond_row,
@@ -1446,23 +1452,24 @@ __global__ __launch_bounds__(kBlock) void pipeline_latent_kernel(const PlanDev p
                                                                  int n_bcond) {
   const int bid = blockIdx.x;
   if (bid < n_cg) {
-    gather_cond_tokens<false>(p, a, bid);
+    gather_cond_tokens<R>(p, a, bid);
     return;
   }
   if (bid < n_ext) {
-    extract_latent<false>(p, a, bid - n_cg);
+    extract_latent<R>(p, a, bid - n_cg);
     return;
   }
-  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
+  blend_body<IN, OUT, R, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
 }
 
-// One step of a pipelined loop (whole plans without conditioning tokens):
-// the extract of one latent and the blend of other tile outputs that share
-// no buffer with it, as one launch.  Grid: the extract's workgroups
+// One step of a pipelined loop (plans without conditioning tokens; R: a
+// rank's share, its tiles' extract and its partial buffer): the extract of
+// one latent and the blend of other tile outputs that share no buffer with
+// it, as one launch.  Grid: the extract's workgroups
 // (positions, then latent rows) and then the blend's, so the blend's fill
 // the compute units as the extract's drain instead of waiting for a kernel
 // boundary.  Each workgroup runs exactly the code of its own kernel.
-template <int IN, int OUT, bool F2>
+template <int IN, int OUT, bool F2, bool R>
 __global__ __launch_bounds__(kBlock) void pipeline_kernel(const PlanDev p, const ExtractArgs a,
                                                           const u32x4* __restrict__ tile_out,
                                                           void* __restrict__ out, int n_ext) {
@@ -1470,29 +1477,36 @@ __global__ __launch_bounds__(kBlock) void pipeline_kernel(const PlanDev p, const
   const int bid = blockIdx.x;
   if (bid < n_ext) {
     if (bid < a.n_pos) {
-      const PosWork w = pos_work<false>(p, a, bid);
-      extract_positions<false>(p, a, sm, w.t, w.slot, w.b, w.d, w.part);
+      const PosWork w = pos_work<R>(p, a, bid);
+      extract_positions<R>(p, a, sm, w.t, w.slot, w.b, w.d, w.part);
       return;
     }
-    extract_latent<false>(p, a, bid - a.n_pos);
+    extract_latent<R>(p, a, bid - a.n_pos);
     return;
   }
-  const int unit = __builtin_amdgcn_readfirstlane((bid - n_ext) * kWaves + (int)(threadIdx.x >> 6));
-  if (unit >= p.gen_units) return;
-  const int rows = p.blend_rows;
-  const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
-  const int w0 = (unit - line * p.blend_chunks) * rows;
-  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
-  const int fh = line - b * (p.F * p.H);
-  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
-  LineCombos lc;
-  lc.init(p, f, h);
-  if (lc.n == 1)
-    blend_line<IN, OUT, 1, false>(p, lc, b, f, h, w0, tile_out, out);
-  else if (!F2 || lc.n == 2)
-    blend_line<IN, OUT, 2, false>(p, lc, b, f, h, w0, tile_out, out);
-  else
-    blend_line<IN, OUT, F2 ? 4 : 2, false>(p, lc, b, f, h, w0, tile_out, out);
+  if constexpr (R) {
+    blend_gen<IN, OUT, R, F2>(p, tile_out, out, bid - n_ext);
+  } else {
+    // the blend's generated rows written out here rather than through
+    // blend_gen: the same code, but hipcc then gives this kernel 63 VGPRs
+    // instead of 65, and the 4K step is ~0.08 us shorter
+    const int unit = __builtin_amdgcn_readfirstlane((bid - n_ext) * kWaves + (int)(threadIdx.x >> 6));
+    if (unit >= p.gen_units) return;
+    const int rows = p.blend_rows;
+    const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
+    const int w0 = (unit - line * p.blend_chunks) * rows;
+    const int b = (int)fastdiv((uint32_t)line, p.by_FH);
+    const int fh = line - b * (p.F * p.H);
+    const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+    LineCombos lc;
+    lc.init(p, f, h);
+    if (lc.n == 1)
+      blend_line<IN, OUT, 1, false>(p, lc, b, f, h, w0, tile_out, out);
+    else if (!F2 || lc.n == 2)
+      blend_line<IN, OUT, 2, false>(p, lc, b, f, h, w0, tile_out, out);
+    else
+      blend_line<IN, OUT, F2 ? 4 : 2, false>(p, lc, b, f, h, w0, tile_out, out);
+  }
 }
 
 // Occupancy caps.  Both kernels move more bytes per microsecond with fewer
@@ -1578,7 +1592,7 @@ hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* c
 }
 
 // The latent gather of one latent and the blend of other tile outputs
-// (whole plans), one launch: conditioning chunks, generated latent rows,
+// (whole and rank plans), one launch: conditioning chunks, generated latent rows,
 // then the blend's conditioning and generated workgroups.
 template <int IN, int OUT>
 hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
@@ -1591,11 +1605,18 @@ hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const 
   const size_t lds = capped_lds(ds, blend_cond_lds(p), kPipelineWgsPerCu);
   const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
-  if (p.ax[0].n > 1)
-    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+  const bool f2 = p.ax[0].n > 1;
+  if (p.world > 1 && f2)
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, true, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_cg, n_ext, n_bcond);
+  else if (p.world > 1)
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, false, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_cg, n_ext, n_bcond);
+  else if (f2)
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, true, false>), grid, block, lds, s, p, a, y, blend_cond_row,
                        blend_cond_k, out, n_cg, n_ext, n_bcond);
   else
-    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+    hipLaunchKernelGGL((pipeline_latent_kernel<IN, OUT, false, false>), grid, block, lds, s, p, a, y, blend_cond_row,
                        blend_cond_k, out, n_cg, n_ext, n_bcond);
   return hipGetLastError();
 }
@@ -1608,10 +1629,15 @@ hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, co
   const size_t lds = capped_lds(ds, 0, kPipelineWgsPerCu);
   const dim3 grid((unsigned)(n_ext + n_gen)), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
-  if (p.ax[0].n > 1)
-    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, true>), grid, block, lds, s, p, a, y, out, n_ext);
+  const bool f2 = p.ax[0].n > 1;
+  if (p.world > 1 && f2)
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, true, true>), grid, block, lds, s, p, a, y, out, n_ext);
+  else if (p.world > 1)
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, false, true>), grid, block, lds, s, p, a, y, out, n_ext);
+  else if (f2)
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, true, false>), grid, block, lds, s, p, a, y, out, n_ext);
   else
-    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, false>), grid, block, lds, s, p, a, y, out, n_ext);
+    hipLaunchKernelGGL((pipeline_kernel<IN, OUT, false, false>), grid, block, lds, s, p, a, y, out, n_ext);
   return hipGetLastError();
 }
 
@@ -2234,13 +2260,6 @@ int tdp_pipeline_latent_step(const tdp_plan* plan, const void* latent, const int
     if (overlap(g.ptr, g.bytes, out, out_bytes))
       return fail(TDP_EINVAL, "%s: the blend writes a buffer the gather reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.world > 1) {  // one after the other
-    st = launch_gather(p, latent, cond_row, tile_lat, s, who);
-    if (st != TDP_OK) return st;
-    const hipError_t e = blend_dispatch(p, tile_out, blend_cond_row, blend_cond_k, out, s);
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: blend launch failed: %s", who, hipGetErrorString(e));
-    return TDP_OK;
-  }
   const ExtractArgs a = extract_args(p, latent, nullptr, tile_lat, nullptr, nullptr, nullptr,
                                      const_cast<int32_t*>(cond_row), nullptr, nullptr);
   const DeviceShape ds = device_shape();
@@ -2295,7 +2314,7 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     if (overlap(r.ptr, r.bytes, out, out_bytes))
       return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.world > 1) {  // one after the other
+  if (p.world > 1 && p.Nc > 0) {  // rank plans with conditioning tokens: one after the other
     st = launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                         static_cast<char*>(workspace), s, who);
     if (st != TDP_OK) return st;
