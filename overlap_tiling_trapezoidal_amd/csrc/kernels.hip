@@ -1348,19 +1348,37 @@ __device__ void blend_cond_direct(const PlanDev& p, const u32x4* __restrict__ ti
   }
 }
 
-// Rank plans: a wave unit (rows [w0, w0 + rwv) of a line) outside the held
-// tiles' box is zero in the partial buffer; written without loads.
-template <int IN, int OUT>
-__device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_t dst0, int w0) {
-  constexpr int E = InVec<IN>::E;
-  const int lane = threadIdx.x & 63;
-  const int r = (int)fastdiv((uint32_t)lane, p.by_lpr), q = lane - r * p.lpr;
-  if (r >= p.rwv || w0 + r >= p.W) return;
-  float z[E];
+// Rank plans: zero-fill workgroup `zl` (a (b, f, h) line of the partial
+// buffer) writes zeros on the line's rows that no box unit writes: rows
+// outside the box's width chunks, or the whole line when it lies outside
+// the box on frames or height.  Plain contiguous stores, 16 bytes where the
+// output row allows (its bytes are always a multiple of 8).
+template <int OUT>
+__device__ void blend_zero_line(const PlanDev& p, void* __restrict__ out, int zl) {
+  const int b = (int)fastdiv((uint32_t)zl, p.by_FH);
+  const int fh = zl - b * (p.F * p.H);
+  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
+  const bool in_box = p.box_nc > 0 && f >= p.box_f0 && f < p.box_f0 + p.box_nf && h >= p.box_h0 &&
+                      h < p.box_h0 + p.box_nh;
+  const int w_lo = in_box ? p.box_c0 * p.blend_rows : p.W;       // [0, w_lo) and [w_hi, W) are zero
+  const int w_hi = in_box ? min(p.W, (p.box_c0 + p.box_nc) * p.blend_rows) : p.W;
+  const int64_t row_bytes = (int64_t)p.C * (OUT == TDP_BF16 ? 2 : 4);
+  char* line = static_cast<char*>(out) + ((int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W) * row_bytes;
+  const int seg[2][2] = {{0, w_lo}, {w_hi, p.W}};
 #pragma unroll
-  for (int e = 0; e < E; ++e) z[e] = 0.0f;
-  LaneIO<IN, OUT>::store(out, dst0 + w0 + r, q, p.vin, z);
-  if (p.lpr + q < p.vin) LaneIO<IN, OUT>::store(out, dst0 + w0 + r, p.lpr + q, p.vin, z);
+  for (int k = 0; k < 2; ++k) {
+    if (seg[k][1] <= seg[k][0]) continue;
+    char* base = line + seg[k][0] * row_bytes;
+    const int64_t bytes = (int64_t)(seg[k][1] - seg[k][0]) * row_bytes;
+    if (row_bytes % 16 == 0) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int64_t i = threadIdx.x; i < bytes / 16; i += kBlock) st_nt(reinterpret_cast<u32x4*>(base) + i, z);
+    } else {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 z = {0u, 0u};
+      for (int64_t i = threadIdx.x; i < bytes / 8; i += kBlock) st_nt(reinterpret_cast<u32x2*>(base) + i, z);
+    }
+  }
 }
 
 // F2: the frame axis is tiled, so a line can have four frame x height
@@ -1368,23 +1386,36 @@ __device__ void blend_zero_rows(const PlanDev& p, void* __restrict__ out, int64_
 // registers).
 // Generated-row workgroup `gid` of a blend: each wave takes one unit (rows
 // [w0, w0 + rwv) of one line), the waves of a workgroup consecutive units.
-// A rank plan writes zeros on units outside its tiles' bounding box.
+// A rank plan's units tile its held tiles' bounding box (as the extract's),
+// and the workgroups after them zero-fill the rest of each line.
 template <int IN, int OUT, bool R, bool F2>
 __device__ void blend_gen(const PlanDev& p, const u32x4* __restrict__ tile_out, void* __restrict__ out, int gid) {
-  const int unit = __builtin_amdgcn_readfirstlane(gid * kWaves + (int)(threadIdx.x >> 6));
-  if (unit >= p.gen_units) return;
+  int line, w0, b, f, h;
   const int rows = p.blend_rows;
-  const int line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
-  const int w0 = (unit - line * p.blend_chunks) * rows;
-  const int b = (int)fastdiv((uint32_t)line, p.by_FH);
-  const int fh = line - b * (p.F * p.H);
-  const int f = (int)fastdiv((uint32_t)fh, p.by_H), h = fh - f * p.H;
   if constexpr (R) {
-    if (f < p.box_f0 || f >= p.box_f0 + p.box_nf || h < p.box_h0 || h >= p.box_h0 + p.box_nh ||
-        w0 >= p.box_w0 + p.box_nw || w0 + rows <= p.box_w0) {
-      blend_zero_rows<IN, OUT>(p, out, (int64_t)b * p.rows + ((int64_t)f * p.H + h) * p.W, w0);
+    const int n_box = (p.gen_units + kWaves - 1) / kWaves;
+    if (gid >= n_box) {
+      blend_zero_line<OUT>(p, out, gid - n_box);
       return;
     }
+    const int unit = __builtin_amdgcn_readfirstlane(gid * kWaves + (int)(threadIdx.x >> 6));
+    if (unit >= p.gen_units) return;
+    line = (int)fastdiv((uint32_t)unit, p.by_box_c);
+    w0 = (p.box_c0 + unit - line * p.box_nc) * rows;
+    b = (int)fastdiv((uint32_t)line, p.by_box_fh);
+    const int fh = line - b * (p.box_nf * p.box_nh);
+    const int fb = (int)fastdiv((uint32_t)fh, p.by_box_h);
+    f = p.box_f0 + fb;
+    h = p.box_h0 + fh - fb * p.box_nh;
+  } else {
+    const int unit = __builtin_amdgcn_readfirstlane(gid * kWaves + (int)(threadIdx.x >> 6));
+    if (unit >= p.gen_units) return;
+    line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
+    w0 = (unit - line * p.blend_chunks) * rows;
+    b = (int)fastdiv((uint32_t)line, p.by_FH);
+    const int fh = line - b * (p.F * p.H);
+    f = (int)fastdiv((uint32_t)fh, p.by_H);
+    h = fh - f * p.H;
   }
   LineCombos lc;
   lc.init(p, f, h);
@@ -1564,6 +1595,9 @@ constexpr int kPipelineWgsPerCu = 4;      // pipeline step (extract and blend in
 
 // The blend's conditioning workgroups, and the LDS of its cached path:
 // rowtab, cap, k, n, list (ints), then 8-aligned int64 bases.
+// Workgroups of a blend's generated rows: its units, and for a rank plan
+// one zero-fill workgroup per line after them.
+int blend_gen_blocks(const PlanDev& p) { return (p.gen_units + kWaves - 1) / kWaves + p.zero_lines; }
 int blend_cond_blocks(const PlanDev& p) { return p.Nc > 0 ? p.B * ((p.Nc + kCondTokens - 1) / kCondTokens) : 0; }
 size_t blend_cond_lds(const PlanDev& p) {
   return p.Nc > 0 && p.T <= kCondTiles
@@ -1574,7 +1608,7 @@ size_t blend_cond_lds(const PlanDev& p) {
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
                         void* out, hipStream_t s) {
-  const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
+  const int n_gen = blend_gen_blocks(p);
   const int n_cond = blend_cond_blocks(p);
   const size_t lds = capped_lds(device_shape(), blend_cond_lds(p), kBlendWgsPerCu);
   const dim3 grid(n_gen + n_cond), block(kBlock);
@@ -1601,7 +1635,7 @@ hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const 
   const int n_cg = gather_cond_blocks(p);
   const int n_ext = n_cg + (p.lat_units + kWaves - 1) / kWaves;
   const int n_bcond = blend_cond_blocks(p);
-  const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
+  const int n_bgen = blend_gen_blocks(p);
   const size_t lds = capped_lds(ds, blend_cond_lds(p), kPipelineWgsPerCu);
   const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
@@ -1625,7 +1659,7 @@ template <int IN, int OUT>
 hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, const void* tile_out, void* out,
                            const DeviceShape& ds, hipStream_t s) {
   const int n_ext = a.n_pos + n_lat;
-  const int n_gen = (p.gen_units + kWaves - 1) / kWaves;
+  const int n_gen = blend_gen_blocks(p);
   const size_t lds = capped_lds(ds, 0, kPipelineWgsPerCu);
   const dim3 grid((unsigned)(n_ext + n_gen)), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
@@ -1652,7 +1686,7 @@ hipError_t launch_pipeline_cond(const PlanDev& p, const ExtractArgs& a, const vo
                                 const DeviceShape& ds, hipStream_t s) {
   const int n_ext = a.n_sel + a.n_pos;
   const int n_bcond = blend_cond_blocks(p);
-  const int n_bgen = (p.gen_units + kWaves - 1) / kWaves;
+  const int n_bgen = blend_gen_blocks(p);
   const size_t sel_lds = (size_t)p.B * 3 * sizeof(float2), bl_lds = blend_cond_lds(p);
   const size_t lds = capped_lds(ds, sel_lds > bl_lds ? sel_lds : bl_lds, kPipelineWgsPerCu);
   const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);

@@ -248,6 +248,10 @@ static int create_plan(const tdp_config* cfg, int32_t world, int32_t rank, tdp_p
     dev.ext_rows = (int32_t)((max_gen + parts - 1) / parts);
   }
   dev.lat_units = world == 1 ? dev.B * dev.F * dev.H * dev.lat_chunks : dev.B * dev.box_nf * dev.box_nh * dev.box_nc;
+  // a rank's blend computes its box units (the extract's) and zero-fills the
+  // rest of every line of its full-size partial buffer, one workgroup a line
+  if (world > 1) dev.gen_units = dev.lat_units;
+  dev.zero_lines = world > 1 ? dev.B * dev.F * dev.H : 0;
   dev.by_box_h = make_fastdiv((uint32_t)(dev.box_nh > 0 ? dev.box_nh : 1));
   dev.by_box_fh = make_fastdiv((uint32_t)(dev.box_nf * dev.box_nh > 0 ? dev.box_nf * dev.box_nh : 1));
   dev.by_box_c = make_fastdiv((uint32_t)(dev.box_nc > 0 ? dev.box_nc : 1));

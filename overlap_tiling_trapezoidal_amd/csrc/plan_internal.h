@@ -142,7 +142,8 @@ struct PlanDev {
   int32_t lpr, rwv;
   int32_t lat_rows, lat_chunks;      // extract: rows per wave unit (rwv), units per line
   int32_t blend_rows, blend_chunks;  // blend: rows per wave unit (rwv), units per line
-  int32_t lat_units, gen_units;      // wave units of extract (whole latent or rank box) and of blend
+  int32_t lat_units, gen_units;      // wave units of extract and of blend (whole latent, or a rank's box)
+  int32_t zero_lines;                // rank plans: B * F * H lines whose rows outside the box the blend zeroes
   FastDiv by_vin, by_lpr, by_H, by_FH, by_lat_chunks, by_blend_chunks;
   // Round-robin share (TDP docs, "What it is": tile t runs on rank t mod
   // world).  world == 1 is the whole plan.  A rank plan holds the tiles with
