@@ -8,7 +8,8 @@ of the first positions call; small cases are also held to the oracle.
 Covers whole plans with and without conditioning tokens (few chunks per
 tile, look-back chunks, fp32 rows, more than 256 tiles, wide rows, 16 384
 tokens), a tiled frame axis, ragged and narrow rows, rank plans, mixed
-dtypes, the refusal of shared buffers and a replayed graph of steps.
+dtypes, the refusal of shared buffers and a replayed graph of steps; then
+every edge case and the 24 seeded random plans of the extract parity tests.
 """
 import numpy as np
 import pytest
@@ -18,6 +19,9 @@ import oracle as O
 import overlap_tiling_trapezoidal_amd as tdp
 from harness import check_blend, check_extract, note, oracle_tile_floats, poisoned_buffers, to_device_latent
 from synth import WORKLOADS, Workload, make_inputs
+from test_gpu_parity import EDGE as PARITY_EDGE
+from test_gpu_parity import _custom_case as custom_case
+from test_gpu_parity import _random_axis as random_axis
 
 pytestmark = pytest.mark.gpu
 
@@ -235,3 +239,63 @@ def test_latent_step_graph_replays(cuda):
         for r in range(R):
             assert np.array_equal(_bits(tiles[r]), ref_tiles[r]), f"replay {rep}: tile set {r}"
             assert np.array_equal(_bits(outs[r]), ref_outs[r]), f"replay {rep}: output {r}"
+
+
+def _halves_equal_extract(plan, inp, cuda, label):
+    """tdp_extract_positions + tdp_extract_latent against tdp_extract on the
+    same inputs, every output bit for bit; returns the split buffers."""
+    lat, pos = _dev(inp, cuda)
+    ref = poisoned_buffers(plan, cuda)
+    note(f"split {label}: tdp_extract")
+    tdp.tdp_extract(plan, lat, pos, **ref)
+    got = poisoned_buffers(plan, cuda)
+    note(f"split {label}: tdp_extract_positions + tdp_extract_latent")
+    _halves(plan, lat, pos, got)
+    torch.cuda.synchronize()
+    for k in OUT_KEYS:
+        assert np.array_equal(_bits(got[k]), _bits(ref[k])), f"{label}: {k} differs from tdp_extract"
+    return lat, got
+
+
+@pytest.mark.parametrize("case", list(PARITY_EDGE))
+def test_split_on_edge_cases(case, cuda):
+    wl, inp = custom_case(**PARITY_EDGE[case])
+    _halves_equal_extract(_plan(wl, out_dtype="f32"), inp, cuda, case)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_split_random_configs(seed, cuda):
+    """The seeded random plans of the extract parity tests (tilings, batch,
+    channels, dtypes, conditioning tokens, positions, normalization): the
+    two halves equal tdp_extract, and the latent step equals the gather and
+    the blend as two calls."""
+    rng = np.random.default_rng(1000 + seed)
+    axes = [random_axis(rng, m) for m in (6, 14, 40)]
+    shape = tuple(d for d, _ in axes)
+    tiling = tuple(t for _, t in axes)
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    channels = int(rng.choice([4, 8, 12, 36]) if dtype == "f32" else rng.choice([8, 16, 24, 48, 128]))
+    batch = int(rng.integers(1, 4))
+    num_cond = int(rng.choice([0, 0, 5, 40, 300]))
+    wl, inp = custom_case(shape, tiling, batch=batch, channels=channels, dtype=dtype, num_cond=num_cond,
+                          seed=seed, random_pos=bool(rng.random() < 0.5))
+    normalize = bool(rng.random() < 0.7)
+    out_dtype = "bf16" if rng.random() < 0.5 else "f32"
+    label = f"seed {seed}: {shape} {tiling} B{batch} C{channels} {dtype} Nc{num_cond} normalize={normalize}"
+    cfg = tdp.make_config(wl.batch, wl.channels, wl.shape, wl.tiling, wl.num_cond, in_dtype=wl.dtype,
+                          out_dtype=out_dtype, normalize=normalize)
+    plan = tdp.tdp_plan_create(cfg)
+    lat, tables = _halves_equal_extract(plan, inp, cuda, label)
+    # latent step: gather this latent, blend the first gather's tiles
+    ref_lat = poisoned_buffers(plan, cuda)["tile_lat"]
+    ref_out = tdp.allocate_output(plan, cuda)
+    tdp.tdp_extract_latent(plan, lat, tables["cond_row"], ref_lat)
+    tdp.tdp_blend(plan, tables["tile_lat"], tables["cond_row"], tables["cond_k"], ref_out)
+    got_lat = poisoned_buffers(plan, cuda)["tile_lat"]
+    got_out = tdp.allocate_output(plan, cuda)
+    note(f"split {label}: tdp_pipeline_latent_step")
+    tdp.tdp_pipeline_latent_step(plan, lat, tables["cond_row"], got_lat, tile_out=tables["tile_lat"],
+                                 blend_cond_row=tables["cond_row"], blend_cond_k=tables["cond_k"], out=got_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(got_lat), _bits(ref_lat)), f"{label}: gather half differs"
+    assert np.array_equal(_bits(got_out), _bits(ref_out)), f"{label}: blend half differs"
