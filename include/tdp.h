@@ -320,7 +320,9 @@ int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
  * the result never depends on the order in which workgroups start and no
  * wait is unbounded.  The default is 256 reads; 0 counts every unpublished
  * chunk at once.  Results are the same for every value.  Process-wide;
- * applies to tdp_extract and tdp_extract_noalloc calls enqueued afterwards.
+ * applies to every call that runs the selection (tdp_extract,
+ * tdp_extract_noalloc, tdp_extract_positions, tdp_pipeline_step) enqueued
+ * afterwards.
  * TDP_EINVAL for polls < 0. */
 int tdp_set_lookback_polls(int32_t polls);
 
