@@ -182,7 +182,8 @@ def stream_bytes(wl, S, e_in, e_out):
 def pixel_rate(torch, tdp, dev, stream, sets=2, reps=8):
     """Blend of decoded pixel tiles for a 4K frame sequence: 8 RGB frames of
     2176 x 3840 bf16 from the 16-tile 4K latent tiling at 32 pixels per cell.
-    Algorithmic bytes: every tile read once plus the output written once."""
+    Algorithmic bytes: every tile read once plus the output written once.
+    The best of three graph-timed passes (the first in a process runs slower)."""
     cfg = tdp.make_pixel_config(1, 3, 8, (68, 120), (32, 32), ((4, 8), (4, 16)), in_dtype="bf16")
     plan = tdp.tdp_pixel_plan_create(cfg)
     tile_elems, out_elems, T = tdp.tdp_pixel_plan_sizes(plan)
@@ -195,7 +196,7 @@ def pixel_rate(torch, tdp, dev, stream, sets=2, reps=8):
         x, out = bufs[i % sets]
         tdp.tdp_pixel_blend(plan, x, out, stream)
 
-    ms = graph_time_ms(torch, stream, run, reps)
+    ms = min(graph_time_ms(torch, stream, run, reps) for _ in range(3))
     nbytes = 2 * (tile_elems + out_elems)
     return {"workload": "8 frames RGB 2176x3840 bf16, 16 tiles (4x4), overlap 256/512 px", "tiles": T,
             "ms": round(ms, 4), "bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}

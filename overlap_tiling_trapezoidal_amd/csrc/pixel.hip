@@ -16,7 +16,10 @@
 // reads per output element).  A workgroup owns a strip of 64 * E output
 // columns (E = elements per 16-byte vector) and kPixRows output rows; each
 // lane computes its columns' width covers and weights once and reuses them
-// for every row, each wave takes consecutive rows.
+// for every row, each wave takes consecutive rows, and a row's loads (up to
+// two height and two width covers) are all issued before it is summed.
+// Issuing the loads of all of a wave's rows first raises the registers to
+// 117 and was slower (4 workgroups per CU); this form keeps 69.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,27 +67,34 @@ __global__ __launch_bounds__(kBlock) void pixel_blend_kernel(const PixelDev p, c
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    // ascending tile index: (i0, j0), (i0, j1), (i1, j0), (i1, j1)
-    for (int hi = 0; hi < ch.n; ++hi) {
+    // ascending tile index: (i0, j0), (i0, j1), (i1, j0), (i1, j1); both
+    // height covers' loads are issued before either is summed
+    u32x4 v[2][2];
+    float wy[2];
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      if (hi >= ch.n) break;  // wave-uniform
       const int i = hi ? ch.t1 : ch.t0;
       const int ph = p.s[0] * (hi ? ch.s1 : ch.s0);
       const int ly = y - p.s[0] * (hi ? ch.a1 : ch.a0);
-      const float wy = ramp(p.ax[0].n, p.o[0], i, ly, ph);
+      wy[hi] = ramp(p.ax[0].n, p.o[0], i, ly, ph);
       const int64_t row0 = (int64_t)bcf * ph + ly;
-      // unconditional loads; a missing second width cover re-reads the first
       const int j1 = two_w ? cw.t1 : cw.t0;
       const int64_t e0 = pixel_tile_offset(p, i, cw.t0) + row0 * pw0 + lx0;
       const int64_t e1 = pixel_tile_offset(p, i, j1) + row0 * (two_w ? pw1 : pw0) + (two_w ? lx1 : lx0);
-      const u32x4 v0 = ld_nt(tiles + e0 / E);
-      u32x4 v1 = v0;
-      if (wave_two) v1 = ld_nt(tiles + e1 / E);
+      v[hi][0] = ld_nt(tiles + e0 / E);
+      v[hi][1] = wave_two ? ld_nt(tiles + e1 / E) : v[hi][0];
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      if (hi >= ch.n) break;
       float a0[E], a1[E];
-      InVec<IN>::unpack(v0, a0);
-      InVec<IN>::unpack(v1, a1);
+      InVec<IN>::unpack(v[hi][0], a0);
+      InVec<IN>::unpack(v[hi][1], a1);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        acc[e] = fmaf(wy * w0[e], a0[e], acc[e]);
-        acc[e] = two_w ? fmaf(wy * w1[e], a1[e], acc[e]) : acc[e];
+        acc[e] = fmaf(wy[hi] * w0[e], a0[e], acc[e]);
+        acc[e] = two_w ? fmaf(wy[hi] * w1[e], a1[e], acc[e]) : acc[e];
       }
     }
     if (col_ok) store_out<OUT, E>(out, (int64_t)r * p.Wp + x, acc);
