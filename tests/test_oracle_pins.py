@@ -328,6 +328,27 @@ def test_selection_hand_built():
     assert np.allclose(out[:, N + 1], 1.0)
 
 
+@pytest.mark.parametrize("name", ["tiny", "conditioned"])
+def test_tables_depend_on_positions_only(name):
+    """Reading g17: the shift (TDP docs, "Position normalization") and the
+    keep rule (TDP docs, "Shared negative (reference) positions") read the
+    positions only.  Two latents on the same positions give the same index
+    maps, counts, kept lists, shifted positions and k, and the second
+    latent's tile rows are its rows taken through the first's index map."""
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    other = make_inputs(wl, seed=wl.seed + 7)["latent"]
+    assert not np.array_equal(other, inp["latent"])
+    a = O.extract(inp["latent"], inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    b = O.extract(other, inp["pos"], wl.shape, wl.tiling, wl.num_cond)
+    assert np.array_equal(a["k"], b["k"]) and np.array_equal(a["keep"], b["keep"])
+    for ta, tb in zip(a["tiles"], b["tiles"]):
+        for key in ("rows", "kept", "offset", "extent", "pos"):
+            assert np.array_equal(np.asarray(ta[key]), np.asarray(tb[key])), key
+        assert ta["n_gen"] == tb["n_gen"]
+        assert np.array_equal(tb["latent"], other[:, ta["rows"], :])
+
+
 def test_reference_tokens_kept_by_every_tile():
     wl = WORKLOADS["conditioned"]
     inp = make_inputs(wl)
