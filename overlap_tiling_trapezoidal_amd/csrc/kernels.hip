@@ -756,12 +756,12 @@ __device__ void extract_positions_copy(const PlanDev& p, const ExtractArgs& a, i
 // the line's frame x height combos (wave-uniform), with no tables and no
 // barrier; the loads are issued before any of that is computed.  A rank
 // plan reads only the rows that one of its tiles covers.
-template <bool R>
+template <bool R, int W = kWaves>
 __device__ void extract_latent(const PlanDev& p, const ExtractArgs& a, int blk) {
   const int V = p.vin, LPR = p.lpr;
   const int rows = p.lat_rows;
   // this wave's unit: the waves of a workgroup take consecutive units
-  const int unit = __builtin_amdgcn_readfirstlane(blk * kWaves + (int)(threadIdx.x >> 6));
+  const int unit = __builtin_amdgcn_readfirstlane(blk * W + (int)(threadIdx.x >> 6));
   if (unit >= p.lat_units) return;
   int b, f, h, w0;
   if constexpr (R) {  // units tile the held tiles' bounding box only
@@ -1388,7 +1388,7 @@ __device__ void blend_zero_line(const PlanDev& p, void* __restrict__ out, int zl
 // [w0, w0 + rwv) of one line), the waves of a workgroup consecutive units.
 // A rank plan's units tile its held tiles' bounding box (as the extract's),
 // and the workgroups after them zero-fill the rest of each line.
-template <int IN, int OUT, bool R, bool F2>
+template <int IN, int OUT, bool R, bool F2, int W = kWaves>
 __device__ void blend_gen(const PlanDev& p, const u32x4* __restrict__ tile_out, void* __restrict__ out, int gid) {
   int line, w0, b, f, h;
   const int rows = p.blend_rows;
@@ -1408,7 +1408,7 @@ __device__ void blend_gen(const PlanDev& p, const u32x4* __restrict__ tile_out, 
     f = p.box_f0 + fb;
     h = p.box_h0 + fh - fb * p.box_nh;
   } else {
-    const int unit = __builtin_amdgcn_readfirstlane(gid * kWaves + (int)(threadIdx.x >> 6));
+    const int unit = __builtin_amdgcn_readfirstlane(gid * W + (int)(threadIdx.x >> 6));
     if (unit >= p.gen_units) return;
     line = (int)fastdiv((uint32_t)unit, p.by_blend_chunks);
     w0 = (unit - line * p.blend_chunks) * rows;
@@ -1449,6 +1449,31 @@ __global__ __launch_bounds__(kBlock) void blend_kernel(const PlanDev p, const u3
                                                        const int32_t* __restrict__ cond_k,
                                                        void* __restrict__ out, int n_gen_blocks) {
   blend_body<IN, OUT, R, F2>(p, tile_out, cond_row, cond_k, out, blockIdx.x, (int)gridDim.x - n_gen_blocks);
+}
+
+// Whole plans without conditioning tokens: the blend in one-wave
+// workgroups, one unit each.  The per-CU cap holds a workgroup's share of
+// the compute unit until its last wave ends; with one wave, a unit that
+// finishes frees its share at once instead of waiting for the slowest of
+// four (4K-class latent: 18.4 -> 17.8 us).
+template <int IN, int OUT, bool F2>
+__global__ __launch_bounds__(64) void blend_wave_kernel(const PlanDev p, const u32x4* __restrict__ tile_out,
+                                                        void* __restrict__ out) {
+  blend_gen<IN, OUT, false, F2, 1>(p, tile_out, out, blockIdx.x);
+}
+
+// The latent step of such a plan in one-wave workgroups: generated latent
+// rows, then the blend's units.
+template <int IN, int OUT, bool F2>
+__global__ __launch_bounds__(64) void pipeline_latent_wave_kernel(const PlanDev p, const ExtractArgs a,
+                                                                  const u32x4* __restrict__ tile_out,
+                                                                  void* __restrict__ out, int n_ext) {
+  const int bid = blockIdx.x;
+  if (bid < n_ext) {
+    extract_latent<false, 1>(p, a, bid);
+    return;
+  }
+  blend_gen<IN, OUT, false, F2, 1>(p, tile_out, out, bid - n_ext);
 }
 
 // One step of a pipelined loop for whole plans with conditioning tokens,
@@ -1590,6 +1615,16 @@ size_t capped_lds(const DeviceShape& d, size_t need, int k) {
 constexpr int kExtractWgsPerCu = 3;       // latent-dominated extracts
 constexpr int kExtractWgsPerCuChain = 2;  // extracts set by their position / selection chains
 constexpr int kBlendWgsPerCu = 4;
+constexpr int kWaveWgsPerCu = 16;         // one-wave workgroups (blend and latent step without conditioning tokens)
+
+// Whole plans without conditioning tokens and more than 16 blend units per
+// compute unit run the blend (and the latent step) in one-wave workgroups.
+// Smaller plans keep four-wave workgroups: there the extra launches of
+// single waves cost more than they free (full-res blend 5.2 -> 5.6 us,
+// LTX-like 3.4 -> 3.8 us with one wave; 4K-class 18.4 -> 17.8 us).
+bool wave_workgroups(const PlanDev& p, const DeviceShape& ds) {
+  return p.Nc == 0 && p.world == 1 && p.gen_units > 16 * (ds.cus > 0 ? ds.cus : 256);
+}
 constexpr int kSelectWgsPerCuLarge = 6;   // selection launches of plans with many chunks per tile
 constexpr int kPipelineWgsPerCu = 4;      // pipeline step (extract and blend in one launch)
 
@@ -1608,12 +1643,23 @@ size_t blend_cond_lds(const PlanDev& p) {
 template <int IN, int OUT>
 hipError_t launch_blend(const PlanDev& p, const void* tile_out, const int32_t* cond_row, const int32_t* cond_k,
                         void* out, hipStream_t s) {
-  const int n_gen = blend_gen_blocks(p);
-  const int n_cond = blend_cond_blocks(p);
-  const size_t lds = capped_lds(device_shape(), blend_cond_lds(p), kBlendWgsPerCu);
-  const dim3 grid(n_gen + n_cond), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   const bool f2 = p.ax[0].n > 1;
+  const DeviceShape ds = device_shape();
+  if (wave_workgroups(p, ds)) {
+    const dim3 wgrid((unsigned)p.gen_units), wblock(64);
+    const size_t wlds = capped_lds(ds, 0, kWaveWgsPerCu);
+    if (wgrid.x == 0) return hipSuccess;
+    if (f2)
+      hipLaunchKernelGGL((blend_wave_kernel<IN, OUT, true>), wgrid, wblock, wlds, s, p, y, out);
+    else
+      hipLaunchKernelGGL((blend_wave_kernel<IN, OUT, false>), wgrid, wblock, wlds, s, p, y, out);
+    return hipGetLastError();
+  }
+  const int n_gen = blend_gen_blocks(p);
+  const int n_cond = blend_cond_blocks(p);
+  const size_t lds = capped_lds(ds, blend_cond_lds(p), kBlendWgsPerCu);
+  const dim3 grid(n_gen + n_cond), block(kBlock);
   if (p.world > 1 && f2)
     hipLaunchKernelGGL((blend_kernel<IN, OUT, true, true>), grid, block, lds, s, p, y, cond_row, cond_k, out, n_gen);
   else if (p.world > 1)
@@ -1632,6 +1678,19 @@ template <int IN, int OUT>
 hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
                                   const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
                                   const DeviceShape& ds, hipStream_t s) {
+  if (wave_workgroups(p, ds)) {
+    const dim3 wgrid((unsigned)(p.lat_units + p.gen_units)), wblock(64);
+    const size_t wlds = capped_lds(ds, 0, kWaveWgsPerCu);
+    if (wgrid.x == 0) return hipSuccess;
+    const u32x4* wy = reinterpret_cast<const u32x4*>(tile_out);
+    if (p.ax[0].n > 1)
+      hipLaunchKernelGGL((pipeline_latent_wave_kernel<IN, OUT, true>), wgrid, wblock, wlds, s, p, a, wy, out,
+                         p.lat_units);
+    else
+      hipLaunchKernelGGL((pipeline_latent_wave_kernel<IN, OUT, false>), wgrid, wblock, wlds, s, p, a, wy, out,
+                         p.lat_units);
+    return hipGetLastError();
+  }
   const int n_cg = gather_cond_blocks(p);
   const int n_ext = n_cg + (p.lat_units + kWaves - 1) / kWaves;
   const int n_bcond = blend_cond_blocks(p);
