@@ -1390,6 +1390,7 @@ __device__ void blend_zero_line(const PlanDev& p, void* __restrict__ out, int zl
 // and the workgroups after them zero-fill the rest of each line.
 template <int IN, int OUT, bool R, bool F2, int W = kWaves>
 __device__ void blend_gen(const PlanDev& p, const u32x4* __restrict__ tile_out, void* __restrict__ out, int gid) {
+  static_assert(!R || W == kWaves, "a rank plan's zero-fill strides by a whole workgroup of kBlock threads");
   int line, w0, b, f, h;
   const int rows = p.blend_rows;
   if constexpr (R) {
