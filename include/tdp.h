@@ -304,7 +304,12 @@ int tdp_plan_quality(const tdp_plan* plan, int32_t world, tdp_quality* out, int6
  * aligned, pos/tile_pos 8-byte aligned; buffers must not overlap and hold
  * the sizes tdp_plan_sizes() reports (the library cannot check sizes).
  * Returns TDP_EGUARD for unguarded plans, TDP_EINVAL for null or misaligned
- * pointers, TDP_EHIP on launch failure. */
+ * pointers, TDP_EHIP on launch failure.  TDP_ESHAPE, nothing enqueued, when
+ * the plan is too large for HIP's launches: every device call of a plan
+ * (extract, blend and their halves and steps) first adds up the work-items
+ * of all the workgroups its launches use and refuses a sum above 2^32 - 1,
+ * the 32-bit work-item count of one launch (only plans of hundreds of
+ * millions of rows reach it; split the batch or the latent). */
 int tdp_extract(const tdp_plan* plan, const void* latent, const float* pos,
                 void* tile_lat, float* tile_pos, int32_t* tile_index,
                 int32_t* tile_count, int32_t* cond_row, int32_t* cond_k,
@@ -454,7 +459,10 @@ int tdp_pipeline_latent_step(const tdp_plan* plan, const void* latent, const int
  * Any other order gives wrong sums.  Calls that share acc must not overlap.
  * tile_out/acc 16-byte aligned device pointers; cond_row and cond_k as for
  * tdp_blend.
- * Returns TDP_EINVAL for a bad tile index or pointer, or a rank plan. */
+ * Returns TDP_EINVAL for a bad tile index or pointer, or a rank plan;
+ * TDP_ESHAPE (nothing enqueued) when this launch or tdp_blend_finish's
+ * would exceed 2^32 - 1 work-items, so a streaming sequence is refused at
+ * its first call; TDP_EHIP when the launch fails. */
 int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const int32_t* cond_row,
                    const int32_t* cond_k, float* acc, void* stream);
 
@@ -463,7 +471,9 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
  * plan's out_dtype into out
  * (round to nearest even for bf16; a copy for fp32, nothing when out == acc).
  * After tdp_blend_tile for every tile in order, out equals tdp_blend's
- * output bit for bit.  16-byte aligned device pointers. */
+ * output bit for bit.  16-byte aligned device pointers.  TDP_EINVAL for a
+ * null or misaligned pointer or a rank plan, TDP_ESHAPE as tdp_blend_tile,
+ * TDP_EHIP when the launch fails. */
 int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* stream);
 
 /* ---- spatial blend of decoded pixel tiles --------------------------------- */
@@ -518,7 +528,10 @@ int tdp_pixel_plan_sizes(const tdp_pixel_plan* plan, int64_t* tile_elems, int64_
  * (wH * wW) * tile, fp32 accumulation from zero, rounded once to out_dtype
  * (the trapezoids of the latent blend in pixel units, so the weights still
  * sum to one: DistVAE docs, "Choosing a tile window"; mold #673, "Scope").
- * Device pointers, 16-byte aligned; tiles holds every tile as packed above. */
+ * Device pointers, 16-byte aligned; tiles holds every tile as packed above.
+ * TDP_EINVAL for a null or misaligned pointer, TDP_ESHAPE (nothing
+ * enqueued) when the launch would exceed 2^32 - 1 work-items, TDP_EHIP when
+ * it fails. */
 int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, void* stream);
 
 /* ---- errors ------------------------------------------------------------ */

@@ -2076,6 +2076,34 @@ int launch_gather(const PlanDev& p, const void* latent, const int32_t* cond_row,
   return TDP_OK;
 }
 
+// A HIP launch counts its work-items in 32 bits.  Every device call of a
+// plan refuses, before its first launch, a plan whose workgroups of every
+// kind its launches use (extent and selection parts, position parts, latent
+// units, gather chunks, blend conditioning and generated units, zero-fill
+// lines) would add up to more work-items than that: the sum bounds each
+// single launch, so no launch of the call can fail on its size after an
+// earlier one has run.
+constexpr int64_t kMaxLaunchItems = 0xffffffffLL;
+int check_launch_size(const PlanDev& p, const char* who) {
+  const int64_t parts = p.pos_parts > p.pos_parts_one ? p.pos_parts : p.pos_parts_one;
+  const int64_t sel = p.Nc > 0 ? (int64_t)p.T * (p.ext_parts + p.n_chunks) : 0;
+  const int64_t wgs = sel + (int64_t)p.T_local * p.B * 3 * parts + (p.lat_units + kWaves - 1) / kWaves +
+                      gather_cond_blocks(p) + blend_cond_blocks(p) + blend_gen_blocks(p);
+  if (wgs * kBlock > kMaxLaunchItems)
+    return fail(TDP_ESHAPE,
+                "%s: the plan's launches need up to %lld work-items, more than the %lld of one HIP launch "
+                "(split the batch or the latent over several plans)",
+                who, (long long)(wgs * kBlock), (long long)kMaxLaunchItems);
+  return TDP_OK;
+}
+
+// Work-items of the streaming blend's finish pass: one thread per four
+// accumulator floats, in whole workgroups.
+int64_t finish_items(const PlanDev& p) {
+  const int64_t n4 = (int64_t)p.B * p.rows * p.C / 4;
+  return (n4 + kBlock - 1) / kBlock * kBlock;
+}
+
 // Checks tdp_extract and tdp_extract_noalloc share (the workspace aside).
 int check_extract(const tdp_plan* plan, const void* latent, const float* pos, const void* tile_lat,
                   const float* tile_pos, const int32_t* tile_index, const int32_t* tile_count, const int32_t* cond_row,
@@ -2093,7 +2121,7 @@ int check_extract(const tdp_plan* plan, const void* latent, const float* pos, co
   if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
       !aligned(cond_row, 4) || !aligned(cond_k, 4))
     return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
-  return TDP_OK;
+  return check_launch_size(p, who);
 }
 
 // Checks of tdp_extract_positions' arguments (the workspace aside).
@@ -2109,7 +2137,7 @@ int check_positions(const tdp_plan* plan, const float* pos, const float* tile_po
   if (!aligned(pos, 8) || !aligned(tile_pos, 8) || !aligned(tile_index, 4) || !aligned(tile_count, 4) ||
       !aligned(cond_row, 4) || !aligned(cond_k, 4))
     return fail(TDP_EINVAL, "%s: pos/tile_pos need 8-byte and int buffers 4-byte alignment", who);
-  return TDP_OK;
+  return check_launch_size(p, who);
 }
 
 // Checks of tdp_extract_latent's arguments (shared with
@@ -2124,7 +2152,7 @@ int check_gather(const tdp_plan* plan, const void* latent, const int32_t* cond_r
   if (!aligned(latent, 16) || !aligned(tile_lat, 16))
     return fail(TDP_EINVAL, "%s: latent and tile_lat must be 16-byte aligned", who);
   if (!aligned(cond_row, 4)) return fail(TDP_EINVAL, "%s: misaligned cond_row", who);
-  return TDP_OK;
+  return check_launch_size(p, who);
 }
 
 // Checks of tdp_blend's arguments (shared with tdp_pipeline_step).
@@ -2139,7 +2167,7 @@ int check_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_
   if (!aligned(tile_out, 16) || !aligned(out, 16))
     return fail(TDP_EINVAL, "%s: tile_out and out must be 16-byte aligned", who);
   if (!aligned(cond_row, 4) || !aligned(cond_k, 4)) return fail(TDP_EINVAL, "%s: misaligned cond_row or cond_k", who);
-  return TDP_OK;
+  return check_launch_size(p, who);
 }
 
 // The blend of a checked plan, by dtypes.
@@ -2265,6 +2293,10 @@ int tdp_blend_tile(const tdp_plan* plan, int32_t t, const void* tile_out, const 
   const int gen_per_b = (slot.gen + rows_per_block - 1) / rows_per_block;
   const int n_gen = p.B * gen_per_b;
   const int n_cond = p.Nc > 0 ? p.B * ((p.Nc + kCondRowsPerBlock - 1) / kCondRowsPerBlock) : 0;
+  if (((int64_t)n_gen + n_cond) * kBlock > kMaxLaunchItems || finish_items(p) > kMaxLaunchItems)
+    return fail(TDP_ESHAPE, "tdp_blend_tile: the tile's launch or the finish pass needs more work-items than the "
+                            "%lld of one HIP launch (split the batch or the latent over several plans)",
+                (long long)kMaxLaunchItems);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   if (p.in_dtype == TDP_BF16)
@@ -2287,6 +2319,9 @@ int tdp_blend_finish(const tdp_plan* plan, const float* acc, void* out, void* st
   if (p.out_dtype == TDP_F32 && static_cast<const void*>(acc) == out) return TDP_OK;
   const int64_t n4 = (int64_t)p.B * p.rows * p.C / 4;  // C * 4 bytes is a multiple of 16
   const int64_t blocks = (n4 + kBlock - 1) / kBlock;
+  if (finish_items(p) > kMaxLaunchItems)
+    return fail(TDP_ESHAPE, "tdp_blend_finish: %lld work-items, more than the %lld of one HIP launch",
+                (long long)finish_items(p), (long long)kMaxLaunchItems);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const f32x4* a4 = reinterpret_cast<const f32x4*>(acc);
   if (p.out_dtype == TDP_BF16)

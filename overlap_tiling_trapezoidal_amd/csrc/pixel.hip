@@ -125,6 +125,13 @@ int tdp_pixel_blend(const tdp_pixel_plan* plan, const void* tiles, void* out, vo
   if (!tiles || !out) return fail(TDP_EINVAL, "tdp_pixel_blend: null device pointer");
   if (!aligned16(tiles) || !aligned16(out)) return fail(TDP_EINVAL, "tdp_pixel_blend: tiles and out must be 16-byte aligned");
   const PixelDev& p = plan->dev;
+  // one launch: (groups of kPixRows rows) x (strips of 64 vectors) workgroups,
+  // whose work-items a HIP launch counts in 32 bits
+  const int64_t E = p.in_dtype == TDP_BF16 ? 8 : 4;
+  const int64_t items = ((int64_t)p.rows + kPixRows - 1) / kPixRows * ((p.Wp + 64 * E - 1) / (64 * E)) * kBlock;
+  if (items > 0xffffffffLL)
+    return fail(TDP_ESHAPE, "tdp_pixel_blend: %lld work-items, more than one HIP launch holds (split the batch "
+                            "or the frames over several plans)", (long long)items);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (p.in_dtype == TDP_BF16)

@@ -65,3 +65,17 @@ def test_pixel_blend_rejects_bad_pointers():
     assert lib.tdp_pixel_blend(plan.handle, null, null, null) == tdp.TDP_EINVAL
     assert lib.tdp_pixel_blend(plan.handle, ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1000), null) == tdp.TDP_EINVAL
     assert lib.tdp_pixel_blend(None, null, null, null) == tdp.TDP_EINVAL
+
+
+@pytest.mark.device_abi
+def test_pixel_blend_refuses_launches_past_32_bit_work_items():
+    """1024 channels of 64 frames of 64 x 128 cells at 32 pixels per cell:
+    2^27 output rows of 4096 pixels, 2^23 row groups times 8 column strips
+    of 256 threads = 2^34 work-items, more than one launch counts; refused
+    on the host before any launch."""
+    import ctypes
+    plan = tdp.tdp_pixel_plan_create(tdp.make_pixel_config(1, 1024, 64, (64, 128), (32, 32), ((2, 8), (2, 16))))
+    lib = tdp.load_library()
+    al = ctypes.c_void_p(1 << 40)
+    assert lib.tdp_pixel_blend(plan.handle, al, ctypes.c_void_p(1 << 41), ctypes.c_void_p(None)) == tdp.TDP_ESHAPE
+    assert "work-items" in tdp.tdp_last_error()

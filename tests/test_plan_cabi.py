@@ -218,6 +218,47 @@ def test_device_calls_reject_bad_plans_before_launch(lib):
 
 
 @pytest.mark.device_abi
+@pytest.mark.parametrize("case", ["rank_zero_fill", "whole_latent_units", "whole_conditioned"])
+def test_device_calls_refuse_launches_past_32_bit_work_items(case, lib):
+    """Plans inside every planner limit whose launches would need more
+    work-items than one HIP launch counts (2^32 - 1) are refused with
+    TDP_ESHAPE by every device call, on the host and before the first
+    launch, so no call leaves partial output.
+    - rank_zero_fill: a rank's blend zero-fills 8192 * 8192 lines, one
+      256-thread workgroup each (2^34 work-items);
+    - whole_latent_units: 2^27 one-row lines of 1024-byte rows, one wave
+      each (2^33);
+    - whole_conditioned: the same with conditioning tokens (the selection
+      and conditioning blend parts add to the sum)."""
+    null = ctypes.c_void_p(None)
+    if case == "rank_zero_fill":
+        cfg = tdp.make_config(1, 8, (8192, 8192, 1), ((1, 0), (2, 8), (1, 0)))
+        plan = tdp.tdp_plan_create_rank(cfg, 2, 0)
+    else:
+        nc = 4096 if case == "whole_conditioned" else 0
+        plan = tdp.tdp_plan_create(tdp.make_config(1, 512, (8192, 16384, 1), ((1, 0), (2, 8), (1, 0)), nc))
+    b = [ctypes.c_void_p((i + 1) << 40) for i in range(16)]   # distinct, aligned, never dereferenced
+    calls = {
+        "tdp_extract": lambda: lib.tdp_extract(plan.handle, *b[:9], null),
+        "tdp_extract_noalloc": lambda: lib.tdp_extract_noalloc(plan.handle, *b[:8], null),
+        "tdp_extract_positions": lambda: lib.tdp_extract_positions(plan.handle, *b[:7], null),
+        "tdp_extract_latent": lambda: lib.tdp_extract_latent(plan.handle, *b[:3], null),
+        "tdp_blend": lambda: lib.tdp_blend(plan.handle, *b[:4], null),
+        "tdp_pipeline_step": lambda: lib.tdp_pipeline_step(plan.handle, *b[:13], null),
+        "tdp_pipeline_latent_step": lambda: lib.tdp_pipeline_latent_step(plan.handle, *b[:7], null),
+    }
+    for name, call in calls.items():
+        assert call() == tdp.TDP_ESHAPE, name
+        assert "work-items" in tdp.tdp_last_error(), (name, tdp.tdp_last_error())
+    if case != "rank_zero_fill":
+        # the streaming blend: its finish pass (one thread per four floats of
+        # a 2^27-row, 512-channel accumulator) is refused at the first tile
+        assert lib.tdp_blend_tile(plan.handle, 0, *b[:3], b[3], null) == tdp.TDP_ESHAPE
+        assert "work-items" in tdp.tdp_last_error()
+        assert lib.tdp_blend_finish(plan.handle, b[0], b[1], null) == tdp.TDP_ESHAPE
+
+
+@pytest.mark.device_abi
 def test_pipeline_step_refuses_before_launch(lib):
     """Bad and overlapping arguments are refused on the host (no GPU call)."""
     plan = plan_for(WORKLOADS["4k"])
