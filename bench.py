@@ -684,7 +684,9 @@ def main():
         scaling = selection_scaling(torch, tdp, dev)
 
     if latent_steps:  # the step is one launch: that kernel is the dominant one
-        dom = ("latent gather + blend, one launch", step_bytes, ms_per_step, "pipeline_latent_kernel")
+        dom = ("latent gather + blend, one launch", step_bytes, ms_per_step,
+               "pipeline_latent_kernel; in one-wave workgroups, pipeline_latent_wave_kernel, for plans without "
+               "conditioning tokens and more than 16 blend units per compute unit")
     elif fused:
         dom = ("extract + blend, one launch", step_bytes, ms_per_step, "pipeline_kernel")
     else:
