@@ -7,8 +7,9 @@ as two calls on the same inputs; the extract half is also held to the
 oracle, and the blend half to the oracle's tolerance.  Covers fused plans
 (bf16 and fp32 rows, bf16 and fp32 output, a tiled frame axis, ragged and
 narrow rows), plans with conditioning tokens (two launches, every dtype
-pairing), rank plans (the two calls one after the other), and a replayed
-graph of steps.
+pairing), rank plans (one launch without conditioning tokens, the two calls
+one after the other with them), seeded random plans of both kinds, and a
+replayed graph of steps.
 """
 import numpy as np
 import pytest
@@ -17,8 +18,8 @@ import torch
 import oracle as O
 import overlap_tiling_trapezoidal_amd as tdp
 from harness import (check_blend, check_extract, note, oracle_tile_floats, plan_for, poisoned_buffers,
-                     to_device_latent)
-from synth import WORKLOADS, Workload, make_inputs
+                     slot_buffer_from_tiles, to_device_latent)
+from synth import WORKLOADS, Workload, make_inputs, random_tile_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +175,73 @@ def test_step_graph_replays(cuda):
         for (w_out, w_lat), s in zip(want, sets):
             assert np.array_equal(_bits(s["out"]), w_out), f"replay {rep}: blend output differs"
             assert np.array_equal(_bits(s["bufs"]["tile_lat"]), w_lat), f"replay {rep}: tile rows differ"
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_step_random_configs(seed, cuda):
+    """Seeded random plans, whole and rank (up to 3 ranks): random tilings on
+    all three axes, batch, channels, row and output dtypes, conditioning
+    tokens, grid or random positions, normalization on or off.  The step
+    extracts latent A and blends random tile outputs laid out on latent B's
+    selection; it must equal the two calls bit for bit, its extract the
+    oracle's, and its blend (a rank's partial for rank plans) the oracle's
+    within tolerance."""
+    from test_gpu_parity import _custom_case, _random_axis
+    rng = np.random.default_rng(5000 + seed)
+    axes = [_random_axis(rng, m) for m in (6, 14, 40)]
+    shape = tuple(d for d, _ in axes)
+    tiling = tuple(t for _, t in axes)
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    channels = int(rng.choice([4, 8, 12, 36]) if dtype == "f32" else rng.choice([8, 16, 24, 48, 128]))
+    batch = int(rng.integers(1, 4))
+    num_cond = int(rng.choice([0, 0, 5, 40, 300]))
+    random_pos = bool(rng.random() < 0.5)
+    normalize = bool(rng.random() < 0.7)
+    out_dtype = "bf16" if rng.random() < 0.5 else "f32"
+    world = int(rng.choice([1, 1, 2, 3]))
+    rank = int(rng.integers(0, world))
+    wl, inp_a = _custom_case(shape, tiling, batch=batch, channels=channels, dtype=dtype, num_cond=num_cond,
+                             seed=seed, random_pos=random_pos)
+    _, inp_b = _custom_case(shape, tiling, batch=batch, channels=channels, dtype=dtype, num_cond=num_cond,
+                            seed=seed + 500, random_pos=random_pos)
+    cfg = tdp.make_config(batch, channels, shape, tiling, num_cond, in_dtype=dtype, out_dtype=out_dtype,
+                          normalize=normalize)
+    plan = tdp.tdp_plan_create(cfg) if world == 1 else tdp.tdp_plan_create_rank(cfg, world, rank)
+    label = (f"seed {seed}: {shape} {tiling} B{batch} C{channels} {dtype}->{out_dtype} Nc{num_cond} "
+             f"world {world} rank {rank} normalize={normalize}")
+    # B: its selection from the library's extract of its positions; its tile
+    # outputs random, in the slot layout, unused slot rows garbage
+    lat_b, pos_b = to_device_latent(inp_b["latent"], cuda), torch.from_numpy(inp_b["pos"]).to(cuda)
+    buf_b = poisoned_buffers(plan, cuda)
+    note(f"pipeline random {label}: extract of B")
+    tdp.tdp_extract(plan, lat_b, pos_b, **buf_b)
+    ex_b = O.extract(inp_b["latent"], inp_b["pos"], shape, tiling, num_cond, normalize=normalize)
+    tiles = [random_tile_outputs(rng, batch, len(et["rows"]), channels, dtype) for et in ex_b["tiles"]]
+    y_np = slot_buffer_from_tiles(plan, tiles, plan.cfg.in_dtype, rng)
+    tile_out = to_device_latent(y_np, cuda) if y_np.dtype == np.uint16 else torch.from_numpy(y_np).to(cuda)
+    lat_a, pos_a = to_device_latent(inp_a["latent"], cuda), torch.from_numpy(inp_a["pos"]).to(cuda)
+
+    def poisoned_out():
+        o = tdp.allocate_output(plan, cuda)
+        o.view(torch.int16 if o.dtype == torch.bfloat16 else torch.int32).fill_(-7)
+        return o
+    ref_a, ref_out = poisoned_buffers(plan, cuda), poisoned_out()
+    note(f"pipeline random {label}: two calls")
+    tdp.tdp_extract(plan, lat_a, pos_a, **ref_a)
+    tdp.tdp_blend(plan, tile_out, buf_b["cond_row"], buf_b["cond_k"], ref_out)
+    got_a, got_out = poisoned_buffers(plan, cuda), poisoned_out()
+    note(f"pipeline random {label}: tdp_pipeline_step")
+    tdp.tdp_pipeline_step(plan, lat_a, pos_a, **got_a, tile_out=tile_out, blend_cond_row=buf_b["cond_row"],
+                          blend_cond_k=buf_b["cond_k"], out=got_out)
+    torch.cuda.synchronize()
+    for k in OUT_KEYS:
+        assert np.array_equal(_bits(got_a[k]), _bits(ref_a[k])), f"{label}: extract output {k} differs"
+    assert np.array_equal(_bits(got_out), _bits(ref_out)), f"{label}: blend output differs"
+    check_extract(plan, got_a, O.extract(inp_a["latent"], inp_a["pos"], shape, tiling, num_cond,
+                                         normalize=normalize), num_cond)
+    ys = [O.bf16_bits_to_f32(y) if y.dtype == np.uint16 else y for y in tiles]
+    if world == 1:
+        ref, mag = O.blend(ys, ex_b, shape, tiling, num_cond)
+    else:
+        ref, mag = O.rank_partial(ys, ex_b, shape, tiling, num_cond, world, rank)
+    check_blend(got_out, ref, mag, plan.cfg.out_dtype)
