@@ -460,10 +460,11 @@ def cpu_baseline(wl, inp, extract_bytes, blend_bytes, budget_s=12.0):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="4k")
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (one: every tile runs locally)")
+    ap.add_argument("--steps", type=int, default=500, help="timed pipelined steps K")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the timed ones")
+    ap.add_argument("--workload", default="4k", choices=("tiny", "ltx", "fullres", "4k", "conditioned"),
+                    help="the workload the headline line times")
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (cache-cold launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
