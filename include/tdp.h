@@ -380,7 +380,8 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * launch, the extract's workgroups first, so the blend's fill the GPU while
  * the extract's drain (a rank's share too: its tiles' extract and its
  * partial buffer); whole plans with conditioning tokens take two launches
- * (the extents with the latent rows, then the selection with the blend);
+ * (the extents with the blend, then the selection with the positions and
+ * the latent rows);
  * rank plans with conditioning tokens enqueue the two calls one after the
  * other.
  * The two halves may run at the same time, so the blend's buffers must be

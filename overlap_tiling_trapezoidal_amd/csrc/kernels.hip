@@ -851,11 +851,10 @@ __device__ inline void xcd_group(int bid, int items, int parts, int& item, int& 
 // all of them.  It also clears what the selection launch counts into: part
 // 0 the tile's look-back flags, and the workgroups together cond_k.  Every
 // tile is reduced, in rank plans too, since k counts the tiles of all
-// ranks.  In the pipeline step the workgroups past the first a.n_ext copy
-// the generated latent rows, which depend on neither the extents nor the
-// selection, so that the bulk of the extract's bytes shares no launch with
-// the blend; a plain extract keeps them in the selection launch, where
-// they stream while the selection's chains wait.
+// ranks.  The generated latent rows go to the selection launch, where they
+// stream while the selection's chains wait; in the pipeline step the
+// extent parts share their launch with the blend instead
+// (extent_blend_kernel).
 template <int NP>
 __device__ void extent_body(const PlanDev& p, const ExtractArgs& a, int bid) {
   __shared__ float2 red[kWaves][NP];
@@ -919,12 +918,9 @@ __device__ void extent_body(const PlanDev& p, const ExtractArgs& a, int bid) {
     __syncthreads();  // red is reused by the next pass
   }
 }
-template <int NP, bool LAT>
+template <int NP>
 __global__ __launch_bounds__(kBlock) void extent_kernel(const PlanDev p, const ExtractArgs a) {
-  if (!LAT || (int)blockIdx.x < a.n_ext)
-    extent_body<NP>(p, a, blockIdx.x);
-  else if constexpr (LAT)
-    extract_latent<false>(p, a, (int)blockIdx.x - a.n_ext);  // whole plans only
+  extent_body<NP>(p, a, blockIdx.x);
 }
 
 // Every position workgroup of a launch: (tile, batch, axis, part) of `bid`.
@@ -969,14 +965,15 @@ __global__ __launch_bounds__(kBlock) void extract_kernel(const PlanDev p, const 
 //                              tile-major: selection and kept rows;
 //   [n_sel, n_sel + n_pos)     positions per (tile, batch, axis, part),
 //                              shifted by the tile's extent parts;
-//   [.., + latent blocks)      generated latent rows per (line, chunk),
-//                              when LAT (else the extent launch copies them).
+//   [.., + latent blocks)      generated latent rows per (line, chunk)
+//                              (none in tdp_extract_positions' launch).
 // Only wave 0 of a selection workgroup waits on others (the flags of the
 // tile's earlier chunks), never without bound.  Rank plans: selection over
 // every tile (k counts the tiles of all ranks), the rest for the held
 // tiles.
-template <bool R, bool SMALL, bool LAT>
-__device__ void select_body(const PlanDev& p, const ExtractArgs& a, int bid) {
+template <bool R, bool SMALL>
+__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
+  const int bid = blockIdx.x;
   if (bid < a.n_sel) {
     extern __shared__ float2 ext_s[];  // dynamic: at least B * 3 (the launch asks for it)
     __shared__ CondShared cs;
@@ -984,17 +981,13 @@ __device__ void select_body(const PlanDev& p, const ExtractArgs& a, int bid) {
     extract_cond_chunk<R, SMALL>(p, a, cs, ext_s, t, bid - t * p.n_chunks);
     return;
   }
-  if (!LAT || bid - a.n_sel < a.n_pos) {
+  if (bid - a.n_sel < a.n_pos) {
     const PosWork w = pos_work<R>(p, a, bid - a.n_sel);
     extract_positions_copy<R>(p, a, w.t, w.b, w.d, w.part,
                               p.normalize ? tile_min_start(p, a, w.t, w.b * 3 + w.d) : 0.0f);
     return;
   }
-  if constexpr (LAT) extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
-}
-template <bool R, bool SMALL>
-__global__ __launch_bounds__(kBlock) void select_kernel(const PlanDev p, const ExtractArgs a) {
-  select_body<R, SMALL, true>(p, a, blockIdx.x);
+  extract_latent<R>(p, a, bid - a.n_sel - a.n_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -1477,23 +1470,25 @@ __global__ __launch_bounds__(64) void pipeline_latent_wave_kernel(const PlanDev 
   blend_gen<IN, OUT, false, F2, 1>(p, tile_out, out, bid - n_ext);
 }
 
-// One step of a pipelined loop for whole plans with conditioning tokens,
-// after the extent launch (which copies the generated latent rows): the
-// selection launch's workgroups (selection, positions), then the blend's
-// (its conditioning rows, then its generated rows), as one launch, so the
-// blend's bulk copy runs under the selection's dependent chains.
-template <int IN, int OUT, bool F2, bool SMALL>
-__global__ __launch_bounds__(kBlock) void pipeline_cond_kernel(const PlanDev p, const ExtractArgs a,
-                                                               const u32x4* __restrict__ tile_out,
-                                                               const int32_t* __restrict__ blend_cond_row,
-                                                               const int32_t* __restrict__ blend_cond_k,
-                                                               void* __restrict__ out, int n_ext, int n_bcond) {
+// The first launch of a pipeline step for whole plans with conditioning
+// tokens: the extent parts of one latent's tiles (short chains of loads),
+// then the blend of other tile outputs (its conditioning rows, then its
+// generated rows), so the blend's bulk copy runs under the extent chains.
+// The selection launch that follows (select_kernel) holds the selection,
+// the positions and the generated latent rows, which stream while the
+// selection's chains wait.  The two halves share no buffer.
+template <int NP, int IN, int OUT, bool F2>
+__global__ __launch_bounds__(kBlock) void extent_blend_kernel(const PlanDev p, const ExtractArgs a,
+                                                              const u32x4* __restrict__ tile_out,
+                                                              const int32_t* __restrict__ blend_cond_row,
+                                                              const int32_t* __restrict__ blend_cond_k,
+                                                              void* __restrict__ out, int n_bcond) {
   const int bid = blockIdx.x;
-  if (bid < n_ext) {
-    select_body<false, SMALL, false>(p, a, bid);
+  if (bid < a.n_ext) {
+    extent_body<NP>(p, a, bid);
     return;
   }
-  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - n_ext, n_bcond);
+  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - a.n_ext, n_bcond);
 }
 
 // One step of a pipelined loop whose positions do not change (R: a rank's share):
@@ -1738,32 +1733,33 @@ hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, co
 // Plans whose tiles have few chunks: no waits, every chunk tested in one pass.
 bool select_small(const PlanDev& p) { return p.n_chunks <= kDirectChunks + 1; }
 
-// The pipeline step of a whole plan with conditioning tokens, after
-// launch_extent: its selection launch and the blend as one launch.
+// The first launch of the pipeline step of a whole plan with conditioning
+// tokens: the extent parts and the blend (extent_blend_kernel).  Sets the
+// position fields of `a` for the selection launch that follows.
 template <int IN, int OUT>
-hipError_t launch_pipeline_cond(const PlanDev& p, const ExtractArgs& a, const void* tile_out,
-                                const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
-                                const DeviceShape& ds, hipStream_t s) {
-  const int n_ext = a.n_sel + a.n_pos;
+hipError_t launch_extent_blend(const PlanDev& p, ExtractArgs& a, const void* tile_out,
+                               const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
+                               const DeviceShape& ds, hipStream_t s) {
   const int n_bcond = blend_cond_blocks(p);
-  const int n_bgen = blend_gen_blocks(p);
-  const size_t sel_lds = (size_t)p.B * 3 * sizeof(float2), bl_lds = blend_cond_lds(p);
-  const size_t lds = capped_lds(ds, sel_lds > bl_lds ? sel_lds : bl_lds, kPipelineWgsPerCu);
-  const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
+  const dim3 grid((unsigned)(a.n_ext + n_bcond + blend_gen_blocks(p))), block(kBlock);
+  const size_t lds = capped_lds(ds, blend_cond_lds(p), kBlendWgsPerCu);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
-  const bool f2 = p.ax[0].n > 1, small = select_small(p);
-  if (f2 && small)
-    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, true, true>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_ext, n_bcond);
+  const bool f2 = p.ax[0].n > 1;
+  if (p.B == 1 && f2)
+    hipLaunchKernelGGL((extent_blend_kernel<3, IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_bcond);
+  else if (p.B == 1)
+    hipLaunchKernelGGL((extent_blend_kernel<3, IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_bcond);
   else if (f2)
-    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, true, false>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_ext, n_bcond);
-  else if (small)
-    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, false, true>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_ext, n_bcond);
+    hipLaunchKernelGGL((extent_blend_kernel<6, IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_bcond);
   else
-    hipLaunchKernelGGL((pipeline_cond_kernel<IN, OUT, false, false>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_ext, n_bcond);
+    hipLaunchKernelGGL((extent_blend_kernel<6, IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
+                       blend_cond_k, out, n_bcond);
+  a.pos_one_pass = 0;
+  a.pos_parts = p.pos_parts;
+  a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
   return hipGetLastError();
 }
 
@@ -1935,29 +1931,44 @@ ExtractArgs extract_args(const PlanDev& p, const void* latent, const float* pos,
   return a;
 }
 
-// The extent launch (Nc > 0), with the generated latent rows when
-// `with_latent` (whole plans); then the selection launch's workgroups are
-// a.n_sel selection, a.n_pos positions (copies: the shift is known) and,
-// unless the extent launch took them, the latent rows.
-int launch_extent(const PlanDev& p, ExtractArgs& a, const DeviceShape& ds, bool with_latent, hipStream_t s,
-                  const char* who) {
-  if (with_latent && p.world > 1) return fail(TDP_EINVAL, "%s: latent rows in the extent launch of a rank plan", who);
-  const int n_lat = with_latent ? (p.lat_units + kWaves - 1) / kWaves : 0;
-  const dim3 egrid((unsigned)(a.n_ext + n_lat)), block(kBlock);
-  const size_t lds = with_latent ? capped_lds(ds, 0, kExtractWgsPerCu) : 0;
-  if (p.B == 1 && with_latent)
-    hipLaunchKernelGGL((extent_kernel<3, true>), egrid, block, lds, s, p, a);
-  else if (p.B == 1)
-    hipLaunchKernelGGL((extent_kernel<3, false>), egrid, block, lds, s, p, a);
-  else if (with_latent)
-    hipLaunchKernelGGL((extent_kernel<6, true>), egrid, block, lds, s, p, a);
+// The extent launch (Nc > 0): the extent parts of every tile.  Sets the
+// position fields of `a` for the selection launch, whose workgroups are
+// a.n_sel selection, a.n_pos positions (copies: the shift is known) and the
+// latent rows.
+int launch_extent(const PlanDev& p, ExtractArgs& a, hipStream_t s, const char* who) {
+  const dim3 egrid((unsigned)a.n_ext), block(kBlock);
+  if (p.B == 1)
+    hipLaunchKernelGGL((extent_kernel<3>), egrid, block, 0, s, p, a);
   else
-    hipLaunchKernelGGL((extent_kernel<6, false>), egrid, block, lds, s, p, a);
+    hipLaunchKernelGGL((extent_kernel<6>), egrid, block, 0, s, p, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TDP_EHIP, "%s: extent launch failed: %s", who, hipGetErrorString(e));
   a.pos_one_pass = 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
+  return TDP_OK;
+}
+
+// The selection launch (Nc > 0, after the extents): a.n_sel selection,
+// a.n_pos position and n_lat latent workgroups.  The dynamic LDS holds the
+// tile's extent and caps the workgroups per CU: plans with few chunks per
+// tile at kExtractWgsPerCu, plans with more (look-back chains, little work
+// per workgroup) at kSelectWgsPerCuLarge.
+int launch_select(const PlanDev& p, const ExtractArgs& a, int n_lat, const DeviceShape& ds, hipStream_t s,
+                  const char* who) {
+  const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat)), block(kBlock);
+  const bool small = select_small(p);
+  const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2), small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
+  if (p.world > 1 && small)
+    hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, lds, s, p, a);
+  else if (p.world > 1)
+    hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, lds, s, p, a);
+  else if (small)
+    hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
+  else
+    hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
   return TDP_OK;
 }
 
@@ -1982,26 +1993,8 @@ int launch_extract(const PlanDev& p, const void* latent, const float* pos, void*
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
   const dim3 block(kBlock);
   if (p.Nc > 0) {
-    const int st = launch_extent(p, a, ds, false, s, who);
-    if (st != TDP_OK) return st;
-    const dim3 sgrid((unsigned)(a.n_sel + a.n_pos + n_lat));
-    // the tile's extent, and a cap on workgroups per CU: plans with few
-    // chunks per tile at kExtractWgsPerCu, plans with more (look-back
-    // chains, little work per workgroup) at kSelectWgsPerCuLarge
-    const bool small = select_small(p);
-    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2),
-                                  small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
-    if (p.world > 1 && small)
-      hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, lds, s, p, a);
-    else if (p.world > 1)
-      hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, lds, s, p, a);
-    else if (small)
-      hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
-    else
-      hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
-    return TDP_OK;
+    const int st = launch_extent(p, a, s, who);
+    return st != TDP_OK ? st : launch_select(p, a, n_lat, ds, s, who);
   }
   const bool latent_bound = plain_setup(p, a, ds, n_lat);
   const dim3 grid(a.n_pos + n_lat);
@@ -2026,24 +2019,9 @@ int launch_positions(const PlanDev& p, const float* pos, float* tile_pos, int32_
   a.copy_latent = 0;
   const DeviceShape ds = device_shape();
   const dim3 block(kBlock);
-  if (p.Nc > 0) {
-    const int st = launch_extent(p, a, ds, false, s, who);
-    if (st != TDP_OK) return st;
-    const dim3 sgrid((unsigned)(a.n_sel + a.n_pos));
-    const bool small = select_small(p);
-    const size_t lds = capped_lds(ds, (size_t)p.B * 3 * sizeof(float2),
-                                  small ? kExtractWgsPerCu : kSelectWgsPerCuLarge);
-    if (p.world > 1 && small)
-      hipLaunchKernelGGL((select_kernel<true, true>), sgrid, block, lds, s, p, a);
-    else if (p.world > 1)
-      hipLaunchKernelGGL((select_kernel<true, false>), sgrid, block, lds, s, p, a);
-    else if (small)
-      hipLaunchKernelGGL((select_kernel<false, true>), sgrid, block, lds, s, p, a);
-    else
-      hipLaunchKernelGGL((select_kernel<false, false>), sgrid, block, lds, s, p, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: selection launch failed: %s", who, hipGetErrorString(e));
-    return TDP_OK;
+  if (p.Nc > 0) {  // no latent workgroups
+    const int st = launch_extent(p, a, s, who);
+    return st != TDP_OK ? st : launch_select(p, a, 0, ds, s, who);
   }
   a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
   const dim3 grid((unsigned)a.n_pos);
@@ -2452,22 +2430,20 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     return TDP_OK;
   }
   const DeviceShape ds = device_shape();
-  if (p.Nc > 0) {  // the extent launch, then the selection launch and the blend as one
+  if (p.Nc > 0) {  // extents and the blend, then the selection launch with the latent rows
     ExtractArgs ca = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
                                   static_cast<char*>(workspace));
-    st = launch_extent(p, ca, ds, true, s, who);
-    if (st != TDP_OK) return st;
     hipError_t e;
     if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_BF16)
-      e = launch_pipeline_cond<TDP_BF16, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+      e = launch_extent_blend<TDP_BF16, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     else if (p.in_dtype == TDP_BF16 && p.out_dtype == TDP_F32)
-      e = launch_pipeline_cond<TDP_BF16, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+      e = launch_extent_blend<TDP_BF16, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     else if (p.in_dtype == TDP_F32 && p.out_dtype == TDP_F32)
-      e = launch_pipeline_cond<TDP_F32, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+      e = launch_extent_blend<TDP_F32, TDP_F32>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     else
-      e = launch_pipeline_cond<TDP_F32, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
+      e = launch_extent_blend<TDP_F32, TDP_BF16>(p, ca, tile_out, blend_cond_row, blend_cond_k, out, ds, s);
     if (e != hipSuccess) return fail(TDP_EHIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
-    return TDP_OK;
+    return launch_select(p, ca, (p.lat_units + kWaves - 1) / kWaves, ds, s, who);
   }
   ExtractArgs a = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k, nullptr);
   const int n_lat = (p.lat_units + kWaves - 1) / kWaves;
