@@ -116,7 +116,7 @@ constexpr int kPosOwnRows = 16;  // position rows per thread one extract positio
 // one chunk of kCondChunk tokens against one tile and finds the tile's kept
 // tokens before its chunk by look-back over the earlier chunks' flags.
 constexpr int kCondChunk = 64;                 // one token per lane of a wave
-constexpr int kExtPartBytes = 24 * 1024;       // position bytes one extent workgroup reads
+constexpr int kExtPartBytes = 48 * 1024;       // position bytes one extent workgroup reads
 constexpr int kMaxExtParts = 64;              // extent parts per tile at most
 
 // Everything a kernel needs about a plan; passed by value (kernel argument).

@@ -20,7 +20,7 @@ import overlap_tiling_trapezoidal_amd as tdp
 from harness import check_extract, note, plan_for, poisoned_buffers, to_device_latent
 from synth import WORKLOADS, Workload, make_inputs
 
-# workspace of 6912 bytes (16484 tokens), then 6656 (the conditioned
+# workspace of 6912 bytes (16484 tokens), then 4096 (the conditioned
 # workload), then none
 CALLS = [
     ("cond_16k", Workload("cond_16k", 2, 128, (2, 12, 20), ((1, 0), (2, 2), (3, 3)), num_cond=16484,
