@@ -1691,7 +1691,11 @@ hipError_t launch_pipeline_latent(const PlanDev& p, const ExtractArgs& a, const 
   const int n_ext = n_cg + (p.lat_units + kWaves - 1) / kWaves;
   const int n_bcond = blend_cond_blocks(p);
   const int n_bgen = blend_gen_blocks(p);
-  const size_t lds = capped_lds(ds, blend_cond_lds(p), kPipelineWgsPerCu);
+  // plans with many conditioning chunks move their rows faster at 6
+  // workgroups per CU (16 384 tokens on the conditioned shape: 48.8 -> 47.3
+  // us per step), plans with few at 4 (1 024 tokens: 18.6 against 18.8)
+  const int cap = p.n_chunks <= kDirectChunks + 1 ? kPipelineWgsPerCu : kSelectWgsPerCuLarge;
+  const size_t lds = capped_lds(ds, blend_cond_lds(p), cap);
   const dim3 grid((unsigned)(n_ext + n_bcond + n_bgen)), block(kBlock);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
   const bool f2 = p.ax[0].n > 1;
