@@ -723,7 +723,7 @@ def main():
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "step_call": ("tdp_pipeline_latent_step (one launch; tables from one tdp_extract_positions)"
                       if latent_steps else "tdp_pipeline_step (one launch)" if fused
-                      else "tdp_pipeline_step (extents, then selection with the blend)"),
+                      else "tdp_pipeline_step (extents with the blend, then selection, positions and latent rows)"),
         "two_calls": {"ms_per_step": round(two_ms, 5), "value": round(step_bytes / (two_ms * 1e-3) / 1e9, 2),
                       "note": ("the same K steps as tdp_extract_latent + tdp_blend" if latent_steps else
                                "the same K steps as tdp_extract + tdp_blend") + ", two calls each"},
