@@ -379,11 +379,9 @@ int tdp_blend(const tdp_plan* plan, const void* tile_out, const int32_t* cond_ro
  * results.  For whole plans without conditioning tokens both run as one
  * launch, the extract's workgroups first, so the blend's fill the GPU while
  * the extract's drain (a rank's share too: its tiles' extract and its
- * partial buffer); whole plans with conditioning tokens take two launches
- * (the extents with the blend, then the selection with the positions and
- * the latent rows);
- * rank plans with conditioning tokens enqueue the two calls one after the
- * other.
+ * partial buffer); plans with conditioning tokens take two launches (the
+ * extents with the blend, then the selection with the positions and the
+ * latent rows), a rank's share too.
  * The two halves may run at the same time, so the blend's buffers must be
  * none of the extract's: TDP_EINVAL, nothing enqueued, when tile_out,
  * blend_cond_row or blend_cond_k overlaps a buffer the extract writes, or

@@ -1470,14 +1470,15 @@ __global__ __launch_bounds__(64) void pipeline_latent_wave_kernel(const PlanDev 
   blend_gen<IN, OUT, false, F2, 1>(p, tile_out, out, bid - n_ext);
 }
 
-// The first launch of a pipeline step for whole plans with conditioning
-// tokens: the extent parts of one latent's tiles (short chains of loads),
-// then the blend of other tile outputs (its conditioning rows, then its
-// generated rows), so the blend's bulk copy runs under the extent chains.
+// The first launch of a pipeline step for plans with conditioning tokens:
+// the extent parts of one latent's tiles (short chains of loads; every
+// tile, since k counts the tiles of all ranks), then the blend of other
+// tile outputs (its conditioning rows, then its generated rows; R: a rank's
+// partial buffer), so the blend's bulk copy runs under the extent chains.
 // The selection launch that follows (select_kernel) holds the selection,
 // the positions and the generated latent rows, which stream while the
 // selection's chains wait.  The two halves share no buffer.
-template <int NP, int IN, int OUT, bool F2>
+template <int NP, int IN, int OUT, bool F2, bool R>
 __global__ __launch_bounds__(kBlock) void extent_blend_kernel(const PlanDev p, const ExtractArgs a,
                                                               const u32x4* __restrict__ tile_out,
                                                               const int32_t* __restrict__ blend_cond_row,
@@ -1488,7 +1489,7 @@ __global__ __launch_bounds__(kBlock) void extent_blend_kernel(const PlanDev p, c
     extent_body<NP>(p, a, bid);
     return;
   }
-  blend_body<IN, OUT, false, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - a.n_ext, n_bcond);
+  blend_body<IN, OUT, R, F2>(p, tile_out, blend_cond_row, blend_cond_k, out, bid - a.n_ext, n_bcond);
 }
 
 // One step of a pipelined loop whose positions do not change (R: a rank's share):
@@ -1737,9 +1738,9 @@ hipError_t launch_pipeline(const PlanDev& p, const ExtractArgs& a, int n_lat, co
 // Plans whose tiles have few chunks: no waits, every chunk tested in one pass.
 bool select_small(const PlanDev& p) { return p.n_chunks <= kDirectChunks + 1; }
 
-// The first launch of the pipeline step of a whole plan with conditioning
-// tokens: the extent parts and the blend (extent_blend_kernel).  Sets the
-// position fields of `a` for the selection launch that follows.
+// The first launch of the pipeline step of a plan with conditioning tokens:
+// the extent parts and the blend (extent_blend_kernel).  Sets the position
+// fields of `a` for the selection launch that follows.
 template <int IN, int OUT>
 hipError_t launch_extent_blend(const PlanDev& p, ExtractArgs& a, const void* tile_out,
                                const int32_t* blend_cond_row, const int32_t* blend_cond_k, void* out,
@@ -1748,19 +1749,21 @@ hipError_t launch_extent_blend(const PlanDev& p, ExtractArgs& a, const void* til
   const dim3 grid((unsigned)(a.n_ext + n_bcond + blend_gen_blocks(p))), block(kBlock);
   const size_t lds = capped_lds(ds, blend_cond_lds(p), kBlendWgsPerCu);
   const u32x4* y = reinterpret_cast<const u32x4*>(tile_out);
-  const bool f2 = p.ax[0].n > 1;
-  if (p.B == 1 && f2)
-    hipLaunchKernelGGL((extent_blend_kernel<3, IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_bcond);
-  else if (p.B == 1)
-    hipLaunchKernelGGL((extent_blend_kernel<3, IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_bcond);
-  else if (f2)
-    hipLaunchKernelGGL((extent_blend_kernel<6, IN, OUT, true>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_bcond);
-  else
-    hipLaunchKernelGGL((extent_blend_kernel<6, IN, OUT, false>), grid, block, lds, s, p, a, y, blend_cond_row,
-                       blend_cond_k, out, n_bcond);
+  const int combo = (p.B == 1 ? 0 : 4) + (p.ax[0].n > 1 ? 2 : 0) + (p.world > 1 ? 1 : 0);
+#define TDP_EB_LAUNCH(NP, F2, R)                                                                                \
+  hipLaunchKernelGGL((extent_blend_kernel<NP, IN, OUT, F2, R>), grid, block, lds, s, p, a, y, blend_cond_row, \
+                     blend_cond_k, out, n_bcond)
+  switch (combo) {
+    case 0: TDP_EB_LAUNCH(3, false, false); break;
+    case 1: TDP_EB_LAUNCH(3, false, true); break;
+    case 2: TDP_EB_LAUNCH(3, true, false); break;
+    case 3: TDP_EB_LAUNCH(3, true, true); break;
+    case 4: TDP_EB_LAUNCH(6, false, false); break;
+    case 5: TDP_EB_LAUNCH(6, false, true); break;
+    case 6: TDP_EB_LAUNCH(6, true, false); break;
+    default: TDP_EB_LAUNCH(6, true, true); break;
+  }
+#undef TDP_EB_LAUNCH
   a.pos_one_pass = 0;
   a.pos_parts = p.pos_parts;
   a.n_pos = p.T_local * p.B * 3 * a.pos_parts;
@@ -2425,14 +2428,6 @@ int tdp_pipeline_step(const tdp_plan* plan, const void* latent, const float* pos
     if (overlap(r.ptr, r.bytes, out, out_bytes))
       return fail(TDP_EINVAL, "%s: the blend writes a buffer the extract reads", who);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p.world > 1 && p.Nc > 0) {  // rank plans with conditioning tokens: one after the other
-    st = launch_extract(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,
-                        static_cast<char*>(workspace), s, who);
-    if (st != TDP_OK) return st;
-    const hipError_t e = blend_dispatch(p, tile_out, blend_cond_row, blend_cond_k, out, s);
-    if (e != hipSuccess) return fail(TDP_EHIP, "%s: blend launch failed: %s", who, hipGetErrorString(e));
-    return TDP_OK;
-  }
   const DeviceShape ds = device_shape();
   if (p.Nc > 0) {  // extents and the blend, then the selection launch with the latent rows
     ExtractArgs ca = extract_args(p, latent, pos, tile_lat, tile_pos, tile_index, tile_count, cond_row, cond_k,

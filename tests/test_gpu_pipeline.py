@@ -7,9 +7,8 @@ as two calls on the same inputs; the extract half is also held to the
 oracle, and the blend half to the oracle's tolerance.  Covers fused plans
 (bf16 and fp32 rows, bf16 and fp32 output, a tiled frame axis, ragged and
 narrow rows), plans with conditioning tokens (two launches, every dtype
-pairing), rank plans (one launch without conditioning tokens, the two calls
-one after the other with them), seeded random plans of both kinds, and a
-replayed graph of steps.
+pairing), rank plans (one launch without conditioning tokens, two with
+them), seeded random plans of both kinds, and a replayed graph of steps.
 """
 import numpy as np
 import pytest
